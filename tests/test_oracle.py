@@ -1,0 +1,320 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Every check below ties the oracle to something else: textbook softmax
+attention (tests/bruteforce.py), closed forms of hand-designed inputs,
+invariants of the method, or designed probe sequences under tests/golden/.
+Method passages: gist.science ART summary sections 2.1-2.4; puntofijo.es
+article on skipping V dequantisation.
+"""
+import glob
+import json
+import os
+
+import numpy as np
+import pytest
+
+import art_inputs as A
+from tests import bruteforce as BF
+from tests.helpers import contiguous_case, designed_case, run_oracle, to_paged
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_case(B=2, Hq=4, Hkv=2, d=16, n=100, seed=0, kv="f32", qd="f32", **params):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, d))
+    K = rng.standard_normal((B, Hkv, n, d))
+    V = rng.standard_normal((B, Hkv, n, d))
+    return contiguous_case(q, K, V, kv=kv, qd=qd, **params)
+
+
+def ntiles(n, T):
+    return -(-n // T)
+
+
+# ---------------------------------------------------------------- P1: full mode = softmax attention
+
+@pytest.mark.parametrize("n", [1, 5, 63, 64, 65, 300])
+@pytest.mark.parametrize("d", [4, 8, 64])
+@pytest.mark.parametrize("T", [1, 3, 16, 64])
+def test_full_mode_equals_bruteforce(n, d, T):
+    c = rand_case(B=1, Hq=2, Hkv=1, d=d, n=n, seed=n * 7 + d + T, tile=T, eps_scale=0.0, eps_dir=0.0)
+    r = run_oracle(c)
+    assert (r.tiles_used == ntiles(n, T)).all()
+    for h in range(2):
+        ref = BF.attention(c, 0, h, n)
+        assert np.allclose(r.out[0, h], ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+def test_full_mode_gqa_ragged_bruteforce(kv):
+    c = rand_case(B=3, Hq=6, Hkv=2, d=32, n=200, seed=3, kv=kv, qd=kv, tile=16,
+                  eps_scale=0.0, eps_dir=0.0)
+    c.ctx_lens[:] = [200, 17, 129]
+    r = run_oracle(c)
+    for b in range(3):
+        n = int(c.ctx_lens[b])
+        assert (r.tiles_used[b] == ntiles(n, 16)).all()
+        for h in range(6):
+            assert np.allclose(r.out[b, h], BF.attention(c, b, h, n), rtol=1e-12, atol=1e-13)
+
+
+def test_single_tile_is_plain_attention_and_zero_context():
+    c = rand_case(B=2, Hq=2, Hkv=1, d=16, n=40, seed=11, tile=64)
+    c.ctx_lens[:] = [40, 0]
+    r = run_oracle(c)
+    assert (r.tiles_used[0] == 1).all()  # one tile: never a comparison
+    assert np.allclose(r.out[0, 1], BF.attention(c, 0, 1, 40), rtol=1e-12, atol=1e-13)
+    assert (r.tiles_used[1] == 0).all() and (r.out[1] == 0).all()
+
+
+# ---------------------------------------------------------------- P2: prefix identity
+
+@pytest.mark.parametrize("seed", range(6))
+def test_stop_equals_attention_over_used_prefix(seed):
+    # loose thresholds so random data stops at various tiles
+    c = rand_case(B=2, Hq=4, Hkv=2, d=16, n=400, seed=100 + seed, tile=8,
+                  eps_scale=0.05, eps_dir=0.02, patience=1 + seed % 3)
+    c.ctx_lens[:] = [400, 397 - 13 * seed]
+    r = run_oracle(c)
+    stopped = 0
+    for b in range(2):
+        n = int(c.ctx_lens[b])
+        for h in range(4):
+            U = int(r.tiles_used[b, h])
+            stopped += U < ntiles(n, 8)
+            ref = BF.attention(c, b, h, min(U * 8, n))
+            assert np.allclose(r.out[b, h], ref, rtol=1e-12, atol=1e-13)
+    assert stopped > 0  # the case must exercise termination
+
+
+# ---------------------------------------------------------------- P3: convexity (weights via one-hot V)
+
+def test_full_mode_weights_are_softmax_and_convex():
+    n = d = 48
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, d)) * 2
+    K = rng.standard_normal((1, 1, n, d))
+    V = np.eye(n)[None, None]  # row j = e_j, so out = the weight vector
+    c = contiguous_case(q, K, V, tile=16, eps_scale=0.0, eps_dir=0.0)
+    w = run_oracle(c).out[0, 0]
+    assert (w >= 0).all() and abs(w.sum() - 1) < 1e-13
+    assert np.allclose(w, BF.attention_weights(c, 0, 0, n), rtol=1e-12, atol=1e-15)
+
+
+def test_outputs_lie_in_value_bounds():
+    c = A.config(2, small=True, seed=4)
+    r = run_oracle(c)
+    G = c.Hq // c.Hkv
+    for h in range(c.Hq):
+        U = int(r.tiles_used[0, h])
+        V = BF.logical_rows(c, "v", 0, h // G, min(U * c.tile, int(c.ctx_lens[0])))
+        assert (r.out[0, h] >= V.min(0) - 1e-12).all() and (r.out[0, h] <= V.max(0) + 1e-12).all()
+
+
+# ---------------------------------------------------------------- P4: bounds on tiles_used
+
+@pytest.mark.parametrize("patience", [1, 2, 4])
+def test_tiles_used_bounds(patience):
+    c = rand_case(B=3, Hq=4, Hkv=4, d=8, n=300, seed=patience, tile=8,
+                  eps_scale=0.2, eps_dir=0.1, patience=patience)
+    c.ctx_lens[:] = [300, 9, 1]
+    r = run_oracle(c)
+    for b in range(3):
+        nt = ntiles(int(c.ctx_lens[b]), 8)
+        assert (r.tiles_used[b] >= min(patience + 1, nt)).all()
+        assert (r.tiles_used[b] <= nt).all()
+
+
+# ---------------------------------------------------------------- P5: constant V closed form
+
+@pytest.mark.parametrize("patience", [1, 3])
+def test_constant_values(patience):
+    rng = np.random.default_rng(9)
+    d, n = 16, 256
+    c_vec = rng.uniform(0.5, 2.0, size=d)
+    q = rng.standard_normal((1, 2, d))
+    K = rng.standard_normal((1, 1, n, d))
+    V = np.broadcast_to(c_vec, (1, 1, n, d))
+    c = contiguous_case(q, K, V, tile=16, eps_scale=1e-9, eps_dir=1e-9, patience=patience)
+    r = run_oracle(c)
+    cv = c.v[0, 0, 0].astype(np.float64)
+    assert (r.tiles_used == patience + 1).all()
+    assert np.allclose(r.out[0], cv, rtol=1e-14, atol=0)
+    full = run_oracle(c, eps_scale=0.0, eps_dir=0.0)
+    assert (full.tiles_used == n // 16).all()  # 0 is never strictly below 0
+
+
+# ---------------------------------------------------------------- P6: designed probe sequences
+
+FIXTURES = sorted(glob.glob(os.path.join(GOLDEN, "*.json")))
+
+
+@pytest.mark.parametrize("path", FIXTURES, ids=[os.path.basename(p) for p in FIXTURES])
+def test_designed_sequences(path):
+    fx = json.load(open(path))
+    c = designed_case(fx)
+    rho = np.asarray(fx["rho"])
+    th = np.asarray(fx["theta"])
+    exp_scale = np.abs(np.diff(rho)) / rho[:-1]
+    exp_dir = 1 - np.cos(np.diff(th))
+    for run in fx["runs"]:
+        r = run_oracle(c, eps_scale=run["eps_scale"], eps_dir=run["eps_dir"],
+                       patience=run["patience"], trace=True)
+        U = int(r.tiles_used[0, 0])
+        assert U == run["tiles_used"], run["why"]
+        tr = r.trace[0, 0]
+        # every evaluated comparison matches the closed form of the design
+        for t in range(1, U):
+            assert abs(tr[t, 2] - exp_scale[t - 1]) < 2e-7, (t, tr[t, 2], exp_scale[t - 1])
+            assert abs(tr[t, 3] - exp_dir[t - 1]) < 2e-7, (t, tr[t, 3], exp_dir[t - 1])
+        assert np.isnan(tr[0, 2]) and np.isnan(tr[0, 3])  # no comparison at tile 0
+        if U < fx["n_tiles"]:
+            assert np.isnan(tr[U, 7])  # tiles after the stop are never visited
+
+
+def test_probe_ignores_dims_beyond_eight():
+    fx = json.load(open(os.path.join(GOLDEN, "and_rule.json")))
+    r1 = run_oracle(designed_case(fx, seed=0))
+    r2 = run_oracle(designed_case(fx, seed=1))  # different distractor in dims 8..15
+    assert (r1.tiles_used == r2.tiles_used).all()
+
+
+# ---------------------------------------------------------------- P7: paged layout
+
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+def test_paged_permutation_invariance(kv):
+    c = rand_case(B=2, Hq=4, Hkv=2, d=16, n=160, seed=21, kv=kv, qd=kv, tile=16,
+                  eps_scale=0.05, eps_dir=0.02)
+    c.ctx_lens[:] = [160, 77]
+    base = run_oracle(c)
+    for s in (1, 2):
+        p = to_paged(c, 16, seed=s, extra_blocks=5)
+        r = run_oracle(p)
+        assert np.array_equal(r.out, base.out) and np.array_equal(r.tiles_used, base.tiles_used)
+
+
+def test_bad_block_id_rejected():
+    c = to_paged(rand_case(B=1, Hq=1, Hkv=1, d=8, n=32, seed=1, tile=16), 16, seed=0)
+    c.block_table[0, 1] = c.k.shape[0]  # one past the last block
+    with pytest.raises(ValueError):
+        run_oracle(c)
+
+
+# ---------------------------------------------------------------- P8: GQA = replicated cache
+
+def test_gqa_equals_replicated_cache():
+    c = rand_case(B=2, Hq=8, Hkv=2, d=16, n=200, seed=31, tile=16, eps_scale=0.05, eps_dir=0.02)
+    rep = contiguous_case(c.q, np.repeat(c.k, 4, axis=1), np.repeat(c.v, 4, axis=1),
+                          c.ctx_lens, tile=16, eps_scale=0.05, eps_dir=0.02)
+    a, b = run_oracle(c), run_oracle(rep)
+    assert np.array_equal(a.out, b.out) and np.array_equal(a.tiles_used, b.tiles_used)
+
+
+# ---------------------------------------------------------------- P9: int8 = dequantised fp32
+
+def test_int8_equals_dequantised_fp32():
+    c = A.config(5, small=True, seed=2, batch=1, ctx=512)
+    deq = lambda codes, sc: (codes.astype(np.float32) * sc.view(np.float16).astype(np.float32)[..., None])
+    f = A.Case(name="deq", B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, q=c.q,
+               k=deq(c.k, c.k_scale), v=deq(c.v, c.v_scale), ctx_lens=c.ctx_lens,
+               block_size=c.block_size, block_table=c.block_table, tile=c.tile)
+    for kw in (dict(v_skip_eps=0.0), dict(v_skip_eps=1e-6),
+               dict(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)):
+        a = run_oracle(c, **kw)
+        b = run_oracle(f, **kw)
+        assert np.array_equal(a.out, b.out) and np.array_equal(a.tiles_used, b.tiles_used)
+
+
+# ---------------------------------------------------------------- P10: V skip
+
+def test_vskip_limits():
+    c = rand_case(B=1, Hq=2, Hkv=1, d=16, n=200, seed=41, tile=16)
+    base = run_oracle(c)
+    zero = run_oracle(c, v_skip_eps=0.0)
+    assert np.array_equal(base.out, zero.out)
+    none_kept = run_oracle(c, v_skip_eps=1.0001, eps_scale=0.0, eps_dir=0.0)
+    assert (none_kept.out == 0).all()  # every exp(s - M) <= 1 < eps
+
+
+def test_vskip_one_hot_weights():
+    # with V = identity rows the output is the weight vector: skipped rows give
+    # exactly 0, kept rows keep their full softmax weight (skipped mass stays in l)
+    n = d = 64
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((1, 1, d)) * 4
+    K = rng.standard_normal((1, 1, n, d))
+    c = contiguous_case(q, K, np.eye(n)[None, None], tile=8, eps_scale=0.0, eps_dir=0.0)
+    eps = 1e-3
+    w_skip = run_oracle(c, v_skip_eps=eps).out[0, 0]
+    w = BF.attention_weights(c, 0, 0, n)
+    zeroed = w_skip == 0
+    assert zeroed.any() and (~zeroed).any()
+    assert np.allclose(w_skip[~zeroed], w[~zeroed], rtol=1e-12, atol=1e-16)
+    assert (w[zeroed] < eps).all()  # a final weight never exceeds exp(s - M_t)
+    # the decision uses the running max: the first tile's top score is never skipped
+    s0 = K[0, 0, :8] @ q[0, 0] / np.sqrt(d)
+    assert not zeroed[int(np.argmax(s0))]
+
+
+def test_vskip_error_bound():
+    c = A.config(3, small=True, seed=6, batch=1, ctx=1024)
+    full = run_oracle(c, eps_scale=0.0, eps_dir=0.0)
+    eps = 1e-3
+    sk = run_oracle(c, eps_scale=0.0, eps_dir=0.0, v_skip_eps=eps, trace=True)
+    G = c.Hq // c.Hkv
+    for h in range(c.Hq):
+        V = BF.logical_rows(c, "v", 0, h // G, 1024)
+        n_skipped = int(1024 - np.nansum(sk.trace[0, h, :, 5]))
+        bound = n_skipped * eps * np.linalg.norm(V, axis=1).max()
+        assert np.linalg.norm(sk.out[0, h] - full.out[0, h]) <= bound + 1e-12
+
+
+# ---------------------------------------------------------------- P11: output awareness
+
+def test_low_weight_large_value_row_delays_the_stop():
+    """A row with a low attention weight but a large value moves the output,
+    so the stop rule does not fire at its tile (ART summary, section 1 and 2.2:
+    low-weight tokens can matter through their values; the criterion watches
+    the output, not the scores)."""
+    rng = np.random.default_rng(77)
+    d, T, n = 32, 16, 16 * 8
+    q = rng.standard_normal((1, 1, d))
+    K = rng.standard_normal((1, 1, n, d))
+    V = np.ones((1, 1, n, d))
+    c0 = contiguous_case(q, K, V, tile=T, eps_scale=1e-3, eps_dir=1e-4)
+    assert run_oracle(c0).tiles_used[0, 0] == 2  # constant V: stable at t=1
+    # plant a row in tile 1 whose logit is -2 sigma and whose value is x50 and rotated
+    qv = c0.q[0, 0].astype(np.float64)
+    sigma = np.linalg.norm(qv) / np.sqrt(d)
+    j = T + 5
+    kp = -2 * sigma * np.sqrt(d) * qv / (qv @ qv)
+    K2 = K.copy(); K2[0, 0, j] = kp
+    V2 = V.copy(); V2[0, 0, j] = 0.0; V2[0, 0, j, 1] = 50.0
+    c1 = contiguous_case(q, K2, V2, tile=T, eps_scale=1e-3, eps_dir=1e-4)
+    r1 = run_oracle(c1, trace=True)
+    w = BF.attention_weights(c1, 0, 0, 2 * T)
+    assert w[j] < 1.0 / (2 * T)                      # key-only view: below-average weight
+    assert r1.trace[0, 0, 1, 2] >= 1e-3 or r1.trace[0, 0, 1, 3] >= 1e-4
+    assert r1.tiles_used[0, 0] > 2                   # the stop moved past the planted tile
+
+
+def test_vskip_uses_running_max_through_the_tile():
+    """Designed scores: tile 0 holds the overall maximum, tile 1's best row sits
+    20 below it, tile 2 holds a row 20 above tile 0's max.  With the running max
+    through the current tile, tile 1's best row is skipped (exp(-20) < eps) even
+    though it tops its own tile, and tile 0's best row is kept even though a
+    later tile exceeds it by 20."""
+    d, T = 8, 4
+    q = np.zeros((1, 1, d)); q[0, 0, 0] = np.sqrt(d)    # score = k[0]
+    K = np.zeros((1, 1, 3 * T, d))
+    K[0, 0, :, 0] = [5, 0, 0, 0,    -15, -30, -30, -30,    25, 0, 0, 0]
+    n = 3 * T
+    V = np.zeros((1, 1, n, n)); V[0, 0] = np.eye(n)
+    K = np.concatenate([K, np.zeros((1, 1, n, n - d))], axis=-1)
+    q = np.concatenate([q, np.zeros((1, 1, n - d))], axis=-1)
+    c = contiguous_case(q, K, V, tile=T, eps_scale=0.0, eps_dir=0.0)
+    w = run_oracle(c, v_skip_eps=1e-6).out[0, 0]
+    assert w[4] == 0.0          # top of tile 1, but exp(-15 - 5) < 1e-6
+    assert w[0] > 0.0           # top of tile 0 when it was read
+    assert w[8] > 0.0
