@@ -148,9 +148,8 @@ def make_case(name, *, B, Hq, Hkv, d, ctx_lens, seed=0, kv_dtype="bf16", q_dtype
     assert Hq % Hkv == 0
     rng = np.random.default_rng(seed)
     max_ctx = int(ctx_lens.max(initial=0))
-    if block_size:
-        max_ctx = -(-max_ctx // block_size) * block_size
-    max_ctx = max(max_ctx, block_size or 1)
+    unit = block_size or 16  # contiguous rows are padded to a multiple of 16 tokens
+    max_ctx = max(-(-max_ctx // unit) * unit, unit)
 
     # 1. queries
     qf = rng.standard_normal((B, Hq, d), dtype=np.float32)

@@ -1,0 +1,137 @@
+/*
+ * art.h -- C ABI of the ART decode-attention library for MI355X (gfx950).
+ *
+ * One decode query per (batch row, query head) attends over that row's KV
+ * cache tile by tile with an online softmax, and the traversal stops early
+ * once a cheap probe of the running output has stabilised (ART, "Runtime
+ * Attention Termination", gist.science technical summary of arXiv
+ * 2606.00024, sections 2.1-2.4).  An optional mode skips the V rows whose
+ * softmax weight is negligible, before they are loaded or dequantised
+ * (puntofijo.es article on skipping V dequantisation in llama.cpp).
+ *
+ * Every pointer passed to art_decode_attention is device memory allocated and
+ * owned by the caller; the library keeps none of them after the call returns,
+ * allocates nothing and never synchronises.  Work is enqueued on `stream`
+ * (a hipStream_t, or NULL for the default stream); results are valid once the
+ * stream has reached that point.  Errors are returned as negative status
+ * codes, never thrown, printed or aborted on; art_last_error() gives detail.
+ */
+#ifndef ART_H
+#define ART_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ART_ABI_VERSION 1
+
+typedef enum {
+    ART_OK = 0,
+    ART_E_NULL = -1,        /* a required pointer is NULL                          */
+    ART_E_SHAPE = -2,       /* sizes inconsistent or out of the supported range    */
+    ART_E_DTYPE = -3,       /* unknown dtype or unsupported q/kv dtype pair        */
+    ART_E_TILE = -4,        /* tile not in {16, 32, 64, 128} or not a multiple of
+                               the page granule                                    */
+    ART_E_PARAM = -5,       /* threshold NaN/negative/infinite, patience < 1, ... */
+    ART_E_WORKSPACE = -6,   /* workspace NULL, misaligned or smaller than needed   */
+    ART_E_HIP = -7          /* a HIP runtime call (launch) failed                  */
+} art_status;
+
+typedef enum { ART_F32 = 0, ART_BF16 = 1, ART_I8 = 2 } art_dtype;
+
+/*
+ * Shape and options of one call.  Layouts are row-major:
+ *   q           [batch][num_q_heads][head_dim]           q_dtype (F32 or BF16)
+ *   k/v cache   paged:      [num_blocks][num_kv_heads][block_size][head_dim]
+ *               contiguous: [batch][num_kv_heads][max_ctx][head_dim]
+ *               kv_dtype F32, BF16, or I8 (then k_scale/v_scale are required)
+ *   k/v scale   fp16 bit patterns, the cache layout without head_dim: one scale
+ *               per (token, KV head); the value of an I8 entry is code * scale
+ *   block_table int32 [batch][max_blocks_per_seq] (paged only): logical page p
+ *               of row b lives in physical block block_table[b][p]
+ *   ctx_lens    int32 [batch]: cached positions of each row (0 allowed)
+ *   out         fp32 [batch][num_q_heads][head_dim]
+ *   tiles_used  int32 [batch][num_q_heads]
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+typedef struct {
+    int32_t batch;               /* >= 0                                              */
+    int32_t num_q_heads;         /* >= 1, multiple of num_kv_heads, at most 16 per KV head */
+    int32_t num_kv_heads;        /* >= 1                                              */
+    int32_t head_dim;            /* 64 or 128                                         */
+    int32_t q_dtype;             /* art_dtype: ART_F32 or ART_BF16                    */
+    int32_t kv_dtype;            /* art_dtype                                         */
+    int32_t block_size;          /* 0 = contiguous cache; else a multiple of 16       */
+    int32_t max_blocks_per_seq;  /* paged: row stride of block_table                  */
+    int32_t num_blocks;          /* paged: valid block ids are 0..num_blocks-1        */
+    int32_t max_ctx;             /* contiguous: row stride in tokens (multiple of 16) */
+    int32_t patience;            /* >= 1: consecutive passing tiles needed to stop    */
+    float v_skip_eps;            /* 0 = off; else skip V row j when exp(s_j - M_t) <
+                                    v_skip_eps, M_t the running max through tile t     */
+    const void* k_scale;         /* I8 caches only (device, fp16 bits)                */
+    const void* v_scale;
+    void* workspace;             /* device scratch, 256-byte aligned, caller-owned    */
+    size_t workspace_bytes;      /* >= art_workspace_bytes(desc, tile)                */
+    int64_t* stats;              /* optional device int64[4] accumulator, or NULL:
+                                    [0] K tiles loaded, [1] V rows loaded,
+                                    [2] tiles loaded after their group had stopped,
+                                    [3] reserved                                      */
+    int32_t max_workers;         /* 0 = library default; else cap on worker waves     */
+} art_desc;
+
+/*
+ * art_decode_attention -- ART-terminated decode attention over a KV cache.
+ *
+ * For every (b, h): the query attends over positions 0..ctx_lens[b]-1 of its
+ * KV head in tiles of `tile` tokens, tile 0 first, with an online softmax
+ * (ART summary, section 2.1).  After each tile t the probe is dims 0..7 of the
+ * normalised running output; from t = 1 on, d_scale = | |x_t| - |x_{t-1}| | /
+ * |x_{t-1}| and d_dir = 1 - cos(x_t, x_{t-1}) (section 2.2).  A tile passes
+ * when d_scale < eps_scale and d_dir < eps_dir; after `patience` consecutive
+ * passing tiles (section 2.3) the head stops, tiles_used[b][h] = t + 1 and the
+ * remaining tiles of that head are never read.  Tile 0 is always evaluated
+ * (section 2.4).  Without a stop, tiles_used = ceil(ctx_len / tile).
+ * out[b][h] = softmax(q k^T / sqrt(head_dim)) v over the used positions.
+ *
+ * eps_scale = eps_dir = 0 (or any threshold <= 0) never stops: full attention,
+ * run by a kernel without the detector when v_skip_eps is 0.
+ * ctx_lens[b] = 0 gives out = 0 and tiles_used = 0.
+ *
+ * Errors detected on the device, per batch row: ctx_lens[b] < 0 or larger than
+ * the cache row capacity, or a block id outside [0, num_blocks) inside a
+ * visited tile -> tiles_used = -1 and out = NaN for the affected heads; no
+ * out-of-range address is ever dereferenced.
+ *
+ * Host-side validation happens before anything is enqueued; device memory is
+ * never read on the host.  Concurrent calls must use distinct workspaces.
+ */
+art_status art_decode_attention(const art_desc* desc, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table,
+                                const int32_t* ctx_lens, int32_t tile, float eps_scale,
+                                float eps_dir, float* out, int32_t* tiles_used, void* stream);
+
+/* Bytes of workspace a call with this desc and tile needs (0 on an invalid desc). */
+size_t art_workspace_bytes(const art_desc* desc, int32_t tile);
+
+/* Host-only validation of everything art_decode_attention checks before
+ * launching (pointers in desc are not dereferenced; q/k/v/out pointers are
+ * not examined here). */
+art_status art_validate(const art_desc* desc, int32_t tile, float eps_scale, float eps_dir);
+
+/* Static description of a status code. */
+const char* art_status_string(int32_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* art_last_error(void);
+
+/* ART_ABI_VERSION of the loaded library. */
+int32_t art_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ART_H */

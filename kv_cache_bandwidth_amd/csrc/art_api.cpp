@@ -1,0 +1,209 @@
+// Host side of the C ABI (include/art.h): argument validation, workspace
+// layout, launch planning.  Never reads device memory, never synchronises.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "art.h"
+#include "art_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+art_status fail(art_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+// worker waves the full-mode split aims for: 256 CUs x 8 resident waves
+constexpr int kTargetWaves = 2048;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool finite_nonneg(float x) { return std::isfinite(x) && x >= 0.f; }
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+// Validates desc/tile/thresholds and fills the shape part of Params.
+art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, art::Params& p) {
+    if (!d) return fail(ART_E_NULL, "desc is NULL");
+    if (d->batch < 0) return fail(ART_E_SHAPE, "batch %d < 0", d->batch);
+    if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+        return fail(ART_E_SHAPE, "head counts must be >= 1 (q %d, kv %d)", d->num_q_heads, d->num_kv_heads);
+    if (d->num_q_heads % d->num_kv_heads)
+        return fail(ART_E_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
+                    d->num_kv_heads);
+    const int G = d->num_q_heads / d->num_kv_heads;
+    if (G > art::kMaxG) return fail(ART_E_SHAPE, "%d query heads per KV head; at most %d supported", G, art::kMaxG);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(ART_E_SHAPE, "head_dim %d; supported: 64, 128", d->head_dim);
+    if (d->q_dtype != ART_F32 && d->q_dtype != ART_BF16)
+        return fail(ART_E_DTYPE, "q_dtype %d; supported: ART_F32, ART_BF16", d->q_dtype);
+    if (d->kv_dtype != ART_F32 && d->kv_dtype != ART_BF16 && d->kv_dtype != ART_I8)
+        return fail(ART_E_DTYPE, "kv_dtype %d unknown", d->kv_dtype);
+    if (d->kv_dtype == ART_I8 && (!d->k_scale || !d->v_scale))
+        return fail(ART_E_NULL, "int8 cache needs k_scale and v_scale");
+    if (tile != 16 && tile != 32 && tile != 64 && tile != 128)
+        return fail(ART_E_TILE, "tile %d; supported: 16, 32, 64, 128", tile);
+    long long cap;
+    if (d->block_size) {
+        if (d->block_size < 16 || d->block_size % 16)
+            return fail(ART_E_SHAPE, "block_size %d must be a positive multiple of 16", d->block_size);
+        if (d->batch > 0 && d->max_blocks_per_seq < 1)
+            return fail(ART_E_SHAPE, "max_blocks_per_seq %d < 1", d->max_blocks_per_seq);
+        if (d->num_blocks < 1) return fail(ART_E_SHAPE, "num_blocks %d < 1", d->num_blocks);
+        cap = (long long)d->max_blocks_per_seq * d->block_size;
+    } else {
+        if (d->max_ctx < 0 || d->max_ctx % 16)
+            return fail(ART_E_SHAPE, "max_ctx %d must be a non-negative multiple of 16", d->max_ctx);
+        cap = d->max_ctx;
+    }
+    if (cap > (1LL << 30)) return fail(ART_E_SHAPE, "row capacity %lld tokens too large", cap);
+    if (!finite_nonneg(eps_scale) || !finite_nonneg(eps_dir))
+        return fail(ART_E_PARAM, "thresholds must be finite and >= 0 (got %g, %g)", eps_scale, eps_dir);
+    if (!finite_nonneg(d->v_skip_eps)) return fail(ART_E_PARAM, "v_skip_eps %g must be finite and >= 0", d->v_skip_eps);
+    if (d->patience < 1) return fail(ART_E_PARAM, "patience %d < 1", d->patience);
+    if (d->max_workers < 0) return fail(ART_E_PARAM, "max_workers %d < 0", d->max_workers);
+
+    p = art::Params{};
+    p.B = d->batch; p.Hq = d->num_q_heads; p.Hkv = d->num_kv_heads; p.G = G; p.D = d->head_dim; p.T = tile;
+    p.q_dtype = d->q_dtype; p.kv_dtype = d->kv_dtype;
+    p.block_size = d->block_size; p.mbps = d->max_blocks_per_seq; p.num_blocks = d->num_blocks;
+    p.max_ctx = d->max_ctx;
+    p.cap = (int)cap;
+    p.nt_max = (int)((cap + tile - 1) / tile);
+    p.NG = d->batch * d->num_kv_heads;
+    p.patience = d->patience;
+    p.art = eps_scale > 0.f && eps_dir > 0.f;
+    p.vskip = d->v_skip_eps > 0.f;
+    p.eps_scale = eps_scale; p.eps_dir = eps_dir; p.v_skip_eps = d->v_skip_eps;
+    p.inv_sqrt_d = 1.f / std::sqrt((float)d->head_dim);
+    p.slot = art::kSlotHeader + G * d->head_dim;
+    // full-mode split plan (part of the workspace layout, so independent of the device)
+    const int target = kTargetWaves;
+    int splits = p.NG ? (target + p.NG - 1) / p.NG : 1;
+    if (splits > p.nt_max) splits = p.nt_max > 0 ? p.nt_max : 1;
+    if (splits < 1) splits = 1;
+    p.tiles_per_split = p.nt_max > 0 ? (p.nt_max + splits - 1) / splits : 1;
+    p.splits = p.nt_max > 0 ? (p.nt_max + p.tiles_per_split - 1) / p.tiles_per_split : 1;
+    return ART_OK;
+}
+
+}  // namespace
+
+namespace art {
+
+Layout workspace_layout(const Params& p) {
+    Layout L{};
+    size_t o = 0;
+    const size_t NG = (size_t)p.NG, G = (size_t)p.G;
+    L.abort_flag = o; o = align256(o + sizeof(int));
+    L.ctl = o; o = align256(o + NG * sizeof(GroupCtl));
+    L.heads = o; o = align256(o + NG * G * sizeof(HeadState));
+    L.acc = o; o = align256(o + NG * G * p.D * sizeof(float));
+    L.ring_tag = o; o = align256(o + NG * kRing * sizeof(int));
+    L.ring = o; o = align256(o + NG * kRing * (size_t)p.slot * sizeof(float));
+    L.vmax_tag = o; o = align256(o + NG * (size_t)p.nt_max * sizeof(int));
+    L.vmax = o; o = align256(o + NG * (size_t)p.nt_max * 16 * sizeof(float));
+    L.partials = o; o = align256(o + NG * (size_t)p.splits * p.slot * sizeof(float));
+    L.total = o;
+    return L;
+}
+
+}  // namespace art
+
+extern "C" {
+
+const char* art_status_string(int32_t s) {
+    switch (s) {
+        case ART_OK: return "ok";
+        case ART_E_NULL: return "a required pointer is NULL";
+        case ART_E_SHAPE: return "inconsistent or unsupported sizes";
+        case ART_E_DTYPE: return "unsupported dtype";
+        case ART_E_TILE: return "unsupported tile";
+        case ART_E_PARAM: return "invalid method parameter";
+        case ART_E_WORKSPACE: return "workspace missing, misaligned or too small";
+        case ART_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* art_last_error(void) { return g_last_error.c_str(); }
+
+int32_t art_abi_version(void) { return ART_ABI_VERSION; }
+
+size_t art_workspace_bytes(const art_desc* desc, int32_t tile) {
+    art::Params p;
+    if (check(desc, tile, 0.f, 0.f, p) != ART_OK) return 0;
+    return art::workspace_layout(p).total;
+}
+
+art_status art_validate(const art_desc* desc, int32_t tile, float eps_scale, float eps_dir) {
+    g_last_error.clear();
+    art::Params p;
+    art_status s = check(desc, tile, eps_scale, eps_dir, p);
+    if (s != ART_OK) return s;
+    const size_t need = art::workspace_layout(p).total;
+    if (!desc->workspace) return fail(ART_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (reinterpret_cast<uintptr_t>(desc->workspace) & 255)
+        return fail(ART_E_WORKSPACE, "workspace not 256-byte aligned");
+    if (desc->workspace_bytes < need)
+        return fail(ART_E_WORKSPACE, "workspace %zu bytes < %zu needed", desc->workspace_bytes, need);
+    return ART_OK;
+}
+
+art_status art_decode_attention(const art_desc* desc, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table,
+                                const int32_t* ctx_lens, int32_t tile, float eps_scale,
+                                float eps_dir, float* out, int32_t* tiles_used, void* stream) {
+    art_status s = art_validate(desc, tile, eps_scale, eps_dir);
+    if (s != ART_OK) return s;
+    art::Params p;
+    check(desc, tile, eps_scale, eps_dir, p);
+    if (p.B == 0) return ART_OK;
+    if (!q || !k_cache || !v_cache || !ctx_lens || !out || !tiles_used)
+        return fail(ART_E_NULL, "q, k_cache, v_cache, ctx_lens, out and tiles_used are required");
+    if (p.block_size && !block_table) return fail(ART_E_NULL, "paged cache needs block_table");
+    p.q = q; p.k = k_cache; p.v = v_cache;
+    p.ks = static_cast<const uint16_t*>(desc->k_scale);
+    p.vs = static_cast<const uint16_t*>(desc->v_scale);
+    p.block_table = block_table; p.ctx_lens = ctx_lens; p.out = out; p.tiles_used = tiles_used;
+    p.stats = reinterpret_cast<long long*>(desc->stats);
+    // persistent grid: as many worker waves as fit at once (two work-groups per CU)
+    long long workers = desc->max_workers ? desc->max_workers : (long long)device_cus() * 8;
+    const long long tiles = (long long)p.NG * p.nt_max;
+    if (workers > tiles) workers = tiles > 0 ? tiles : 1;
+    p.workers = (int)workers;
+    const art::Layout L = art::workspace_layout(p);
+    char* ws = static_cast<char*>(desc->workspace);
+    p.abort_flag = reinterpret_cast<int*>(ws + L.abort_flag);
+    p.ctl = reinterpret_cast<art::GroupCtl*>(ws + L.ctl);
+    p.heads = reinterpret_cast<art::HeadState*>(ws + L.heads);
+    p.acc = reinterpret_cast<float*>(ws + L.acc);
+    p.ring_tag = reinterpret_cast<int*>(ws + L.ring_tag);
+    p.ring = reinterpret_cast<float*>(ws + L.ring);
+    p.vmax_tag = reinterpret_cast<int*>(ws + L.vmax_tag);
+    p.vmax = reinterpret_cast<float*>(ws + L.vmax);
+    p.partials = reinterpret_cast<float*>(ws + L.partials);
+    const int rc = (p.art || p.vskip) ? art::launch_art(p, stream) : art::launch_full(p, stream);
+    if (rc != 0) return fail(ART_E_HIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)rc));
+    return ART_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal declarations shared by the host API (art_api.cpp) and the kernels
+// (art_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "art.h"
+
+namespace art {
+
+constexpr int kRing = 64;         // ring slots per group (tiles in flight ahead of the frontier)
+constexpr int kMaxG = 16;         // query heads per KV head
+constexpr int kWavesPerWG = 4;    // independent worker waves per work-group
+constexpr int kSpinLimit = 1 << 20; // iterations of any wait before the kernel gives up
+constexpr int kSlotHeader = 48;   // floats before the accumulator block of a partial:
+                                  // [0,16) tile max per head, [16,32) tile sum per head,
+                                  // [32] error flag (as int), [33] V rows kept (as int)
+
+// Per-group control block; each field group on its own 128-byte line.
+struct alignas(128) GroupCtl {
+    int next;          // tile allocation counter (atomic)
+    int pad0[31];
+    int lock;          // frontier lock (atomic)
+    int frontier;      // tiles folded into the group's running state
+    int bound;         // tiles that may still be allocated: ceil(n/T), lowered once every head stopped
+    int nt;            // tiles of the group
+    int n;             // ctx_len of the row
+    int pad1[27];
+};
+
+// Running state of one query head, owned by whoever holds the group lock.
+struct alignas(16) HeadState {
+    float M;       // running max score
+    float L;       // running softmax sum
+    int streak;    // consecutive passing tiles
+    int U;         // tiles_used once finished, -1 while active
+    int err;       // a visited tile had an invalid block id
+    float pn;      // norm of the previous probe
+    int pad[2];
+    float prev[8]; // previous probe x(t-1)
+};
+
+struct Params {
+    // shape
+    int B, Hq, Hkv, G, D, T;
+    int q_dtype, kv_dtype;
+    int block_size, mbps, num_blocks, max_ctx;
+    int cap;            // tokens a row can hold
+    int nt_max;         // ceil(cap / T)
+    int NG;             // B * Hkv groups
+    // method
+    int patience;
+    int art;            // stop rule active
+    int vskip;          // V-row skip active
+    float eps_scale, eps_dir, v_skip_eps, inv_sqrt_d;
+    // inputs / outputs (device)
+    const void* q;
+    const void* k;
+    const void* v;
+    const uint16_t* ks;
+    const uint16_t* vs;
+    const int* block_table;
+    const int* ctx_lens;
+    float* out;
+    int* tiles_used;
+    long long* stats;
+    // workspace regions (device)
+    int* abort_flag;    // set when a wait exceeded kSpinLimit: workers exit, heads stay unfinished
+    GroupCtl* ctl;
+    HeadState* heads;   // [NG][G]
+    float* acc;         // [NG][G][D]
+    int* ring_tag;      // [NG][kRing]
+    float* ring;        // [NG][kRing][slot]
+    int* vmax_tag;      // [NG][nt_max]
+    float* vmax;        // [NG][nt_max][16]
+    float* partials;    // [NG][splits][slot]
+    int slot;           // floats per partial: kSlotHeader + G*D
+    // launch
+    int workers;        // worker waves of the persistent kernel
+    int splits;         // full mode: workers per group
+    int tiles_per_split;
+};
+
+// Workspace layout for a Params (offsets in bytes, all 256-byte aligned).
+struct Layout {
+    size_t abort_flag, ctl, heads, acc, ring_tag, ring, vmax_tag, vmax, partials, total;
+};
+Layout workspace_layout(const Params& p);
+
+// Kernel launches (art_kernels.hip); return a hipError_t value.
+int launch_art(const Params& p, void* stream);
+int launch_full(const Params& p, void* stream);
+
+}  // namespace art
