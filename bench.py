@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of ART-terminated decode attention on one MI355X.
+
+A step is one art_decode_attention call (ART mode, thresholds 1e-3 / 1e-4,
+patience 1) over the whole batch of the 32K-context Llama-3-8B-shaped workload
+(batch 16, 32 query / 8 KV heads, head dim 128, bf16 paged KV cache with
+16-token blocks under a seeded random block permutation, temperature giving the
+top 5 % of keys ~90 % of the softmax mass), inputs resident in HBM.
+
+Each timed step is bracketed by HIP events on the launch stream; between
+steps (outside the events) a 1 GiB buffer is written so the 256 MB Infinity
+Cache and the L2s hold none of the cache.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 3] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes(case, used_g, kv_rows_loaded=None):
+    """Bytes the method must move for one step (see the measurement notes):
+    K and V rows of the tiles each group reads (V only where loaded when rows
+    are skipped), their int8 scales, the block-table entries of those tiles,
+    the queries, the outputs and tiles_used."""
+    e = case.k.dtype.itemsize
+    rows = np.minimum(used_g.astype(np.int64) * case.tile, case.ctx_lens[:, None].astype(np.int64))
+    k_rows = int(rows.sum())
+    v_rows = k_rows if kv_rows_loaded is None else int(kv_rows_loaded)
+    per_row = case.d * e + (2 if case.kv_dtype == "i8" else 0)
+    kv = (k_rows + v_rows) * per_row
+    table = 0
+    if case.block_size:
+        table = int(np.ceil(rows / case.block_size).sum()) * 4
+    q = case.q.nbytes
+    out = case.B * case.Hq * case.d * 4 + case.B * case.Hq * 4
+    return kv + table + q + out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-full", action="store_true", help="skip the full-attention comparison")
+    ap.add_argument("--flush-mb", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the decode-attention path is single-GPU "
+              "(sharding across GPUs is a design note, not built). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import art_inputs as A
+    import kv_cache_bandwidth_amd as art
+    from tests.gpu_util import to_device
+
+    log(f"generating workload config {args.config} (seed {args.seed})")
+    t0 = time.time()
+    case = A.config(args.config, seed=args.seed)
+    log(f"generated in {time.time() - t0:.1f}s: {A.WORKLOADS[args.config]}")
+    dev = to_device(case)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device="cuda")
+    G = case.Hq // case.Hkv
+
+    def call(eps_scale, eps_dir, v_skip, stats=None, ws=None, out=None, used=None):
+        return art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], block_table=dev["bt"],
+                                    tile=case.tile, eps_scale=eps_scale, eps_dir=eps_dir,
+                                    patience=case.patience, v_skip_eps=v_skip, k_scale=dev["ks"],
+                                    v_scale=dev["vs"], stats=stats, workspace=ws, out=out,
+                                    tiles_used=used)
+
+    def timed(eps_scale, eps_dir, v_skip, steps, warmup):
+        out, used = call(eps_scale, eps_dir, v_skip)
+        ws = torch.empty(art.workspace_bytes(_desc(eps_scale), case.tile), dtype=torch.uint8,
+                         device="cuda")
+        for _ in range(warmup):
+            flush_buf.fill_(1)
+            call(eps_scale, eps_dir, v_skip, ws=ws, out=out, used=used)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t_wall = time.perf_counter()
+        for e0, e1 in evs:
+            flush_buf.fill_(1)
+            e0.record(stream)
+            call(eps_scale, eps_dir, v_skip, ws=ws, out=out, used=used)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        return ms, wall, out, used
+
+    def _desc(eps):
+        return art.make_desc(batch=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
+                             head_dim=case.d, q_dtype=1 if case.q_dtype == "bf16" else 0,
+                             kv_dtype={"f32": 0, "bf16": 1, "i8": 2}[case.kv_dtype],
+                             block_size=case.block_size,
+                             max_blocks_per_seq=case.block_table.shape[1] if case.block_size else 0,
+                             num_blocks=case.num_blocks,
+                             max_ctx=0 if case.block_size else case.max_ctx,
+                             patience=case.patience)
+
+    es, ed, vk = case.eps_scale, case.eps_dir, case.v_skip_eps
+    # counters of one ART call: tiles loaded (speculative ones included), V rows loaded
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    out, used = call(es, ed, vk, stats=stats)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy()
+    used_np = used.cpu().numpy()
+    log(f"ART call: mean tiles_used {used_np.mean():.1f}, tiles loaded {int(st[0])}")
+
+    log(f"timing ART mode: {args.warmup} warmup + {args.steps} steps")
+    ms, wall, out, used = timed(es, ed, vk, args.steps, args.warmup)
+    used_np = used.cpu().numpy()
+    used_g = used_np.reshape(case.B, case.Hkv, G).max(axis=-1)
+    nt = -(-case.ctx_lens // case.tile)
+    mean_ms = statistics.mean(ms)
+    med_ms = statistics.median(ms)
+    b_alg = alg_bytes(case, used_g, kv_rows_loaded=int(st[1]) if vk > 0 else None)
+    achieved = b_alg / (mean_ms * 1e-3) / 1e9
+    head_skip = 1.0 - used_np.sum() / (nt[:, None] * case.Hq).sum()
+    kv_read = np.minimum(used_g * case.tile, case.ctx_lens[:, None]).sum()
+    byte_skip = 1.0 - kv_read / (case.ctx_lens.astype(np.int64).sum() * case.Hkv)
+    tiles_needed = int(np.ceil(np.minimum(used_g * case.tile, case.ctx_lens[:, None]) / case.tile).sum())
+    res = {
+        "metric": "decode-attn us/step (ART, 32K ctx) + achieved HBM GB/s, roofline %, % KV tiles skipped",
+        "value": round(mean_ms * 1e3, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": A.WORKLOADS[args.config], "batch": case.B, "q_heads": case.Hq,
+                   "kv_heads": case.Hkv, "head_dim": case.d, "ctx": int(case.ctx_lens[0]),
+                   "tile": case.tile, "eps_scale": es, "eps_dir": ed, "patience": case.patience,
+                   "v_skip_eps": vk},
+        "us_per_step_median": round(med_ms * 1e3, 2),
+        "us_per_step_p10_p90": [round(float(np.percentile(ms, 10)) * 1e3, 2),
+                                round(float(np.percentile(ms, 90)) * 1e3, 2)],
+        "kv_tiles_skipped_head_level": round(float(head_skip), 4),
+        "kv_bytes_skipped": round(float(byte_skip), 4),
+        "tiles_loaded": int(st[0]),
+        "tiles_needed": tiles_needed,
+        "speculative_tiles": int(st[0]) - tiles_needed,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_step": int(b_alg)},
+        "wall_s_timed_region": round(wall, 4),
+    }
+
+    if not args.no_full:
+        log("timing full attention (thresholds 0)")
+        ms_f, _, out_f, used_f = timed(0.0, 0.0, 0.0, args.steps, args.warmup)
+        mf = statistics.mean(ms_f)
+        b_full = alg_bytes(case, np.broadcast_to(nt[:, None], used_g.shape))
+        res["full_attention"] = {"us_per_step": round(mf * 1e3, 2),
+                                 "achieved_GBs": round(b_full / (mf * 1e-3) / 1e9, 1),
+                                 "frac": round(b_full / (mf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        res["speedup_vs_full"] = round(mf / mean_ms, 3)
+        # detector overhead: the ART path with thresholds that never pass
+        ms_n, _, _, _ = timed(1e-30, 1e-30, 0.0, max(5, args.steps // 2), 2)
+        res["never_firing_art_us_per_step"] = round(statistics.mean(ms_n) * 1e3, 2)
+
+    if not args.no_cpu:
+        import oracle
+        threads = oracle.default_threads()
+        log(f"CPU oracle baseline on {threads} threads")
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            r = oracle.decode(case.q, case.k, case.v, case.ctx_lens, tile=case.tile, eps_scale=es,
+                              eps_dir=ed, patience=case.patience, v_skip_eps=vk,
+                              block_table=case.block_table, block_size=case.block_size,
+                              k_scale=case.k_scale, v_scale=case.v_scale, threads=threads)
+            times.append(time.perf_counter() - t0)
+        cpu_us = statistics.median(times) * 1e6
+        res["cpu_baseline"] = {"value": round(cpu_us, 1), "unit": "us/step", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the whole step ({case.B} rows x {case.Hq} heads), fp64, "
+                                         f"median of 3 on {platform.processor() or platform.machine()}"}
+        res["parity_vs_oracle"] = {
+            "tiles_used_equal": int((used.cpu().numpy() == r.tiles_used).sum()),
+            "heads": int(r.tiles_used.size),
+            "max_abs_out": float(np.abs(out.cpu().numpy().astype(np.float64) - r.out).max())}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

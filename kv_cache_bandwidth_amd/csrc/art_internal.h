@@ -9,10 +9,11 @@
 
 namespace art {
 
-constexpr int kRing = 64;         // ring slots per group (tiles in flight ahead of the frontier)
+constexpr int kRing = 128;        // ring slots per group (tiles in flight ahead of the frontier)
 constexpr int kMaxG = 16;         // query heads per KV head
 constexpr int kWavesPerWG = 4;    // independent worker waves per work-group
-constexpr int kSpinLimit = 1 << 20; // iterations of any wait before the kernel gives up
+constexpr unsigned long long kWaitTicks = 50000000ull;  // 0.5 s of the 100 MHz device clock:
+                                                      // longest any wait may last before the kernel gives up
 constexpr int kSlotHeader = 48;   // floats before the accumulator block of a partial:
                                   // [0,16) tile max per head, [16,32) tile sum per head,
                                   // [32] error flag (as int), [33] V rows kept (as int)
@@ -26,7 +27,8 @@ struct alignas(128) GroupCtl {
     int bound;         // tiles that may still be allocated: ceil(n/T), lowered once every head stopped
     int nt;            // tiles of the group
     int n;             // ctx_len of the row
-    int pad1[27];
+    int seen;          // tiles past the frontier already decided (incomplete window)
+    int pad1[26];
 };
 
 // Running state of one query head, owned by whoever holds the group lock.
@@ -66,7 +68,7 @@ struct Params {
     int* tiles_used;
     long long* stats;
     // workspace regions (device)
-    int* abort_flag;    // set when a wait exceeded kSpinLimit: workers exit, heads stay unfinished
+    int* abort_flag;    // set when a wait outlasted kWaitTicks: workers exit, heads stay unfinished
     GroupCtl* ctl;
     HeadState* heads;   // [NG][G]
     float* acc;         // [NG][G][D]

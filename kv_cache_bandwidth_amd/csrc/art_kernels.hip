@@ -25,10 +25,25 @@
 //  * Full mode (no stop rule, no V skip): a static split of each group's tiles
 //    over worker waves, each keeping a running state in registers, followed
 //    by an in-order combine of the splits.
+//
+// Tile computation.  bf16/int8 caches with head dim 128 and bf16 queries use
+// matrix cores for the scores: each 16-token page of K is the A operand of
+// four v_mfma_f32_16x16x32_bf16 (one per 32 head dims) against the group's
+// queries as the B operand (heads padded to 16 columns).  Softmax and the
+// P.V accumulation run on the vector ALUs from 128-bit V loads (one wave
+// instruction reads four whole 256-byte rows).  Other shapes use a plain
+// vector-ALU tile.
+//
+// Cross-wave data.  Everything one wave publishes for another (ring slots,
+// the group's running state, tile maxima, counters) is written and read with
+// agent-scope relaxed atomics, which gfx950 performs as coherent (sc1)
+// accesses; a producer waits for its stores to complete before it stores the
+// flag that publishes them.  No L2 writeback or invalidate is ever issued.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "art_internal.h"
 
@@ -37,34 +52,42 @@ namespace {
 
 constexpr float kNegInf = -INFINITY;
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// ------------------------------------------------------------------ atomics (agent scope)
-__device__ __forceinline__ int ld_rlx(const int* p) {
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// wave index within the work-group (wave-uniform, so kept in a scalar register)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// lane 0's value, as a wave-uniform (scalar) value
+__device__ __forceinline__ int bcast0(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ------------------------------------------------------------------ coherent accesses
+template <class T>
+__device__ __forceinline__ T cld(const T* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int ld_acq(const int* p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_sc(const int* p) {
-    return __hip_atomic_load(p, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_rlx(int* p, int v) {
+template <class T>
+__device__ __forceinline__ void cst(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_sc(int* p, int v) {
-    __hip_atomic_store(p, v, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int faa(int* p, int v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ bool cas_sc(int* p, int expect, int desired) {
-    return __hip_atomic_compare_exchange_strong(p, &expect, desired, __ATOMIC_SEQ_CST,
-                                                __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ bool cas(int* p, int expect, int desired) {
+    return __hip_atomic_compare_exchange_strong(p, &expect, desired, __ATOMIC_RELAXED,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_rel() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acq() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// Waits until every memory access this wave issued has completed.  Shared
+// data is only accessed coherently, so completed stores are visible to any
+// later coherent load: a flag stored after drain() publishes them.
+__device__ __forceinline__ void drain() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 // orders LDS accesses of one wave (lanes of a wave may read what others wrote)
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -90,30 +113,32 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
+__device__ __forceinline__ float sbyte(uint32_t w, int k) { return (float)(int)(int8_t)(w >> (8 * k)); }
+// two small integers (|x| <= 127) as a packed bf16 pair: exact, since they need at most 8 bits
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    return (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
+}
 
 // Eight consecutive cache elements starting at element `off` (a multiple of 8), widened to fp32.
 template <int KV>
 __device__ __forceinline__ void load8(const void* base, long long off, float (&o)[8]) {
     if constexpr (KV == ART_F32) {
-        typedef float f4 __attribute__((ext_vector_type(4)));
         const f4* p = reinterpret_cast<const f4*>(static_cast<const float*>(base) + off);
         f4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
         o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
         o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
     } else if constexpr (KV == ART_BF16) {
-        typedef unsigned u4 __attribute__((ext_vector_type(4)));
         const u4* p = reinterpret_cast<const u4*>(static_cast<const uint16_t*>(base) + off);
         u4 a = __builtin_nontemporal_load(p);
         o[0] = bf16lo(a.x); o[1] = bf16hi(a.x); o[2] = bf16lo(a.y); o[3] = bf16hi(a.y);
         o[4] = bf16lo(a.z); o[5] = bf16hi(a.z); o[6] = bf16lo(a.w); o[7] = bf16hi(a.w);
     } else {
-        typedef unsigned u2 __attribute__((ext_vector_type(2)));
         const u2* p = reinterpret_cast<const u2*>(static_cast<const int8_t*>(base) + off);
         u2 a = __builtin_nontemporal_load(p);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            o[i] = (float)(int8_t)(a.x >> (8 * i));
-            o[4 + i] = (float)(int8_t)(a.y >> (8 * i));
+            o[i] = sbyte(a.x, i);
+            o[4 + i] = sbyte(a.y, i);
         }
     }
 }
@@ -124,7 +149,6 @@ __device__ __forceinline__ void load_small(const void* base, long long off, floa
     if constexpr (KV == ART_F32) {
         const float* p = static_cast<const float*>(base) + off;
         if constexpr (APL == 2) {
-            typedef float f2 __attribute__((ext_vector_type(2)));
             f2 a = __builtin_nontemporal_load(reinterpret_cast<const f2*>(p));
             o[0] = a.x; o[1] = a.y;
         } else {
@@ -142,7 +166,7 @@ __device__ __forceinline__ void load_small(const void* base, long long off, floa
         const int8_t* p = static_cast<const int8_t*>(base) + off;
         if constexpr (APL == 2) {
             uint16_t w = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
-            o[0] = (float)(int8_t)(w & 0xff); o[1] = (float)(int8_t)(w >> 8);
+            o[0] = sbyte(w, 0); o[1] = sbyte(w, 1);
         } else {
             o[0] = (float)__builtin_nontemporal_load(p);
         }
@@ -160,16 +184,53 @@ __device__ __forceinline__ long long row_index(const Params& P, int b, int g, in
     return ((long long)blk * P.Hkv + g) * P.block_size + (j % P.block_size);
 }
 
-// ------------------------------------------------------------------ generic tile (VALU)
+// ------------------------------------------------------------------ tile output
 //
-// One wave computes one tile: lane l scores token t*T + l (+64), the tile max
-// and sum per head are wave reductions, the kept weights go through LDS and the
-// V accumulation maps lane l to head dims l*APL .. l*APL+APL-1.
+// "Fold mapping", shared by every consumer of partials: lane l serves head
+// hb*4 + (l >> 4) of head block hb and head dims 8*(l & 15) .. +7.
+template <int HBM>
+struct TileOutT {
+    float m[kMaxG];   // tile max per head (wave-uniform)
+    float l[kMaxG];   // tile softmax sum per head, relative to m (wave-uniform)
+    float a[HBM][8];  // V accumulator, fold mapping (head blocks 0..HBM-1)
+    int err;          // an invalid block id was met
+    int kept;         // V rows loaded
+};
+
+struct FoldLanes {
+    int hl, cid, HB;
+    bool cvalid;
+    __device__ FoldLanes(const Params& P) {
+        const int lane = lane_id();
+        hl = lane >> 4;
+        cid = lane & 15;
+        HB = (P.G + 3) >> 2;
+        cvalid = cid < (P.D >> 3);
+    }
+};
+
+// ------------------------------------------------------------------ generic tile (vector ALU)
+//
+// Any dtype, head dim 64 or 128, G <= 16.  Lane l scores token t*T + l (+64),
+// the tile max and sum per head are wave reductions, the kept weights go
+// through LDS and the V accumulation maps lane l to head dims l*APL..; the
+// accumulator is finally transposed to the fold mapping through LDS.
 template <int D, int KV>
 struct GenericTile {
     static constexpr int APL = D / 64;
+    static constexpr int HBM = 4;
+    using Out = TileOutT<HBM>;
 
-    __device__ static void load_q(const Params& P, int b, int g, float* q_lds) {
+    __host__ __device__ static size_t lds_floats(const Params& P) {
+        return (size_t)P.G * D + (size_t)(P.G * P.T > P.G * D ? P.G * P.T : P.G * D);
+    }
+
+    float* q_lds;
+    float* p_lds;
+
+    __device__ void load_q(const Params& P, int b, int g, float* lds) {
+        q_lds = lds;
+        p_lds = lds + P.G * D;
         const int lane = lane_id();
         for (int i = lane; i < P.G * D; i += 64) {
             const long long off = ((long long)b * P.Hq + (long long)g * P.G) * D + i;
@@ -179,12 +240,8 @@ struct GenericTile {
         wave_lds_sync();
     }
 
-    // Returns false if `hook` asked to abandon the tile.  hook(m_loc, Mt) fills
-    // Mt with the running max through this tile (used by the V skip only).
     template <class Hook>
-    __device__ static bool compute(const Params& P, int b, int g, int n, int t, const float* q_lds,
-                                   float* p_lds, float (&m_loc)[kMaxG], float (&l_loc)[kMaxG],
-                                   float (&acc)[kMaxG][APL], int& err, int& kept, Hook&& hook) {
+    __device__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
         const int lane = lane_id();
         const int G = P.G, T = P.T;
         const int j0 = t * T;
@@ -225,17 +282,17 @@ struct GenericTile {
                 }
             }
         }
-        err |= (__ballot(bad) != 0ull);
+        o.err = __ballot(bad) != 0ull;
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h) {
             float mx = kNegInf;
 #pragma unroll
             for (int ps = 0; ps < 2; ++ps)
                 if (valid[ps]) mx = fmaxf(mx, s[ps][h]);
-            m_loc[h] = h < G ? wave_max(mx) : kNegInf;
+            o.m[h] = h < G ? wave_max(mx) : kNegInf;
         }
         float Mt[kMaxG];
-        if (!hook(m_loc, Mt)) return false;
+        if (!hook(o.m, Mt)) return false;
         float lsum[kMaxG];
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h) lsum[h] = 0.f;
@@ -247,7 +304,7 @@ struct GenericTile {
 #pragma unroll
             for (int h = 0; h < kMaxG; ++h) {
                 if (h < G) {
-                    const float p = valid[ps] ? expf(s[ps][h] - m_loc[h]) : 0.f;
+                    const float p = valid[ps] ? expf(s[ps][h] - o.m[h]) : 0.f;
                     lsum[h] += p;
                     const bool keep = valid[ps] && (!P.vskip || expf(s[ps][h] - Mt[h]) >= P.v_skip_eps);
                     row_keep |= keep;
@@ -257,13 +314,14 @@ struct GenericTile {
             keep_mask[ps] = __ballot(row_keep);
         }
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h) l_loc[h] = h < G ? wave_sum(lsum[h]) : 0.f;
+        for (int h = 0; h < kMaxG; ++h) o.l[h] = h < G ? wave_sum(lsum[h]) : 0.f;
         wave_lds_sync();
+        float acc[kMaxG][APL];
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h)
 #pragma unroll
             for (int i = 0; i < APL; ++i) acc[h][i] = 0.f;
-        kept = __builtin_popcountll(keep_mask[0]) + __builtin_popcountll(keep_mask[1]);
+        o.kept = __builtin_popcountll(keep_mask[0]) + __builtin_popcountll(keep_mask[1]);
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
             uint64_t m = keep_mask[ps];
@@ -287,53 +345,597 @@ struct GenericTile {
                 }
             }
         }
-        wave_lds_sync();  // p_lds is rewritten by the next tile
+        // transpose the accumulator to the fold mapping (p_lds is free again)
+        wave_lds_sync();
+        float* x = p_lds;
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h)
+            if (h < G)
+#pragma unroll
+                for (int i = 0; i < APL; ++i) x[h * D + lane * APL + i] = acc[h][i];
+        wave_lds_sync();
+        const int hl = lane >> 4, cid = lane & 15;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            const int h = hb * 4 + hl;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                o.a[hb][j] = (h < G && 8 * cid < D) ? x[h * D + 8 * cid + j] : 0.f;
+        }
+        wave_lds_sync();
         return true;
     }
+};
 
-    // Store a tile (or split) partial in the common slot format.
-    __device__ static void store_partial(const Params& P, float* slot, const float (&m)[kMaxG],
-                                         const float (&l)[kMaxG], const float (&acc)[kMaxG][APL],
-                                         int err, int kept) {
-        const int lane = lane_id();
-        if (lane == 0) {
+// ------------------------------------------------------------------ matrix-core tile
+//
+// bf16 or int8 cache, head dim 128, bf16 queries, G <= 8, tile of PAGES
+// 16-token pages.  Scores: lane l holds the A operand row l&15 of a page
+// (128-bit loads of head dims 32s + 8(l>>4) .. +7 for s = 0..3) and the B
+// operand column l&15 = head; the 16x16 result gives lane l the scores of
+// tokens 4(l>>4)+i of that page for head l&15.  P.V: lane l accumulates head
+// dims 8(l&15)..+7 over rows 4v + (l>>4) of every page, reading the kept
+// weights of its rows from LDS; the four row groups are summed through LDS
+// into the fold mapping at the end.
+template <int KV, int PAGES, int GMAX>
+struct FastTile {
+    static constexpr int T = 16 * PAGES;
+    static constexpr int D = 128;
+    static constexpr int EB = KV == ART_I8 ? 1 : 2;  // bytes per cache element
+    static constexpr int HBM = GMAX / 4;
+    using Out = TileOutT<HBM>;
+    typedef typename std::conditional<KV == ART_I8, u2, u4>::type kvec;  // 8 elements
+
+    __host__ __device__ static size_t lds_floats(const Params& P) {
+        return (size_t)(T * GMAX > 4 * P.G * D ? T * GMAX : 4 * P.G * D);
+    }
+
+    bf16x8 qB[4];
+    float* lds;
+
+    __device__ void load_q(const Params& P, int b, int g, float* lds_wave) {
+        lds = lds_wave;
+        const int lane = lane_id(), h = lane & 15, kg = lane >> 4;
+        const uint16_t* q = static_cast<const uint16_t*>(P.q);
 #pragma unroll
-            for (int h = 0; h < kMaxG; ++h) {
-                if (h < P.G) {
-                    slot[h] = m[h];
-                    slot[16 + h] = l[h];
+        for (int s = 0; s < 4; ++s) {
+            u4 v = {0u, 0u, 0u, 0u};
+            if (h < P.G)
+                v = *reinterpret_cast<const u4*>(q + ((long long)b * P.Hq + (long long)g * P.G + h) * D +
+                                                 32 * s + 8 * kg);
+            qB[s] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    __device__ static kvec load_kv(const void* base, long long elem) {
+        return __builtin_nontemporal_load(
+            reinterpret_cast<const kvec*>(static_cast<const char*>(base) + elem * EB));
+    }
+
+    template <class Hook>
+    __device__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
+        const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+        const int G = P.G;
+        const int tok0 = t * T;
+        // pages of the tile: first row index and validity (wave-uniform)
+        long long prow[PAGES];
+        bool pval[PAGES];
+        int bad = 0;
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p) {
+            const int tokp = tok0 + 16 * p;
+            pval[p] = tokp < n;
+            prow[p] = 0;
+            if (pval[p]) {
+                bool ok = true;
+                prow[p] = row_index(P, b, g, tokp, ok);
+                if (!ok) { pval[p] = false; bad = 1; }
+            }
+        }
+        // K loads (A operand layout) and, without V skip, the V loads right away
+        const kvec zero = {};
+        kvec kr[PAGES][4], vr[PAGES][4];
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                kr[p][s] = pval[p] ? load_kv(P.k, (prow[p] + r16) * D + 32 * s + 8 * rg) : zero;
+        if (!P.vskip) {
+#pragma unroll
+            for (int p = 0; p < PAGES; ++p)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 4 * v + rg;
+                    vr[p][v] = (pval[p] && tok0 + 16 * p + row < n)
+                                   ? load_kv(P.v, (prow[p] + row) * D + 8 * r16) : zero;
+                }
+        }
+        // int8 key scales of the score rows 4*rg + i of every page
+        float ksc[PAGES][4];
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ksc[p][i] = P.inv_sqrt_d;
+        if constexpr (KV == ART_I8) {
+#pragma unroll
+            for (int p = 0; p < PAGES; ++p) {
+                if (pval[p]) {
+                    const u2 w = *reinterpret_cast<const u2*>(P.ks + prow[p] + 4 * rg);
+                    ksc[p][0] = f16_to_f32(w.x & 0xffff) * P.inv_sqrt_d;
+                    ksc[p][1] = f16_to_f32(w.x >> 16) * P.inv_sqrt_d;
+                    ksc[p][2] = f16_to_f32(w.y & 0xffff) * P.inv_sqrt_d;
+                    ksc[p][3] = f16_to_f32(w.y >> 16) * P.inv_sqrt_d;
                 }
             }
-            reinterpret_cast<int*>(slot)[32] = err;
-            reinterpret_cast<int*>(slot)[33] = kept;
         }
+        // scores on the matrix cores
+        float s[PAGES][4];
+        float mx = kNegInf;
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
-            if (h < P.G) {
-                float* dst = slot + kSlotHeader + h * D + lane * APL;
+        for (int p = 0; p < PAGES; ++p) {
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < APL; ++i) dst[i] = acc[h][i];
+            for (int st = 0; st < 4; ++st) {
+                bf16x8 a;
+                if constexpr (KV == ART_I8) {
+                    const u2 w = kr[p][st];
+                    u4 c;
+                    c.x = bf16_pair(sbyte(w.x, 0), sbyte(w.x, 1));
+                    c.y = bf16_pair(sbyte(w.x, 2), sbyte(w.x, 3));
+                    c.z = bf16_pair(sbyte(w.y, 0), sbyte(w.y, 1));
+                    c.w = bf16_pair(sbyte(w.y, 2), sbyte(w.y, 3));
+                    a = __builtin_bit_cast(bf16x8, c);
+                } else {
+                    a = __builtin_bit_cast(bf16x8, kr[p][st]);
+                }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[st], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = pval[p] && tok0 + 16 * p + 4 * rg + i < n;
+                s[p][i] = valid ? acc[i] * ksc[p][i] : kNegInf;
+                mx = fmaxf(mx, s[p][i]);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));  // tile max of head r16, in every lane of that head
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) o.m[h] = (h < GMAX && h < G) ? __shfl(mx, h) : kNegInf;
+        float Mt[kMaxG];
+        if (!hook(o.m, Mt)) return false;
+        float mt = Mt[0];
+#pragma unroll
+        for (int h = 1; h < GMAX; ++h)
+            if (r16 == h) mt = Mt[h];
+        // weights: exp(s - tile max); the V skip compares against the running max
+        float* pl = lds;  // [T tokens][GMAX heads]
+        float lsum = 0.f;
+        uint64_t keep_rows = 0;
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = s[p][i] != kNegInf;
+                const float pr = valid ? expf(s[p][i] - mx) : 0.f;
+                lsum += pr;
+                const bool keep = valid && r16 < G && (!P.vskip || expf(s[p][i] - mt) >= P.v_skip_eps);
+                const int tok = 16 * p + 4 * rg + i;
+                if (r16 < GMAX) pl[tok * GMAX + r16] = keep ? pr : 0.f;
+                const uint64_t bal = __ballot(keep);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if ((bal >> (16 * q)) & 0xffffull) keep_rows |= 1ull << (16 * p + 4 * q + i);
+            }
+        }
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) o.l[h] = (h < GMAX && h < G) ? __shfl(lsum, h) : 0.f;
+        o.err = __ballot(bad) != 0ull;
+        o.kept = __builtin_popcountll(keep_rows);
+        if (P.vskip) {
+            // V rows no head keeps are neither loaded nor dequantised
+#pragma unroll
+            for (int p = 0; p < PAGES; ++p)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 4 * v + rg;
+                    vr[p][v] = (pval[p] && ((keep_rows >> (16 * p + row)) & 1ull))
+                                   ? load_kv(P.v, (prow[p] + row) * D + 8 * r16) : zero;
+                }
+        }
+        wave_lds_sync();
+        // P.V on the vector ALUs
+        float acc[GMAX][8];
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tok = 16 * p + 4 * v + rg;
+                float pw[GMAX];
+                const f4 w0 = *reinterpret_cast<const f4*>(pl + tok * GMAX);
+                pw[0] = w0.x; pw[1] = w0.y; pw[2] = w0.z; pw[3] = w0.w;
+                if constexpr (GMAX == 8) {
+                    const f4 w1 = *reinterpret_cast<const f4*>(pl + tok * GMAX + 4);
+                    pw[4] = w1.x; pw[5] = w1.y; pw[6] = w1.z; pw[7] = w1.w;
+                }
+                float vf[8];
+                if constexpr (KV == ART_I8) {
+                    const float vs =
+                        (pval[p] && tok0 + tok < n) ? f16_to_f32(P.vs[prow[p] + 4 * v + rg]) : 0.f;
+#pragma unroll
+                    for (int h = 0; h < GMAX; ++h) pw[h] *= vs;
+                    const u2 w = vr[p][v];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        vf[k] = sbyte(w.x, k);
+                        vf[4 + k] = sbyte(w.y, k);
+                    }
+                } else {
+                    const u4 w = vr[p][v];
+                    vf[0] = bf16lo(w.x); vf[1] = bf16hi(w.x); vf[2] = bf16lo(w.y); vf[3] = bf16hi(w.y);
+                    vf[4] = bf16lo(w.z); vf[5] = bf16hi(w.z); vf[6] = bf16lo(w.w); vf[7] = bf16hi(w.w);
+                }
+#pragma unroll
+                for (int h = 0; h < GMAX; ++h) {
+                    if (h < G) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pw[h], vf[j], acc[h][j]);
+                    }
+                }
+            }
+        }
+        // sum the four row groups into the fold mapping
+        wave_lds_sync();
+        float* x = lds;  // [4 row groups][G][128]
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h < G) {
+                f4* d = reinterpret_cast<f4*>(x + (rg * G + h) * D + 8 * r16);
+                d[0] = f4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+                d[1] = f4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+            }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            const int h = hb * 4 + rg;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o.a[hb][j] = 0.f;
+            if (h < G) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f4* src = reinterpret_cast<const f4*>(x + (q * G + h) * D + 8 * r16);
+                    const f4 u = src[0], w = src[1];
+                    o.a[hb][0] += u.x; o.a[hb][1] += u.y; o.a[hb][2] += u.z; o.a[hb][3] += u.w;
+                    o.a[hb][4] += w.x; o.a[hb][5] += w.y; o.a[hb][6] += w.z; o.a[hb][7] += w.w;
+                }
+            }
+        }
+        wave_lds_sync();
+        return true;
+    }
+};
+
+// ------------------------------------------------------------------ streamed matrix-core tiles
+//
+// bf16 or int8 cache, head dim 128, bf16 queries, G <= GMAX (4 or 8), tiles
+// of 64 tokens, no V skip.  A wave streams 32-token units (two 16-token
+// pages) through a two-deep pipeline: while one unit is consumed, the next
+// one is loading.  Every load instruction of a wave reads whole rows (1 KB of
+// contiguous memory for bf16):
+//  * K goes straight to LDS (global_load_lds_dwordx4, no registers) with the
+//    16-byte chunks of each row permuted by XOR with the row index, so the
+//    matrix-core operand reads below are free of bank conflicts;
+//  * V goes to registers in the layout the P.V accumulation uses.
+// Scores: lane l reads from LDS the A operand row l&15 of a page (head dims
+// 32s + 8(l>>4) .. +7 for s = 0..3) and holds the B operand column l&15 =
+// head (queries, heads padded to 16 columns); the 16x16 result gives lane l
+// the scores of tokens 4(l>>4)+i of the page for head l&15.  P.V: lane l
+// accumulates head dims 8(l&15)..+7 over rows 4v + (l>>4) of each page, with
+// the weights of its rows read from LDS.  Units of one tile (ART mode) or of
+// a whole split range (full mode) accumulate into one running (max, sum,
+// accumulator) state that flush() reduces into the fold mapping.
+template <int KV, int GMAX>
+struct Stream {
+    static constexpr int D = 128, UP = 2, T = 64, PAGES = 4;
+    static constexpr int EB = KV == ART_I8 ? 1 : 2;
+    static constexpr int HBM = GMAX / 4;
+    static constexpr int ROWB = D * EB;          // bytes of one cache row
+    static constexpr int PAGEB = 16 * ROWB;      // bytes of one 16-row page
+    static constexpr int KDMA = PAGEB / 1024;    // LDS-direct loads per page
+    static constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+    // vector-memory instructions one issue() emits (all unconditional)
+    static constexpr int OPS = UP * (4 + KDMA + (KV == ART_I8 ? 5 : 0));
+    // resident waves per SIMD the register budget is cut for (two when it fits without heavy spills)
+    static constexpr int MIN_WAVES = GMAX == 4 ? 2 : 1;
+    using Out = TileOutT<HBM>;
+    typedef typename std::conditional<KV == ART_I8, u2, u4>::type vvec;
+
+    __host__ __device__ static size_t lds_floats(const Params&) { return (2 * UP * PAGEB) / 4 + 32 * GMAX; }
+
+    struct TileRef {             // one tile of one group (wave-uniform)
+        int grp, t, n;
+        long long prow[PAGES];   // row index of the first token of each page
+        int pmask;               // bit p: page p starts below n and has a valid block
+        int err;                 // an invalid block id was met in the tile
+    };
+
+    vvec vb[2][UP][4];
+    float ksc[2][UP][4];         // int8: key scale / sqrt(d) of the score rows
+    float vsc[2][UP][4];         // int8: value scale of the P.V rows
+    bf16x8 qB[4];
+    float m_run, l_run;
+    float acc[GMAX][8];
+    char* kl;                    // LDS: [2 buffers][UP pages][PAGEB]
+    float* pl;                   // LDS: [32 tokens][GMAX heads]
+
+    __device__ void init(float* lds_wave) {
+        kl = reinterpret_cast<char*>(lds_wave);
+        pl = lds_wave + (2 * UP * PAGEB) / 4;
+        reset();
+    }
+
+    __device__ void reset() {
+        m_run = kNegInf;
+        l_run = 0.f;
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+    }
+
+    __device__ void load_q(const Params& P, int grp) {
+        const int b = grp / P.Hkv, g = grp % P.Hkv;
+        const int lane = lane_id(), h = lane & 15, kg = lane >> 4;
+        const uint16_t* q = static_cast<const uint16_t*>(P.q);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u4 v = {0u, 0u, 0u, 0u};
+            if (h < P.G)
+                v = *reinterpret_cast<const u4*>(q + ((long long)b * P.Hq + (long long)g * P.G + h) * D +
+                                                 32 * s + 8 * kg);
+            qB[s] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    __device__ static void resolve(const Params& P, int grp, int t, TileRef& r) {
+        const int b = grp / P.Hkv, g = grp % P.Hkv;
+        r.grp = grp;
+        r.t = t;
+        r.n = P.ctx_lens[b];
+        r.pmask = 0;
+        r.err = 0;
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p) {
+            const int tokp = t * T + 16 * p;
+            r.prow[p] = 0;
+            if (tokp < r.n) {
+                bool ok = true;
+                r.prow[p] = row_index(P, b, g, tokp, ok);
+                if (ok) r.pmask |= 1 << p;
+                else r.err = 1;
             }
         }
     }
-};
 
-// ------------------------------------------------------------------ fold of partials
-//
-// Lane mapping used by the fold, the combine and the init: lane l serves head
-// hb*4 + (l >> 4) of head block hb and head dims 8*(l & 15) .. +7.
-struct FoldLanes {
-    int hl, cid, HB;
-    bool cvalid;
-    __device__ FoldLanes(const Params& P) {
-        const int lane = lane_id();
-        hl = lane >> 4;
-        cid = lane & 15;
-        HB = (P.G + 3) >> 2;
-        cvalid = cid < (P.D >> 3);
+    // Issue the loads of unit u (pages 2u, 2u+1) of tile r into buffer BUF:
+    // exactly OPS unconditional vector-memory instructions.  Pages outside the
+    // sequence (or with an invalid block) read the first rows of the cache
+    // instead; consume() masks them.
+    template <int BUF>
+    __device__ void issue(const Params& P, const TileRef& r, int u) {
+        const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+        // keep every load of this unit after the previous unit's LDS reads and
+        // before the next unit's loads: the waits count instructions in order
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pp = 0; pp < UP; ++pp) {
+            const int p = UP * u + pp;
+            const long long pr = ((r.pmask >> p) & 1) ? r.prow[p] : 0;
+            const char* vbase = static_cast<const char*>(P.v) + pr * ROWB;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 4 * v + rg;
+                vb[BUF][pp][v] = __builtin_nontemporal_load(
+                    reinterpret_cast<const vvec*>(vbase + row * ROWB + 8 * EB * r16));
+            }
+            if constexpr (KV == ART_I8) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) vsc[BUF][pp][v] = f16_to_f32(P.vs[pr + 4 * v + rg]);
+                const u2 w = *reinterpret_cast<const u2*>(P.ks + pr + 4 * rg);
+                ksc[BUF][pp][0] = f16_to_f32(w.x & 0xffff) * P.inv_sqrt_d;
+                ksc[BUF][pp][1] = f16_to_f32(w.x >> 16) * P.inv_sqrt_d;
+                ksc[BUF][pp][2] = f16_to_f32(w.y & 0xffff) * P.inv_sqrt_d;
+                ksc[BUF][pp][3] = f16_to_f32(w.y >> 16) * P.inv_sqrt_d;
+            }
+            const char* kbase = static_cast<const char*>(P.k) + pr * ROWB;
+            char* dst = kl + (BUF * UP + pp) * PAGEB;
+#pragma unroll
+            for (int i = 0; i < KDMA; ++i) {
+                // 1 KB per instruction: LDS chunk (row, c) receives global chunk c ^ (row % CPR)
+                const int row = i * (1024 / ROWB) + lane / CPR;
+                const int c = (lane % CPR) ^ (row % CPR);
+                __builtin_amdgcn_global_load_lds(kbase + row * ROWB + 16 * c,
+                                                 (__attribute__((address_space(3))) void*)(dst + 1024 * i),
+                                                 16, 0, 2 /* nt */);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    template <int N>
+    __device__ static void wait_vm() {
+        static_assert(N < 64, "vmcnt has 6 bits");
+        __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    }
+
+    // Fold unit u of tile r (loaded in buffer BUF) into the running state.
+    // `pending`: the next unit's loads were issued after this one's.
+    template <int BUF>
+    __device__ void consume(const Params& P, const TileRef& r, int u, bool pending) {
+        const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+        const int G = P.G;
+        __builtin_amdgcn_sched_barrier(0);
+        if (pending) wait_vm<OPS>();  // this unit's loads, K in LDS included, have landed
+        else wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        float s[UP][4];
+        float mu = kNegInf;
+#pragma unroll
+        for (int pp = 0; pp < UP; ++pp) {
+            const int p = UP * u + pp;
+            const char* kp = kl + (BUF * UP + pp) * PAGEB;
+            f4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                bf16x8 a;
+                if constexpr (KV == ART_I8) {
+                    // 8 bytes: head dims 32st + 8rg .. +7 of row r16
+                    const int c = (2 * st + (rg >> 1)) ^ (r16 % CPR);
+                    const u2 w = *reinterpret_cast<const u2*>(kp + r16 * ROWB + 16 * c + 8 * (rg & 1));
+                    u4 cv;
+                    cv.x = bf16_pair(sbyte(w.x, 0), sbyte(w.x, 1));
+                    cv.y = bf16_pair(sbyte(w.x, 2), sbyte(w.x, 3));
+                    cv.z = bf16_pair(sbyte(w.y, 0), sbyte(w.y, 1));
+                    cv.w = bf16_pair(sbyte(w.y, 2), sbyte(w.y, 3));
+                    a = __builtin_bit_cast(bf16x8, cv);
+                } else {
+                    const int c = (4 * st + rg) ^ r16;
+                    a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u4*>(kp + r16 * ROWB + 16 * c));
+                }
+                a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[st], a4, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = ((r.pmask >> p) & 1) && r.t * T + 16 * p + 4 * rg + i < r.n;
+                const float sc = KV == ART_I8 ? ksc[BUF][pp][i] : P.inv_sqrt_d;
+                s[pp][i] = valid ? a4[i] * sc : kNegInf;
+                mu = fmaxf(mu, s[pp][i]);
+            }
+        }
+        mu = fmaxf(mu, __shfl_xor(mu, 16));
+        mu = fmaxf(mu, __shfl_xor(mu, 32));
+        const float m_new = fmaxf(m_run, mu);
+        const float alpha = m_run == kNegInf ? 0.f : expf(m_run - m_new);
+        float lsum = 0.f;
+        wave_lds_sync();  // the previous unit's P.V reads of pl are done
+#pragma unroll
+        for (int pp = 0; pp < UP; ++pp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pr = s[pp][i] != kNegInf ? expf(s[pp][i] - m_new) : 0.f;
+                lsum += pr;
+                if (r16 < GMAX) pl[(16 * pp + 4 * rg + i) * GMAX + r16] = pr;
+            }
+        l_run = alpha * l_run + lsum;
+        m_run = m_new;
+        float ah[GMAX];
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) ah[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+        wave_lds_sync();
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h)
+            if (h < G)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[h][j] *= ah[h];
+        // rows outside the sequence hold whatever the fallback rows hold: zero them
+        const bool full = ((r.pmask >> (UP * u)) & 3) == 3 && r.t * T + 32 * (u + 1) <= r.n;
+        if (full) pv_accumulate<BUF, false>(P, r, u);
+        else pv_accumulate<BUF, true>(P, r, u);
+    }
+
+    template <int BUF, bool MASK>
+    __device__ void pv_accumulate(const Params& P, const TileRef& r, int u) {
+        const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+        const int G = P.G;
+#pragma unroll
+        for (int pp = 0; pp < UP; ++pp) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tok = 16 * pp + 4 * v + rg;
+                bool rv = true;
+                if constexpr (MASK) rv = ((r.pmask >> (UP * u + pp)) & 1) && r.t * T + 32 * u + tok < r.n;
+                float pw[GMAX];
+                const f4 w0 = *reinterpret_cast<const f4*>(pl + tok * GMAX);
+                pw[0] = w0.x; pw[1] = w0.y; pw[2] = w0.z; pw[3] = w0.w;
+                if constexpr (GMAX == 8) {
+                    const f4 w1 = *reinterpret_cast<const f4*>(pl + tok * GMAX + 4);
+                    pw[4] = w1.x; pw[5] = w1.y; pw[6] = w1.z; pw[7] = w1.w;
+                }
+                float vf[8];
+                if constexpr (KV == ART_I8) {
+#pragma unroll
+                    for (int h = 0; h < GMAX; ++h) pw[h] *= vsc[BUF][pp][v];
+                    const u2 w = vb[BUF][pp][v];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        vf[k] = sbyte(w.x, k);
+                        vf[4 + k] = sbyte(w.y, k);
+                    }
+                } else {
+                    const u4 w = vb[BUF][pp][v];
+                    vf[0] = bf16lo(w.x); vf[1] = bf16hi(w.x); vf[2] = bf16lo(w.y); vf[3] = bf16hi(w.y);
+                    vf[4] = bf16lo(w.z); vf[5] = bf16hi(w.z); vf[6] = bf16lo(w.w); vf[7] = bf16hi(w.w);
+                }
+                if constexpr (MASK) {
+#pragma unroll
+                    for (int h = 0; h < GMAX; ++h) pw[h] = rv ? pw[h] : 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) vf[j] = rv ? vf[j] : 0.f;
+                }
+#pragma unroll
+                for (int h = 0; h < GMAX; ++h)
+                    if (h < G)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pw[h], vf[j], acc[h][j]);
+            }
+        }
+    }
+
+    // Reduce the running state into the fold mapping and reset it.  The four
+    // row groups (lanes l, l^16, l^32, l^48) are summed by a two-step
+    // reduce-scatter: after it, lane l holds head 4hb + (l>>4) of each block.
+    __device__ void flush(const Params& P, Out& o) {
+        const int lane = lane_id(), rg = lane >> 4;
+        const int G = P.G;
+        float lt = l_run + __shfl_xor(l_run, 16);
+        lt += __shfl_xor(lt, 32);
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            o.m[h] = (h < GMAX && h < G) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), h))
+                                         : kNegInf;
+            o.l[h] = (h < GMAX && h < G) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), h)) : 0.f;
+        }
+        const bool hi2 = rg >> 1, hi1 = rg & 1;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            // step 1 (lanes l ^ 32): keep heads 4hb + 2*hi2 + {0,1}, send the other pair
+            float keep[2][8];
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float mine_lo = acc[4 * hb + e][j], mine_hi = acc[4 * hb + 2 + e][j];
+                    const float send = hi2 ? mine_lo : mine_hi;
+                    keep[e][j] = (hi2 ? mine_hi : mine_lo) + __shfl_xor(send, 32);
+                }
+            // step 2 (lanes l ^ 16): keep head 4hb + 2*hi2 + hi1
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float send = hi1 ? keep[0][j] : keep[1][j];
+                o.a[hb][j] = (hi1 ? keep[1][j] : keep[0][j]) + __shfl_xor(send, 16);
+            }
+        }
+        reset();
     }
 };
 
+// ------------------------------------------------------------------ output of a finished head
 __device__ __forceinline__ void write_head_out(const Params& P, int grp, int h, const FoldLanes& fl,
                                                const float (&a8)[8], float L, int err, int U) {
     const int b = grp / P.Hkv, g = grp % P.Hkv;
@@ -347,221 +949,411 @@ __device__ __forceinline__ void write_head_out(const Params& P, int grp, int h, 
     if (fl.cid == 0) P.tiles_used[row] = err ? -1 : U;
 }
 
-// Try to take the group lock and fold every ready tile in order.
+// ------------------------------------------------------------------ give-up path of every wait
+__device__ void give_up(const Params& P) { cst(P.abort_flag, 1); }
+__device__ bool aborted(const Params& P) { return cld(P.abort_flag) != 0; }
+
+// Wall-clock budget of any single wait (device real-time counter, 100 MHz):
+// past it the kernel gives up, so no wait can hang the GPU.
+struct Deadline {
+    unsigned long long t0;
+    __device__ Deadline() : t0(wall_clock64()) {}
+    __device__ bool passed() const { return wall_clock64() - t0 > kWaitTicks; }
+};
+
+// ------------------------------------------------------------------ ring publication
+//
+// publish_data() stores a partial into its slot and returns a coherent
+// re-read of the last word it stored.  publish_flag() consumes that value
+// before storing the tag: vector memory operations of a wave complete in
+// issue order, so once the re-read has returned, every slot store before it
+// has completed -- and loads issued in between (the next unit's prefetch)
+// may still be in flight.
+template <int HBM>
+__device__ int publish_data(const Params& P, int grp, int t, const TileOutT<HBM>& o) {
+    const int lane = lane_id();
+    const FoldLanes fl(P);
+    float* slot = P.ring + ((long long)grp * kRing + (t & (kRing - 1))) * P.slot;
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        if (hb < fl.HB && h < P.G && fl.cvalid) {
+            float* a = slot + kSlotHeader + h * P.D + 8 * fl.cid;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cst(a + j, o.a[hb][j]);
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            if (h < P.G) {
+                cst(slot + h, o.m[h]);
+                cst(slot + 16 + h, o.l[h]);
+            }
+        }
+        cst(reinterpret_cast<int*>(slot) + 32, o.err);
+        cst(reinterpret_cast<int*>(slot) + 33, o.kept);
+    }
+    return cld(reinterpret_cast<const int*>(slot) + 33);
+}
+
+__device__ void publish_flag(const Params& P, int grp, int t, int token) {
+    asm volatile("" ::"v"(token) : "memory");  // wait for the re-read (and so for the slot stores)
+    if (lane_id() == 0) cst(&P.ring_tag[(long long)grp * kRing + (t & (kRing - 1))], t + 1);
+    // The flag must be visible before this wave tries the group lock: either
+    // the lock holder's re-check after unlocking sees the flag, or our lock
+    // attempt sees the lock released (store, complete, then read on both sides).
+    drain();
+}
+
+// ------------------------------------------------------------------ fold of ready tiles
+//
+// (m, l, a) := (m, l, a) (+) (m2, l2, a2): online-softmax merge, left = earlier
+__device__ __forceinline__ void sm_merge(float& m, float& l, float (&a)[8], float m2, float l2,
+                                         const float (&a2)[8]) {
+    const float mn = fmaxf(m, m2);
+    if (mn == kNegInf) return;
+    const float w1 = m == kNegInf ? 0.f : expf(m - mn);
+    const float w2 = m2 == kNegInf ? 0.f : expf(m2 - mn);
+    l = w1 * l + w2 * l2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = w1 * a[j] + w2 * a2[j];
+    m = mn;
+}
+
+// Per-head committed state of the group, kept in registers by the lock holder
+// (fold mapping: lane 16*hl + cid, head 4*hb + hl, dims 8*cid .. +7).
+template <int HBM>
+struct FoldState {
+    float M[HBM], L[HBM], pn[HBM], prev[HBM][8], A[HBM][8];
+    int streak[HBM], err[HBM], U[HBM];
+};
+
+// Decides the tiles f .. f+k-1 (k <= 16) for head block hb, from the committed
+// state S.  Writes the output of every head that stops; when `commit`, folds
+// the whole window into S (heads that did not stop).  Returns the number of
+// heads (of this block, counted in lane 16*hl) still active afterwards.
+template <int HBM>
+__device__ int fold_window(const Params& P, int grp, int hb, int f, int k, int nt, bool commit, FoldState<HBM>& S,
+                           int& ug) {
+    const int lane = lane_id();
+    const FoldLanes fl(P);
+    const int G = P.G, D = P.D;
+    const int i = lane & 15;  // tile of the window (decision lanes)
+    const int row0 = lane & ~15;
+    const int h = hb * 4 + fl.hl;
+    const bool act = h < G && S.U[hb] < 0;
+    if (__ballot(act) == 0ull) return 0;
+    // probe dims of the committed accumulator, from lane 16*hl (cid 0) of the row
+    float Ap[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Ap[j] = __shfl(S.A[hb][j], row0);
+    // tile partials of the window, probe dims only
+    const bool tv = act && i < k;
+    const float* slot = P.ring + ((long long)grp * kRing + ((f + i) & (kRing - 1))) * P.slot;
+    const float mi = tv ? cld(slot + h) : kNegInf;
+    const float li = tv ? cld(slot + 16 + h) : 0.f;
+    const int ei = tv ? cld(reinterpret_cast<const int*>(slot) + 32) : 0;
+    float sa[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sa[j] = tv ? cld(slot + kSlotHeader + h * D + j) : 0.f;
+    // inclusive scan over the 16 lanes of the row
+    float sm = mi, sl = li;
+#pragma unroll
+    for (int dd = 1; dd < 16; dd <<= 1) {
+        const int src = row0 | ((i >= dd) ? i - dd : i);
+        float om = __shfl(sm, src), ol = __shfl(sl, src);
+        float oa[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oa[j] = __shfl(sa[j], src);
+        if (i >= dd) {
+            sm_merge(om, ol, oa, sm, sl, sa);  // earlier (+) mine
+            sm = om; sl = ol;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sa[j] = oa[j];
+        }
+    }
+    // seed with the committed state: S_i = S_in (+) scan_i
+    float rm = S.M[hb], rl = S.L[hb], ra[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ra[j] = Ap[j];
+    sm_merge(rm, rl, ra, sm, sl, sa);
+    // probe after tile f+i and its predecessor's
+    float x[8], xn2 = 0.f;
+    const float invL = 1.f / rl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        x[j] = ra[j] * invL;
+        xn2 += x[j] * x[j];
+    }
+    const float xn = sqrtf(xn2);
+    const int srcp = row0 | (i > 0 ? i - 1 : 0);
+    float ppn = __shfl(xn, srcp), pp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pp[j] = __shfl(x[j], srcp);
+    if (i == 0) {
+        ppn = S.pn[hb];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pp[j] = S.prev[hb][j];
+    }
+    bool pass = false;
+    if (tv && f + i >= 1) {
+        float ds, dd;
+        if (xn == 0.f || ppn == 0.f) {
+            ds = dd = INFINITY;
+        } else {
+            ds = fabsf(xn - ppn) / ppn;
+            // 1 - cos as half the squared distance of the unit vectors
+            const float ix = 1.f / xn, ip = 1.f / ppn;
+            float s2 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float dl = x[j] * ix - pp[j] * ip;
+                s2 += dl * dl;
+            }
+            dd = 0.5f * s2;
+        }
+        pass = P.art && ds < P.eps_scale && dd < P.eps_dir;
+    }
+    const unsigned pbits = (unsigned)(__ballot(pass) >> row0) & 0xffffu;
+    // the stop: streaks of passing tiles, tile 0 never compared
+    int st = S.streak[hb], istop = -1;
+    for (int q = 0; q < k; ++q) {
+        if (f + q >= 1) {
+            st = ((pbits >> q) & 1u) ? st + 1 : 0;
+            if (st >= P.patience) { istop = q; break; }
+        }
+    }
+    const bool stops = istop >= 0;
+    const bool last = f + k >= nt;  // no stop: every tile is used
+    const bool update = stops || commit;
+    const int ilast = stops ? istop : k - 1;
+    const int rowl = row0 | ilast;
+    const float M_last = __shfl(rm, rowl), L_last = __shfl(rl, rowl);
+    const float xn_last = __shfl(xn, rowl);
+    float x_last[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x_last[j] = __shfl(x[j], rowl);
+    const unsigned ebits = (unsigned)(__ballot(ei != 0 && i <= ilast) >> row0) & 0xffffu;
+    // accumulator over all dims with the tiles up to ilast: loads in two
+    // groups of eight tiles, each issued before it is used
+    float A[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) A[j] = S.A[hb][j];
+    if (update) {
+        const float w_in = S.M[hb] == kNegInf ? 0.f : expf(S.M[hb] - M_last);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) A[j] *= w_in;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        float wq[8], aq[8][8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+            const int q = 8 * half + qq;
+            const float mq = __shfl(mi, row0 | q);
+            const bool use = act && update && q <= ilast && fl.cvalid;
+            wq[qq] = use ? expf(mq - M_last) : 0.f;
+            const float* sq = P.ring + ((long long)grp * kRing + ((f + q) & (kRing - 1))) * P.slot +
+                              kSlotHeader + h * D + 8 * fl.cid;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) aq[qq][j] = use ? cld(sq + j) : 0.f;
+        }
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) A[j] = fmaf(wq[qq], aq[qq][j], A[j]);
+    }
+    const int err = S.err[hb] | (ebits != 0u);
+    const int U = stops ? f + istop + 1 : (commit && last ? nt : -1);
+    int still = 0;
+    if (act) {
+        if (U >= 0) {
+            write_head_out(P, grp, h, fl, A, L_last, err, U);
+            ug = max(ug, U);
+            S.U[hb] = U;
+        } else {
+            still = fl.cid == 0 ? 1 : 0;
+            if (commit) {
+                S.M[hb] = M_last; S.L[hb] = L_last; S.streak[hb] = st; S.err[hb] = err; S.pn[hb] = xn_last;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) { S.prev[hb][j] = x_last[j]; S.A[hb][j] = A[j]; }
+            }
+        }
+    }
+    return still;
+}
+
+// Try to take the group lock and fold ready tiles, in order, into the group's
+// running state.  Tiles are decided in windows of up to 16 that start at the
+// frontier, a multiple of 16: for each head, lanes 16*(head%4) + i hold tile
+// f+i's partial restricted to the probe dims; an inclusive online-softmax scan
+// over the 16 lanes, seeded with the head's committed state, gives the running
+// output after every tile of the window, hence every probe, both stability
+// metrics and the streak; the first tile whose streak reaches the patience is
+// the head's stop.  A head that stops gets its output from the committed state
+// and the tiles up to its stop.  The other heads' state (over all head dims) is
+// committed only for a complete window (or the last tiles of the group), so
+// every result is computed in the same order whatever the timing: the output
+// is deterministic.  An incomplete window is decided again only once at least
+// four more of its tiles are ready.  One lock holding folds up to 64 tiles.
+template <int HBM>
 __device__ void try_advance(const Params& P, int grp) {
     GroupCtl* C = P.ctl + grp;
     const int lane = lane_id();
     const FoldLanes fl(P);
     const int G = P.G, D = P.D;
+    const Deadline dl;
     for (;;) {
-        int got = 0;
-        if (lane == 0) got = cas_sc(&C->lock, 0, 1);
-        if (!__shfl(got, 0)) return;
-        int f = ld_rlx(&C->frontier);
-        const int nt = ld_rlx(&C->nt);
-        if (f >= ld_rlx(&C->bound)) {
-            // the group has finished: its heads are written, nothing more to fold
-            fence_rel();
-            if (lane == 0) st_sc(&C->lock, 0);
+        if (dl.passed()) {
+            if (lane == 0) give_up(P);
             return;
         }
-        float M[4], L[4], a8[4][8], prev[4][8], pn[4];
-        int streak[4], U[4], err[4];
+        int got = 0;
+        if (lane == 0) got = cas(&C->lock, 0, 1);
+        if (!bcast0(got)) return;
+        int f = cld(&C->frontier);
+        const int nt = cld(&C->nt);
+        if (f >= cld(&C->bound)) {
+            // the group has finished: its heads are written, nothing more to fold
+            drain();
+            if (lane == 0) cst(&C->lock, 0);
+            return;
+        }
+        const int seen = cld(&C->seen);
+        const int tau = f + lane;
+        const bool ok =
+            tau < nt && cld(&P.ring_tag[(long long)grp * kRing + (tau & (kRing - 1))]) == tau + 1;
+        const uint64_t msk = __ballot(ok);
+        const int kall = (~msk == 0ull) ? 64 : __builtin_ctzll(~msk);
+        int probe = f + kall;  // first tile whose arrival allows progress
+        const bool worth = kall >= 16 || (kall > 0 && f + kall >= nt) || kall >= seen + 4;
+        if (!worth) {
+            drain();
+            if (lane == 0) cst(&C->lock, 0);
+            drain();
+            int again = 0;
+            if (lane == 0 && kall >= 0)
+                again = probe < nt && cld(&P.ring_tag[(long long)grp * kRing + (probe & (kRing - 1))]) == probe + 1;
+            if (!bcast0(again)) return;
+            continue;
+        }
+        // committed state of the group's heads
+        FoldState<HBM> S;
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
+        for (int hb = 0; hb < HBM; ++hb) {
             const int h = hb * 4 + fl.hl;
-            U[hb] = 0;  // absent heads count as finished
-            M[hb] = kNegInf; L[hb] = 0.f; pn[hb] = 0.f; streak[hb] = 0; err[hb] = 0;
+            S.U[hb] = 0;
+            S.M[hb] = kNegInf; S.L[hb] = 0.f; S.pn[hb] = 0.f; S.streak[hb] = 0; S.err[hb] = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { a8[hb][i] = 0.f; prev[hb][i] = 0.f; }
+            for (int j = 0; j < 8; ++j) { S.prev[hb][j] = 0.f; S.A[hb][j] = 0.f; }
             if (hb < fl.HB && h < G) {
-                const HeadState& hs = P.heads[(long long)grp * G + h];
-                M[hb] = hs.M; L[hb] = hs.L; streak[hb] = hs.streak; U[hb] = hs.U; err[hb] = hs.err;
-                pn[hb] = hs.pn;
+                HeadState* hs = P.heads + (long long)grp * G + h;
+                S.U[hb] = cld(&hs->U);
+                S.M[hb] = cld(&hs->M); S.L[hb] = cld(&hs->L); S.streak[hb] = cld(&hs->streak);
+                S.err[hb] = cld(&hs->err); S.pn[hb] = cld(&hs->pn);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) prev[hb][i] = hs.prev[i];
-                if (fl.cvalid) {
-                    const float* a = P.acc + ((long long)grp * G + h) * D + 8 * fl.cid;
+                for (int j = 0; j < 8; ++j) S.prev[hb][j] = cld(&hs->prev[j]);
+                if (fl.cvalid && S.M[hb] != kNegInf) {
+                    const float* ap = P.acc + ((long long)grp * G + h) * D + 8 * fl.cid;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) a8[hb][i] = a[i];
+                    for (int j = 0; j < 8; ++j) S.A[hb][j] = cld(ap + j);
                 }
             }
         }
         bool finished = false;
-        for (;;) {
-            const int tau = f + lane;
-            const bool ok = tau < nt &&
-                            ld_rlx(&P.ring_tag[(long long)grp * kRing + (tau & (kRing - 1))]) == tau + 1;
-            const uint64_t m = __ballot(ok);
-            const int k = (~m == 0ull) ? 64 : __builtin_ctzll(~m);
-            if (k == 0) break;
-            fence_acq();
-            int folded = 0;
-            for (int i = 0; i < k; ++i) {
-                const int tt = f + i;
-                const float* slot = P.ring + ((long long)grp * kRing + (tt & (kRing - 1))) * P.slot;
-                const int serr = reinterpret_cast<const int*>(slot)[32];
-                int n_active = 0;
+        int ug = 0, new_seen = 0;
+        const int end = f + kall;  // tiles f .. end-1 are ready
+        while (f < end) {
+            const int fb = f;
+            const int kw = min(16, end - f);
+            const bool commit = kw == 16 || fb + kw >= nt;
+            int still = 0;
 #pragma unroll
-                for (int hb = 0; hb < 4; ++hb) {
-                    const int h = hb * 4 + fl.hl;
-                    const bool active = hb < fl.HB && h < G && U[hb] < 0;
-                    int stop = 0;
-                    if (active) {
-                        const float ml = slot[h], ll = slot[16 + h];
-                        const float mn = fmaxf(M[hb], ml);
-                        const float al = M[hb] == kNegInf ? 0.f : expf(M[hb] - mn);
-                        const float be = expf(ml - mn);
-                        L[hb] = al * L[hb] + be * ll;
-                        if (fl.cvalid) {
-                            const float* a = slot + kSlotHeader + h * D + 8 * fl.cid;
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) a8[hb][j] = al * a8[hb][j] + be * a[j];
-                        }
-                        M[hb] = mn;
-                        err[hb] |= serr;
-                        if (fl.cid == 0) {
-                            // probe: dims 0..7 of the normalised running output
-                            float x[8], xn2 = 0.f;
-                            const float invL = 1.f / L[hb];
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) {
-                                x[j] = a8[hb][j] * invL;
-                                xn2 += x[j] * x[j];
-                            }
-                            const float xn = sqrtf(xn2);
-                            if (tt >= 1) {
-                                float ds, dd;
-                                if (xn == 0.f || pn[hb] == 0.f) {
-                                    ds = dd = INFINITY;
-                                } else {
-                                    ds = fabsf(xn - pn[hb]) / pn[hb];
-                                    // 1 - cos as half the squared distance of the unit vectors
-                                    const float ix = 1.f / xn, ip = 1.f / pn[hb];
-                                    float s2 = 0.f;
-#pragma unroll
-                                    for (int j = 0; j < 8; ++j) {
-                                        const float dlt = x[j] * ix - prev[hb][j] * ip;
-                                        s2 += dlt * dlt;
-                                    }
-                                    dd = 0.5f * s2;
-                                }
-                                const bool pass = P.art && ds < P.eps_scale && dd < P.eps_dir;
-                                streak[hb] = pass ? streak[hb] + 1 : 0;
-                                stop = streak[hb] >= P.patience;
-                            }
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) prev[hb][j] = x[j];
-                            pn[hb] = xn;
-                        }
-                    }
-                    stop = __shfl(stop, lane & ~15);
-                    if (stop) {
-                        U[hb] = tt + 1;
-                        write_head_out(P, grp, h, fl, a8[hb], L[hb], err[hb], U[hb]);
-                    }
-                    n_active += (fl.cid == 0 && hb < fl.HB && h < G && U[hb] < 0) ? 1 : 0;
-                }
-                ++folded;
-                if (__ballot(n_active > 0) == 0ull) {
-                    finished = true;
-                    break;
-                }
+            for (int hb = 0; hb < HBM; ++hb)
+                if (hb < fl.HB) still += fold_window<HBM>(P, grp, hb, fb, kw, nt, commit, S, ug);
+            if (__ballot(still > 0) == 0ull) {
+                finished = true;
+                break;
             }
-            f += folded;
-            if (finished || f >= nt) break;
-        }
-        if (!finished && f >= nt) {
-            // no stop: every tile was used
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb) {
-                const int h = hb * 4 + fl.hl;
-                if (hb < fl.HB && h < G && U[hb] < 0) {
-                    U[hb] = nt;
-                    write_head_out(P, grp, h, fl, a8[hb], L[hb], err[hb], nt);
-                }
+            if (!commit) {
+                new_seen = kw;
+                break;
             }
-            finished = true;
+            f = fb + kw;
         }
+        probe = f + new_seen;
+        // write back the committed state of the heads still active
         if (!finished) {
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) {
+            for (int hb = 0; hb < HBM; ++hb) {
                 const int h = hb * 4 + fl.hl;
                 if (hb < fl.HB && h < G) {
-                    HeadState& hs = P.heads[(long long)grp * G + h];
+                    HeadState* hs = P.heads + (long long)grp * G + h;
                     if (fl.cid == 0) {
-                        hs.M = M[hb]; hs.L = L[hb]; hs.streak = streak[hb]; hs.U = U[hb];
-                        hs.err = err[hb]; hs.pn = pn[hb];
+                        cst(&hs->U, S.U[hb]);
+                        if (S.U[hb] < 0) {
+                            cst(&hs->M, S.M[hb]); cst(&hs->L, S.L[hb]); cst(&hs->streak, S.streak[hb]);
+                            cst(&hs->err, S.err[hb]); cst(&hs->pn, S.pn[hb]);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) hs.prev[i] = prev[hb][i];
+                            for (int j = 0; j < 8; ++j) cst(&hs->prev[j], S.prev[hb][j]);
+                        }
                     }
-                    if (fl.cvalid && U[hb] < 0) {
-                        float* a = P.acc + ((long long)grp * G + h) * D + 8 * fl.cid;
+                    if (fl.cvalid && S.U[hb] < 0) {
+                        float* ap = P.acc + ((long long)grp * G + h) * D + 8 * fl.cid;
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) a[i] = a8[hb][i];
+                        for (int j = 0; j < 8; ++j) cst(ap + j, S.A[hb][j]);
                     }
                 }
             }
         }
+        int ugw = ug;  // every head has stopped: the group used max(tiles_used) tiles
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ugw = max(ugw, __shfl_xor(ugw, o));
+        drain();
         if (lane == 0) {
-            st_rlx(&C->frontier, f);
-            if (finished) st_rlx(&C->bound, f);
+            cst(&C->frontier, finished ? ugw : f);
+            cst(&C->seen, new_seen);
+            if (finished) cst(&C->bound, ugw);
         }
-        fence_rel();
-        if (lane == 0) st_sc(&C->lock, 0);
+        drain();
+        if (lane == 0) cst(&C->lock, 0);
         if (finished) return;
         // a tile finished while we held the lock may have found it taken
+        drain();
         int again = 0;
         if (lane == 0)
-            again = f < nt && ld_sc(&P.ring_tag[(long long)grp * kRing + (f & (kRing - 1))]) == f + 1;
-        if (!__shfl(again, 0)) return;
+            again = probe < nt && cld(&P.ring_tag[(long long)grp * kRing + (probe & (kRing - 1))]) == probe + 1;
+        if (!bcast0(again)) return;
     }
 }
 
 // ------------------------------------------------------------------ tile scheduling
-// >= 0: the tile taken; -1: group exhausted; -2: ring full (try elsewhere)
+// Claims the next tile of group grp: >= 0 the tile; -1 the group has no tile
+// left; -2 its ring is full (claim elsewhere).  A tile t is only claimed while
+// t < frontier + kRing, so its ring slot (that of tile t - kRing, already
+// folded) is free from the moment it is claimed.
 __device__ int take_tile(const Params& P, int grp) {
-    int r = 0;
+    int r = -1;
     if (lane_id() == 0) {
         GroupCtl* C = P.ctl + grp;
-        const int bd = ld_rlx(&C->bound), nx = ld_rlx(&C->next);
-        if (nx >= bd) {
-            r = -1;
-        } else if (nx - ld_rlx(&C->frontier) >= kRing) {
+        for (int spin = 0; spin < 64; ++spin) {
+            const int nx = cld(&C->next);
+            if (nx >= cld(&C->bound)) { r = -1; break; }
+            if (nx - cld(&C->frontier) >= kRing) { r = -2; break; }
+            if (cas(&C->next, nx, nx + 1)) { r = nx; break; }
             r = -2;
-        } else {
-            const int t = faa(&C->next, 1);
-            r = t < ld_rlx(&C->bound) ? t : -1;
         }
     }
-    return __shfl(r, 0);
-}
-
-// Records that a wait ran past kSpinLimit; every worker then leaves.
-__device__ void give_up(const Params& P) { st_rlx(P.abort_flag, 1); }
-__device__ bool aborted(const Params& P) { return ld_rlx(P.abort_flag) != 0; }
-
-// Waits until slot t % kRing is free; false if the group stopped before tile t
-// (or the kernel is giving up).
-__device__ bool wait_slot(const Params& P, int grp, int t) {
-    int ok = 1;
-    if (lane_id() == 0) {
-        GroupCtl* C = P.ctl + grp;
-        for (int spin = 0;; ++spin) {
-            if (t >= ld_rlx(&C->bound)) { ok = 0; break; }
-            if (t - ld_acq(&C->frontier) < kRing) break;
-            if (spin >= kSpinLimit) { give_up(P); ok = 0; break; }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    return __shfl(ok, 0) != 0;
+    return bcast0(r);
 }
 
 // Next group with tiles left (and room in its ring), scanning forward from grp; -1 when none.
 __device__ int next_group(const Params& P, int grp) {
     const int lane = lane_id();
+    const Deadline dl;
     for (int spin = 0;; ++spin) {
-        if (spin >= kSpinLimit || aborted(P)) {
+        if (dl.passed() || aborted(P)) {
             if (lane == 0) give_up(P);
             return -1;
         }
@@ -572,7 +1364,7 @@ __device__ int next_group(const Params& P, int grp) {
             bool has = false, room = false;
             if (k < P.NG) {
                 GroupCtl* C = P.ctl + cand;
-                const int nx = ld_rlx(&C->next), bd = ld_rlx(&C->bound), fr = ld_rlx(&C->frontier);
+                const int nx = cld(&C->next), bd = cld(&C->bound), fr = cld(&C->frontier);
                 has = nx < bd;
                 room = nx - fr < kRing;
             }
@@ -581,8 +1373,57 @@ __device__ int next_group(const Params& P, int grp) {
             any_left |= __ballot(has) != 0ull;
         }
         if (!any_left) return -1;
-        __builtin_amdgcn_s_sleep(8);
+        // every group with tiles left has a full ring: back off (up to ~10 us)
+        for (int z = 0; z < (1 << min(spin, 5)); ++z) __builtin_amdgcn_s_sleep(127);
     }
+}
+
+// Claims a tile, moving on to other groups when grp has none; false when no
+// group has tiles left.  May wait for ring space, so a wave calls it only
+// while it holds no unpublished tile (an unpublished tile can be the one its
+// group's frontier waits for).
+__device__ bool claim(const Params& P, int& grp, int& t) {
+    const Deadline dl;
+    for (;;) {
+        if (aborted(P)) return false;
+        if (dl.passed()) {
+            if (lane_id() == 0) give_up(P);
+            return false;
+        }
+        t = take_tile(P, grp);
+        if (t >= 0) return true;
+        grp = next_group(P, grp);
+        if (grp < 0) return false;
+    }
+}
+
+// One attempt, never waiting: a tile of grp, else of the first group found
+// with tiles and ring space.  Used to claim ahead while holding a tile.
+__device__ bool try_claim(const Params& P, int& grp, int& t) {
+    t = take_tile(P, grp);
+    if (t >= 0) return true;
+    const int lane = lane_id();
+    for (int base = 0; base < P.NG; base += 64) {
+        const int k = base + lane;
+        const int cand = (grp + 1 + k) % P.NG;
+        bool ok = false;
+        if (k < P.NG) {
+            GroupCtl* C = P.ctl + cand;
+            const int nx = cld(&C->next);
+            ok = nx < cld(&C->bound) && nx - cld(&C->frontier) < kRing;
+        }
+        const uint64_t m = __ballot(ok);
+        if (m) {
+            const int g2 = (grp + 1 + base + __builtin_ctzll(m)) % P.NG;
+            t = take_tile(P, g2);
+            if (t >= 0) {
+                grp = g2;
+                return true;
+            }
+            return false;
+        }
+    }
+    return false;
 }
 
 // ------------------------------------------------------------------ kernels
@@ -595,7 +1436,7 @@ __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
     const int nt = (bad || n == 0) ? 0 : (n + P.T - 1) / P.T;
     GroupCtl* C = P.ctl + grp;
     if (tid == 0) {
-        C->next = 0; C->lock = 0; C->frontier = 0; C->bound = nt; C->nt = nt; C->n = n;
+        C->next = 0; C->lock = 0; C->frontier = 0; C->bound = nt; C->nt = nt; C->n = n; C->seen = 0;
         if (grp == 0) *P.abort_flag = 0;
     }
     for (int h = tid; h < P.G; h += blockDim.x) {
@@ -603,7 +1444,6 @@ __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
         hs.M = kNegInf; hs.L = 0.f; hs.streak = 0; hs.U = nt > 0 ? -1 : 0; hs.err = 0; hs.pn = 0.f;
         for (int i = 0; i < 8; ++i) hs.prev[i] = 0.f;
     }
-    for (int i = tid; i < P.G * P.D; i += blockDim.x) P.acc[(long long)grp * P.G * P.D + i] = 0.f;
     for (int i = tid; i < kRing; i += blockDim.x) P.ring_tag[(long long)grp * kRing + i] = 0;
     if (P.vskip)
         for (int i = tid; i < P.nt_max; i += blockDim.x) P.vmax_tag[(long long)grp * P.nt_max + i] = 0;
@@ -615,36 +1455,33 @@ __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
     for (int h = tid; h < P.G; h += blockDim.x) P.tiles_used[row0 + h] = nt > 0 ? -2 : (bad ? -1 : 0);
 }
 
-template <int D, int KV>
+__device__ __forceinline__ void count_stats(const Params& P, unsigned long long tiles, unsigned long long rows) {
+    if (P.stats && lane_id() == 0) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 0), tiles);
+        atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 1), rows);
+    }
+}
+
+// One tile at a time (generic and matrix-core tiles; the V skip needs this path).
+template <class Tile>
 __global__ __launch_bounds__(256) void art_persistent_kernel(Params P) {
-    using Tile = GenericTile<D, KV>;
     extern __shared__ float lds[];
     const int wv = wave_id(), lane = lane_id();
-    const int per_wave = P.G * D + P.G * P.T;
-    float* q_lds = lds + wv * per_wave;
-    float* p_lds = q_lds + P.G * D;
+    float* lds_wave = lds + wv * Tile::lds_floats(P);
     const int worker = blockIdx.x * kWavesPerWG + wv;
     if (worker >= P.workers) return;
     int grp = worker % P.NG;
     int qgrp = -1;
-    for (;;) {
-        if (aborted(P)) break;
-        const int t = take_tile(P, grp);
-        if (t < 0) {
-            grp = next_group(P, grp);
-            if (grp < 0) break;
-            continue;
-        }
+    Tile tile;
+    int t;
+    while (claim(P, grp, t)) {
         const int b = grp / P.Hkv, g = grp % P.Hkv;
         if (grp != qgrp) {
-            Tile::load_q(P, b, g, q_lds);
+            tile.load_q(P, b, g, lds_wave);
             qgrp = grp;
         }
-        if (!wait_slot(P, grp, t)) continue;
         GroupCtl* C = P.ctl + grp;
-        const int n = ld_rlx(&C->n);
-        float m_loc[kMaxG], l_loc[kMaxG], acc[kMaxG][Tile::APL];
-        int err = 0, kept = 0;
+        const int n = P.ctx_lens[b];
         const int vbase = grp * P.nt_max;
         auto hook = [&](const float (&ml)[kMaxG], float (&Mt)[kMaxG]) -> bool {
 #pragma unroll
@@ -655,56 +1492,103 @@ __global__ __launch_bounds__(256) void art_persistent_kernel(Params P) {
             if (lane == 0)
 #pragma unroll
                 for (int h = 0; h < kMaxG; ++h)
-                    if (h < P.G) vm[h] = ml[h];
-            fence_rel();
-            if (lane == 0) st_rlx(&P.vmax_tag[vbase + t], 1);
+                    if (h < P.G) cst(vm + h, ml[h]);
+            drain();
+            if (lane == 0) cst(&P.vmax_tag[vbase + t], 1);
+            const Deadline dl;
             for (int base = 0; base < t; base += 64) {
                 const int tau = base + lane;
                 const bool need = tau < t;
-                for (int spin = 0;; ++spin) {
-                    const bool ready = !need || ld_rlx(&P.vmax_tag[vbase + tau]) != 0;
+                for (;;) {
+                    const bool ready = !need || cld(&P.vmax_tag[vbase + tau]) != 0;
                     if (__ballot(!ready) == 0ull) break;
-                    if (ld_rlx(&C->bound) <= t) return false;
-                    if (spin >= kSpinLimit) {
+                    if (cld(&C->bound) <= t) return false;
+                    if (dl.passed()) {
                         if (lane == 0) give_up(P);
                         return false;
                     }
                     __builtin_amdgcn_s_sleep(1);
                 }
-                fence_acq();
                 const float* src = P.vmax + ((long long)vbase + tau) * 16;
 #pragma unroll
                 for (int h = 0; h < kMaxG; ++h) {
-                    if (h < P.G) Mt[h] = fmaxf(Mt[h], wave_max(need ? src[h] : kNegInf));
+                    if (h < P.G) Mt[h] = fmaxf(Mt[h], wave_max(need ? cld(src + h) : kNegInf));
                 }
             }
             return true;
         };
-        if (!Tile::compute(P, b, g, n, t, q_lds, p_lds, m_loc, l_loc, acc, err, kept, hook)) continue;
-        float* slot = P.ring + ((long long)grp * kRing + (t & (kRing - 1))) * P.slot;
-        Tile::store_partial(P, slot, m_loc, l_loc, acc, err, kept);
-        fence_rel();
-        if (lane == 0) {
-            st_rlx(&P.ring_tag[(long long)grp * kRing + (t & (kRing - 1))], t + 1);
-            if (P.stats) {
-                atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 0), 1ull);
-                atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 1), (unsigned long long)kept);
-            }
-        }
-        try_advance(P, grp);
+        typename Tile::Out o;
+        if (!tile.compute(P, b, g, n, t, hook, o)) continue;
+        const int token = publish_data(P, grp, t, o);
+        publish_flag(P, grp, t, token);
+        count_stats(P, 1ull, (unsigned long long)o.kept);
+        try_advance<Tile::HBM>(P, grp);
     }
 }
 
-template <int D, int KV>
+// Streamed matrix-core tiles: the next tile is claimed, and its first units
+// loaded, while the current one is computed.
+template <class S>
+__global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P) {
+    extern __shared__ float lds[];
+    const int wv = wave_id();
+    const int worker = blockIdx.x * kWavesPerWG + wv;
+    if (worker >= P.workers) return;
+    S st;
+    st.init(lds + wv * S::lds_floats(P));
+    int grp = worker % P.NG;
+    int tc, tn;
+    typename S::TileRef C, N;
+    bool haveC = claim(P, grp, tc);  // holds nothing yet: may wait
+    if (haveC) {
+        S::resolve(P, grp, tc, C);
+        st.template issue<0>(P, C, 0);
+        st.template issue<1>(P, C, 1);
+    }
+    int qgrp = -1;
+    while (haveC) {
+        if (C.grp != qgrp) {
+            st.load_q(P, C.grp);
+            qgrp = C.grp;
+        }
+        // claim the next tile ahead, without waiting (C is not published yet)
+        const bool haveN = try_claim(P, grp, tn);
+        if (haveN) S::resolve(P, grp, tn, N);
+        st.template consume<0>(P, C, 0, true);
+        if (haveN) st.template issue<0>(P, N, 0);
+        st.template consume<1>(P, C, 1, haveN);
+        if (haveN) st.template issue<1>(P, N, 1);
+        typename S::Out o;
+        st.flush(P, o);
+        o.err = C.err;
+        const int rows = min(S::T, max(0, C.n - C.t * S::T));
+        o.kept = rows;
+        const int token = publish_data(P, C.grp, C.t, o);
+        publish_flag(P, C.grp, C.t, token);
+        count_stats(P, 1ull, (unsigned long long)rows);
+        try_advance<S::HBM>(P, C.grp);
+        if (haveN) {
+            C = N;
+        } else {
+            haveC = claim(P, grp, tc);  // holds nothing now: may wait
+            if (haveC) {
+                S::resolve(P, grp, tc, C);
+                st.template issue<0>(P, C, 0);
+                st.template issue<1>(P, C, 1);
+            }
+        }
+    }
+}
+
+// Full mode, one tile at a time: split sp of group grp covers a fixed tile range.
+template <class Tile>
 __global__ __launch_bounds__(256) void art_full_kernel(Params P) {
-    using Tile = GenericTile<D, KV>;
     extern __shared__ float lds[];
     const int wv = wave_id(), lane = lane_id();
-    const int per_wave = P.G * D + P.G * P.T;
-    float* q_lds = lds + wv * per_wave;
-    float* p_lds = q_lds + P.G * D;
+    float* lds_wave = lds + wv * Tile::lds_floats(P);
     const int worker = blockIdx.x * kWavesPerWG + wv;
     if (worker >= P.NG * P.splits) return;
+    const FoldLanes fl(P);
     const int grp = worker / P.splits, sp = worker % P.splits;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
     const int n = P.ctx_lens[b];
@@ -712,43 +1596,133 @@ __global__ __launch_bounds__(256) void art_full_kernel(Params P) {
     const int nt = bad ? 0 : (n + P.T - 1) / P.T;
     const int t0 = sp * P.tiles_per_split;
     const int t1 = min(t0 + P.tiles_per_split, nt);
-    float M[kMaxG], L[kMaxG], A[kMaxG][Tile::APL];
+    constexpr int HBM = Tile::HBM;
+    float M[HBM], L[HBM], A[HBM][8];
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-        M[h] = kNegInf; L[h] = 0.f;
+    for (int hb = 0; hb < HBM; ++hb) {
+        M[hb] = kNegInf; L[hb] = 0.f;
 #pragma unroll
-        for (int i = 0; i < Tile::APL; ++i) A[h][i] = 0.f;
+        for (int j = 0; j < 8; ++j) A[hb][j] = 0.f;
     }
     int err = 0, kept_total = 0;
-    if (t0 < t1) Tile::load_q(P, b, g, q_lds);
+    Tile tile;
+    if (t0 < t1) tile.load_q(P, b, g, lds_wave);
     auto hook = [&](const float (&ml)[kMaxG], float (&Mt)[kMaxG]) -> bool {
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h) Mt[h] = ml[h];
         return true;
     };
     for (int t = t0; t < t1; ++t) {
-        float ml[kMaxG], ll[kMaxG], a[kMaxG][Tile::APL];
-        int kept = 0;
-        Tile::compute(P, b, g, n, t, q_lds, p_lds, ml, ll, a, err, kept, hook);
-        kept_total += kept;
+        typename Tile::Out o;
+        tile.compute(P, b, g, n, t, hook, o);
+        err |= o.err;
+        kept_total += o.kept;
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
-            if (h < P.G) {
-                const float mn = fmaxf(M[h], ml[h]);
-                const float al = M[h] == kNegInf ? 0.f : expf(M[h] - mn);
-                const float be = expf(ml[h] - mn);
-                L[h] = al * L[h] + be * ll[h];
+        for (int hb = 0; hb < HBM; ++hb) {
+            const int h = hb * 4 + fl.hl;
+            // this lane's head: select its tile max and sum from the uniform arrays
+            float ml = kNegInf, ll = 0.f;
 #pragma unroll
-                for (int i = 0; i < Tile::APL; ++i) A[h][i] = al * A[h][i] + be * a[h][i];
-                M[h] = mn;
+            for (int hh = 0; hh < kMaxG; ++hh)
+                if (hh == h) { ml = o.m[hh]; ll = o.l[hh]; }
+            if (hb < fl.HB && h < P.G) {
+                const float mn = fmaxf(M[hb], ml);
+                const bool first = M[hb] == kNegInf;
+                const float al = first ? 0.f : expf(M[hb] - mn);
+                const float be = expf(ml - mn);
+                L[hb] = al * L[hb] + be * ll;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    A[hb][j] = first ? be * o.a[hb][j] : al * A[hb][j] + be * o.a[hb][j];
+                M[hb] = mn;
             }
         }
     }
     float* slot = P.partials + ((long long)grp * P.splits + sp) * P.slot;
-    Tile::store_partial(P, slot, M, L, A, err, kept_total);
-    if (P.stats && lane == 0 && t1 > t0) {
-        atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 0), (unsigned long long)(t1 - t0));
-        atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 1), (unsigned long long)kept_total);
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        if (hb < fl.HB && h < P.G) {
+            if (fl.cid == 0) {
+                slot[h] = M[hb];
+                slot[16 + h] = L[hb];
+            }
+            if (fl.cvalid) {
+                float* a = slot + kSlotHeader + h * P.D + 8 * fl.cid;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a[j] = A[hb][j];
+            }
+        }
+    }
+    if (lane == 0) {
+        reinterpret_cast<int*>(slot)[32] = err;
+        reinterpret_cast<int*>(slot)[33] = kept_total;
+    }
+    if (t1 > t0) count_stats(P, (unsigned long long)(t1 - t0), (unsigned long long)kept_total);
+}
+
+// Full mode, streamed: one running state over the whole split range.
+template <class S>
+__global__ __launch_bounds__(256, S::MIN_WAVES) void art_full_stream_kernel(Params P) {
+    extern __shared__ float lds[];
+    const int wv = wave_id(), lane = lane_id();
+    const int worker = blockIdx.x * kWavesPerWG + wv;
+    if (worker >= P.NG * P.splits) return;
+    const FoldLanes fl(P);
+    const int grp = worker / P.splits, sp = worker % P.splits;
+    const int b = grp / P.Hkv;
+    const int n = P.ctx_lens[b];
+    const bool bad = n < 0 || n > P.cap;
+    const int nt = bad ? 0 : (n + S::T - 1) / S::T;
+    const int t0 = sp * P.tiles_per_split;
+    const int t1 = min(t0 + P.tiles_per_split, nt);
+    S st;
+    st.init(lds + wv * S::lds_floats(P));
+    int err = 0;
+    typename S::Out o;
+    if (t0 < t1) {
+        st.load_q(P, grp);
+        typename S::TileRef C, N;
+        S::resolve(P, grp, t0, C);
+        st.template issue<0>(P, C, 0);
+        st.template issue<1>(P, C, 1);
+        for (int t = t0; t < t1; ++t) {
+            const bool more = t + 1 < t1;
+            if (more) S::resolve(P, grp, t + 1, N);
+            err |= C.err;
+            st.template consume<0>(P, C, 0, true);
+            if (more) st.template issue<0>(P, N, 0);
+            st.template consume<1>(P, C, 1, more);
+            if (more) st.template issue<1>(P, N, 1);
+            C = N;
+        }
+    }
+    st.flush(P, o);
+    float* slot = P.partials + ((long long)grp * P.splits + sp) * P.slot;
+#pragma unroll
+    for (int hb = 0; hb < S::HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        if (hb < fl.HB && h < P.G && fl.cvalid) {
+            float* a = slot + kSlotHeader + h * P.D + 8 * fl.cid;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = o.a[hb][j];
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            if (h < P.G) {
+                slot[h] = o.m[h];
+                slot[16 + h] = o.l[h];
+            }
+        }
+        const int rows = t1 > t0 ? min(n, t1 * S::T) - t0 * S::T : 0;
+        reinterpret_cast<int*>(slot)[32] = err;
+        reinterpret_cast<int*>(slot)[33] = rows;
+        if (t1 > t0 && P.stats) {
+            atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 0), (unsigned long long)(t1 - t0));
+            atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 1), (unsigned long long)rows);
+        }
     }
 }
 
@@ -774,13 +1748,14 @@ __global__ __launch_bounds__(64) void art_combine_kernel(Params P) {
             if (!(ll > 0.f)) continue;  // empty split
             const float ml = slot[h];
             const float mn = fmaxf(M, ml);
-            const float al = M == kNegInf ? 0.f : expf(M - mn);
+            const bool first = M == kNegInf;
+            const float al = first ? 0.f : expf(M - mn);
             const float be = expf(ml - mn);
             L = al * L + be * ll;
             if (fl.cvalid) {
                 const float* a = slot + kSlotHeader + h * D + 8 * fl.cid;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) a8[j] = al * a8[j] + be * a[j];
+                for (int j = 0; j < 8; ++j) a8[j] = first ? be * a[j] : al * a8[j] + be * a[j];
             }
             M = mn;
         }
@@ -795,52 +1770,81 @@ __global__ __launch_bounds__(64) void art_combine_kernel(Params P) {
     }
 }
 
-template <int D, int KV>
-int launch_art_t(const Params& p, hipStream_t s) {
+// ------------------------------------------------------------------ launches
+template <class K, class Tile>
+int launch_persistent(const Params& p, hipStream_t s, K kernel) {
     hipLaunchKernelGGL(art_init_kernel, dim3(p.NG), dim3(256), 0, s, p);
-    const size_t lds = (size_t)kWavesPerWG * (p.G * D + p.G * p.T) * sizeof(float);
+    const size_t lds = (size_t)kWavesPerWG * Tile::lds_floats(p) * sizeof(float);
     const int blocks = (p.workers + kWavesPerWG - 1) / kWavesPerWG;
-    hipLaunchKernelGGL((art_persistent_kernel<D, KV>), dim3(blocks), dim3(256), lds, s, p);
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), lds, s, p);
     return (int)hipGetLastError();
 }
 
-template <int D, int KV>
-int launch_full_t(const Params& p, hipStream_t s) {
-    const size_t lds = (size_t)kWavesPerWG * (p.G * D + p.G * p.T) * sizeof(float);
+template <class K, class Tile>
+int launch_split(const Params& p, hipStream_t s, K kernel) {
+    const size_t lds = (size_t)kWavesPerWG * Tile::lds_floats(p) * sizeof(float);
     const int blocks = (p.NG * p.splits + kWavesPerWG - 1) / kWavesPerWG;
-    hipLaunchKernelGGL((art_full_kernel<D, KV>), dim3(blocks), dim3(256), lds, s, p);
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), lds, s, p);
     hipLaunchKernelGGL(art_combine_kernel, dim3(p.NG), dim3(64), 0, s, p);
     return (int)hipGetLastError();
+}
+
+// Matrix-core tiles serve bf16/int8 caches with head dim 128, bf16 queries,
+// at most 8 query heads per KV head and tiles of 16, 32 or 64 tokens; 64-token
+// tiles without the V skip are streamed.
+bool fast_path(const Params& p) {
+    return p.D == 128 && p.q_dtype == ART_BF16 && (p.kv_dtype == ART_BF16 || p.kv_dtype == ART_I8) &&
+           p.G <= 8 && (p.T == 16 || p.T == 32 || p.T == 64);
+}
+bool stream_path(const Params& p) { return fast_path(p) && p.T == 64 && !p.vskip; }
+
+template <class Tile>
+int run_tile(const Params& p, hipStream_t s, bool art) {
+    if (art) return launch_persistent<decltype(&art_persistent_kernel<Tile>), Tile>(p, s, &art_persistent_kernel<Tile>);
+    return launch_split<decltype(&art_full_kernel<Tile>), Tile>(p, s, &art_full_kernel<Tile>);
+}
+
+template <class S>
+int run_stream(const Params& p, hipStream_t s, bool art) {
+    if (art) return launch_persistent<decltype(&art_stream_kernel<S>), S>(p, s, &art_stream_kernel<S>);
+    return launch_split<decltype(&art_full_stream_kernel<S>), S>(p, s, &art_full_stream_kernel<S>);
+}
+
+template <int KV, int GMAX>
+int run_fast(const Params& p, hipStream_t s, bool art) {
+    if (stream_path(p)) return run_stream<Stream<KV, GMAX>>(p, s, art);
+    if (p.T == 64) return run_tile<FastTile<KV, 4, GMAX>>(p, s, art);
+    if (p.T == 32) return run_tile<FastTile<KV, 2, GMAX>>(p, s, art);
+    return run_tile<FastTile<KV, 1, GMAX>>(p, s, art);
+}
+
+int run(const Params& p, hipStream_t s, bool art) {
+    if (fast_path(p)) {
+        if (p.kv_dtype == ART_BF16) return p.G <= 4 ? run_fast<ART_BF16, 4>(p, s, art) : run_fast<ART_BF16, 8>(p, s, art);
+        return p.G <= 4 ? run_fast<ART_I8, 4>(p, s, art) : run_fast<ART_I8, 8>(p, s, art);
+    }
+    if (p.D == 64) {
+        if (p.kv_dtype == ART_F32) return run_tile<GenericTile<64, ART_F32>>(p, s, art);
+        if (p.kv_dtype == ART_BF16) return run_tile<GenericTile<64, ART_BF16>>(p, s, art);
+        return run_tile<GenericTile<64, ART_I8>>(p, s, art);
+    }
+    if (p.kv_dtype == ART_F32) return run_tile<GenericTile<128, ART_F32>>(p, s, art);
+    if (p.kv_dtype == ART_BF16) return run_tile<GenericTile<128, ART_BF16>>(p, s, art);
+    return run_tile<GenericTile<128, ART_I8>>(p, s, art);
 }
 
 }  // namespace
 
 int launch_art(const Params& p, void* stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (p.NG == 0) return 0;
-    if (p.D == 64) {
-        if (p.kv_dtype == ART_F32) return launch_art_t<64, ART_F32>(p, s);
-        if (p.kv_dtype == ART_BF16) return launch_art_t<64, ART_BF16>(p, s);
-        return launch_art_t<64, ART_I8>(p, s);
-    }
-    if (p.kv_dtype == ART_F32) return launch_art_t<128, ART_F32>(p, s);
-    if (p.kv_dtype == ART_BF16) return launch_art_t<128, ART_BF16>(p, s);
-    return launch_art_t<128, ART_I8>(p, s);
+    return run(p, static_cast<hipStream_t>(stream), true);
 }
 
 int launch_full(const Params& p, void* stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (p.NG == 0) return 0;
-    if (p.D == 64) {
-        if (p.kv_dtype == ART_F32) return launch_full_t<64, ART_F32>(p, s);
-        if (p.kv_dtype == ART_BF16) return launch_full_t<64, ART_BF16>(p, s);
-        return launch_full_t<64, ART_I8>(p, s);
-    }
-    if (p.kv_dtype == ART_F32) return launch_full_t<128, ART_F32>(p, s);
-    if (p.kv_dtype == ART_BF16) return launch_full_t<128, ART_BF16>(p, s);
-    return launch_full_t<128, ART_I8>(p, s);
+    return run(p, static_cast<hipStream_t>(stream), false);
 }
 
 }  // namespace art
