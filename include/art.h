@@ -79,7 +79,7 @@ typedef struct {
                                     [0] K tiles loaded, [1] V rows loaded,
                                     [2] tiles loaded after their group had stopped,
                                     [3] reserved                                      */
-    int32_t max_workers;         /* 0 = library default; else cap on worker waves     */
+    int32_t max_workers;         /* 0 = library default; > 0: work-sharing engine     */
 } art_desc;
 
 /*

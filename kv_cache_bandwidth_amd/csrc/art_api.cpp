@@ -31,15 +31,6 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool finite_nonneg(float x) { return std::isfinite(x) && x >= 0.f; }
 
-int device_cus() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256;
-    return cus;
-}
-
 // Validates desc/tile/thresholds and fills the shape part of Params.
 art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, art::Params& p) {
     if (!d) return fail(ART_E_NULL, "desc is NULL");
@@ -115,8 +106,6 @@ Layout workspace_layout(const Params& p) {
     const size_t NG = (size_t)p.NG, G = (size_t)p.G;
     L.abort_flag = o; o = align256(o + sizeof(int));
     L.ctl = o; o = align256(o + NG * sizeof(GroupCtl));
-    L.heads = o; o = align256(o + NG * G * sizeof(HeadState));
-    L.acc = o; o = align256(o + NG * G * p.D * sizeof(float));
     L.ring_tag = o; o = align256(o + NG * kRing * sizeof(int));
     L.ring = o; o = align256(o + NG * kRing * (size_t)p.slot * sizeof(float));
     L.vmax_tag = o; o = align256(o + NG * (size_t)p.nt_max * sizeof(int));
@@ -185,8 +174,11 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     p.vs = static_cast<const uint16_t*>(desc->v_scale);
     p.block_table = block_table; p.ctx_lens = ctx_lens; p.out = out; p.tiles_used = tiles_used;
     p.stats = reinterpret_cast<long long*>(desc->stats);
-    // persistent grid: as many worker waves as fit at once (two work-groups per CU)
-    long long workers = desc->max_workers ? desc->max_workers : (long long)device_cus() * 8;
+    // persistent grid (ART mode): one decider wave per group, up to
+    // kMaxDeciders, and the requested number of tile workers (0: as many as
+    // are resident alongside the deciders, settled at launch)
+    p.deciders = p.NG < art::kMaxDeciders ? p.NG : art::kMaxDeciders;
+    long long workers = desc->max_workers;
     const long long tiles = (long long)p.NG * p.nt_max;
     if (workers > tiles) workers = tiles > 0 ? tiles : 1;
     p.workers = (int)workers;
@@ -194,8 +186,6 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     char* ws = static_cast<char*>(desc->workspace);
     p.abort_flag = reinterpret_cast<int*>(ws + L.abort_flag);
     p.ctl = reinterpret_cast<art::GroupCtl*>(ws + L.ctl);
-    p.heads = reinterpret_cast<art::HeadState*>(ws + L.heads);
-    p.acc = reinterpret_cast<float*>(ws + L.acc);
     p.ring_tag = reinterpret_cast<int*>(ws + L.ring_tag);
     p.ring = reinterpret_cast<float*>(ws + L.ring);
     p.vmax_tag = reinterpret_cast<int*>(ws + L.vmax_tag);

@@ -11,36 +11,23 @@ namespace art {
 
 constexpr int kRing = 128;        // ring slots per group (tiles in flight ahead of the frontier)
 constexpr int kMaxG = 16;         // query heads per KV head
-constexpr int kWavesPerWG = 4;    // independent worker waves per work-group
+constexpr int kWavesPerWG = 4;    // independent waves per work-group
+constexpr int kMaxDeciders = 512; // decider waves at most (one per group up to this many groups)
 constexpr unsigned long long kWaitTicks = 50000000ull;  // 0.5 s of the 100 MHz device clock:
                                                       // longest any wait may last before the kernel gives up
 constexpr int kSlotHeader = 48;   // floats before the accumulator block of a partial:
                                   // [0,16) tile max per head, [16,32) tile sum per head,
                                   // [32] error flag (as int), [33] V rows kept (as int)
 
-// Per-group control block; each field group on its own 128-byte line.
+// Per-group control block; the allocation counter on its own 128-byte line.
 struct alignas(128) GroupCtl {
     int next;          // tile allocation counter (atomic)
     int pad0[31];
-    int lock;          // frontier lock (atomic)
-    int frontier;      // tiles folded into the group's running state
+    int frontier;      // tiles folded into the group's running state (written by its decider)
     int bound;         // tiles that may still be allocated: ceil(n/T), lowered once every head stopped
     int nt;            // tiles of the group
     int n;             // ctx_len of the row
-    int seen;          // tiles past the frontier already decided (incomplete window)
-    int pad1[26];
-};
-
-// Running state of one query head, owned by whoever holds the group lock.
-struct alignas(16) HeadState {
-    float M;       // running max score
-    float L;       // running softmax sum
-    int streak;    // consecutive passing tiles
-    int U;         // tiles_used once finished, -1 while active
-    int err;       // a visited tile had an invalid block id
-    float pn;      // norm of the previous probe
-    int pad[2];
-    float prev[8]; // previous probe x(t-1)
+    int pad1[28];
 };
 
 struct Params {
@@ -70,8 +57,6 @@ struct Params {
     // workspace regions (device)
     int* abort_flag;    // set when a wait outlasted kWaitTicks: workers exit, heads stay unfinished
     GroupCtl* ctl;
-    HeadState* heads;   // [NG][G]
-    float* acc;         // [NG][G][D]
     int* ring_tag;      // [NG][kRing]
     float* ring;        // [NG][kRing][slot]
     int* vmax_tag;      // [NG][nt_max]
@@ -79,14 +64,15 @@ struct Params {
     float* partials;    // [NG][splits][slot]
     int slot;           // floats per partial: kSlotHeader + G*D
     // launch
-    int workers;        // worker waves of the persistent kernel
+    int deciders;       // decider waves of the persistent kernel (each owns whole groups)
+    int workers;        // tile worker waves of the persistent kernel
     int splits;         // full mode: workers per group
     int tiles_per_split;
 };
 
 // Workspace layout for a Params (offsets in bytes, all 256-byte aligned).
 struct Layout {
-    size_t abort_flag, ctl, heads, acc, ring_tag, ring, vmax_tag, vmax, partials, total;
+    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, total;
 };
 Layout workspace_layout(const Params& p);
 

@@ -95,6 +95,15 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // ------------------------------------------------------------------ wave reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -193,6 +202,8 @@ struct TileOutT {
     float m[kMaxG];   // tile max per head (wave-uniform)
     float l[kMaxG];   // tile softmax sum per head, relative to m (wave-uniform)
     float a[HBM][8];  // V accumulator, fold mapping (head blocks 0..HBM-1)
+    float mf[HBM];    // streamed tiles: m of the lane's head in the fold mapping
+    float lf[HBM];    // streamed tiles: l of the lane's head in the fold mapping
     int err;          // an invalid block id was met
     int kept;         // V rows loaded
 };
@@ -228,7 +239,7 @@ struct GenericTile {
     float* q_lds;
     float* p_lds;
 
-    __device__ void load_q(const Params& P, int b, int g, float* lds) {
+    __device__ __forceinline__ void load_q(const Params& P, int b, int g, float* lds) {
         q_lds = lds;
         p_lds = lds + P.G * D;
         const int lane = lane_id();
@@ -241,7 +252,7 @@ struct GenericTile {
     }
 
     template <class Hook>
-    __device__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
+    __device__ __forceinline__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
         const int lane = lane_id();
         const int G = P.G, T = P.T;
         const int j0 = t * T;
@@ -393,7 +404,7 @@ struct FastTile {
     bf16x8 qB[4];
     float* lds;
 
-    __device__ void load_q(const Params& P, int b, int g, float* lds_wave) {
+    __device__ __forceinline__ void load_q(const Params& P, int b, int g, float* lds_wave) {
         lds = lds_wave;
         const int lane = lane_id(), h = lane & 15, kg = lane >> 4;
         const uint16_t* q = static_cast<const uint16_t*>(P.q);
@@ -413,7 +424,7 @@ struct FastTile {
     }
 
     template <class Hook>
-    __device__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
+    __device__ __forceinline__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         const int G = P.G;
         const int tok0 = t * T;
@@ -653,6 +664,8 @@ struct Stream {
     static constexpr int OPS = UP * (4 + KDMA + (KV == ART_I8 ? 5 : 0));
     // resident waves per SIMD the register budget is cut for (two when it fits without heavy spills)
     static constexpr int MIN_WAVES = GMAX == 4 ? 2 : 1;
+    // waves of a team (one work-group, one CU): as many as are resident on a CU
+    static constexpr int TEAM = 4 * MIN_WAVES;
     using Out = TileOutT<HBM>;
     typedef typename std::conditional<KV == ART_I8, u2, u4>::type vvec;
 
@@ -674,13 +687,13 @@ struct Stream {
     char* kl;                    // LDS: [2 buffers][UP pages][PAGEB]
     float* pl;                   // LDS: [32 tokens][GMAX heads]
 
-    __device__ void init(float* lds_wave) {
+    __device__ __forceinline__ void init(float* lds_wave) {
         kl = reinterpret_cast<char*>(lds_wave);
         pl = lds_wave + (2 * UP * PAGEB) / 4;
         reset();
     }
 
-    __device__ void reset() {
+    __device__ __forceinline__ void reset() {
         m_run = kNegInf;
         l_run = 0.f;
 #pragma unroll
@@ -689,7 +702,7 @@ struct Stream {
             for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
     }
 
-    __device__ void load_q(const Params& P, int grp) {
+    __device__ __forceinline__ void load_q(const Params& P, int grp) {
         const int b = grp / P.Hkv, g = grp % P.Hkv;
         const int lane = lane_id(), h = lane & 15, kg = lane >> 4;
         const uint16_t* q = static_cast<const uint16_t*>(P.q);
@@ -703,7 +716,7 @@ struct Stream {
         }
     }
 
-    __device__ static void resolve(const Params& P, int grp, int t, TileRef& r) {
+    __device__ __forceinline__ static void resolve(const Params& P, int grp, int t, TileRef& r) {
         const int b = grp / P.Hkv, g = grp % P.Hkv;
         r.grp = grp;
         r.t = t;
@@ -728,7 +741,7 @@ struct Stream {
     // sequence (or with an invalid block) read the first rows of the cache
     // instead; consume() masks them.
     template <int BUF>
-    __device__ void issue(const Params& P, const TileRef& r, int u) {
+    __device__ __forceinline__ void issue(const Params& P, const TileRef& r, int u) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         // keep every load of this unit after the previous unit's LDS reads and
         // before the next unit's loads: the waits count instructions in order
@@ -777,7 +790,7 @@ struct Stream {
     // Fold unit u of tile r (loaded in buffer BUF) into the running state.
     // `pending`: the next unit's loads were issued after this one's.
     template <int BUF>
-    __device__ void consume(const Params& P, const TileRef& r, int u, bool pending) {
+    __device__ __forceinline__ void consume(const Params& P, const TileRef& r, int u, bool pending) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         const int G = P.G;
         __builtin_amdgcn_sched_barrier(0);
@@ -850,7 +863,7 @@ struct Stream {
     }
 
     template <int BUF, bool MASK>
-    __device__ void pv_accumulate(const Params& P, const TileRef& r, int u) {
+    __device__ __forceinline__ void pv_accumulate(const Params& P, const TileRef& r, int u) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         const int G = P.G;
 #pragma unroll
@@ -900,7 +913,7 @@ struct Stream {
     // Reduce the running state into the fold mapping and reset it.  The four
     // row groups (lanes l, l^16, l^32, l^48) are summed by a two-step
     // reduce-scatter: after it, lane l holds head 4hb + (l>>4) of each block.
-    __device__ void flush(const Params& P, Out& o) {
+    __device__ __forceinline__ void flush(const Params& P, Out& o) {
         const int lane = lane_id(), rg = lane >> 4;
         const int G = P.G;
         float lt = l_run + __shfl_xor(l_run, 16);
@@ -910,6 +923,12 @@ struct Stream {
             o.m[h] = (h < GMAX && h < G) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), h))
                                          : kNegInf;
             o.l[h] = (h < GMAX && h < G) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), h)) : 0.f;
+        }
+        // lane h holds head h: copies for the fold mapping (lane l serves head 4hb + (l >> 4))
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            o.mf[hb] = 4 * hb + rg < G ? __shfl(m_run, 4 * hb + rg) : kNegInf;
+            o.lf[hb] = 4 * hb + rg < G ? __shfl(lt, 4 * hb + rg) : 0.f;
         }
         const bool hi2 = rg >> 1, hi1 = rg & 1;
 #pragma unroll
@@ -950,8 +969,8 @@ __device__ __forceinline__ void write_head_out(const Params& P, int grp, int h, 
 }
 
 // ------------------------------------------------------------------ give-up path of every wait
-__device__ void give_up(const Params& P) { cst(P.abort_flag, 1); }
-__device__ bool aborted(const Params& P) { return cld(P.abort_flag) != 0; }
+__device__ __forceinline__ void give_up(const Params& P) { cst(P.abort_flag, 1); }
+__device__ __forceinline__ bool aborted(const Params& P) { return cld(P.abort_flag) != 0; }
 
 // Wall-clock budget of any single wait (device real-time counter, 100 MHz):
 // past it the kernel gives up, so no wait can hang the GPU.
@@ -970,7 +989,7 @@ struct Deadline {
 // has completed -- and loads issued in between (the next unit's prefetch)
 // may still be in flight.
 template <int HBM>
-__device__ int publish_data(const Params& P, int grp, int t, const TileOutT<HBM>& o) {
+__device__ __forceinline__ int publish_data(const Params& P, int grp, int t, const TileOutT<HBM>& o) {
     const int lane = lane_id();
     const FoldLanes fl(P);
     float* slot = P.ring + ((long long)grp * kRing + (t & (kRing - 1))) * P.slot;
@@ -997,13 +1016,9 @@ __device__ int publish_data(const Params& P, int grp, int t, const TileOutT<HBM>
     return cld(reinterpret_cast<const int*>(slot) + 33);
 }
 
-__device__ void publish_flag(const Params& P, int grp, int t, int token) {
+__device__ __forceinline__ void publish_flag(const Params& P, int grp, int t, int token) {
     asm volatile("" ::"v"(token) : "memory");  // wait for the re-read (and so for the slot stores)
     if (lane_id() == 0) cst(&P.ring_tag[(long long)grp * kRing + (t & (kRing - 1))], t + 1);
-    // The flag must be visible before this wave tries the group lock: either
-    // the lock holder's re-check after unlocking sees the flag, or our lock
-    // attempt sees the lock released (store, complete, then read on both sides).
-    drain();
 }
 
 // ------------------------------------------------------------------ fold of ready tiles
@@ -1034,7 +1049,7 @@ struct FoldState {
 // the whole window into S (heads that did not stop).  Returns the number of
 // heads (of this block, counted in lane 16*hl) still active afterwards.
 template <int HBM>
-__device__ int fold_window(const Params& P, int grp, int hb, int f, int k, int nt, bool commit, FoldState<HBM>& S,
+__device__ __forceinline__ int fold_window(const Params& P, int grp, int hb, int f, int k, int nt, bool commit, FoldState<HBM>& S,
                            int& ug) {
     const int lane = lane_id();
     const FoldLanes fl(P);
@@ -1184,147 +1199,100 @@ __device__ int fold_window(const Params& P, int grp, int hb, int f, int k, int n
     return still;
 }
 
-// Try to take the group lock and fold ready tiles, in order, into the group's
-// running state.  Tiles are decided in windows of up to 16 that start at the
-// frontier, a multiple of 16: for each head, lanes 16*(head%4) + i hold tile
-// f+i's partial restricted to the probe dims; an inclusive online-softmax scan
-// over the 16 lanes, seeded with the head's committed state, gives the running
+// Decider of one group.  It owns the group's running state (in registers)
+// and polls the ring: tiles are decided in windows of up to 16 that start at
+// the frontier, a multiple of 16.  For each head, lanes 16*(head%4) + i hold
+// tile f+i's partial restricted to the probe dims; an inclusive online-softmax
+// scan over the 16 lanes, seeded with the committed state, gives the running
 // output after every tile of the window, hence every probe, both stability
 // metrics and the streak; the first tile whose streak reaches the patience is
-// the head's stop.  A head that stops gets its output from the committed state
-// and the tiles up to its stop.  The other heads' state (over all head dims) is
-// committed only for a complete window (or the last tiles of the group), so
-// every result is computed in the same order whatever the timing: the output
-// is deterministic.  An incomplete window is decided again only once at least
-// four more of its tiles are ready.  One lock holding folds up to 64 tiles.
+// the head's stop, and the head's output is the committed state merged with
+// the tiles up to its stop.  A window is decided again whenever more of its
+// tiles are ready (the scan value of lane i depends on lanes 0..i only, so
+// every decision is the same whatever the arrival order); the other heads'
+// state, over all head dims, is committed only for a complete window (or the
+// group's last tiles), so every result is computed in the same order whatever
+// the timing: the output is deterministic.  Committing moves the frontier,
+// which frees ring slots; once every head has stopped the allocation bound
+// drops to the stop, so no later tile is claimed.
 template <int HBM>
-__device__ void try_advance(const Params& P, int grp) {
+__device__ __forceinline__ void decide_group(const Params& P, int grp) {
     GroupCtl* C = P.ctl + grp;
     const int lane = lane_id();
     const FoldLanes fl(P);
-    const int G = P.G, D = P.D;
-    const Deadline dl;
+    const int nt = cld(&C->nt);
+    if (nt == 0) return;  // empty or invalid row: written by the init kernel
+    FoldState<HBM> S;
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        S.U[hb] = (hb < fl.HB && h < P.G) ? -1 : 0;
+        S.M[hb] = kNegInf; S.L[hb] = 0.f; S.pn[hb] = 0.f; S.streak[hb] = 0; S.err[hb] = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { S.prev[hb][j] = 0.f; S.A[hb][j] = 0.f; }
+    }
+    int f = 0;        // committed tiles
+    int decided = 0;  // tiles of the window at f already decided
+    int ug = 0;       // largest tiles_used of the heads stopped so far
+    Deadline dl;
     for (;;) {
-        if (dl.passed()) {
-            if (lane == 0) give_up(P);
-            return;
-        }
-        int got = 0;
-        if (lane == 0) got = cas(&C->lock, 0, 1);
-        if (!bcast0(got)) return;
-        int f = cld(&C->frontier);
-        const int nt = cld(&C->nt);
-        if (f >= cld(&C->bound)) {
-            // the group has finished: its heads are written, nothing more to fold
-            drain();
-            if (lane == 0) cst(&C->lock, 0);
-            return;
-        }
-        const int seen = cld(&C->seen);
         const int tau = f + lane;
         const bool ok =
             tau < nt && cld(&P.ring_tag[(long long)grp * kRing + (tau & (kRing - 1))]) == tau + 1;
         const uint64_t msk = __ballot(ok);
-        const int kall = (~msk == 0ull) ? 64 : __builtin_ctzll(~msk);
-        int probe = f + kall;  // first tile whose arrival allows progress
-        const bool worth = kall >= 16 || (kall > 0 && f + kall >= nt) || kall >= seen + 4;
-        if (!worth) {
-            drain();
-            if (lane == 0) cst(&C->lock, 0);
-            drain();
-            int again = 0;
-            if (lane == 0 && kall >= 0)
-                again = probe < nt && cld(&P.ring_tag[(long long)grp * kRing + (probe & (kRing - 1))]) == probe + 1;
-            if (!bcast0(again)) return;
+        int kall = (~msk == 0ull) ? 64 : __builtin_ctzll(~msk);
+        if (kall <= decided) {
+            if (dl.passed() || aborted(P)) {
+                if (lane == 0) give_up(P);
+                return;
+            }
+            __builtin_amdgcn_s_sleep(2);
             continue;
         }
-        // committed state of the group's heads
-        FoldState<HBM> S;
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            const int h = hb * 4 + fl.hl;
-            S.U[hb] = 0;
-            S.M[hb] = kNegInf; S.L[hb] = 0.f; S.pn[hb] = 0.f; S.streak[hb] = 0; S.err[hb] = 0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { S.prev[hb][j] = 0.f; S.A[hb][j] = 0.f; }
-            if (hb < fl.HB && h < G) {
-                HeadState* hs = P.heads + (long long)grp * G + h;
-                S.U[hb] = cld(&hs->U);
-                S.M[hb] = cld(&hs->M); S.L[hb] = cld(&hs->L); S.streak[hb] = cld(&hs->streak);
-                S.err[hb] = cld(&hs->err); S.pn[hb] = cld(&hs->pn);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) S.prev[hb][j] = cld(&hs->prev[j]);
-                if (fl.cvalid && S.M[hb] != kNegInf) {
-                    const float* ap = P.acc + ((long long)grp * G + h) * D + 8 * fl.cid;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) S.A[hb][j] = cld(ap + j);
-                }
-            }
-        }
+        dl = Deadline();
         bool finished = false;
-        int ug = 0, new_seen = 0;
-        const int end = f + kall;  // tiles f .. end-1 are ready
-        while (f < end) {
-            const int fb = f;
-            const int kw = min(16, end - f);
-            const bool commit = kw == 16 || fb + kw >= nt;
+        for (;;) {
+            const int kw = min(16, kall);
+            const bool commit = kw == 16 || f + kw >= nt;
             int still = 0;
-#pragma unroll
-            for (int hb = 0; hb < HBM; ++hb)
-                if (hb < fl.HB) still += fold_window<HBM>(P, grp, hb, fb, kw, nt, commit, S, ug);
+            static_for<0, HBM>([&](auto hbc) {
+                constexpr int hb = decltype(hbc)::value;  // a constant: the state stays in registers
+                if (hb < fl.HB) still += fold_window<HBM>(P, grp, hb, f, kw, nt, commit, S, ug);
+            });
             if (__ballot(still > 0) == 0ull) {
                 finished = true;
                 break;
             }
             if (!commit) {
-                new_seen = kw;
+                decided = kw;
                 break;
             }
-            f = fb + kw;
+            f += kw;
+            kall -= kw;
+            decided = 0;
+            if (kall == 0) break;
         }
-        probe = f + new_seen;
-        // write back the committed state of the heads still active
-        if (!finished) {
+        if (finished) {
+            // every head has stopped: the group used max(tiles_used) tiles
+            int ugw = ug;
 #pragma unroll
-            for (int hb = 0; hb < HBM; ++hb) {
-                const int h = hb * 4 + fl.hl;
-                if (hb < fl.HB && h < G) {
-                    HeadState* hs = P.heads + (long long)grp * G + h;
-                    if (fl.cid == 0) {
-                        cst(&hs->U, S.U[hb]);
-                        if (S.U[hb] < 0) {
-                            cst(&hs->M, S.M[hb]); cst(&hs->L, S.L[hb]); cst(&hs->streak, S.streak[hb]);
-                            cst(&hs->err, S.err[hb]); cst(&hs->pn, S.pn[hb]);
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) cst(&hs->prev[j], S.prev[hb][j]);
-                        }
-                    }
-                    if (fl.cvalid && S.U[hb] < 0) {
-                        float* ap = P.acc + ((long long)grp * G + h) * D + 8 * fl.cid;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) cst(ap + j, S.A[hb][j]);
-                    }
-                }
+            for (int o = 32; o > 0; o >>= 1) ugw = max(ugw, __shfl_xor(ugw, o));
+            if (lane == 0) {
+                cst(&C->bound, ugw);
+                cst(&C->frontier, ugw);
             }
+            return;
         }
-        int ugw = ug;  // every head has stopped: the group used max(tiles_used) tiles
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) ugw = max(ugw, __shfl_xor(ugw, o));
-        drain();
-        if (lane == 0) {
-            cst(&C->frontier, finished ? ugw : f);
-            cst(&C->seen, new_seen);
-            if (finished) cst(&C->bound, ugw);
-        }
-        drain();
-        if (lane == 0) cst(&C->lock, 0);
-        if (finished) return;
-        // a tile finished while we held the lock may have found it taken
-        drain();
-        int again = 0;
-        if (lane == 0)
-            again = probe < nt && cld(&P.ring_tag[(long long)grp * kRing + (probe & (kRing - 1))]) == probe + 1;
-        if (!bcast0(again)) return;
+        if (lane == 0) cst(&C->frontier, f);
+    }
+}
+
+// Decider wave d serves groups d, d + deciders, ... one after the other.
+template <int HBM>
+__device__ __forceinline__ void decider(const Params& P, int d) {
+    for (int grp = d; grp < P.NG; grp += P.deciders) {
+        if (aborted(P)) return;
+        decide_group<HBM>(P, grp);
     }
 }
 
@@ -1333,7 +1301,7 @@ __device__ void try_advance(const Params& P, int grp) {
 // left; -2 its ring is full (claim elsewhere).  A tile t is only claimed while
 // t < frontier + kRing, so its ring slot (that of tile t - kRing, already
 // folded) is free from the moment it is claimed.
-__device__ int take_tile(const Params& P, int grp) {
+__device__ __forceinline__ int take_tile(const Params& P, int grp) {
     int r = -1;
     if (lane_id() == 0) {
         GroupCtl* C = P.ctl + grp;
@@ -1349,7 +1317,7 @@ __device__ int take_tile(const Params& P, int grp) {
 }
 
 // Next group with tiles left (and room in its ring), scanning forward from grp; -1 when none.
-__device__ int next_group(const Params& P, int grp) {
+__device__ __forceinline__ int next_group(const Params& P, int grp) {
     const int lane = lane_id();
     const Deadline dl;
     for (int spin = 0;; ++spin) {
@@ -1373,8 +1341,9 @@ __device__ int next_group(const Params& P, int grp) {
             any_left |= __ballot(has) != 0ull;
         }
         if (!any_left) return -1;
-        // every group with tiles left has a full ring: back off (up to ~10 us)
-        for (int z = 0; z < (1 << min(spin, 5)); ++z) __builtin_amdgcn_s_sleep(127);
+        // every group with tiles left has a full ring: back off (about 1 to 4 us)
+        if (spin < 4) __builtin_amdgcn_s_sleep(32);
+        else __builtin_amdgcn_s_sleep(127);
     }
 }
 
@@ -1382,7 +1351,7 @@ __device__ int next_group(const Params& P, int grp) {
 // group has tiles left.  May wait for ring space, so a wave calls it only
 // while it holds no unpublished tile (an unpublished tile can be the one its
 // group's frontier waits for).
-__device__ bool claim(const Params& P, int& grp, int& t) {
+__device__ __forceinline__ bool claim(const Params& P, int& grp, int& t) {
     const Deadline dl;
     for (;;) {
         if (aborted(P)) return false;
@@ -1397,35 +1366,6 @@ __device__ bool claim(const Params& P, int& grp, int& t) {
     }
 }
 
-// One attempt, never waiting: a tile of grp, else of the first group found
-// with tiles and ring space.  Used to claim ahead while holding a tile.
-__device__ bool try_claim(const Params& P, int& grp, int& t) {
-    t = take_tile(P, grp);
-    if (t >= 0) return true;
-    const int lane = lane_id();
-    for (int base = 0; base < P.NG; base += 64) {
-        const int k = base + lane;
-        const int cand = (grp + 1 + k) % P.NG;
-        bool ok = false;
-        if (k < P.NG) {
-            GroupCtl* C = P.ctl + cand;
-            const int nx = cld(&C->next);
-            ok = nx < cld(&C->bound) && nx - cld(&C->frontier) < kRing;
-        }
-        const uint64_t m = __ballot(ok);
-        if (m) {
-            const int g2 = (grp + 1 + base + __builtin_ctzll(m)) % P.NG;
-            t = take_tile(P, g2);
-            if (t >= 0) {
-                grp = g2;
-                return true;
-            }
-            return false;
-        }
-    }
-    return false;
-}
-
 // ------------------------------------------------------------------ kernels
 __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
     const int grp = blockIdx.x;
@@ -1436,13 +1376,8 @@ __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
     const int nt = (bad || n == 0) ? 0 : (n + P.T - 1) / P.T;
     GroupCtl* C = P.ctl + grp;
     if (tid == 0) {
-        C->next = 0; C->lock = 0; C->frontier = 0; C->bound = nt; C->nt = nt; C->n = n; C->seen = 0;
+        C->next = 0; C->frontier = 0; C->bound = nt; C->nt = nt; C->n = n;
         if (grp == 0) *P.abort_flag = 0;
-    }
-    for (int h = tid; h < P.G; h += blockDim.x) {
-        HeadState& hs = P.heads[(long long)grp * P.G + h];
-        hs.M = kNegInf; hs.L = 0.f; hs.streak = 0; hs.U = nt > 0 ? -1 : 0; hs.err = 0; hs.pn = 0.f;
-        for (int i = 0; i < 8; ++i) hs.prev[i] = 0.f;
     }
     for (int i = tid; i < kRing; i += blockDim.x) P.ring_tag[(long long)grp * kRing + i] = 0;
     if (P.vskip)
@@ -1468,7 +1403,12 @@ __global__ __launch_bounds__(256) void art_persistent_kernel(Params P) {
     extern __shared__ float lds[];
     const int wv = wave_id(), lane = lane_id();
     float* lds_wave = lds + wv * Tile::lds_floats(P);
-    const int worker = blockIdx.x * kWavesPerWG + wv;
+    const int gw = blockIdx.x * kWavesPerWG + wv;
+    if (gw < P.deciders) {
+        decider<Tile::HBM>(P, gw);
+        return;
+    }
+    const int worker = gw - P.deciders;
     if (worker >= P.workers) return;
     int grp = worker % P.NG;
     int qgrp = -1;
@@ -1522,42 +1462,40 @@ __global__ __launch_bounds__(256) void art_persistent_kernel(Params P) {
         const int token = publish_data(P, grp, t, o);
         publish_flag(P, grp, t, token);
         count_stats(P, 1ull, (unsigned long long)o.kept);
-        try_advance<Tile::HBM>(P, grp);
     }
 }
 
-// Streamed matrix-core tiles: the next tile is claimed, and its first units
-// loaded, while the current one is computed.
+// Streamed matrix-core tiles, one tile per claim.  The wave holds no loaded
+// data while it publishes and folds, so the fold's registers never compete
+// with a prefetch (the other resident waves keep the memory system busy), and
+// the wave holds no unpublished tile when it next claims, so it may wait.
 template <class S>
 __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P) {
     extern __shared__ float lds[];
     const int wv = wave_id();
-    const int worker = blockIdx.x * kWavesPerWG + wv;
+    const int gw = blockIdx.x * kWavesPerWG + wv;
+    if (gw < P.deciders) {
+        decider<S::HBM>(P, gw);
+        return;
+    }
+    const int worker = gw - P.deciders;
     if (worker >= P.workers) return;
     S st;
     st.init(lds + wv * S::lds_floats(P));
     int grp = worker % P.NG;
-    int tc, tn;
-    typename S::TileRef C, N;
-    bool haveC = claim(P, grp, tc);  // holds nothing yet: may wait
-    if (haveC) {
-        S::resolve(P, grp, tc, C);
-        st.template issue<0>(P, C, 0);
-        st.template issue<1>(P, C, 1);
-    }
+    int t;
     int qgrp = -1;
-    while (haveC) {
-        if (C.grp != qgrp) {
+    typename S::TileRef C;
+    while (claim(P, grp, t)) {
+        S::resolve(P, grp, t, C);
+        if (C.grp != qgrp) {  // before the tile's loads: consume() counts those in issue order
             st.load_q(P, C.grp);
             qgrp = C.grp;
         }
-        // claim the next tile ahead, without waiting (C is not published yet)
-        const bool haveN = try_claim(P, grp, tn);
-        if (haveN) S::resolve(P, grp, tn, N);
+        st.template issue<0>(P, C, 0);
+        st.template issue<1>(P, C, 1);
         st.template consume<0>(P, C, 0, true);
-        if (haveN) st.template issue<0>(P, N, 0);
-        st.template consume<1>(P, C, 1, haveN);
-        if (haveN) st.template issue<1>(P, N, 1);
+        st.template consume<1>(P, C, 1, false);
         typename S::Out o;
         st.flush(P, o);
         o.err = C.err;
@@ -1566,18 +1504,295 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P)
         const int token = publish_data(P, C.grp, C.t, o);
         publish_flag(P, C.grp, C.t, token);
         count_stats(P, 1ull, (unsigned long long)rows);
-        try_advance<S::HBM>(P, C.grp);
-        if (haveN) {
-            C = N;
-        } else {
-            haveC = claim(P, grp, tc);  // holds nothing now: may wait
-            if (haveC) {
-                S::resolve(P, grp, tc, C);
-                st.template issue<0>(P, C, 0);
-                st.template issue<1>(P, C, 1);
+    }
+}
+
+// ------------------------------------------------------------------ team kernel (one work-group per group)
+//
+// A team of kTeam waves on one CU (all the waves a CU holds of this kernel:
+// eight, or four when a wave needs more than 256 registers) serves one group,
+// in rounds: in round r,
+// wave w computes tile r*kTeam + w (its loads were issued during the previous
+// round) and issues the loads of its next tile before the round's decision.
+// The waves exchange through LDS only what the stop rule needs, each tile's
+// (max, sum, probe dims) per head; wave 0 then decides the round's tiles in
+// order exactly as the ring fold does (inclusive online-softmax scan over the
+// round seeded with the committed probe state), and every wave merges its
+// tile into its own running state for the heads that use it.  At the end the
+// kTeam running states are merged in wave order: the result does not depend
+// on timing.  At most one round of loads is speculative.
+constexpr int kXch = 12;  // floats per (tile, head) in the exchange: m, l, probe dims 0..7, err
+
+// Committed probe state of one head, kept in LDS between rounds (wave 0 only).
+struct DecideRec {
+    float M, L, pn;
+    int streak, err, U;
+    float prev[8], Ap[8];
+    float pad[2];
+};
+static_assert(sizeof(DecideRec) == 24 * sizeof(float), "LDS record layout");
+
+// Decides the tiles of round r for every active head and publishes, per head
+// h, its tiles_used (-1 while active) in ctl[h] and its error flag in
+// ctl[kMaxG + h].
+template <int HBM, int TEAM>
+__device__ __forceinline__ void team_decide(const Params& P, int r, int nt, DecideRec* recs, const float* xp,
+                                            int* ctl) {
+    const int lane = lane_id();
+    const int i = lane & 15, hl = lane >> 4, row0 = lane & ~15;
+    const int G = P.G;
+    const int f = r * TEAM;
+    const int kw = min(TEAM, nt - f);
+    static_for<0, HBM>([&](auto hbc) {
+        constexpr int hb = decltype(hbc)::value;
+        const int h = hb * 4 + hl;
+        DecideRec& D = recs[h < G ? h : 0];
+        const bool act = h < G && D.U < 0;
+        if (__ballot(act) == 0ull) return;
+        const bool tv = act && i < kw;
+        const float* e = xp + (i * kMaxG + (tv ? h : 0)) * kXch;
+        float mi = kNegInf, li = 0.f, sa[8];
+        int ei = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sa[j] = 0.f;
+        if (tv) {
+            mi = e[0];
+            li = e[1];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sa[j] = e[2 + j];
+            ei = __float_as_int(e[10]);
+        }
+        // inclusive scan over the 16 lanes of the row
+        float sm = mi, sl = li;
+#pragma unroll
+        for (int dd = 1; dd < 16; dd <<= 1) {
+            const int src = row0 | ((i >= dd) ? i - dd : i);
+            float om = __shfl(sm, src), ol = __shfl(sl, src);
+            float oa[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) oa[j] = __shfl(sa[j], src);
+            if (i >= dd) {
+                sm_merge(om, ol, oa, sm, sl, sa);  // earlier (+) mine
+                sm = om; sl = ol;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sa[j] = oa[j];
             }
         }
+        // running state after tile f+i: committed (+) scan_i
+        float rm = D.M, rl = D.L, ra[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ra[j] = D.Ap[j];
+        sm_merge(rm, rl, ra, sm, sl, sa);
+        float x[8], xn2 = 0.f;
+        const float invL = 1.f / rl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x[j] = ra[j] * invL;
+            xn2 += x[j] * x[j];
+        }
+        const float xn = sqrtf(xn2);
+        const int srcp = row0 | (i > 0 ? i - 1 : 0);
+        float ppn = __shfl(xn, srcp), pp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pp[j] = __shfl(x[j], srcp);
+        if (i == 0) {
+            ppn = D.pn;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pp[j] = D.prev[j];
+        }
+        bool pass = false;
+        if (tv && f + i >= 1) {
+            float ds, dd;
+            if (xn == 0.f || ppn == 0.f) {
+                ds = dd = INFINITY;
+            } else {
+                ds = fabsf(xn - ppn) / ppn;
+                // 1 - cos as half the squared distance of the unit vectors
+                const float ix = 1.f / xn, ip = 1.f / ppn;
+                float s2 = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float dl = x[j] * ix - pp[j] * ip;
+                    s2 += dl * dl;
+                }
+                dd = 0.5f * s2;
+            }
+            pass = ds < P.eps_scale && dd < P.eps_dir;
+        }
+        const unsigned pbits = (unsigned)(__ballot(pass) >> row0) & 0xffffu;
+        // the stop: streaks of passing tiles, tile 0 never compared
+        int st = D.streak, istop = -1;
+        for (int q = 0; q < kw; ++q) {
+            if (f + q >= 1) {
+                st = ((pbits >> q) & 1u) ? st + 1 : 0;
+                if (st >= P.patience) {
+                    istop = q;
+                    break;
+                }
+            }
+        }
+        const bool stops = istop >= 0;
+        const int ilast = stops ? istop : kw - 1;
+        const int rowl = row0 | ilast;
+        const unsigned ebits = (unsigned)(__ballot(ei != 0 && i <= ilast) >> row0) & 0xffffu;
+        const float M_last = __shfl(rm, rowl), L_last = __shfl(rl, rowl), xn_last = __shfl(xn, rowl);
+        float A_last[8], x_last[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            A_last[j] = __shfl(ra[j], rowl);
+            x_last[j] = __shfl(x[j], rowl);
+        }
+        const int err = D.err | (ebits != 0u);
+        const int U = stops ? f + istop + 1 : (f + kw >= nt ? nt : -1);  // no stop: every tile is used
+        wave_lds_sync();  // every lane has read the record
+        if (act && i == 0) {
+            D.err = err;
+            D.U = U;
+            if (!stops) {
+                D.M = M_last; D.L = L_last; D.pn = xn_last; D.streak = st;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) { D.Ap[j] = A_last[j]; D.prev[j] = x_last[j]; }
+            }
+            ctl[h] = U;
+            ctl[kMaxG + h] = err;
+        }
+    });
+}
+
+template <class S>
+__global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
+    extern __shared__ float lds[];
+    constexpr int HBM = S::HBM, kTeam = S::TEAM;
+    const int wv = wave_id(), lane = lane_id();
+    const FoldLanes fl(P);
+    const int G = P.G;
+    const int grp = blockIdx.x;
+    const int b = grp / P.Hkv, g = grp % P.Hkv;
+    const int n = P.ctx_lens[b];
+    const bool bad = n < 0 || n > P.cap;
+    const int nt = (bad || n == 0) ? 0 : (n + S::T - 1) / S::T;
+    const size_t wave_floats = S::lds_floats(P);
+    float* xp = lds + kTeam * wave_floats;                           // [kTeam][kMaxG][kXch]
+    int* ctl = reinterpret_cast<int*>(xp + kTeam * kMaxG * kXch);    // [2][kMaxG]
+    DecideRec* recs = reinterpret_cast<DecideRec*>(ctl + 2 * kMaxG);  // [kMaxG]
+    if (nt == 0) {
+        // empty row: zero output, no tiles; invalid length: NaN, -1
+        if (wv == 0) {
+            const long long row0 = (long long)b * P.Hq + (long long)g * G;
+            for (int k = lane; k < G * P.D; k += 64) P.out[row0 * P.D + k] = bad ? NAN : 0.f;
+            for (int h = lane; h < G; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
+        }
+        return;
     }
+    S st;
+    st.init(lds + wv * wave_floats);
+    st.load_q(P, grp);
+    typename S::TileRef C, N;
+    if (wv < nt) {
+        S::resolve(P, grp, wv, C);
+        st.template issue<0>(P, C, 0);
+        st.template issue<1>(P, C, 1);
+    }
+    // this wave's running state over the tiles it merged (fold mapping)
+    float Mw[HBM], Lw[HBM], Aw[HBM][8];
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        Mw[hb] = kNegInf;
+        Lw[hb] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Aw[hb][j] = 0.f;
+    }
+    if (wv == 0 && lane < kMaxG) {
+        ctl[lane] = -1;
+        ctl[kMaxG + lane] = 0;
+        DecideRec& d = recs[lane];
+        d.M = kNegInf; d.L = 0.f; d.pn = 0.f; d.streak = 0; d.err = 0; d.U = -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { d.prev[j] = 0.f; d.Ap[j] = 0.f; }
+    }
+    unsigned long long loaded = 0, rows = 0;
+    for (int r = 0;; ++r) {
+        const int t = r * kTeam + wv;
+        const bool valid = t < nt;
+        typename S::Out o;
+        if (valid) {
+            st.template consume<0>(P, C, 0, true);
+            st.template consume<1>(P, C, 1, false);
+            st.flush(P, o);
+            o.err = C.err;
+            ++loaded;
+            rows += min(S::T, n - t * S::T);
+        }
+        // this tile's (max, sum) of the lane's heads, and its probe data from
+        // the lanes holding head dims 0..7
+        float om[HBM], ol[HBM];
+        static_for<0, HBM>([&](auto hbc) {
+            constexpr int hb = decltype(hbc)::value;
+            om[hb] = valid ? o.mf[hb] : kNegInf;
+            ol[hb] = valid ? o.lf[hb] : 0.f;
+            const int h = hb * 4 + fl.hl;
+            if (hb < fl.HB && h < G && fl.cid == 0) {
+                float* e = xp + (wv * kMaxG + h) * kXch;
+                e[0] = om[hb];
+                e[1] = ol[hb];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) e[2 + j] = valid ? o.a[hb][j] : 0.f;
+                e[10] = __int_as_float(valid ? o.err : 0);
+            }
+        });
+        // the next tile's loads fly during the decision
+        const int tn = t + kTeam;
+        if (tn < nt) {
+            S::resolve(P, grp, tn, N);
+            st.template issue<0>(P, N, 0);
+            st.template issue<1>(P, N, 1);
+        }
+        __syncthreads();
+        if (wv == 0) team_decide<HBM, kTeam>(P, r, nt, recs, xp, ctl);
+        __syncthreads();
+        bool active = false;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            const int h = hb * 4 + fl.hl;
+            const int U = h < G ? ctl[h] : 0;
+            if (valid && h < G && (U < 0 || t < U)) sm_merge(Mw[hb], Lw[hb], Aw[hb], om[hb], ol[hb], o.a[hb]);
+        }
+        for (int h = 0; h < G; ++h) active |= ctl[h] < 0;
+        if (!active) break;
+        C = N;
+    }
+    // a speculative tile's loads may still be landing (in LDS too)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // merge the running states in wave order, through each wave's LDS
+    float* mine = lds + wv * wave_floats;
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        float* e = mine + (hb * 64 + lane) * 10;
+        e[0] = Mw[hb];
+        e[1] = Lw[hb];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[2 + j] = Aw[hb][j];
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            const int h = hb * 4 + fl.hl;
+            float M = kNegInf, L = 0.f, A[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) A[j] = 0.f;
+            for (int w = 0; w < kTeam; ++w) {
+                const float* e = lds + w * wave_floats + (hb * 64 + lane) * 10;
+                float a2[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a2[j] = e[2 + j];
+                sm_merge(M, L, A, e[0], e[1], a2);
+            }
+            if (hb < fl.HB && h < G) write_head_out(P, grp, h, fl, A, L, ctl[kMaxG + h], ctl[h]);
+        }
+    }
+    count_stats(P, loaded, rows);
 }
 
 // Full mode, one tile at a time: split sp of group grp covers a fixed tile range.
@@ -1771,11 +1986,27 @@ __global__ __launch_bounds__(64) void art_combine_kernel(Params P) {
 }
 
 // ------------------------------------------------------------------ launches
+// Persistent grid: the deciders first (the lowest work-groups are dispatched
+// first, so they are resident from the start), then the tile workers; without
+// a requested worker count, as many as are resident together with them.
 template <class K, class Tile>
-int launch_persistent(const Params& p, hipStream_t s, K kernel) {
-    hipLaunchKernelGGL(art_init_kernel, dim3(p.NG), dim3(256), 0, s, p);
+int launch_persistent(const Params& p0, hipStream_t s, K kernel) {
+    Params p = p0;
     const size_t lds = (size_t)kWavesPerWG * Tile::lds_floats(p) * sizeof(float);
-    const int blocks = (p.workers + kWavesPerWG - 1) / kWavesPerWG;
+    if (p.workers == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds);
+        if (e != hipSuccess) return (int)e;
+        const long long resident = (long long)max(per_cu, 1) * cus * kWavesPerWG;
+        long long w = resident - p.deciders;
+        const long long tiles = (long long)p.NG * p.nt_max;
+        if (w > tiles) w = tiles;
+        p.workers = (int)max(w, 1LL);
+    }
+    hipLaunchKernelGGL(art_init_kernel, dim3(p.NG), dim3(256), 0, s, p);
+    const int blocks = (p.deciders + p.workers + kWavesPerWG - 1) / kWavesPerWG;
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), lds, s, p);
     return (int)hipGetLastError();
 }
@@ -1805,7 +2036,17 @@ int run_tile(const Params& p, hipStream_t s, bool art) {
 }
 
 template <class S>
+int launch_team(const Params& p, hipStream_t s) {
+    const size_t lds = ((size_t)S::TEAM * S::lds_floats(p) + (size_t)S::TEAM * kMaxG * kXch + 2 * kMaxG) * sizeof(float) +
+                       kMaxG * sizeof(DecideRec);
+    hipLaunchKernelGGL(art_team_kernel<S>, dim3(p.NG), dim3(S::TEAM * 64), lds, s, p);
+    return (int)hipGetLastError();
+}
+
+template <class S>
 int run_stream(const Params& p, hipStream_t s, bool art) {
+    // a requested worker count selects the work-sharing engine
+    if (art && p.workers == 0) return launch_team<S>(p, s);
     if (art) return launch_persistent<decltype(&art_stream_kernel<S>), S>(p, s, &art_stream_kernel<S>);
     return launch_split<decltype(&art_full_stream_kernel<S>), S>(p, s, &art_full_stream_kernel<S>);
 }

@@ -17,7 +17,7 @@ def _run_and_check(case, label, **kw):
     log(f"[parity] {label}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} d={case.d} "
         f"ctx={case.ctx_lens.tolist()[:4]} kv={case.kv_dtype} T={case.tile} {kw}")
     out, used = run_gpu(case, **kw)
-    r = check_parity(case, out, used, **kw)
+    r = check_parity(case, out, used, **{k: v for k, v in kw.items() if k != "max_workers"})
     log(f"[parity] {label}: max_abs={r['max_abs']:.3e} near={r['near']} "
         f"mean tiles_used={np.mean(r['tiles_used']):.1f}")
     return out, used, r
@@ -136,12 +136,21 @@ def test_deterministic_repeats():
 
 
 def test_worker_count_does_not_change_results():
+    # a worker count selects the work-sharing engine (decider waves + tile
+    # workers); its results must not depend on how many workers there are
     c = A.config(3, small=True)
     dev = to_device(c)
-    o0, u0 = run_gpu(c, dev)
-    for w in (1, 3, 17, 64):
+    o0, u0 = run_gpu(c, dev, max_workers=64)
+    for w in (1, 3, 17, 300):
         o, u = run_gpu(c, dev, max_workers=w)
         assert np.array_equal(u, u0) and np.array_equal(o, o0)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_work_sharing_engine(n):
+    # the engine used for few groups, forced here on the named workloads
+    c = A.config(n, small=n != 2)
+    _run_and_check(c, f"config{n} work-sharing art", max_workers=96)
 
 
 def test_invalid_block_and_length_reported_per_row():
