@@ -1509,172 +1509,229 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P)
 
 // ------------------------------------------------------------------ team kernel (one work-group per group)
 //
-// A team of kTeam waves on one CU (all the waves a CU holds of this kernel:
-// eight, or four when a wave needs more than 256 registers) serves one group,
-// in rounds: in round r,
-// wave w computes tile r*kTeam + w (its loads were issued during the previous
-// round) and issues the loads of its next tile before the round's decision.
-// The waves exchange through LDS only what the stop rule needs, each tile's
-// (max, sum, probe dims) per head; wave 0 then decides the round's tiles in
-// order exactly as the ring fold does (inclusive online-softmax scan over the
-// round seeded with the committed probe state), and every wave merges its
-// tile into its own running state for the heads that use it.  At the end the
-// kTeam running states are merged in wave order: the result does not depend
-// on timing.  At most one round of loads is speculative.
-constexpr int kXch = 12;  // floats per (tile, head) in the exchange: m, l, probe dims 0..7, err
+// The waves of one work-group (one CU) serve one group.  Waves 1.. are tile
+// workers: worker i streams tiles i, i + nw, i + 2nw, ... (nw workers), the
+// loads of each tile issued before the previous one is handed over, and
+// hands every tile's partial (max, sum and V accumulator per head, in the
+// fold mapping) to wave 0 through a ring of LDS slots.  Wave 0 folds the
+// tiles one at a time in tile order into the group's running state, which is
+// the sequential traversal itself: after each tile the probe of every active
+// head is compared with the previous one, a head whose streak reaches the
+// patience stops and its output is written at once, and once every head has
+// stopped the bound in LDS drops so that no worker fetches a further tile
+// (at most one tile per worker is loaded speculatively).  No barrier after
+// the start: the hand-over is an LDS store of the slot, a wait for it to
+// complete, then the tag.
+constexpr int kTeamRing = 8;       // LDS slots between the workers and the decider
+constexpr int kSlotLane = 10;      // floats per lane per head block in a slot: m, l, 8 dims
 
-// Committed probe state of one head, kept in LDS between rounds (wave 0 only).
-struct DecideRec {
-    float M, L, pn;
-    int streak, err, U;
-    float prev[8], Ap[8];
-    float pad[2];
+struct TeamShared {
+    int tag[kTeamRing];  // t + 1 once slot t % kTeamRing holds tile t
+    int err[kTeamRing];  // the tile met an invalid block id
+    int frontier;        // tiles folded by the decider
+    int bound;           // tiles that may still be fetched
 };
-static_assert(sizeof(DecideRec) == 24 * sizeof(float), "LDS record layout");
 
-// Decides the tiles of round r for every active head and publishes, per head
-// h, its tiles_used (-1 while active) in ctl[h] and its error flag in
-// ctl[kMaxG + h].
-template <int HBM, int TEAM>
-__device__ __forceinline__ void team_decide(const Params& P, int r, int nt, DecideRec* recs, const float* xp,
-                                            int* ctl) {
+__device__ __forceinline__ int lds_ld(const int* p) { return *static_cast<const volatile int*>(p); }
+__device__ __forceinline__ void lds_st(int* p, int v) { *static_cast<volatile int*>(p) = v; }
+// waits for this wave's LDS accesses only (vector-memory loads stay in flight)
+__device__ __forceinline__ void wait_lds() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <class S>
+__device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int nt, int idx, int nw, S& st,
+                                            float* ring, TeamShared* sh) {
+    constexpr int HBM = S::HBM;
     const int lane = lane_id();
-    const int i = lane & 15, hl = lane >> 4, row0 = lane & ~15;
-    const int G = P.G;
-    const int f = r * TEAM;
-    const int kw = min(TEAM, nt - f);
-    static_for<0, HBM>([&](auto hbc) {
-        constexpr int hb = decltype(hbc)::value;
-        const int h = hb * 4 + hl;
-        DecideRec& D = recs[h < G ? h : 0];
-        const bool act = h < G && D.U < 0;
-        if (__ballot(act) == 0ull) return;
-        const bool tv = act && i < kw;
-        const float* e = xp + (i * kMaxG + (tv ? h : 0)) * kXch;
-        float mi = kNegInf, li = 0.f, sa[8];
-        int ei = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sa[j] = 0.f;
-        if (tv) {
-            mi = e[0];
-            li = e[1];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sa[j] = e[2 + j];
-            ei = __float_as_int(e[10]);
+    int t = idx;
+    if (t >= nt) return;
+    typename S::TileRef C, N;
+    st.load_q(P, grp);  // before the tile's loads: consume() counts those in issue order
+    S::resolve(P, grp, t, C);
+    st.template issue<0>(P, C, 0);
+    st.template issue<1>(P, C, 1);
+    // tiles (and rows) fetched, counted when their loads are issued
+    unsigned long long loaded = 1, rows = min(S::T, n - t * S::T);
+    for (;;) {
+        if (t >= lds_ld(&sh->bound)) break;  // the group stopped before this tile
+        st.template consume<0>(P, C, 0, true);
+        st.template consume<1>(P, C, 1, false);
+        typename S::Out o;
+        st.flush(P, o);
+        const int tn = t + nw;
+        const bool haveN = tn < nt && tn < lds_ld(&sh->bound);
+        if (haveN) {
+            S::resolve(P, grp, tn, N);
+            st.template issue<0>(P, N, 0);
+            st.template issue<1>(P, N, 1);
+            ++loaded;
+            rows += min(S::T, n - tn * S::T);
         }
-        // inclusive scan over the 16 lanes of the row
-        float sm = mi, sl = li;
+        // the slot of tile t is free once the decider has folded tile t - kTeamRing
+        const Deadline dl;
+        while (t - kTeamRing >= lds_ld(&sh->frontier) && t < lds_ld(&sh->bound) && !dl.passed())
+            __builtin_amdgcn_s_sleep(1);
+        if (t < lds_ld(&sh->bound) && t - kTeamRing < lds_ld(&sh->frontier)) {
+            float* slot = ring + (t % kTeamRing) * (HBM * kSlotLane * 64);
 #pragma unroll
-        for (int dd = 1; dd < 16; dd <<= 1) {
-            const int src = row0 | ((i >= dd) ? i - dd : i);
-            float om = __shfl(sm, src), ol = __shfl(sl, src);
-            float oa[8];
+            for (int hb = 0; hb < HBM; ++hb) {
+                float* e = slot + hb * kSlotLane * 64 + lane;
+                e[0] = o.mf[hb];
+                e[64] = o.lf[hb];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) oa[j] = __shfl(sa[j], src);
-            if (i >= dd) {
-                sm_merge(om, ol, oa, sm, sl, sa);  // earlier (+) mine
-                sm = om; sl = ol;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sa[j] = oa[j];
+                for (int j = 0; j < 8; ++j) e[64 * (2 + j)] = o.a[hb][j];
             }
+            if (lane == 0) lds_st(&sh->err[t % kTeamRing], C.err);
+            wait_lds();  // the slot is written before its tag
+            if (lane == 0) lds_st(&sh->tag[t % kTeamRing], t + 1);
         }
-        // running state after tile f+i: committed (+) scan_i
-        float rm = D.M, rl = D.L, ra[8];
+        if (!haveN) break;
+        t = tn;
+        C = N;
+    }
+    // loads of a tile fetched past the stop may still be landing (in LDS too)
+    __builtin_amdgcn_s_waitcnt(0);
+    count_stats(P, loaded, rows);
+}
+
+// Folds tiles 0, 1, ... of the group in order; writes each head's output as it
+// stops.  A wait longer than kWaitTicks (impossible unless a worker faulted)
+// ends the group: its unfinished heads get tiles_used = -2 and NaN.
+template <int HBM>
+__device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const float* ring,
+                                             TeamShared* sh) {
+    const int lane = lane_id();
+    const FoldLanes fl(P);
+    const int G = P.G, row0 = lane & ~15;
+    float M[HBM], L[HBM], A[HBM][8], prev[HBM][8], pn[HBM];
+    int streak[HBM], U[HBM], err[HBM];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ra[j] = D.Ap[j];
-        sm_merge(rm, rl, ra, sm, sl, sa);
-        float x[8], xn2 = 0.f;
-        const float invL = 1.f / rl;
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        M[hb] = kNegInf; L[hb] = 0.f; pn[hb] = 0.f; streak[hb] = 0; err[hb] = 0;
+        U[hb] = (hb < fl.HB && h < G) ? -1 : 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            x[j] = ra[j] * invL;
-            xn2 += x[j] * x[j];
+        for (int j = 0; j < 8; ++j) { A[hb][j] = 0.f; prev[hb][j] = 0.f; }
+    }
+    int ug = 0;  // largest tiles_used so far
+    bool finished = false, gave_up = false;
+    Deadline dl;
+    for (int f = 0; f < nt; ++f) {
+        const int s = f % kTeamRing;
+        while (lds_ld(&sh->tag[s]) != f + 1) {
+            if (dl.passed()) {
+                gave_up = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
         }
-        const float xn = sqrtf(xn2);
-        const int srcp = row0 | (i > 0 ? i - 1 : 0);
-        float ppn = __shfl(xn, srcp), pp[8];
+        if (gave_up) break;
+        dl = Deadline();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the slot is read after its tag
+        const int et = lds_ld(&sh->err[s]);
+        const float* slot = ring + s * (HBM * kSlotLane * 64);
+        bool any = false;
+        static_for<0, HBM>([&](auto hbc) {
+            constexpr int hb = decltype(hbc)::value;
+            const int h = hb * 4 + fl.hl;
+            const bool act = U[hb] < 0;
+            bool pass = false;
+            if (act) {
+                const float* e = slot + hb * kSlotLane * 64 + lane;
+                const float mt = e[0], lt = e[64];
+                const float Mn = fmaxf(M[hb], mt);
+                const float al = M[hb] == kNegInf ? 0.f : expf(M[hb] - Mn);
+                const float be = mt == kNegInf ? 0.f : expf(mt - Mn);
+                L[hb] = al * L[hb] + be * lt;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pp[j] = __shfl(x[j], srcp);
-        if (i == 0) {
-            ppn = D.pn;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pp[j] = D.prev[j];
-        }
-        bool pass = false;
-        if (tv && f + i >= 1) {
-            float ds, dd;
-            if (xn == 0.f || ppn == 0.f) {
-                ds = dd = INFINITY;
-            } else {
-                ds = fabsf(xn - ppn) / ppn;
-                // 1 - cos as half the squared distance of the unit vectors
-                const float ix = 1.f / xn, ip = 1.f / ppn;
-                float s2 = 0.f;
+                for (int j = 0; j < 8; ++j) A[hb][j] = al * A[hb][j] + be * e[64 * (2 + j)];
+                M[hb] = Mn;
+                err[hb] |= et;
+                // probe: head dims 0..7 are this row's lane 16*hl (cid 0)
+                const float invL = 1.f / L[hb];
+                float x[8], xn2 = 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float dl = x[j] * ix - pp[j] * ip;
-                    s2 += dl * dl;
+                    x[j] = A[hb][j] * invL;
+                    xn2 += x[j] * x[j];
                 }
-                dd = 0.5f * s2;
+                const float xn = sqrtf(xn2);
+                if (f >= 1) {
+                    float ds, dd;
+                    if (xn == 0.f || pn[hb] == 0.f) {
+                        ds = dd = INFINITY;
+                    } else {
+                        ds = fabsf(xn - pn[hb]) / pn[hb];
+                        // 1 - cos as half the squared distance of the unit vectors
+                        const float ix = 1.f / xn, ip = 1.f / pn[hb];
+                        float s2 = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float dl2 = x[j] * ix - prev[hb][j] * ip;
+                            s2 += dl2 * dl2;
+                        }
+                        dd = 0.5f * s2;
+                    }
+                    pass = ds < P.eps_scale && dd < P.eps_dir;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) prev[hb][j] = x[j];
+                pn[hb] = xn;
             }
-            pass = ds < P.eps_scale && dd < P.eps_dir;
-        }
-        const unsigned pbits = (unsigned)(__ballot(pass) >> row0) & 0xffffu;
-        // the stop: streaks of passing tiles, tile 0 never compared
-        int st = D.streak, istop = -1;
-        for (int q = 0; q < kw; ++q) {
-            if (f + q >= 1) {
-                st = ((pbits >> q) & 1u) ? st + 1 : 0;
-                if (st >= P.patience) {
-                    istop = q;
-                    break;
+            // the row's decision is that of its lane 16*hl
+            const bool pass_row = __shfl(pass ? 1 : 0, row0) != 0;
+            if (act && f >= 1) {
+                streak[hb] = pass_row ? streak[hb] + 1 : 0;
+                if (streak[hb] >= P.patience) {
+                    U[hb] = f + 1;
+                    ug = max(ug, U[hb]);
+                    write_head_out(P, grp, h, fl, A[hb], L[hb], err[hb], U[hb]);
                 }
             }
+            any |= U[hb] < 0;
+        });
+        if (__ballot(any) == 0ull) {
+            finished = true;
+            break;
         }
-        const bool stops = istop >= 0;
-        const int ilast = stops ? istop : kw - 1;
-        const int rowl = row0 | ilast;
-        const unsigned ebits = (unsigned)(__ballot(ei != 0 && i <= ilast) >> row0) & 0xffffu;
-        const float M_last = __shfl(rm, rowl), L_last = __shfl(rl, rowl), xn_last = __shfl(xn, rowl);
-        float A_last[8], x_last[8];
+        if (lane == 0) lds_st(&sh->frontier, f + 1);
+    }
+    // heads that never stopped used every tile (or the group gave up)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            A_last[j] = __shfl(ra[j], rowl);
-            x_last[j] = __shfl(x[j], rowl);
-        }
-        const int err = D.err | (ebits != 0u);
-        const int U = stops ? f + istop + 1 : (f + kw >= nt ? nt : -1);  // no stop: every tile is used
-        wave_lds_sync();  // every lane has read the record
-        if (act && i == 0) {
-            D.err = err;
-            D.U = U;
-            if (!stops) {
-                D.M = M_last; D.L = L_last; D.pn = xn_last; D.streak = st;
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        if (U[hb] < 0) {
+            if (gave_up) {
+                const FoldLanes f2 = fl;
+                float nan8[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) { D.Ap[j] = A_last[j]; D.prev[j] = x_last[j]; }
+                for (int j = 0; j < 8; ++j) nan8[j] = NAN;
+                write_head_out(P, grp, h, f2, nan8, 1.f, 0, -2);
+            } else {
+                write_head_out(P, grp, h, fl, A[hb], L[hb], err[hb], nt);
             }
-            ctl[h] = U;
-            ctl[kMaxG + h] = err;
         }
-    });
+    }
+    int ugw = finished ? ug : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ugw = max(ugw, __shfl_xor(ugw, o));
+    if (lane == 0) lds_st(&sh->bound, finished ? ugw : (gave_up ? 0 : nt));
 }
 
 template <class S>
 __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     extern __shared__ float lds[];
-    constexpr int HBM = S::HBM, kTeam = S::TEAM;
+    constexpr int HBM = S::HBM, TEAM = S::TEAM;
     const int wv = wave_id(), lane = lane_id();
-    const FoldLanes fl(P);
     const int G = P.G;
     const int grp = blockIdx.x;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
     const int n = P.ctx_lens[b];
     const bool bad = n < 0 || n > P.cap;
     const int nt = (bad || n == 0) ? 0 : (n + S::T - 1) / S::T;
-    const size_t wave_floats = S::lds_floats(P);
-    float* xp = lds + kTeam * wave_floats;                           // [kTeam][kMaxG][kXch]
-    int* ctl = reinterpret_cast<int*>(xp + kTeam * kMaxG * kXch);    // [2][kMaxG]
-    DecideRec* recs = reinterpret_cast<DecideRec*>(ctl + 2 * kMaxG);  // [kMaxG]
     if (nt == 0) {
         // empty row: zero output, no tiles; invalid length: NaN, -1
         if (wv == 0) {
@@ -1684,115 +1741,33 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
         }
         return;
     }
-    S st;
-    st.init(lds + wv * wave_floats);
-    st.load_q(P, grp);
-    typename S::TileRef C, N;
-    if (wv < nt) {
-        S::resolve(P, grp, wv, C);
-        st.template issue<0>(P, C, 0);
-        st.template issue<1>(P, C, 1);
-    }
-    // this wave's running state over the tiles it merged (fold mapping)
-    float Mw[HBM], Lw[HBM], Aw[HBM][8];
-#pragma unroll
-    for (int hb = 0; hb < HBM; ++hb) {
-        Mw[hb] = kNegInf;
-        Lw[hb] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) Aw[hb][j] = 0.f;
-    }
-    if (wv == 0 && lane < kMaxG) {
-        ctl[lane] = -1;
-        ctl[kMaxG + lane] = 0;
-        DecideRec& d = recs[lane];
-        d.M = kNegInf; d.L = 0.f; d.pn = 0.f; d.streak = 0; d.err = 0; d.U = -1;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { d.prev[j] = 0.f; d.Ap[j] = 0.f; }
-    }
-    unsigned long long loaded = 0, rows = 0;
-    for (int r = 0;; ++r) {
-        const int t = r * kTeam + wv;
-        const bool valid = t < nt;
-        typename S::Out o;
-        if (valid) {
-            st.template consume<0>(P, C, 0, true);
-            st.template consume<1>(P, C, 1, false);
-            st.flush(P, o);
-            o.err = C.err;
-            ++loaded;
-            rows += min(S::T, n - t * S::T);
+    const size_t wave_floats = S::lds_floats(P);
+    float* ring = lds + (TEAM - 1) * wave_floats;  // [kTeamRing][HBM][kSlotLane][64]
+    TeamShared* sh = reinterpret_cast<TeamShared*>(ring + kTeamRing * HBM * kSlotLane * 64);
+    if (wv == 0) {
+        if (lane < kTeamRing) {
+            sh->tag[lane] = 0;
+            sh->err[lane] = 0;
         }
-        // this tile's (max, sum) of the lane's heads, and its probe data from
-        // the lanes holding head dims 0..7
-        float om[HBM], ol[HBM];
-        static_for<0, HBM>([&](auto hbc) {
-            constexpr int hb = decltype(hbc)::value;
-            om[hb] = valid ? o.mf[hb] : kNegInf;
-            ol[hb] = valid ? o.lf[hb] : 0.f;
-            const int h = hb * 4 + fl.hl;
-            if (hb < fl.HB && h < G && fl.cid == 0) {
-                float* e = xp + (wv * kMaxG + h) * kXch;
-                e[0] = om[hb];
-                e[1] = ol[hb];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) e[2 + j] = valid ? o.a[hb][j] : 0.f;
-                e[10] = __int_as_float(valid ? o.err : 0);
-            }
-        });
-        // the next tile's loads fly during the decision
-        const int tn = t + kTeam;
-        if (tn < nt) {
-            S::resolve(P, grp, tn, N);
-            st.template issue<0>(P, N, 0);
-            st.template issue<1>(P, N, 1);
+        if (lane == 0) {
+            sh->frontier = 0;
+            sh->bound = nt;
         }
-        __syncthreads();
-        if (wv == 0) team_decide<HBM, kTeam>(P, r, nt, recs, xp, ctl);
-        __syncthreads();
-        bool active = false;
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            const int h = hb * 4 + fl.hl;
-            const int U = h < G ? ctl[h] : 0;
-            if (valid && h < G && (U < 0 || t < U)) sm_merge(Mw[hb], Lw[hb], Aw[hb], om[hb], ol[hb], o.a[hb]);
-        }
-        for (int h = 0; h < G; ++h) active |= ctl[h] < 0;
-        if (!active) break;
-        C = N;
-    }
-    // a speculative tile's loads may still be landing (in LDS too)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // merge the running states in wave order, through each wave's LDS
-    float* mine = lds + wv * wave_floats;
-#pragma unroll
-    for (int hb = 0; hb < HBM; ++hb) {
-        float* e = mine + (hb * 64 + lane) * 10;
-        e[0] = Mw[hb];
-        e[1] = Lw[hb];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[2 + j] = Aw[hb][j];
     }
     __syncthreads();
     if (wv == 0) {
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            const int h = hb * 4 + fl.hl;
-            float M = kNegInf, L = 0.f, A[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) A[j] = 0.f;
-            for (int w = 0; w < kTeam; ++w) {
-                const float* e = lds + w * wave_floats + (hb * 64 + lane) * 10;
-                float a2[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) a2[j] = e[2 + j];
-                sm_merge(M, L, A, e[0], e[1], a2);
-            }
-            if (hb < fl.HB && h < G) write_head_out(P, grp, h, fl, A, L, ctl[kMaxG + h], ctl[h]);
-        }
+        team_decider<HBM>(P, grp, nt, ring, sh);
+    } else {
+        S st;
+        st.init(lds + (wv - 1) * wave_floats);
+        team_worker<S>(P, grp, n, nt, wv - 1, TEAM - 1, st, ring, sh);
     }
-    count_stats(P, loaded, rows);
+}
+
+template <class S>
+size_t team_lds_bytes(const Params& p) {
+    return ((size_t)(S::TEAM - 1) * S::lds_floats(p) + (size_t)kTeamRing * S::HBM * kSlotLane * 64) * sizeof(float) +
+           sizeof(TeamShared);
 }
 
 // Full mode, one tile at a time: split sp of group grp covers a fixed tile range.
@@ -2037,9 +2012,7 @@ int run_tile(const Params& p, hipStream_t s, bool art) {
 
 template <class S>
 int launch_team(const Params& p, hipStream_t s) {
-    const size_t lds = ((size_t)S::TEAM * S::lds_floats(p) + (size_t)S::TEAM * kMaxG * kXch + 2 * kMaxG) * sizeof(float) +
-                       kMaxG * sizeof(DecideRec);
-    hipLaunchKernelGGL(art_team_kernel<S>, dim3(p.NG), dim3(S::TEAM * 64), lds, s, p);
+    hipLaunchKernelGGL(art_team_kernel<S>, dim3(p.NG), dim3(S::TEAM * 64), team_lds_bytes<S>(p), s, p);
     return (int)hipGetLastError();
 }
 
