@@ -95,6 +95,9 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// e^x from the hardware base-2 exponential (a couple of ulp; e^-inf = 0)
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
 // f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -736,6 +739,46 @@ struct Stream {
         }
     }
 
+    // The block ids of tile t (paged caches): lane p < PAGES loads page p's
+    // entry with a vector load, so that it can be issued well before the tile
+    // is resolved, and complete with the tile loads issued before it.
+    __device__ __forceinline__ static int fetch_blocks(const Params& P, int grp, int n, int t) {
+        const int lane = lane_id(), b = grp / P.Hkv;
+        const int tokp = t * T + 16 * lane;
+        int blk = 0;
+        if (P.block_size && lane < PAGES && tokp < n) blk = P.block_table[(long long)b * P.mbps + tokp / P.block_size];
+        return blk;
+    }
+
+    // resolve() from the block ids fetch_blocks() returned for tile t
+    __device__ __forceinline__ static void resolve_from(const Params& P, int grp, int n, int t, int blkv, TileRef& r) {
+        const int b = grp / P.Hkv, g = grp % P.Hkv;
+        r.grp = grp;
+        r.t = t;
+        r.n = n;
+        r.pmask = 0;
+        r.err = 0;
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p) {
+            const int tokp = t * T + 16 * p;
+            r.prow[p] = 0;
+            if (tokp < n) {
+                if (P.block_size == 0) {
+                    r.prow[p] = ((long long)b * P.Hkv + g) * P.max_ctx + tokp;
+                    r.pmask |= 1 << p;
+                } else {
+                    const int blk = __builtin_amdgcn_readlane(blkv, p);
+                    if (blk < 0 || blk >= P.num_blocks) {
+                        r.err = 1;
+                    } else {
+                        r.prow[p] = ((long long)blk * P.Hkv + g) * P.block_size + tokp % P.block_size;
+                        r.pmask |= 1 << p;
+                    }
+                }
+            }
+        }
+    }
+
     // Issue the loads of unit u (pages 2u, 2u+1) of tile r into buffer BUF:
     // exactly OPS unconditional vector-memory instructions.  Pages outside the
     // sequence (or with an invalid block) read the first rows of the cache
@@ -834,14 +877,14 @@ struct Stream {
         mu = fmaxf(mu, __shfl_xor(mu, 16));
         mu = fmaxf(mu, __shfl_xor(mu, 32));
         const float m_new = fmaxf(m_run, mu);
-        const float alpha = m_run == kNegInf ? 0.f : expf(m_run - m_new);
+        const float alpha = m_run == kNegInf ? 0.f : exp_fast(m_run - m_new);
         float lsum = 0.f;
         wave_lds_sync();  // the previous unit's P.V reads of pl are done
 #pragma unroll
         for (int pp = 0; pp < UP; ++pp)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pr = s[pp][i] != kNegInf ? expf(s[pp][i] - m_new) : 0.f;
+                const float pr = s[pp][i] != kNegInf ? exp_fast(s[pp][i] - m_new) : 0.f;
                 lsum += pr;
                 if (r16 < GMAX) pl[(16 * pp + 4 * rg + i) * GMAX + r16] = pr;
             }
@@ -1532,8 +1575,12 @@ struct TeamShared {
     int bound;           // tiles that may still be fetched
 };
 
-__device__ __forceinline__ int lds_ld(const int* p) { return *static_cast<const volatile int*>(p); }
-__device__ __forceinline__ void lds_st(int* p, int v) { *static_cast<volatile int*>(p) = v; }
+// Control words in LDS, accessed as LDS (a volatile access through a generic
+// pointer would become a flat access, which also waits for the wave's
+// outstanding global loads).
+typedef __attribute__((address_space(3))) volatile int lds_vint;
+__device__ __forceinline__ int lds_ld(const int* p) { return *(const lds_vint*)(p); }
+__device__ __forceinline__ void lds_st(int* p, int v) { *(lds_vint*)(p) = v; }
 // waits for this wave's LDS accesses only (vector-memory loads stay in flight)
 __device__ __forceinline__ void wait_lds() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1553,6 +1600,7 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     S::resolve(P, grp, t, C);
     st.template issue<0>(P, C, 0);
     st.template issue<1>(P, C, 1);
+    int blkN = S::fetch_blocks(P, grp, n, t + nw);  // block ids of the next tile
     // tiles (and rows) fetched, counted when their loads are issued
     unsigned long long loaded = 1, rows = min(S::T, n - t * S::T);
     for (;;) {
@@ -1564,9 +1612,10 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
         const int tn = t + nw;
         const bool haveN = tn < nt && tn < lds_ld(&sh->bound);
         if (haveN) {
-            S::resolve(P, grp, tn, N);
+            S::resolve_from(P, grp, n, tn, blkN, N);
             st.template issue<0>(P, N, 0);
             st.template issue<1>(P, N, 1);
+            blkN = S::fetch_blocks(P, grp, n, tn + nw);
             ++loaded;
             rows += min(S::T, n - tn * S::T);
         }
@@ -1643,8 +1692,8 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                 const float* e = slot + hb * kSlotLane * 64 + lane;
                 const float mt = e[0], lt = e[64];
                 const float Mn = fmaxf(M[hb], mt);
-                const float al = M[hb] == kNegInf ? 0.f : expf(M[hb] - Mn);
-                const float be = mt == kNegInf ? 0.f : expf(mt - Mn);
+                const float al = M[hb] == kNegInf ? 0.f : exp_fast(M[hb] - Mn);
+                const float be = mt == kNegInf ? 0.f : exp_fast(mt - Mn);
                 L[hb] = al * L[hb] + be * lt;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) A[hb][j] = al * A[hb][j] + be * e[64 * (2 + j)];
@@ -1682,7 +1731,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                 pn[hb] = xn;
             }
             // the row's decision is that of its lane 16*hl
-            const bool pass_row = __shfl(pass ? 1 : 0, row0) != 0;
+            const bool pass_row = ((__ballot(pass && fl.cid == 0) >> row0) & 1ull) != 0ull;
             if (act && f >= 1) {
                 streak[hb] = pass_row ? streak[hb] + 1 : 0;
                 if (streak[hb] >= P.patience) {
