@@ -14,9 +14,9 @@ Values are drawn in float32 (or float64 where a construction needs it) and
 rounded once to the stored type with round-to-nearest-even, so the oracle and
 the GPU read identical bytes.
 
-The five named workloads follow the decode-attention configurations of the
-benchmark statement; ``small`` shrinks batch and context for oracle-speed
-tests while keeping every structural feature.
+The five named workloads (``WORKLOADS``) are decode-attention configurations
+from a single fp32 head up to 128K-token paged caches; ``small`` shrinks batch
+and context for oracle-speed tests while keeping every structural feature.
 """
 from __future__ import annotations
 

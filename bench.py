@@ -35,6 +35,29 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def recorded_traffic(path, kernel_src):
+    """HBM bytes per launch recorded from hardware counters (FETCH_SIZE and
+    WRITE_SIZE, each scaled by its reading for a plain copy of known size), or
+    None when the kernel source has changed since they were taken."""
+    import hashlib
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        with open(kernel_src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("kernel_source_sha256") != sha:
+            return None
+        fetch = float(kv["fetch_kib_per_launch"]) / float(kv["fetch_copy_factor"])
+        write = float(kv["write_kib_per_launch"]) / float(kv["write_copy_factor"])
+        return int(round((fetch + write) * 1024))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def alg_bytes(case, used_g, kv_rows_loaded=None):
     """Bytes the method must move for one step (see the measurement notes):
     K and V rows of the tiles each group reads (V only where loaded when rows
@@ -64,6 +87,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-full", action="store_true", help="skip the full-attention comparison")
     ap.add_argument("--flush-mb", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (a known-size "
+                         "reference for hardware byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode-attention path is single-GPU "
@@ -71,6 +97,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     import art_inputs as A
     import kv_cache_bandwidth_amd as art
     from tests.gpu_util import to_device
@@ -171,7 +206,11 @@ def main():
         "tiles_needed": tiles_needed,
         "speculative_tiles": int(st[0]) - tiles_needed,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(
+                         os.path.join(ROOT, "profiles", "traffic_art_team_kernel_ctx32k.txt"),
+                         os.path.join(ROOT, "kv_cache_bandwidth_amd", "csrc", "art_kernels.hip"))
+                     if args.config == 3 else None,
                      "alg_bytes_per_step": int(b_alg)},
         "wall_s_timed_region": round(wall, 4),
     }
