@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define ART_ABI_VERSION 1
+#define ART_ABI_VERSION 2
 
 typedef enum {
     ART_OK = 0,
@@ -80,6 +80,10 @@ typedef struct {
                                     [2] tiles loaded after their group had stopped,
                                     [3] reserved                                      */
     int32_t max_workers;         /* 0 = library default; > 0: work-sharing engine     */
+    int32_t team_helpers;        /* team engine (ART, streamed tiles): helper work-groups
+                                    per group on other CUs, 0..3; 0 = none (default).
+                                    Used only where every work-group of the launch can
+                                    be resident at once; results do not depend on it  */
 } art_desc;
 
 /*

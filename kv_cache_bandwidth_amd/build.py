@@ -14,6 +14,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit multiply-add fusion: the kernels write their fused
+    # multiply-adds out, so every inlined copy of a computation rounds alike
+    "-ffp-contract=off",
 ]
 
 

@@ -2,6 +2,7 @@
 // layout, launch planning.  Never reads device memory, never synchronises.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -13,6 +14,11 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Call counter: every call gets its own epoch, which the team kernel stamps on
+// the words it shares through the workspace, so that none left by an earlier
+// call is taken for one of this call.
+std::atomic<unsigned> g_epoch{0};
 
 art_status fail(art_status s, const char* fmt, ...) {
     char buf[512];
@@ -71,6 +77,8 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     if (!finite_nonneg(d->v_skip_eps)) return fail(ART_E_PARAM, "v_skip_eps %g must be finite and >= 0", d->v_skip_eps);
     if (d->patience < 1) return fail(ART_E_PARAM, "patience %d < 1", d->patience);
     if (d->max_workers < 0) return fail(ART_E_PARAM, "max_workers %d < 0", d->max_workers);
+    if (d->team_helpers < 0 || d->team_helpers > art::kMaxHelpers)
+        return fail(ART_E_PARAM, "team_helpers %d not in 0..%d", d->team_helpers, art::kMaxHelpers);
 
     p = art::Params{};
     p.B = d->batch; p.Hq = d->num_q_heads; p.Hkv = d->num_kv_heads; p.G = G; p.D = d->head_dim; p.T = tile;
@@ -111,6 +119,10 @@ Layout workspace_layout(const Params& p) {
     L.vmax_tag = o; o = align256(o + NG * (size_t)p.nt_max * sizeof(int));
     L.vmax = o; o = align256(o + NG * (size_t)p.nt_max * 16 * sizeof(float));
     L.partials = o; o = align256(o + NG * (size_t)p.splits * p.slot * sizeof(float));
+    const size_t HB = (size_t)(p.G + 3) / 4;
+    L.team_ring = o; o = align256(o + NG * kTeamRingG * HB * kTeamSlotLane * 64 * sizeof(float));
+    L.team_tag = o; o = align256(o + NG * kTeamRingG * sizeof(unsigned long long));
+    L.team_ctl = o; o = align256(o + NG * 2 * sizeof(unsigned long long));
     L.total = o;
     return L;
 }
@@ -182,6 +194,7 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     const long long tiles = (long long)p.NG * p.nt_max;
     if (workers > tiles) workers = tiles > 0 ? tiles : 1;
     p.workers = (int)workers;
+    p.helpers = desc->team_helpers;
     const art::Layout L = art::workspace_layout(p);
     char* ws = static_cast<char*>(desc->workspace);
     p.abort_flag = reinterpret_cast<int*>(ws + L.abort_flag);
@@ -191,6 +204,11 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     p.vmax_tag = reinterpret_cast<int*>(ws + L.vmax_tag);
     p.vmax = reinterpret_cast<float*>(ws + L.vmax);
     p.partials = reinterpret_cast<float*>(ws + L.partials);
+    p.team_ring = reinterpret_cast<float*>(ws + L.team_ring);
+    p.team_tag = reinterpret_cast<unsigned long long*>(ws + L.team_tag);
+    p.team_ctl = reinterpret_cast<unsigned long long*>(ws + L.team_ctl);
+    p.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    if (p.epoch == 0) p.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;  // 0 never stamps
     const int rc = (p.art || p.vskip) ? art::launch_art(p, stream) : art::launch_full(p, stream);
     if (rc != 0) return fail(ART_E_HIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)rc));
     return ART_OK;

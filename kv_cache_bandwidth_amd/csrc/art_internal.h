@@ -13,6 +13,9 @@ constexpr int kRing = 128;        // ring slots per group (tiles in flight ahead
 constexpr int kMaxG = 16;         // query heads per KV head
 constexpr int kWavesPerWG = 4;    // independent waves per work-group
 constexpr int kMaxDeciders = 512; // decider waves at most (one per group up to this many groups)
+constexpr int kTeamRingG = 32;    // global ring slots per group for the tiles of helper teams
+constexpr int kTeamSlotLane = 10; // floats per lane per head block in a team slot: m, l, 8 dims
+constexpr int kMaxHelpers = 3;    // helper work-groups per group at most (team engine)
 constexpr unsigned long long kWaitTicks = 50000000ull;  // 0.5 s of the 100 MHz device clock:
                                                       // longest any wait may last before the kernel gives up
 constexpr int kSlotHeader = 48;   // floats before the accumulator block of a partial:
@@ -62,6 +65,11 @@ struct Params {
     int* vmax_tag;      // [NG][nt_max]
     float* vmax;        // [NG][nt_max][16]
     float* partials;    // [NG][splits][slot]
+    float* team_ring;   // [NG][kTeamRingG][HB][kTeamSlotLane][64]: tiles of helper teams
+    unsigned long long* team_tag;  // [NG][kTeamRingG]: (epoch << 32) | (tile + 1)
+    unsigned long long* team_ctl;  // [NG][2]: (epoch << 32) | frontier, (epoch << 32) | bound
+    unsigned epoch;     // distinct per call: stale team words of earlier calls never match
+    int helpers;        // helper work-groups per group (team kernel)
     int slot;           // floats per partial: kSlotHeader + G*D
     // launch
     int deciders;       // decider waves of the persistent kernel (each owns whole groups)
@@ -72,7 +80,7 @@ struct Params {
 
 // Workspace layout for a Params (offsets in bytes, all 256-byte aligned).
 struct Layout {
-    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, total;
+    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, team_ring, team_tag, team_ctl, total;
 };
 Layout workspace_layout(const Params& p);
 

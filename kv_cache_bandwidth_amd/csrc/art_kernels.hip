@@ -888,7 +888,7 @@ struct Stream {
                 lsum += pr;
                 if (r16 < GMAX) pl[(16 * pp + 4 * rg + i) * GMAX + r16] = pr;
             }
-        l_run = alpha * l_run + lsum;
+        l_run = fmaf(alpha, l_run, lsum);
         m_run = m_new;
         float ah[GMAX];
 #pragma unroll
@@ -1073,9 +1073,9 @@ __device__ __forceinline__ void sm_merge(float& m, float& l, float (&a)[8], floa
     if (mn == kNegInf) return;
     const float w1 = m == kNegInf ? 0.f : expf(m - mn);
     const float w2 = m2 == kNegInf ? 0.f : expf(m2 - mn);
-    l = w1 * l + w2 * l2;
+    l = fmaf(w1, l, w2 * l2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = w1 * a[j] + w2 * a2[j];
+    for (int j = 0; j < 8; ++j) a[j] = fmaf(w1, a[j], w2 * a2[j]);
     m = mn;
 }
 
@@ -1142,7 +1142,7 @@ __device__ __forceinline__ int fold_window(const Params& P, int grp, int hb, int
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         x[j] = ra[j] * invL;
-        xn2 += x[j] * x[j];
+        xn2 = fmaf(x[j], x[j], xn2);
     }
     const float xn = sqrtf(xn2);
     const int srcp = row0 | (i > 0 ? i - 1 : 0);
@@ -1166,8 +1166,8 @@ __device__ __forceinline__ int fold_window(const Params& P, int grp, int hb, int
             float s2 = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float dl = x[j] * ix - pp[j] * ip;
-                s2 += dl * dl;
+                const float dl = fmaf(x[j], ix, -(pp[j] * ip));
+                s2 = fmaf(dl, dl, s2);
             }
             dd = 0.5f * s2;
         }
@@ -1550,28 +1550,36 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P)
     }
 }
 
-// ------------------------------------------------------------------ team kernel (one work-group per group)
+// ------------------------------------------------------------------ team kernel (work-groups per group)
 //
-// The waves of one work-group (one CU) serve one group.  Waves 1.. are tile
-// workers: worker i streams tiles i, i + nw, i + 2nw, ... (nw workers), the
-// loads of each tile issued before the previous one is handed over, and
-// hands every tile's partial (max, sum and V accumulator per head, in the
-// fold mapping) to wave 0 through a ring of LDS slots.  Wave 0 folds the
-// tiles one at a time in tile order into the group's running state, which is
-// the sequential traversal itself: after each tile the probe of every active
-// head is compared with the previous one, a head whose streak reaches the
-// patience stops and its output is written at once, and once every head has
-// stopped the bound in LDS drops so that no worker fetches a further tile
-// (at most one tile per worker is loaded speculatively).  No barrier after
-// the start: the hand-over is an LDS store of the slot, a wait for it to
-// complete, then the tag.
-constexpr int kTeamRing = 8;       // LDS slots between the workers and the decider
-constexpr int kSlotLane = 10;      // floats per lane per head block in a slot: m, l, 8 dims
+// A group is served by a primary work-group and, when the chip has room for
+// them alongside every primary, up to kMaxHelpers helper work-groups on other
+// CUs.  Wave 0 of the primary is the decider; its other waves, and every wave
+// of the helpers, are tile workers.  Tiles are assigned statically: over
+// every W consecutive tiles the first nA go to the primary's workers in turn
+// and the rest to the helpers' workers in turn, so every worker streams its
+// own arithmetic sequence of tiles, the loads of each issued before the
+// previous one is handed over.  A worker hands each tile's partial (max, sum
+// and V accumulator per head, in the fold mapping) to the decider: primary
+// workers through a ring of LDS slots (store, wait for LDS, tag), helper
+// workers through a ring in global memory (coherent stores, a re-read of the
+// last word, then the tag).  The decider folds the tiles one at a time in tile
+// order into the group's running state, which is the sequential traversal
+// itself: after each tile the probe of every active head is compared with the
+// previous one, a head whose streak reaches the patience stops and its output
+// is written at once, and once every head has stopped the bound drops (in LDS
+// and in global memory), so that no worker fetches a further tile: at most
+// one tile per worker, two for a helper, is loaded past the stop.  Helpers
+// are launched cooperatively, so every work-group of the grid is resident.
+// Words shared through global memory carry the call's epoch, so that none
+// left by an earlier call is taken for one of this call.
+constexpr int kTeamRing = 8;  // LDS slots between the primary's workers and the decider
+constexpr int kSlotLane = kTeamSlotLane;
 
 struct TeamShared {
-    int tag[kTeamRing];  // t + 1 once slot t % kTeamRing holds tile t
+    int tag[kTeamRing];  // t + 1 once slot (ordinal of t among the primary's tiles) % kTeamRing holds tile t
     int err[kTeamRing];  // the tile met an invalid block id
-    int frontier;        // tiles folded by the decider
+    int frontier;        // the primary's tiles folded by the decider (a count of ordinals)
     int bound;           // tiles that may still be fetched
 };
 
@@ -1588,57 +1596,130 @@ __device__ __forceinline__ void wait_lds() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <class S>
-__device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int nt, int idx, int nw, S& st,
-                                            float* ring, TeamShared* sh) {
+// epoch-stamped words
+__device__ __forceinline__ unsigned long long stamp(unsigned epoch, unsigned v) {
+    return ((unsigned long long)epoch << 32) | v;
+}
+__device__ __forceinline__ int unstamp(unsigned long long w, unsigned epoch, int dflt) {
+    return (unsigned)(w >> 32) == epoch ? (int)(unsigned)w : dflt;
+}
+
+// Static assignment of a group's tiles to the workers of its teams.
+struct TeamPlan {
+    int nA, nH, W;  // primary workers, helper workers (all helpers), period
+    __device__ TeamPlan(int nA_, int nH_) : nA(nA_), nH(nH_), W(nA_ + nH_) {}
+    __device__ bool primary(int t) const { return t % W < nA; }
+    __device__ int ordA(int t) const { return (t / W) * nA + t % W; }  // among the primary's tiles
+    __device__ int tileA(int o) const { return (o / nA) * W + o % nA; }
+    __device__ int ordH(int t) const { return (t / W) * nH + t % W - nA; }  // among the helpers' tiles
+    __device__ int tileH(int o) const { return (o / nH) * W + nA + o % nH; }
+};
+
+// One tile worker: tiles first, first + W, ... of the group.  PRIMARY: hands
+// over through LDS; else through the group's global ring.
+template <class S, bool PRIMARY>
+__device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int nt, int first, const TeamPlan& plan,
+                                            S& st, float* ring, TeamShared* sh) {
     constexpr int HBM = S::HBM;
     const int lane = lane_id();
-    int t = idx;
+    int t = first;
     if (t >= nt) return;
+    // ordinal of tile t among the primary's (or the helpers') tiles; a slot is
+    // free once the decider has folded the ordinal a ring's length before
+    int o1 = PRIMARY ? first : first - plan.nA;
+    const int ostep = PRIMARY ? plan.nA : plan.nH;
+    unsigned long long* gctl = P.team_ctl + 2 * grp;
     typename S::TileRef C, N;
     st.load_q(P, grp);  // before the tile's loads: consume() counts those in issue order
     S::resolve(P, grp, t, C);
     st.template issue<0>(P, C, 0);
     st.template issue<1>(P, C, 1);
-    int blkN = S::fetch_blocks(P, grp, n, t + nw);  // block ids of the next tile
+    int blkN = S::fetch_blocks(P, grp, n, t + plan.W);  // block ids of the next tile
+    // helpers: the group's bound and frontier, loaded before a tile's loads and
+    // read once those have landed (a tile late at worst)
+    unsigned long long wb = 0, wf = 0;
+    int bnd = nt, frt = 0;
     // tiles (and rows) fetched, counted when their loads are issued
     unsigned long long loaded = 1, rows = min(S::T, n - t * S::T);
     for (;;) {
-        if (t >= lds_ld(&sh->bound)) break;  // the group stopped before this tile
+        if constexpr (PRIMARY) bnd = lds_ld(&sh->bound);
+        if (t >= bnd) break;  // the group stopped before this tile
         st.template consume<0>(P, C, 0, true);
+        if constexpr (!PRIMARY) {
+            bnd = unstamp(wb, P.epoch, bnd);
+            frt = unstamp(wf, P.epoch, frt);
+        }
         st.template consume<1>(P, C, 1, false);
         typename S::Out o;
         st.flush(P, o);
-        const int tn = t + nw;
-        const bool haveN = tn < nt && tn < lds_ld(&sh->bound);
+        const int tn = t + plan.W;
+        if constexpr (PRIMARY) bnd = lds_ld(&sh->bound);
+        const bool haveN = tn < nt && tn < bnd;
         if (haveN) {
             S::resolve_from(P, grp, n, tn, blkN, N);
+            if constexpr (!PRIMARY) {
+                wb = cld(gctl + 1);
+                wf = cld(gctl + 0);
+            }
             st.template issue<0>(P, N, 0);
             st.template issue<1>(P, N, 1);
-            blkN = S::fetch_blocks(P, grp, n, tn + nw);
+            blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
             ++loaded;
             rows += min(S::T, n - tn * S::T);
         }
-        // the slot of tile t is free once the decider has folded tile t - kTeamRing
-        const Deadline dl;
-        while (t - kTeamRing >= lds_ld(&sh->frontier) && t < lds_ld(&sh->bound) && !dl.passed())
-            __builtin_amdgcn_s_sleep(1);
-        if (t < lds_ld(&sh->bound) && t - kTeamRing < lds_ld(&sh->frontier)) {
-            float* slot = ring + (t % kTeamRing) * (HBM * kSlotLane * 64);
-#pragma unroll
-            for (int hb = 0; hb < HBM; ++hb) {
-                float* e = slot + hb * kSlotLane * 64 + lane;
-                e[0] = o.mf[hb];
-                e[64] = o.lf[hb];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) e[64 * (2 + j)] = o.a[hb][j];
+        // hand tile t over once its slot's previous tile has been folded
+        if constexpr (PRIMARY) {
+            const int s = o1 % kTeamRing;
+            if (o1 - kTeamRing >= lds_ld(&sh->frontier)) {
+                const Deadline dl;
+                while (o1 - kTeamRing >= lds_ld(&sh->frontier) && t < lds_ld(&sh->bound) && !dl.passed())
+                    __builtin_amdgcn_s_sleep(1);
             }
-            if (lane == 0) lds_st(&sh->err[t % kTeamRing], C.err);
-            wait_lds();  // the slot is written before its tag
-            if (lane == 0) lds_st(&sh->tag[t % kTeamRing], t + 1);
+            if (t < lds_ld(&sh->bound) && o1 - kTeamRing < lds_ld(&sh->frontier)) {
+                float* slot = ring + s * (HBM * kSlotLane * 64);
+#pragma unroll
+                for (int hb = 0; hb < HBM; ++hb) {
+                    float* e = slot + hb * kSlotLane * 64 + lane;
+                    e[0] = o.mf[hb];
+                    e[64] = o.lf[hb];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) e[64 * (2 + j)] = o.a[hb][j];
+                }
+                if (lane == 0) lds_st(&sh->err[s], C.err);
+                wait_lds();  // the slot is written before its tag
+                if (lane == 0) lds_st(&sh->tag[s], t + 1);
+            }
+        } else {
+            const int s = o1 % kTeamRingG;
+            if (o1 - kTeamRingG >= frt) {
+                const Deadline dl;
+                while (o1 - kTeamRingG >= frt && t < bnd && !dl.passed()) {
+                    __builtin_amdgcn_s_sleep(8);
+                    bnd = unstamp(cld(gctl + 1), P.epoch, bnd);
+                    frt = unstamp(cld(gctl + 0), P.epoch, frt);
+                }
+            }
+            if (t < bnd && o1 - kTeamRingG < frt) {
+                float* slot = P.team_ring + ((long long)grp * kTeamRingG + s) * (HBM * kSlotLane * 64);
+#pragma unroll
+                for (int hb = 0; hb < HBM; ++hb) {
+                    float* e = slot + hb * kSlotLane * 64 + lane;
+                    cst(e, o.mf[hb]);
+                    cst(e + 64, o.lf[hb]);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) cst(e + 64 * (2 + j), o.a[hb][j]);
+                }
+                // the re-read returns once every store before it has completed
+                const float last = cld(slot + (HBM - 1) * kSlotLane * 64 + 64 * 9 + lane);
+                asm volatile("" ::"v"(last) : "memory");
+                if (lane == 0)
+                    cst(P.team_tag + (long long)grp * kTeamRingG + s,
+                        stamp(P.epoch, (unsigned)(t + 1) | ((unsigned)C.err << 31)));
+            }
         }
         if (!haveN) break;
         t = tn;
+        o1 += ostep;
         C = N;
     }
     // loads of a tile fetched past the stop may still be landing (in LDS too)
@@ -1646,151 +1727,300 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     count_stats(P, loaded, rows);
 }
 
-// Folds tiles 0, 1, ... of the group in order; writes each head's output as it
-// stops.  A wait longer than kWaitTicks (impossible unless a worker faulted)
-// ends the group: its unfinished heads get tiles_used = -2 and NaN.
+// sum of squares of 8 values as a balanced tree (short dependency chain)
+__device__ __forceinline__ float sumsq8(const float (&v)[8]) {
+    const float a = fmaf(v[1], v[1], v[0] * v[0]), b = fmaf(v[3], v[3], v[2] * v[2]);
+    const float c = fmaf(v[5], v[5], v[4] * v[4]), d = fmaf(v[7], v[7], v[6] * v[6]);
+    return (a + b) + (c + d);
+}
+
+// Running state of the group's heads, in the decider (fold mapping).
 template <int HBM>
-__device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const float* ring,
-                                             TeamShared* sh) {
-    const int lane = lane_id();
-    const FoldLanes fl(P);
-    const int G = P.G, row0 = lane & ~15;
+struct DeciderState {
     float M[HBM], L[HBM], A[HBM][8], prev[HBM][8], pn[HBM];
     int streak[HBM], U[HBM], err[HBM];
+    int ug;  // largest tiles_used so far
+};
+
+// Folds tile f (this lane's m, l and 8 accumulator values per head block, and
+// the tile's error flag) into D; writes the output of each head that stops.
+// Returns true once every head has stopped.
+template <int HBM>
+__device__ __forceinline__ bool fold_tile(const Params& P, int grp, const FoldLanes& fl, DeciderState<HBM>& D, int f,
+                                          const float (&mt)[HBM], const float (&lt)[HBM], const float (&at)[HBM][8],
+                                          int et) {
+    const int lane = lane_id(), row0 = lane & ~15;
+    bool any = false;
+    static_for<0, HBM>([&](auto hbc) {
+        constexpr int hb = decltype(hbc)::value;
+        const int h = hb * 4 + fl.hl;
+        const bool act = D.U[hb] < 0;
+        bool pass = false;
+        if (act) {
+            const float Mn = fmaxf(D.M[hb], mt[hb]);
+            const float al = D.M[hb] == kNegInf ? 0.f : exp_fast(D.M[hb] - Mn);
+            const float be = mt[hb] == kNegInf ? 0.f : exp_fast(mt[hb] - Mn);
+            D.L[hb] = fmaf(al, D.L[hb], be * lt[hb]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) D.A[hb][j] = fmaf(al, D.A[hb][j], be * at[hb][j]);
+            D.M[hb] = Mn;
+            D.err[hb] |= et;
+            // probe: head dims 0..7 are this row's lane 16*hl (cid 0); the
+            // hardware reciprocal and square root (about 1 ulp) keep the
+            // per-tile chain short
+            const float invL = __builtin_amdgcn_rcpf(D.L[hb]);
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = D.A[hb][j] * invL;
+            const float xn = __builtin_amdgcn_sqrtf(sumsq8(x));
+            if (f >= 1) {
+                float ds, dd;
+                if (xn == 0.f || D.pn[hb] == 0.f) {
+                    ds = dd = INFINITY;
+                } else {
+                    const float ix = __builtin_amdgcn_rcpf(xn), ip = __builtin_amdgcn_rcpf(D.pn[hb]);
+                    ds = fabsf(xn - D.pn[hb]) * ip;
+                    // 1 - cos as half the squared distance of the unit vectors
+                    float dl2[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) dl2[j] = fmaf(x[j], ix, -(D.prev[hb][j] * ip));
+                    dd = 0.5f * sumsq8(dl2);
+                }
+                pass = ds < P.eps_scale && dd < P.eps_dir;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) D.prev[hb][j] = x[j];
+            D.pn[hb] = xn;
+        }
+        // the row's decision is that of its lane 16*hl
+        const bool pass_row = ((__ballot(pass && fl.cid == 0) >> row0) & 1ull) != 0ull;
+        if (act && f >= 1) {
+            D.streak[hb] = pass_row ? D.streak[hb] + 1 : 0;
+            if (D.streak[hb] >= P.patience) {
+                D.U[hb] = f + 1;
+                D.ug = max(D.ug, D.U[hb]);
+                write_head_out(P, grp, h, fl, D.A[hb], D.L[hb], D.err[hb], D.U[hb]);
+            }
+        }
+        any |= D.U[hb] < 0;
+    });
+    return __ballot(any) == 0ull;
+}
+
+// Folds tiles 0, 1, ... of the group in order: the primary's from LDS, the
+// helpers' from the global ring, a batch at a time.  A wait longer than
+// kWaitTicks (impossible unless a worker faulted) ends the group: its
+// unfinished heads get tiles_used = -2 and NaN.
+template <int HBM>
+__device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const TeamPlan& plan, const float* ring,
+                                             TeamShared* sh) {
+    constexpr int kBatch = 8 / HBM;  // helper tiles loaded at once
+    const int lane = lane_id();
+    const FoldLanes fl(P);
+    const int G = P.G;
+    unsigned long long* gctl = P.team_ctl + 2 * grp;
+    const unsigned long long* gtag = P.team_tag + (long long)grp * kTeamRingG;
+    DeciderState<HBM> D;
 #pragma unroll
     for (int hb = 0; hb < HBM; ++hb) {
         const int h = hb * 4 + fl.hl;
-        M[hb] = kNegInf; L[hb] = 0.f; pn[hb] = 0.f; streak[hb] = 0; err[hb] = 0;
-        U[hb] = (hb < fl.HB && h < G) ? -1 : 0;
+        D.M[hb] = kNegInf; D.L[hb] = 0.f; D.pn[hb] = 0.f; D.streak[hb] = 0; D.err[hb] = 0;
+        D.U[hb] = (hb < fl.HB && h < G) ? -1 : 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { A[hb][j] = 0.f; prev[hb][j] = 0.f; }
+        for (int j = 0; j < 8; ++j) { D.A[hb][j] = 0.f; D.prev[hb][j] = 0.f; }
     }
-    int ug = 0;  // largest tiles_used so far
+    D.ug = 0;
     bool finished = false, gave_up = false;
-    Deadline dl;
-    for (int f = 0; f < nt; ++f) {
-        const int s = f % kTeamRing;
-        while (lds_ld(&sh->tag[s]) != f + 1) {
-            if (dl.passed()) {
-                gave_up = true;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        if (gave_up) break;
-        dl = Deadline();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the slot is read after its tag
-        const int et = lds_ld(&sh->err[s]);
+    // A primary tile's slot: the tag is read first and the data right after,
+    // without a wait in between.  A wave's LDS accesses execute in order and a
+    // worker stores the data before the tag, so when the tag shows the tile the
+    // data read after it is that tile's.  The next tile's slot is read while
+    // the current one is folded.
+    auto read_slot = [&](int s, int& tag, int& err, float (&mt)[HBM], float (&lt)[HBM], float (&at)[HBM][8]) {
+        tag = lds_ld(&sh->tag[s]);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        err = lds_ld(&sh->err[s]);
         const float* slot = ring + s * (HBM * kSlotLane * 64);
-        bool any = false;
-        static_for<0, HBM>([&](auto hbc) {
-            constexpr int hb = decltype(hbc)::value;
-            const int h = hb * 4 + fl.hl;
-            const bool act = U[hb] < 0;
-            bool pass = false;
-            if (act) {
-                const float* e = slot + hb * kSlotLane * 64 + lane;
-                const float mt = e[0], lt = e[64];
-                const float Mn = fmaxf(M[hb], mt);
-                const float al = M[hb] == kNegInf ? 0.f : exp_fast(M[hb] - Mn);
-                const float be = mt == kNegInf ? 0.f : exp_fast(mt - Mn);
-                L[hb] = al * L[hb] + be * lt;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) A[hb][j] = al * A[hb][j] + be * e[64 * (2 + j)];
-                M[hb] = Mn;
-                err[hb] |= et;
-                // probe: head dims 0..7 are this row's lane 16*hl (cid 0)
-                const float invL = 1.f / L[hb];
-                float x[8], xn2 = 0.f;
+        for (int hb = 0; hb < HBM; ++hb) {
+            const float* e = slot + hb * kSlotLane * 64 + lane;
+            mt[hb] = e[0];
+            lt[hb] = e[64];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    x[j] = A[hb][j] * invL;
-                    xn2 += x[j] * x[j];
-                }
-                const float xn = sqrtf(xn2);
-                if (f >= 1) {
-                    float ds, dd;
-                    if (xn == 0.f || pn[hb] == 0.f) {
-                        ds = dd = INFINITY;
-                    } else {
-                        ds = fabsf(xn - pn[hb]) / pn[hb];
-                        // 1 - cos as half the squared distance of the unit vectors
-                        const float ix = 1.f / xn, ip = 1.f / pn[hb];
-                        float s2 = 0.f;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float dl2 = x[j] * ix - prev[hb][j] * ip;
-                            s2 += dl2 * dl2;
-                        }
-                        dd = 0.5f * s2;
-                    }
-                    pass = ds < P.eps_scale && dd < P.eps_dir;
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) prev[hb][j] = x[j];
-                pn[hb] = xn;
-            }
-            // the row's decision is that of its lane 16*hl
-            const bool pass_row = ((__ballot(pass && fl.cid == 0) >> row0) & 1ull) != 0ull;
-            if (act && f >= 1) {
-                streak[hb] = pass_row ? streak[hb] + 1 : 0;
-                if (streak[hb] >= P.patience) {
-                    U[hb] = f + 1;
-                    ug = max(ug, U[hb]);
-                    write_head_out(P, grp, h, fl, A[hb], L[hb], err[hb], U[hb]);
-                }
-            }
-            any |= U[hb] < 0;
-        });
-        if (__ballot(any) == 0ull) {
-            finished = true;
-            break;
+            for (int j = 0; j < 8; ++j) at[hb][j] = e[64 * (2 + j)];
         }
-        if (lane == 0) lds_st(&sh->frontier, f + 1);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    // tags of the helpers' tiles t0 .. t0 + cnt - 1 (helper ordinals h0 ..): lane i polls one
+    auto poll_tags = [&](int h0, int cnt) -> unsigned long long {
+        return lane < cnt ? cld(gtag + (h0 + lane) % kTeamRingG) : 0ull;
+    };
+    auto tags_ready = [&](unsigned long long tg, int t0, int cnt) {
+        const bool ok = lane >= cnt ||
+                        ((unsigned)(tg >> 32) == P.epoch && ((unsigned)tg & 0x7fffffffu) == (unsigned)(t0 + lane + 1));
+        return __ballot(!ok) == 0ull;
+    };
+    // position: tile f, f % W = pk, oA of the primary's and oH of the helpers' tiles folded
+    int f = 0, pk = 0, oA = 0, oH = 0;
+    int tagc = 0, errc = 0;
+    float mtc[HBM], ltc[HBM], atc[HBM][8];
+    read_slot(0, tagc, errc, mtc, ltc, atc);
+    // tags of the helpers' tiles of the current period, polled when the period starts
+    unsigned long long tgp = 0;
+    int hp0 = plan.nA, hpc = 0;
+    if (plan.nH) {
+        hpc = max(0, min(plan.nH, nt - hp0));
+        tgp = poll_tags(0, hpc);
+    }
+    while (f < nt) {
+        if (pk < plan.nA) {
+            const int s = oA % kTeamRing;
+            if (tagc != f + 1) {
+                // not there yet: poll the tag alone (the workers use LDS too), then read the slot
+                const Deadline dl;
+                while (lds_ld(&sh->tag[s]) != f + 1) {
+                    if (dl.passed()) {
+                        gave_up = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (gave_up) break;
+                read_slot(s, tagc, errc, mtc, ltc, atc);
+            }
+            float mt[HBM], lt[HBM], at[HBM][8];
+            const int et = errc;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                mt[hb] = mtc[hb];
+                lt[hb] = ltc[hb];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) at[hb][j] = atc[hb][j];
+            }
+            // the next tile's slot, if it is the primary's too
+            if (f + 1 < nt && (pk + 1 < plan.nA || (pk + 1 == plan.W && plan.nA > 0)))
+                read_slot((oA + 1) % kTeamRing, tagc, errc, mtc, ltc, atc);
+            finished = fold_tile<HBM>(P, grp, fl, D, f, mt, lt, at, et);
+            ++f;
+            ++oA;
+            if (++pk == plan.W) pk = 0;
+            if (pk == 0 && plan.nH && f < nt) {
+                hp0 = f + plan.nA;
+                hpc = max(0, min(plan.nH, nt - hp0));
+                tgp = poll_tags(oH, hpc);
+            }
+        } else {
+            // the helpers' tiles of this period (from hp0, helper ordinals from
+            // oH - (f - hp0)), a batch of up to kBatch at a time
+            const int h0 = oH - (f - hp0);
+            const int bcnt = min(kBatch, hp0 + hpc - f);
+            if (!tags_ready(tgp, hp0, hpc)) {
+                const Deadline dl;
+                for (;;) {
+                    if (dl.passed()) {
+                        gave_up = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                    tgp = poll_tags(h0, hpc);
+                    if (tags_ready(tgp, hp0, hpc)) break;
+                }
+                if (gave_up) break;
+            }
+            const int errl = (int)((unsigned)tgp >> 31);
+            float mt[kBatch][HBM], lt[kBatch][HBM], at[kBatch][HBM][8];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int si = (oH + i) % kTeamRingG;
+                const float* slot = P.team_ring + ((long long)grp * kTeamRingG + si) * (HBM * kSlotLane * 64);
+#pragma unroll
+                for (int hb = 0; hb < HBM; ++hb) {
+                    const float* e = slot + hb * kSlotLane * 64 + lane;
+                    const bool v = i < bcnt;
+                    mt[i][hb] = v ? cld(e) : kNegInf;
+                    lt[i][hb] = v ? cld(e + 64) : 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) at[i][hb][j] = v ? cld(e + 64 * (2 + j)) : 0.f;
+                }
+            }
+            // the next period's first (primary) slot, read while this batch is folded
+            if (f + bcnt < nt && pk + bcnt == plan.W) read_slot(oA % kTeamRing, tagc, errc, mtc, ltc, atc);
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (i < bcnt && !finished) {
+                    finished = fold_tile<HBM>(P, grp, fl, D, f, mt[i], lt[i], at[i], __shfl(errl, f - hp0));
+                    ++f;
+                    ++oH;
+                    if (++pk == plan.W) pk = 0;
+                }
+            }
+            if (pk == 0 && f < nt) {
+                hp0 = f + plan.nA;
+                hpc = max(0, min(plan.nH, nt - hp0));
+                tgp = poll_tags(oH, hpc);
+            }
+        }
+        if (finished) break;
+        if (lane == 0) {
+            lds_st(&sh->frontier, oA);
+            if (plan.nH) cst(gctl + 0, stamp(P.epoch, (unsigned)oH));
+        }
     }
     // heads that never stopped used every tile (or the group gave up)
 #pragma unroll
     for (int hb = 0; hb < HBM; ++hb) {
         const int h = hb * 4 + fl.hl;
-        if (U[hb] < 0) {
+        if (D.U[hb] < 0) {
             if (gave_up) {
-                const FoldLanes f2 = fl;
                 float nan8[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) nan8[j] = NAN;
-                write_head_out(P, grp, h, f2, nan8, 1.f, 0, -2);
+                write_head_out(P, grp, h, fl, nan8, 1.f, 0, -2);
             } else {
-                write_head_out(P, grp, h, fl, A[hb], L[hb], err[hb], nt);
+                write_head_out(P, grp, h, fl, D.A[hb], D.L[hb], D.err[hb], nt);
             }
         }
     }
-    int ugw = finished ? ug : 0;
+    int ugw = finished ? D.ug : 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ugw = max(ugw, __shfl_xor(ugw, o));
-    if (lane == 0) lds_st(&sh->bound, finished ? ugw : (gave_up ? 0 : nt));
+    const int bound = finished ? ugw : (gave_up ? 0 : nt);
+    if (lane == 0) {
+        lds_st(&sh->bound, bound);
+        if (plan.nH) cst(gctl + 1, stamp(P.epoch, (unsigned)bound));
+    }
 }
 
+// Grid: NG primaries, then P.helpers rounds of NG helpers (helper r of group
+// g is work-group (1 + r) * NG + g).
 template <class S>
 __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     extern __shared__ float lds[];
     constexpr int HBM = S::HBM, TEAM = S::TEAM;
     const int wv = wave_id(), lane = lane_id();
     const int G = P.G;
-    const int grp = blockIdx.x;
+    const int grp = blockIdx.x % P.NG, team = blockIdx.x / P.NG;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
     const int n = P.ctx_lens[b];
     const bool bad = n < 0 || n > P.cap;
     const int nt = (bad || n == 0) ? 0 : (n + S::T - 1) / S::T;
     if (nt == 0) {
         // empty row: zero output, no tiles; invalid length: NaN, -1
-        if (wv == 0) {
+        if (team == 0 && wv == 0) {
             const long long row0 = (long long)b * P.Hq + (long long)g * G;
             for (int k = lane; k < G * P.D; k += 64) P.out[row0 * P.D + k] = bad ? NAN : 0.f;
             for (int h = lane; h < G; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
         }
         return;
     }
+    const TeamPlan plan(TEAM - 1, P.helpers * TEAM);
     const size_t wave_floats = S::lds_floats(P);
+    if (team > 0) {
+        S st;
+        st.init(lds + wv * wave_floats);
+        team_worker<S, false>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st, nullptr, nullptr);
+        return;
+    }
     float* ring = lds + (TEAM - 1) * wave_floats;  // [kTeamRing][HBM][kSlotLane][64]
     TeamShared* sh = reinterpret_cast<TeamShared*>(ring + kTeamRing * HBM * kSlotLane * 64);
     if (wv == 0) {
@@ -1805,18 +2035,22 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     }
     __syncthreads();
     if (wv == 0) {
-        team_decider<HBM>(P, grp, nt, ring, sh);
+        // the decider's per-tile chain is latency-bound: let its SIMD issue it first
+        __builtin_amdgcn_s_setprio(3);
+        team_decider<HBM>(P, grp, nt, plan, ring, sh);
     } else {
         S st;
         st.init(lds + (wv - 1) * wave_floats);
-        team_worker<S>(P, grp, n, nt, wv - 1, TEAM - 1, st, ring, sh);
+        team_worker<S, true>(P, grp, n, nt, wv - 1, plan, st, ring, sh);
     }
 }
 
 template <class S>
 size_t team_lds_bytes(const Params& p) {
-    return ((size_t)(S::TEAM - 1) * S::lds_floats(p) + (size_t)kTeamRing * S::HBM * kSlotLane * 64) * sizeof(float) +
-           sizeof(TeamShared);
+    const size_t primary = ((size_t)(S::TEAM - 1) * S::lds_floats(p) + (size_t)kTeamRing * S::HBM * kSlotLane * 64) *
+                               sizeof(float) + sizeof(TeamShared);
+    const size_t helper = (size_t)S::TEAM * S::lds_floats(p) * sizeof(float);
+    return primary > helper ? primary : helper;
 }
 
 // Full mode, one tile at a time: split sp of group grp covers a fixed tile range.
@@ -1869,10 +2103,10 @@ __global__ __launch_bounds__(256) void art_full_kernel(Params P) {
                 const bool first = M[hb] == kNegInf;
                 const float al = first ? 0.f : expf(M[hb] - mn);
                 const float be = expf(ml - mn);
-                L[hb] = al * L[hb] + be * ll;
+                L[hb] = fmaf(al, L[hb], be * ll);
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    A[hb][j] = first ? be * o.a[hb][j] : al * A[hb][j] + be * o.a[hb][j];
+                    A[hb][j] = first ? be * o.a[hb][j] : fmaf(al, A[hb][j], be * o.a[hb][j]);
                 M[hb] = mn;
             }
         }
@@ -1990,11 +2224,11 @@ __global__ __launch_bounds__(64) void art_combine_kernel(Params P) {
             const bool first = M == kNegInf;
             const float al = first ? 0.f : expf(M - mn);
             const float be = expf(ml - mn);
-            L = al * L + be * ll;
+            L = fmaf(al, L, be * ll);
             if (fl.cvalid) {
                 const float* a = slot + kSlotHeader + h * D + 8 * fl.cid;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) a8[j] = first ? be * a[j] : al * a8[j] + be * a[j];
+                for (int j = 0; j < 8; ++j) a8[j] = first ? be * a[j] : fmaf(al, a8[j], be * a[j]);
             }
             M = mn;
         }
@@ -2059,9 +2293,35 @@ int run_tile(const Params& p, hipStream_t s, bool art) {
     return launch_split<decltype(&art_full_kernel<Tile>), Tile>(p, s, &art_full_kernel<Tile>);
 }
 
+// Helpers (as many as requested, up to what fits) only where every
+// work-group of the grid can be resident at once (cooperative launch); else
+// the primaries alone.
 template <class S>
-int launch_team(const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL(art_team_kernel<S>, dim3(p.NG), dim3(S::TEAM * 64), team_lds_bytes<S>(p), s, p);
+int launch_team(const Params& p0, hipStream_t s) {
+    Params p = p0;
+    const size_t lds = team_lds_bytes<S>(p);
+    p.helpers = 0;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (p0.helpers > 0 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_team_kernel<S>, S::TEAM * 64, lds) == hipSuccess &&
+        per_cu > 0) {
+        const long long resident = (long long)per_cu * cus;
+        long long h = resident / p.NG - 1;
+        if (h > p0.helpers) h = p0.helpers;
+        if (h > 0) {
+            p.helpers = (int)h;
+            void* args[] = {&p};
+            const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&art_team_kernel<S>),
+                                                            dim3(p.NG * (1 + p.helpers)), dim3(S::TEAM * 64), args,
+                                                            (unsigned)lds, s);
+            if (e == hipSuccess) return 0;
+            (void)hipGetLastError();  // cannot be resident together: primaries alone
+            p.helpers = 0;
+        }
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(art_team_kernel<S>, dim3(p.NG), dim3(S::TEAM * 64), lds, s, p);
     return (int)hipGetLastError();
 }
 

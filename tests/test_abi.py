@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = art.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.art_abi_version() == 1
+    assert lib.art_abi_version() == 2
 
 
 def desc(**kw):
@@ -70,6 +70,8 @@ def test_valid_desc_passes():
     (dict(v_skip_eps=-1.0), -5),
     (dict(v_skip_eps=float("nan")), -5),
     (dict(max_workers=-3), -5),
+    (dict(team_helpers=-1), -5),
+    (dict(team_helpers=4), -5),
 ])
 def test_bad_desc_rejected(kw, code):
     assert B.validate(desc(**kw), 64, 1e-3, 1e-4) == code

@@ -17,7 +17,7 @@ def _run_and_check(case, label, **kw):
     log(f"[parity] {label}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} d={case.d} "
         f"ctx={case.ctx_lens.tolist()[:4]} kv={case.kv_dtype} T={case.tile} {kw}")
     out, used = run_gpu(case, **kw)
-    r = check_parity(case, out, used, **{k: v for k, v in kw.items() if k != "max_workers"})
+    r = check_parity(case, out, used, **{k: v for k, v in kw.items() if k not in ("max_workers", "team_helpers")})
     log(f"[parity] {label}: max_abs={r['max_abs']:.3e} near={r['near']} "
         f"mean tiles_used={np.mean(r['tiles_used']):.1f}")
     return out, used, r
@@ -144,6 +144,39 @@ def test_worker_count_does_not_change_results():
     for w in (1, 3, 17, 300):
         o, u = run_gpu(c, dev, max_workers=w)
         assert np.array_equal(u, u0) and np.array_equal(o, o0)
+
+
+@pytest.mark.parametrize("helpers", [1, 3])
+def test_helper_work_groups_do_not_change_results(helpers):
+    # helper work-groups on other CUs take some of each group's tiles; every
+    # tile's partial is computed alike and folded in the same order, so the
+    # results are those without helpers, bit for bit
+    c = A.config(3, small=True)
+    dev = to_device(c)
+    o_art, u_art = run_gpu(c, dev)
+    for kw in (dict(), dict(eps_scale=1e-30, eps_dir=1e-30)):
+        o0, u0 = run_gpu(c, dev, **kw)
+        o1, u1 = run_gpu(c, dev, team_helpers=helpers, **kw)
+        assert np.array_equal(u1, u0) and np.array_equal(o1, o0)
+    o0, u0 = o_art, u_art
+    # and with more groups than the chip can give further CUs: the helpers are dropped
+    import dataclasses
+    pad = 18
+    c2 = dataclasses.replace(
+        c, B=c.B + pad,
+        q=np.concatenate([c.q, np.zeros((pad,) + c.q.shape[1:], c.q.dtype)]),
+        block_table=np.concatenate([c.block_table, np.zeros((pad, c.block_table.shape[1]), c.block_table.dtype)]),
+        ctx_lens=np.concatenate([c.ctx_lens, np.zeros(pad, c.ctx_lens.dtype)]))
+    o2, u2 = run_gpu(c2, team_helpers=helpers)
+    assert np.array_equal(u2[:c.B], u0) and np.array_equal(o2[:c.B], o0)
+    assert (u2[c.B:] == 0).all() and (o2[c.B:] == 0).all()
+
+
+def test_helper_work_groups_parity():
+    c = A.config(2, sink_mode="sqrt_d")
+    _run_and_check(c, "config2 art, 3 helper work-groups per group", team_helpers=3)
+    c = A.config(4, small=True)
+    _run_and_check(c, "config4-small art, 1 helper work-group per group", team_helpers=1)
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
