@@ -2199,38 +2199,78 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_full_stream_kernel(Para
     }
 }
 
-// One wave per group: merge the splits in order and write the outputs.
-__global__ __launch_bounds__(64) void art_combine_kernel(Params P) {
+// One work-group of kCombineWaves waves per group merges the splits and
+// writes the outputs.  Wave w takes splits w, w + kCombineWaves, ...: it first
+// finds their largest max per head, then sums their weighted sums and
+// accumulators (independent loads, many in flight); the waves' results are
+// then merged in wave order through LDS.  The order is fixed: the output is
+// deterministic.
+constexpr int kCombineWaves = 4;
+
+__global__ __launch_bounds__(64 * kCombineWaves) void art_combine_kernel(Params P) {
+    __shared__ float part[kCombineWaves][4][64][10];  // per wave, head block, lane: M, L, 8 dims
+    __shared__ int perr[kCombineWaves];
     const int grp = blockIdx.x;
+    const int wv = wave_id(), lane = lane_id();
     const FoldLanes fl(P);
     const int G = P.G, D = P.D;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
     const int n = P.ctx_lens[b];
     const bool bad = n < 0 || n > P.cap;
     const int nt = bad ? 0 : (n + P.T - 1) / P.T;
+    const float* base = P.partials + (long long)grp * P.splits * P.slot;
+    int err = 0;
+    for (int sp = wv; sp < P.splits; sp += kCombineWaves)
+        err |= reinterpret_cast<const int*>(base + (long long)sp * P.slot)[32];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        float M = kNegInf, L = 0.f, A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (hb < fl.HB && h < G) {
+            // splits with no rows (l = 0) take no part
+#pragma unroll 8
+            for (int sp = wv; sp < P.splits; sp += kCombineWaves) {
+                const float* slot = base + (long long)sp * P.slot;
+                const float ll = slot[16 + h];
+                M = fmaxf(M, ll > 0.f ? slot[h] : kNegInf);
+            }
+            if (M != kNegInf) {
+#pragma unroll 4
+                for (int sp = wv; sp < P.splits; sp += kCombineWaves) {
+                    const float* slot = base + (long long)sp * P.slot;
+                    const float ll = slot[16 + h];
+                    const float w = ll > 0.f ? expf(slot[h] - M) : 0.f;
+                    L = fmaf(w, ll, L);
+                    if (fl.cvalid) {
+                        const float* a = slot + kSlotHeader + h * D + 8 * fl.cid;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) A[j] = fmaf(w, a[j], A[j]);
+                    }
+                }
+            }
+        }
+        float* e = part[wv][hb][lane];
+        e[0] = M;
+        e[1] = L;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[2 + j] = A[j];
+    }
+    if (lane == 0) perr[wv] = err;
+    __syncthreads();
+    if (wv != 0) return;
+    for (int w = 1; w < kCombineWaves; ++w) err |= perr[w];
+    if (bad) err = 1;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
         const int h = hb * 4 + fl.hl;
         if (hb >= fl.HB || h >= G) continue;
-        float M = kNegInf, L = 0.f, a8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        int err = bad ? 1 : 0;
-        for (int sp = 0; sp < P.splits; ++sp) {
-            const float* slot = P.partials + ((long long)grp * P.splits + sp) * P.slot;
-            const float ll = slot[16 + h];
-            err |= reinterpret_cast<const int*>(slot)[32];
-            if (!(ll > 0.f)) continue;  // empty split
-            const float ml = slot[h];
-            const float mn = fmaxf(M, ml);
-            const bool first = M == kNegInf;
-            const float al = first ? 0.f : expf(M - mn);
-            const float be = expf(ml - mn);
-            L = fmaf(al, L, be * ll);
-            if (fl.cvalid) {
-                const float* a = slot + kSlotHeader + h * D + 8 * fl.cid;
+        float M = kNegInf, L = 0.f, A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int w = 0; w < kCombineWaves; ++w) {
+            const float* e = part[w][hb][lane];
+            float a2[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) a8[j] = first ? be * a[j] : fmaf(al, a8[j], be * a[j]);
-            }
-            M = mn;
+            for (int j = 0; j < 8; ++j) a2[j] = e[2 + j];
+            sm_merge(M, L, A, e[0], e[1], a2);
         }
         if (nt == 0 && !bad) {
             const long long row = (long long)b * P.Hq + (long long)g * G + h;
@@ -2238,7 +2278,7 @@ __global__ __launch_bounds__(64) void art_combine_kernel(Params P) {
                 for (int j = 0; j < 8; ++j) P.out[row * D + 8 * fl.cid + j] = 0.f;
             if (fl.cid == 0) P.tiles_used[row] = 0;
         } else {
-            write_head_out(P, grp, h, fl, a8, L, err, nt);
+            write_head_out(P, grp, h, fl, A, L, err, nt);
         }
     }
 }
@@ -2274,7 +2314,7 @@ int launch_split(const Params& p, hipStream_t s, K kernel) {
     const size_t lds = (size_t)kWavesPerWG * Tile::lds_floats(p) * sizeof(float);
     const int blocks = (p.NG * p.splits + kWavesPerWG - 1) / kWavesPerWG;
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), lds, s, p);
-    hipLaunchKernelGGL(art_combine_kernel, dim3(p.NG), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(art_combine_kernel, dim3(p.NG), dim3(64 * kCombineWaves), 0, s, p);
     return (int)hipGetLastError();
 }
 
