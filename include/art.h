@@ -78,7 +78,9 @@ typedef struct {
     int64_t* stats;              /* optional device int64[4] accumulator, or NULL:
                                     [0] K tiles loaded, [1] V rows loaded,
                                     [2] tiles loaded after their group had stopped,
-                                    [3] reserved                                      */
+                                    [3] (query head, position) pairs whose V row was
+                                        skipped (v_skip_eps > 0; counted by the
+                                        default engine for 64-token tiles only)       */
     int32_t max_workers;         /* 0 = library default; > 0: work-sharing engine     */
     int32_t team_helpers;        /* team engine (ART, streamed tiles): helper work-groups
                                     per group on other CUs, 0..3; 0 = none (default).
@@ -107,7 +109,10 @@ typedef struct {
  * Errors detected on the device, per batch row: ctx_lens[b] < 0 or larger than
  * the cache row capacity, or a block id outside [0, num_blocks) inside a
  * visited tile -> tiles_used = -1 and out = NaN for the affected heads; no
- * out-of-range address is ever dereferenced.
+ * out-of-range address is ever dereferenced.  Should a wait between the
+ * cooperating waves of a call outlast half a second (the GPU was shared with
+ * a starving workload), the heads not yet decided report tiles_used = -2 and
+ * out = NaN instead of hanging.
  *
  * Host-side validation happens before anything is enqueued; device memory is
  * never read on the host.  Concurrent calls must use distinct workspaces.

@@ -113,6 +113,11 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -672,7 +677,7 @@ struct Stream {
     using Out = TileOutT<HBM>;
     typedef typename std::conditional<KV == ART_I8, u2, u4>::type vvec;
 
-    __host__ __device__ static size_t lds_floats(const Params&) { return (2 * UP * PAGEB) / 4 + 32 * GMAX; }
+    __host__ __device__ static size_t lds_floats(const Params&) { return (2 * UP * PAGEB) / 4 + 64 * GMAX; }
 
     struct TileRef {             // one tile of one group (wave-uniform)
         int grp, t, n;
@@ -688,7 +693,7 @@ struct Stream {
     float m_run, l_run;
     float acc[GMAX][8];
     char* kl;                    // LDS: [2 buffers][UP pages][PAGEB]
-    float* pl;                   // LDS: [32 tokens][GMAX heads]
+    float* pl;                   // LDS: [64 tokens][GMAX heads] (a unit uses the first 32)
 
     __device__ __forceinline__ void init(float* lds_wave) {
         kl = reinterpret_cast<char*>(lds_wave);
@@ -830,17 +835,12 @@ struct Stream {
         __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
     }
 
-    // Fold unit u of tile r (loaded in buffer BUF) into the running state.
-    // `pending`: the next unit's loads were issued after this one's.
+    // Scores of unit u (loaded in buffer BUF): s[pp][i] is token 16pp + 4(lane>>4) + i
+    // of the unit for head lane & 15 (-inf outside the sequence); returns the
+    // unit's max per head (lane & 15), over the whole wave.
     template <int BUF>
-    __device__ __forceinline__ void consume(const Params& P, const TileRef& r, int u, bool pending) {
+    __device__ __forceinline__ float scores(const Params& P, const TileRef& r, int u, float (&s)[UP][4]) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
-        const int G = P.G;
-        __builtin_amdgcn_sched_barrier(0);
-        if (pending) wait_vm<OPS>();  // this unit's loads, K in LDS included, have landed
-        else wait_vm<0>();
-        __builtin_amdgcn_sched_barrier(0);
-        float s[UP][4];
         float mu = kNegInf;
 #pragma unroll
         for (int pp = 0; pp < UP; ++pp) {
@@ -876,6 +876,21 @@ struct Stream {
         }
         mu = fmaxf(mu, __shfl_xor(mu, 16));
         mu = fmaxf(mu, __shfl_xor(mu, 32));
+        return mu;
+    }
+
+    // Fold unit u of tile r (loaded in buffer BUF) into the running state.
+    // `pending`: the next unit's loads were issued after this one's.
+    template <int BUF>
+    __device__ __forceinline__ void consume(const Params& P, const TileRef& r, int u, bool pending) {
+        const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+        const int G = P.G;
+        __builtin_amdgcn_sched_barrier(0);
+        if (pending) wait_vm<OPS>();  // this unit's loads, K in LDS included, have landed
+        else wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        float s[UP][4];
+        const float mu = scores<BUF>(P, r, u, s);
         const float m_new = fmaxf(m_run, mu);
         const float alpha = m_run == kNegInf ? 0.f : exp_fast(m_run - m_new);
         float lsum = 0.f;
@@ -901,12 +916,67 @@ struct Stream {
                 for (int j = 0; j < 8; ++j) acc[h][j] *= ah[h];
         // rows outside the sequence hold whatever the fallback rows hold: zero them
         const bool full = ((r.pmask >> (UP * u)) & 3) == 3 && r.t * T + 32 * (u + 1) <= r.n;
-        if (full) pv_accumulate<BUF, false>(P, r, u);
-        else pv_accumulate<BUF, true>(P, r, u);
+        if (full) pv_accumulate<BUF, false>(P, r, u, 0);
+        else pv_accumulate<BUF, true>(P, r, u, 0);
+    }
+
+    // The whole tile r (both units loaded) under the V-skip rule: the scores of
+    // both units give the tile max m; chain(m) returns M, the running max
+    // through this tile, for the lane's head (lane & 15); a row j of head h
+    // enters P.V only when exp(s_hj - M_h) >= v_skip_eps, while its weight
+    // exp(s_hj - m_h) always enters l.  The tile becomes the running state
+    // (the state is empty before: a tile at a time).  Returns the number of
+    // (head, row) pairs left out, counted in lane 0.
+    template <class Chain>
+    __device__ __forceinline__ int consume_tile_vskip(const Params& P, const TileRef& r, Chain&& chain) {
+        const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+        const int G = P.G;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<OPS>();
+        __builtin_amdgcn_sched_barrier(0);
+        float s0[UP][4], s1[UP][4];
+        float mu = scores<0>(P, r, 0, s0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        mu = fmaxf(mu, scores<1>(P, r, 1, s1));
+        const float M = chain(mu);
+        float lsum = 0.f;
+        int skipped = 0;
+        wave_lds_sync();  // the previous tile's P.V reads of pl are done
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int pp = 0; pp < UP; ++pp)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sv = u ? s1[pp][i] : s0[pp][i];
+                    const bool valid = sv != kNegInf;
+                    const float pr = valid ? exp_fast(sv - mu) : 0.f;
+                    const bool keep = valid && expf(sv - M) >= P.v_skip_eps;
+                    lsum += pr;
+                    skipped += (valid && !keep && r16 < G) ? 1 : 0;
+                    if (r16 < GMAX) pl[(32 * u + 16 * pp + 4 * rg + i) * GMAX + r16] = keep ? pr : 0.f;
+                }
+        l_run = lsum;
+        m_run = mu;
+        wave_lds_sync();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bool full = ((r.pmask >> (UP * u)) & 3) == 3 && r.t * T + 32 * (u + 1) <= r.n;
+            if (u == 0) {
+                if (full) pv_accumulate<0, false>(P, r, 0, 0);
+                else pv_accumulate<0, true>(P, r, 0, 0);
+            } else {
+                if (full) pv_accumulate<1, false>(P, r, 1, 32);
+                else pv_accumulate<1, true>(P, r, 1, 32);
+            }
+        }
+        return wave_sum_int(skipped);
     }
 
     template <int BUF, bool MASK>
-    __device__ __forceinline__ void pv_accumulate(const Params& P, const TileRef& r, int u) {
+    __device__ __forceinline__ void pv_accumulate(const Params& P, const TileRef& r, int u, int pbase) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         const int G = P.G;
 #pragma unroll
@@ -917,10 +987,10 @@ struct Stream {
                 bool rv = true;
                 if constexpr (MASK) rv = ((r.pmask >> (UP * u + pp)) & 1) && r.t * T + 32 * u + tok < r.n;
                 float pw[GMAX];
-                const f4 w0 = *reinterpret_cast<const f4*>(pl + tok * GMAX);
+                const f4 w0 = *reinterpret_cast<const f4*>(pl + (pbase + tok) * GMAX);
                 pw[0] = w0.x; pw[1] = w0.y; pw[2] = w0.z; pw[3] = w0.w;
                 if constexpr (GMAX == 8) {
-                    const f4 w1 = *reinterpret_cast<const f4*>(pl + tok * GMAX + 4);
+                    const f4 w1 = *reinterpret_cast<const f4*>(pl + (pbase + tok) * GMAX + 4);
                     pw[4] = w1.x; pw[5] = w1.y; pw[6] = w1.z; pw[7] = w1.w;
                 }
                 float vf[8];
@@ -1576,11 +1646,17 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P)
 constexpr int kTeamRing = 8;  // LDS slots between the primary's workers and the decider
 constexpr int kSlotLane = kTeamSlotLane;
 
+constexpr int kChain = 8;     // LDS slots of the running-max chain (V skip)
+
 struct TeamShared {
     int tag[kTeamRing];  // t + 1 once slot (ordinal of t among the primary's tiles) % kTeamRing holds tile t
     int err[kTeamRing];  // the tile met an invalid block id
     int frontier;        // the primary's tiles folded by the decider (a count of ordinals)
     int bound;           // tiles that may still be fetched
+    // V skip: the running max through tile t, per head, in slot t % kChain
+    // (its tag t + 1 once written)
+    int ptag[kChain];
+    float pmax[kChain][16];
 };
 
 // Control words in LDS, accessed as LDS (a volatile access through a generic
@@ -1617,11 +1693,13 @@ struct TeamPlan {
 
 // One tile worker: tiles first, first + W, ... of the group.  PRIMARY: hands
 // over through LDS; else through the group's global ring.
-template <class S, bool PRIMARY>
+template <class S, bool PRIMARY, bool VSKIP>
 __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int nt, int first, const TeamPlan& plan,
                                             S& st, float* ring, TeamShared* sh) {
+    static_assert(PRIMARY || !VSKIP, "the V skip's running-max chain lives in the primary's LDS");
     constexpr int HBM = S::HBM;
     const int lane = lane_id();
+    unsigned long long skipped = 0;  // (head, row) pairs left out of P.V
     int t = first;
     if (t >= nt) return;
     // ordinal of tile t among the primary's (or the helpers') tiles; a slot is
@@ -1644,12 +1722,35 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     for (;;) {
         if constexpr (PRIMARY) bnd = lds_ld(&sh->bound);
         if (t >= bnd) break;  // the group stopped before this tile
-        st.template consume<0>(P, C, 0, true);
-        if constexpr (!PRIMARY) {
-            bnd = unstamp(wb, P.epoch, bnd);
-            frt = unstamp(wf, P.epoch, frt);
+        if constexpr (VSKIP) {
+            // the running max through tile t: that through tile t - 1 (from its
+            // worker, through LDS) and this tile's
+            auto chain = [&](float mu) -> float {
+                float M = mu;
+                if (t > 0) {
+                    const int sp = (t - 1) % kChain;
+                    if (lds_ld(&sh->ptag[sp]) != t) {
+                        const Deadline dl;
+                        while (lds_ld(&sh->ptag[sp]) != t && !dl.passed()) __builtin_amdgcn_s_sleep(1);
+                    }
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the value is read after its tag
+                    M = fmaxf(M, __int_as_float(lds_ld(reinterpret_cast<const int*>(&sh->pmax[sp][lane & 15]))));
+                }
+                const int sn = t % kChain;
+                if (lane < 16) lds_st(reinterpret_cast<int*>(&sh->pmax[sn][lane]), __float_as_int(M));
+                wait_lds();
+                if (lane == 0) lds_st(&sh->ptag[sn], t + 1);
+                return M;
+            };
+            skipped += (unsigned)st.consume_tile_vskip(P, C, chain);
+        } else {
+            st.template consume<0>(P, C, 0, true);
+            if constexpr (!PRIMARY) {
+                bnd = unstamp(wb, P.epoch, bnd);
+                frt = unstamp(wf, P.epoch, frt);
+            }
+            st.template consume<1>(P, C, 1, false);
         }
-        st.template consume<1>(P, C, 1, false);
         typename S::Out o;
         st.flush(P, o);
         const int tn = t + plan.W;
@@ -1725,6 +1826,7 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     // loads of a tile fetched past the stop may still be landing (in LDS too)
     __builtin_amdgcn_s_waitcnt(0);
     count_stats(P, loaded, rows);
+    if (VSKIP && P.stats && lane == 0) atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 3), skipped);
 }
 
 // sum of squares of 8 values as a balanced tree (short dependency chain)
@@ -1993,7 +2095,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
 
 // Grid: NG primaries, then P.helpers rounds of NG helpers (helper r of group
 // g is work-group (1 + r) * NG + g).
-template <class S>
+template <class S, bool VSKIP>
 __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     extern __shared__ float lds[];
     constexpr int HBM = S::HBM, TEAM = S::TEAM;
@@ -2018,7 +2120,8 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     if (team > 0) {
         S st;
         st.init(lds + wv * wave_floats);
-        team_worker<S, false>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st, nullptr, nullptr);
+        if constexpr (!VSKIP)
+            team_worker<S, false, false>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st, nullptr, nullptr);
         return;
     }
     float* ring = lds + (TEAM - 1) * wave_floats;  // [kTeamRing][HBM][kSlotLane][64]
@@ -2032,6 +2135,7 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
             sh->frontier = 0;
             sh->bound = nt;
         }
+        if (lane < kChain) sh->ptag[lane] = 0;
     }
     __syncthreads();
     if (wv == 0) {
@@ -2041,7 +2145,7 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     } else {
         S st;
         st.init(lds + (wv - 1) * wave_floats);
-        team_worker<S, true>(P, grp, n, nt, wv - 1, plan, st, ring, sh);
+        team_worker<S, true, VSKIP>(P, grp, n, nt, wv - 1, plan, st, ring, sh);
     }
 }
 
@@ -2325,7 +2429,12 @@ bool fast_path(const Params& p) {
     return p.D == 128 && p.q_dtype == ART_BF16 && (p.kv_dtype == ART_BF16 || p.kv_dtype == ART_I8) &&
            p.G <= 8 && (p.T == 16 || p.T == 32 || p.T == 64);
 }
-bool stream_path(const Params& p) { return fast_path(p) && p.T == 64 && !p.vskip; }
+// Streamed 64-token tiles: the team engine (ART, with or without the V
+// skip), the ring engine (ART without the V skip, when a worker count is
+// requested) and full mode.
+bool stream_path(const Params& p, bool art) {
+    return fast_path(p) && p.T == 64 && (!p.vskip || (art && p.workers == 0));
+}
 
 template <class Tile>
 int run_tile(const Params& p, hipStream_t s, bool art) {
@@ -2336,15 +2445,15 @@ int run_tile(const Params& p, hipStream_t s, bool art) {
 // Helpers (as many as requested, up to what fits) only where every
 // work-group of the grid can be resident at once (cooperative launch); else
 // the primaries alone.
-template <class S>
+template <class S, bool VSKIP>
 int launch_team(const Params& p0, hipStream_t s) {
     Params p = p0;
     const size_t lds = team_lds_bytes<S>(p);
     p.helpers = 0;
     int dev = 0, cus = 0, per_cu = 0;
-    if (p0.helpers > 0 && hipGetDevice(&dev) == hipSuccess &&
+    if (!VSKIP && p0.helpers > 0 && hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_team_kernel<S>, S::TEAM * 64, lds) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_team_kernel<S, VSKIP>, S::TEAM * 64, lds) == hipSuccess &&
         per_cu > 0) {
         const long long resident = (long long)per_cu * cus;
         long long h = resident / p.NG - 1;
@@ -2352,7 +2461,7 @@ int launch_team(const Params& p0, hipStream_t s) {
         if (h > 0) {
             p.helpers = (int)h;
             void* args[] = {&p};
-            const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&art_team_kernel<S>),
+            const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&art_team_kernel<S, VSKIP>),
                                                             dim3(p.NG * (1 + p.helpers)), dim3(S::TEAM * 64), args,
                                                             (unsigned)lds, s);
             if (e == hipSuccess) return 0;
@@ -2361,21 +2470,21 @@ int launch_team(const Params& p0, hipStream_t s) {
         }
     }
     (void)hipGetLastError();
-    hipLaunchKernelGGL(art_team_kernel<S>, dim3(p.NG), dim3(S::TEAM * 64), lds, s, p);
+    hipLaunchKernelGGL((art_team_kernel<S, VSKIP>), dim3(p.NG), dim3(S::TEAM * 64), lds, s, p);
     return (int)hipGetLastError();
 }
 
 template <class S>
 int run_stream(const Params& p, hipStream_t s, bool art) {
     // a requested worker count selects the work-sharing engine
-    if (art && p.workers == 0) return launch_team<S>(p, s);
+    if (art && p.workers == 0) return p.vskip ? launch_team<S, true>(p, s) : launch_team<S, false>(p, s);
     if (art) return launch_persistent<decltype(&art_stream_kernel<S>), S>(p, s, &art_stream_kernel<S>);
     return launch_split<decltype(&art_full_stream_kernel<S>), S>(p, s, &art_full_stream_kernel<S>);
 }
 
 template <int KV, int GMAX>
 int run_fast(const Params& p, hipStream_t s, bool art) {
-    if (stream_path(p)) return run_stream<Stream<KV, GMAX>>(p, s, art);
+    if (stream_path(p, art)) return run_stream<Stream<KV, GMAX>>(p, s, art);
     if (p.T == 64) return run_tile<FastTile<KV, 4, GMAX>>(p, s, art);
     if (p.T == 32) return run_tile<FastTile<KV, 2, GMAX>>(p, s, art);
     return run_tile<FastTile<KV, 1, GMAX>>(p, s, art);
