@@ -119,10 +119,9 @@ Layout workspace_layout(const Params& p) {
     L.vmax_tag = o; o = align256(o + NG * (size_t)p.nt_max * sizeof(int));
     L.vmax = o; o = align256(o + NG * (size_t)p.nt_max * 16 * sizeof(float));
     L.partials = o; o = align256(o + NG * (size_t)p.splits * p.slot * sizeof(float));
-    const size_t HB = (size_t)(p.G + 3) / 4;
-    L.team_ring = o; o = align256(o + NG * kTeamRingG * HB * kTeamSlotLane * 64 * sizeof(float));
-    L.team_tag = o; o = align256(o + NG * kTeamRingG * sizeof(unsigned long long));
-    L.team_ctl = o; o = align256(o + NG * 2 * sizeof(unsigned long long));
+    const size_t NT = NG <= (size_t)kTeamHelpGroups ? NG : 0;  // groups that helpers may serve
+    L.team_ring = o; o = align256(o + NT * team_words(p.G) * sizeof(unsigned long long));
+    L.team_ctl = o; o = align256(o + NT * kTeamCtl * sizeof(unsigned long long));
     L.total = o;
     return L;
 }
@@ -204,8 +203,7 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     p.vmax_tag = reinterpret_cast<int*>(ws + L.vmax_tag);
     p.vmax = reinterpret_cast<float*>(ws + L.vmax);
     p.partials = reinterpret_cast<float*>(ws + L.partials);
-    p.team_ring = reinterpret_cast<float*>(ws + L.team_ring);
-    p.team_tag = reinterpret_cast<unsigned long long*>(ws + L.team_tag);
+    p.team_ring = reinterpret_cast<unsigned long long*>(ws + L.team_ring);
     p.team_ctl = reinterpret_cast<unsigned long long*>(ws + L.team_ctl);
     p.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
     if (p.epoch == 0) p.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;  // 0 never stamps

@@ -13,9 +13,14 @@ constexpr int kRing = 128;        // ring slots per group (tiles in flight ahead
 constexpr int kMaxG = 16;         // query heads per KV head
 constexpr int kWavesPerWG = 4;    // independent waves per work-group
 constexpr int kMaxDeciders = 512; // decider waves at most (one per group up to this many groups)
-constexpr int kTeamRingG = 32;    // global ring slots per group for the tiles of helper teams
-constexpr int kTeamSlotLane = 10; // floats per lane per head block in a team slot: m, l, 8 dims
-constexpr int kMaxHelpers = 3;    // helper work-groups per group at most (team engine)
+// team engine, words shared through the workspace (per group)
+constexpr int kTeamRingG = 64;    // probe-record slots for the helpers' tiles (a power of two)
+constexpr int kTeamRecW = 11;     // 64-bit words per (tile, head) record: max, sum, probe dims 0..7, error flag
+constexpr int kTeamRecHeads = 8;  // heads per record slot (streamed tiles serve up to 8 query heads per KV head)
+constexpr int kTeamStateW = 10;   // 64-bit words per lane per head block of a helper's final state: m, l, 8 dims
+constexpr int kMaxHelpers = 3;    // helper work-groups per group at most
+constexpr int kTeamCtl = 16;      // control words: [0] helper records released, [1] bound, [4..11] per-head decision
+constexpr int kTeamHelpGroups = 512;  // helpers serve launches of at most this many groups (workspace sized for them)
 constexpr unsigned long long kWaitTicks = 50000000ull;  // 0.5 s of the 100 MHz device clock:
                                                       // longest any wait may last before the kernel gives up
 constexpr int kSlotHeader = 48;   // floats before the accumulator block of a partial:
@@ -65,9 +70,10 @@ struct Params {
     int* vmax_tag;      // [NG][nt_max]
     float* vmax;        // [NG][nt_max][16]
     float* partials;    // [NG][splits][slot]
-    float* team_ring;   // [NG][kTeamRingG][HB][kTeamSlotLane][64]: tiles of helper teams
-    unsigned long long* team_tag;  // [NG][kTeamRingG]: (epoch << 32) | (tile + 1)
-    unsigned long long* team_ctl;  // [NG][2]: (epoch << 32) | frontier, (epoch << 32) | bound
+    unsigned long long* team_ring;  // [NG][team_words(G)]: the helpers' probe records
+                                    // [kTeamRingG][kTeamRecW][kTeamRecHeads], then their final running
+                                    // states [kMaxHelpers][HB][kTeamStateW][64]; (tag << 32) | value bits
+    unsigned long long* team_ctl;   // [NG][kTeamCtl]: (epoch << 32) | value
     unsigned epoch;     // distinct per call: stale team words of earlier calls never match
     int helpers;        // helper work-groups per group (team kernel)
     int slot;           // floats per partial: kSlotHeader + G*D
@@ -78,9 +84,14 @@ struct Params {
     int tiles_per_split;
 };
 
+// 64-bit words of team_ring per group
+constexpr size_t team_words(int G) {
+    return (size_t)kTeamRingG * kTeamRecW * kTeamRecHeads + (size_t)kMaxHelpers * ((G + 3) / 4) * kTeamStateW * 64;
+}
+
 // Workspace layout for a Params (offsets in bytes, all 256-byte aligned).
 struct Layout {
-    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, team_ring, team_tag, team_ctl, total;
+    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, team_ring, team_ctl, total;
 };
 Layout workspace_layout(const Params& p);
 

@@ -664,6 +664,7 @@ struct Stream {
     static constexpr int D = 128, UP = 2, T = 64, PAGES = 4;
     static constexpr int EB = KV == ART_I8 ? 1 : 2;
     static constexpr int HBM = GMAX / 4;
+    static constexpr int HEADS = GMAX;           // query heads per KV head at most
     static constexpr int ROWB = D * EB;          // bytes of one cache row
     static constexpr int PAGEB = 16 * ROWB;      // bytes of one 16-row page
     static constexpr int KDMA = PAGEB / 1024;    // LDS-direct loads per page
@@ -751,7 +752,8 @@ struct Stream {
         const int lane = lane_id(), b = grp / P.Hkv;
         const int tokp = t * T + 16 * lane;
         int blk = 0;
-        if (P.block_size && lane < PAGES && tokp < n) blk = P.block_table[(long long)b * P.mbps + tokp / P.block_size];
+        if (P.block_size && lane < PAGES && tokp < n)
+            blk = P.block_table[(long long)b * P.mbps + (unsigned)tokp / (unsigned)P.block_size];
         return blk;
     }
 
@@ -776,7 +778,7 @@ struct Stream {
                     if (blk < 0 || blk >= P.num_blocks) {
                         r.err = 1;
                     } else {
-                        r.prow[p] = ((long long)blk * P.Hkv + g) * P.block_size + tokp % P.block_size;
+                        r.prow[p] = ((long long)blk * P.Hkv + g) * P.block_size + (unsigned)tokp % (unsigned)P.block_size;
                         r.pmask |= 1 << p;
                     }
                 }
@@ -1622,39 +1624,64 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P)
 
 // ------------------------------------------------------------------ team kernel (work-groups per group)
 //
-// A group is served by a primary work-group and, when the chip has room for
-// them alongside every primary, up to kMaxHelpers helper work-groups on other
-// CUs.  Wave 0 of the primary is the decider; its other waves, and every wave
-// of the helpers, are tile workers.  Tiles are assigned statically: over
-// every W consecutive tiles the first nA go to the primary's workers in turn
-// and the rest to the helpers' workers in turn, so every worker streams its
-// own arithmetic sequence of tiles, the loads of each issued before the
-// previous one is handed over.  A worker hands each tile's partial (max, sum
-// and V accumulator per head, in the fold mapping) to the decider: primary
-// workers through a ring of LDS slots (store, wait for LDS, tag), helper
-// workers through a ring in global memory (coherent stores, a re-read of the
-// last word, then the tag).  The decider folds the tiles one at a time in tile
-// order into the group's running state, which is the sequential traversal
-// itself: after each tile the probe of every active head is compared with the
-// previous one, a head whose streak reaches the patience stops and its output
-// is written at once, and once every head has stopped the bound drops (in LDS
-// and in global memory), so that no worker fetches a further tile: at most
-// one tile per worker, two for a helper, is loaded past the stop.  Helpers
-// are launched cooperatively, so every work-group of the grid is resident.
-// Words shared through global memory carry the call's epoch, so that none
-// left by an earlier call is taken for one of this call.
-constexpr int kTeamRing = 8;  // LDS slots between the primary's workers and the decider
-constexpr int kSlotLane = kTeamSlotLane;
+// A group is served by a primary work-group and, where every work-group of
+// the launch fits on the chip at once, up to kMaxHelpers helper work-groups
+// on other CUs.  Wave 0 of the primary decides; every other wave is a tile
+// worker.  Tiles are assigned statically: over every W consecutive tiles the
+// first nA go to the primary's workers in turn and the rest to the helpers'
+// workers in turn, so each worker streams its own arithmetic sequence of
+// tiles, the loads of the next one issued before the current one is handed
+// over.
+//
+// For every tile a worker hands over, per head, a probe record: the tile's
+// softmax max and sum, its accumulator on head dims 0..7 (the probe dims)
+// and its error flag.  Primary workers write records to LDS (data, a wait
+// for LDS, then the slot's tag); helpers write them to global memory as
+// 64-bit words whose upper half names the call (epoch) and the lap of the
+// ring slot, so the decider recognises a record word by word and no store
+// has to wait for another.  A worker keeps each tile's whole partial until
+// the tile is decided, then merges it into its own running state for every
+// head that uses the tile.
+//
+// The decider takes the tiles in aligned blocks of kBlock: lane i of a
+// 16-lane row (one row per head) holds tile f0 + i's record, and an
+// inclusive online-softmax scan along the row (DPP row shifts), merged with
+// the state committed before the block, gives the probe state after every
+// tile of the block.  Lane i's value depends on tiles f0 .. f0 + i only, so
+// the tiles of a block are decided as soon as their prefix is complete, with
+// the same values however the records trickled in.  Both stability metrics,
+// the streak and the stop then follow for every tile in order.  Per head the
+// decider publishes how many tiles are decided, or tiles_used once the head
+// stops; once every head has stopped the bound drops and no worker loads a
+// further tile.  At the end the workers' running states are merged in a
+// fixed order (the primary's workers, then the helpers'), so the output does
+// not depend on timing.
+constexpr int kProbeRing = 64;  // LDS record slots, by ordinal among the primary's tiles (a power of two)
+constexpr int kBlock = 16;      // tiles the decider scans together
+constexpr int kChain = 8;       // LDS slots of the running-max chain (V skip)
+constexpr int kRecF = 12;       // floats per LDS record: max, sum, probe dims 0..7, error flag, pad
 
-constexpr int kChain = 8;     // LDS slots of the running-max chain (V skip)
+// decision word of a head
+constexpr int kHdStop = 1 << 30;         // the head stopped; the count is its tiles_used
+constexpr int kHdGaveUp = 1 << 29;       // a wait outlasted kWaitTicks: the head reports -2
+constexpr int kHdCount = (1 << 29) - 1;  // else the count is the number of tiles decided
 
+// whether tile q enters a head's output under its decision word: 1 yes, 0 no, -1 not decided yet
+__device__ __forceinline__ int tile_fate(int w, int q) {
+    if (w & kHdStop) return q < (w & kHdCount) ? 1 : 0;
+    if (w & kHdGaveUp) return 0;
+    return q < (w & kHdCount) ? 1 : -1;
+}
+
+template <int GMAX>
 struct TeamShared {
-    int tag[kTeamRing];  // t + 1 once slot (ordinal of t among the primary's tiles) % kTeamRing holds tile t
-    int err[kTeamRing];  // the tile met an invalid block id
-    int frontier;        // the primary's tiles folded by the decider (a count of ordinals)
-    int bound;           // tiles that may still be fetched
-    // V skip: the running max through tile t, per head, in slot t % kChain
-    // (its tag t + 1 once written)
+    int tag[kProbeRing];                  // t + 1 once the slot holds tile t's records
+    float rec[kProbeRing][GMAX][kRecF];   // probe records of the primary's tiles
+    int released;                         // the primary's ordinals whose slots may be reused
+    int bound;                            // tiles that may still be loaded
+    int word[GMAX];                       // decision word per head
+    int err[GMAX];                        // final: a used tile met an invalid block id
+    // V skip: the running max through tile t, per head, in slot t % kChain (its tag t + 1 once written)
     int ptag[kChain];
     float pmax[kChain][16];
 };
@@ -1672,66 +1699,217 @@ __device__ __forceinline__ void wait_lds() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// epoch-stamped words
+// epoch-stamped control words
 __device__ __forceinline__ unsigned long long stamp(unsigned epoch, unsigned v) {
     return ((unsigned long long)epoch << 32) | v;
 }
 __device__ __forceinline__ int unstamp(unsigned long long w, unsigned epoch, int dflt) {
     return (unsigned)(w >> 32) == epoch ? (int)(unsigned)w : dflt;
 }
+// tagged data words: (tag << 32) | bits of the value
+__device__ __forceinline__ unsigned long long tagw(unsigned tag, float v) {
+    return ((unsigned long long)tag << 32) | (unsigned)__float_as_int(v);
+}
+__device__ __forceinline__ float untag(unsigned long long w) { return __int_as_float((int)(unsigned)w); }
+// tag of helper record ordinal o: the call and the lap of its slot (a slot is
+// rewritten only after the decider has taken the previous lap, so a word is
+// either of this lap or of the one before)
+__device__ __forceinline__ unsigned rec_tag(unsigned epoch, int o) {
+    return epoch * 2u + (unsigned)((o / kTeamRingG) & 1);
+}
+
+// row_shr:D within 16-lane rows; lanes i < D of a row get `old`
+template <int D>
+__device__ __forceinline__ float row_shr(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x110 + D, 0xf, 0xf, false));
+}
+
+// sum of squares of 8 values as a balanced tree (short dependency chain)
+__device__ __forceinline__ float sumsq8(const float (&v)[8]) {
+    const float a = fmaf(v[1], v[1], v[0] * v[0]), b = fmaf(v[3], v[3], v[2] * v[2]);
+    const float c = fmaf(v[5], v[5], v[4] * v[4]), d = fmaf(v[7], v[7], v[6] * v[6]);
+    return (a + b) + (c + d);
+}
+
+// (m, l, a) := (m, l, a) (+) (m2, l2, a2) with the hardware exponential:
+// the decider's merges, which only feed the probe
+__device__ __forceinline__ void sm_merge_fast(float& m, float& l, float (&a)[8], float m2, float l2,
+                                              const float (&a2)[8]) {
+    const float mn = fmaxf(m, m2);
+    const float w1 = m == kNegInf ? 0.f : exp_fast(m - mn);
+    const float w2 = m2 == kNegInf ? 0.f : exp_fast(m2 - mn);
+    l = fmaf(w1, l, w2 * l2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = fmaf(w1, a[j], w2 * a2[j]);
+    m = mn;
+}
+
+// The first tile q < kk of a block at which a head's streak of passing tiles
+// reaches `patience` (-1 if none), from bit q of p = tile q passes and the
+// streak s0 (< patience) carried into the block; sk = the streak after tile
+// kk - 1.
+__device__ __forceinline__ int first_stop(unsigned p, int kk, int s0, int patience, int& sk) {
+    const unsigned valid = (1u << kk) - 1u;  // kk <= 16
+    p &= valid;
+    const int need0 = patience - s0;        // the leading run continues the carried streak
+    const int lead = __builtin_ctz(~p);     // ones from tile 0 on
+    int stop = -1;
+    if (lead >= need0) {
+        stop = need0 - 1;
+    } else if (patience <= 16) {
+        // bit q of x: tiles q .. q + patience - 1 all pass
+        unsigned x = p;
+        for (int k = 1; k < patience; ++k) x &= p >> k;
+        if (x) stop = __builtin_ctz(x) + patience - 1;
+    }
+    const unsigned z = ~p & valid;          // failing tiles
+    sk = z == 0u ? s0 + kk : kk - 1 - (31 - __builtin_clz(z));
+    return stop;
+}
 
 // Static assignment of a group's tiles to the workers of its teams.
 struct TeamPlan {
     int nA, nH, W;  // primary workers, helper workers (all helpers), period
     __device__ TeamPlan(int nA_, int nH_) : nA(nA_), nH(nH_), W(nA_ + nH_) {}
-    __device__ bool primary(int t) const { return t % W < nA; }
-    __device__ int ordA(int t) const { return (t / W) * nA + t % W; }  // among the primary's tiles
-    __device__ int tileA(int o) const { return (o / nA) * W + o % nA; }
-    __device__ int ordH(int t) const { return (t / W) * nH + t % W - nA; }  // among the helpers' tiles
-    __device__ int tileH(int o) const { return (o / nH) * W + nA + o % nH; }
 };
 
-// One tile worker: tiles first, first + W, ... of the group.  PRIMARY: hands
-// over through LDS; else through the group's global ring.
+// A group's words in global memory.
+struct TeamGlobal {
+    unsigned long long* rec;     // [kTeamRingG][kTeamRecW][kTeamRecHeads]
+    unsigned long long* hstate;  // [kMaxHelpers][HB][kTeamStateW][64]
+    unsigned long long* ctl;     // [kTeamCtl]
+    __device__ TeamGlobal(const Params& P, int grp) {
+        rec = P.team_ring + (long long)grp * team_words(P.G);
+        hstate = rec + kTeamRingG * kTeamRecW * kTeamRecHeads;
+        ctl = P.team_ctl + (long long)grp * kTeamCtl;
+    }
+};
+
+// (max, sum, accumulator) per head block in the fold mapping: a tile's
+// partial or a running state
+template <int HBM>
+struct Part {
+    float m[HBM], l[HBM], a[HBM][8];
+    __device__ __forceinline__ void clear() {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            m[hb] = kNegInf;
+            l[hb] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[hb][j] = 0.f;
+        }
+    }
+};
+
+// One tile worker: tiles first, first + W, ... of the group, merged into ws.
+// PRIMARY: records and decisions through LDS; else through global memory.
 template <class S, bool PRIMARY, bool VSKIP>
 __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int nt, int first, const TeamPlan& plan,
-                                            S& st, float* ring, TeamShared* sh) {
+                                            S& st, TeamShared<S::HEADS>* sh, Part<S::HBM>& ws) {
     static_assert(PRIMARY || !VSKIP, "the V skip's running-max chain lives in the primary's LDS");
     constexpr int HBM = S::HBM;
     const int lane = lane_id();
-    unsigned long long skipped = 0;  // (head, row) pairs left out of P.V
+    const FoldLanes fl(P);
+    const TeamGlobal tg(P, grp);
+    ws.clear();
     int t = first;
     if (t >= nt) return;
-    // ordinal of tile t among the primary's (or the helpers') tiles; a slot is
-    // free once the decider has folded the ordinal a ring's length before
+    // ordinal of tile t among the primary's (or the helpers') tiles; its slot
+    // may be written once the decider has released the ordinal a ring before
     int o1 = PRIMARY ? first : first - plan.nA;
     const int ostep = PRIMARY ? plan.nA : plan.nH;
-    unsigned long long* gctl = P.team_ctl + 2 * grp;
-    typename S::TileRef C, N;
+    constexpr int ring = PRIMARY ? kProbeRing : kTeamRingG;
+    // the decisions as last seen: this lane's head's word per head block, the
+    // bound and the released ordinals.  Helpers load the global words before a
+    // tile's loads and take them once those have landed.
+    int hw[HBM];
+    int bnd = nt, rel = 0;
+    unsigned long long qw[HBM], qb = 0, qr = 0;
+    auto head_ok = [&](int hb) { return hb < fl.HB && hb * 4 + fl.hl < P.G; };
+    auto read_lds = [&]() {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) hw[hb] = head_ok(hb) ? lds_ld(&sh->word[hb * 4 + fl.hl]) : (kHdStop | 0);
+        bnd = lds_ld(&sh->bound);
+        rel = lds_ld(&sh->released);
+    };
+    auto load_glb = [&]() {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) qw[hb] = cld(tg.ctl + 4 + min(hb * 4 + fl.hl, kTeamRecHeads - 1));
+        qb = cld(tg.ctl + 1);
+        qr = cld(tg.ctl + 0);
+    };
+    auto take_glb = [&]() {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) hw[hb] = head_ok(hb) ? unstamp(qw[hb], P.epoch, 0) : (kHdStop | 0);
+        bnd = unstamp(qb, P.epoch, nt);
+        rel = unstamp(qr, P.epoch, 0);
+    };
+    auto refresh = [&]() {
+        if constexpr (PRIMARY) {
+            read_lds();
+        } else {
+            load_glb();
+            take_glb();
+        }
+    };
+    // the tile awaiting its decision
+    Part<HBM> q0;
+    int t0 = 0, np = 0;
+    bool gv = false;  // a wait outlasted kWaitTicks
+    // merges (or drops) the pending tile once every head has decided it
+    auto try_front = [&]() -> bool {
+        int fate[HBM];
+        bool und = false;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            fate[hb] = tile_fate(hw[hb], t0);
+            und |= fate[hb] < 0;
+        }
+        if (__ballot(und) != 0ull) return false;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (fate[hb] > 0) sm_merge(ws.m[hb], ws.l[hb], ws.a[hb], q0.m[hb], q0.l[hb], q0.a[hb]);
+        np = 0;
+        return true;
+    };
+    // waits until the pending tile is decided, and merges it
+    auto retire = [&]() {
+        if (np == 0 || try_front()) return;
+        const Deadline dl;
+        for (;;) {
+            __builtin_amdgcn_s_sleep(PRIMARY ? 1 : 4);
+            refresh();
+            if (try_front()) return;
+            if (dl.passed()) {
+                gv = true;
+                np = 0;
+                return;
+            }
+        }
+    };
+
+    typename S::TileRef C;
+    if constexpr (!PRIMARY) load_glb();
     st.load_q(P, grp);  // before the tile's loads: consume() counts those in issue order
     S::resolve(P, grp, t, C);
     st.template issue<0>(P, C, 0);
     st.template issue<1>(P, C, 1);
     int blkN = S::fetch_blocks(P, grp, n, t + plan.W);  // block ids of the next tile
-    // helpers: the group's bound and frontier, loaded before a tile's loads and
-    // read once those have landed (a tile late at worst)
-    unsigned long long wb = 0, wf = 0;
-    int bnd = nt, frt = 0;
-    // tiles (and rows) fetched, counted when their loads are issued
-    unsigned long long loaded = 1, rows = min(S::T, n - t * S::T);
+    // tiles (and rows) loaded, counted when their loads are issued
+    unsigned long long loaded = 1, rows = min(S::T, n - t * S::T), skipped = 0;
     for (;;) {
-        if constexpr (PRIMARY) bnd = lds_ld(&sh->bound);
-        if (t >= bnd) break;  // the group stopped before this tile
         if constexpr (VSKIP) {
             // the running max through tile t: that through tile t - 1 (from its
             // worker, through LDS) and this tile's
             auto chain = [&](float mu) -> float {
                 float M = mu;
                 if (t > 0) {
+                    // (a tile past the group's stop may wait for one never loaded: it is dropped anyway)
                     const int sp = (t - 1) % kChain;
                     if (lds_ld(&sh->ptag[sp]) != t) {
                         const Deadline dl;
-                        while (lds_ld(&sh->ptag[sp]) != t && !dl.passed()) __builtin_amdgcn_s_sleep(1);
+                        while (lds_ld(&sh->ptag[sp]) != t && t < lds_ld(&sh->bound) && !dl.passed())
+                            __builtin_amdgcn_s_sleep(1);
                     }
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the value is read after its tag
                     M = fmaxf(M, __int_as_float(lds_ld(reinterpret_cast<const int*>(&sh->pmax[sp][lane & 15]))));
@@ -1745,351 +1923,387 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
             skipped += (unsigned)st.consume_tile_vskip(P, C, chain);
         } else {
             st.template consume<0>(P, C, 0, true);
-            if constexpr (!PRIMARY) {
-                bnd = unstamp(wb, P.epoch, bnd);
-                frt = unstamp(wf, P.epoch, frt);
-            }
             st.template consume<1>(P, C, 1, false);
         }
         typename S::Out o;
         st.flush(P, o);
-        const int tn = t + plan.W;
-        if constexpr (PRIMARY) bnd = lds_ld(&sh->bound);
-        const bool haveN = tn < nt && tn < bnd;
-        if (haveN) {
-            S::resolve_from(P, grp, n, tn, blkN, N);
-            if constexpr (!PRIMARY) {
-                wb = cld(gctl + 1);
-                wf = cld(gctl + 0);
+        if constexpr (PRIMARY) read_lds();
+        else take_glb();
+        if (t >= bnd) break;  // past the group's stop: no head uses the tile
+        // the previous tile's decision (by now, as a rule, known)
+        retire();
+        if (gv) break;
+        // its record slot must have been released (the decider releases no
+        // further slot once the group is done: then the tile is past the bound)
+        if (o1 - ring >= rel) {
+            const Deadline dl;
+            for (;;) {
+                __builtin_amdgcn_s_sleep(PRIMARY ? 1 : 4);
+                if constexpr (PRIMARY) {
+                    rel = lds_ld(&sh->released);
+                    bnd = lds_ld(&sh->bound);
+                } else {
+                    rel = unstamp(cld(tg.ctl + 0), P.epoch, 0);
+                    bnd = unstamp(cld(tg.ctl + 1), P.epoch, nt);
+                }
+                if (o1 - ring < rel || t >= bnd) break;
+                if (dl.passed()) {
+                    gv = true;
+                    break;
+                }
             }
-            st.template issue<0>(P, N, 0);
-            st.template issue<1>(P, N, 1);
-            blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
-            ++loaded;
-            rows += min(S::T, n - tn * S::T);
+            if (gv || t >= bnd) break;
         }
-        // hand tile t over once its slot's previous tile has been folded
+        // the record: lane 16*hl (cid 0) holds head 4hb + hl's probe dims
+        const int s = o1 & (ring - 1);
         if constexpr (PRIMARY) {
-            const int s = o1 % kTeamRing;
-            if (o1 - kTeamRing >= lds_ld(&sh->frontier)) {
-                const Deadline dl;
-                while (o1 - kTeamRing >= lds_ld(&sh->frontier) && t < lds_ld(&sh->bound) && !dl.passed())
-                    __builtin_amdgcn_s_sleep(1);
-            }
-            if (t < lds_ld(&sh->bound) && o1 - kTeamRing < lds_ld(&sh->frontier)) {
-                float* slot = ring + s * (HBM * kSlotLane * 64);
 #pragma unroll
-                for (int hb = 0; hb < HBM; ++hb) {
-                    float* e = slot + hb * kSlotLane * 64 + lane;
-                    e[0] = o.mf[hb];
-                    e[64] = o.lf[hb];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) e[64 * (2 + j)] = o.a[hb][j];
+            for (int hb = 0; hb < HBM; ++hb) {
+                if (fl.cid == 0 && head_ok(hb)) {
+                    float* e = sh->rec[s][hb * 4 + fl.hl];
+                    *reinterpret_cast<f4*>(e) = f4{o.mf[hb], o.lf[hb], o.a[hb][0], o.a[hb][1]};
+                    *reinterpret_cast<f4*>(e + 4) = f4{o.a[hb][2], o.a[hb][3], o.a[hb][4], o.a[hb][5]};
+                    *reinterpret_cast<f4*>(e + 8) = f4{o.a[hb][6], o.a[hb][7], __int_as_float(C.err), 0.f};
                 }
-                if (lane == 0) lds_st(&sh->err[s], C.err);
-                wait_lds();  // the slot is written before its tag
-                if (lane == 0) lds_st(&sh->tag[s], t + 1);
             }
+            wait_lds();  // the records are written before their tag
+            if (lane == 0) lds_st(&sh->tag[s], t + 1);
         } else {
-            const int s = o1 % kTeamRingG;
-            if (o1 - kTeamRingG >= frt) {
-                const Deadline dl;
-                while (o1 - kTeamRingG >= frt && t < bnd && !dl.passed()) {
-                    __builtin_amdgcn_s_sleep(8);
-                    bnd = unstamp(cld(gctl + 1), P.epoch, bnd);
-                    frt = unstamp(cld(gctl + 0), P.epoch, frt);
-                }
-            }
-            if (t < bnd && o1 - kTeamRingG < frt) {
-                float* slot = P.team_ring + ((long long)grp * kTeamRingG + s) * (HBM * kSlotLane * 64);
+            const unsigned tag = rec_tag(P.epoch, o1);
 #pragma unroll
-                for (int hb = 0; hb < HBM; ++hb) {
-                    float* e = slot + hb * kSlotLane * 64 + lane;
-                    cst(e, o.mf[hb]);
-                    cst(e + 64, o.lf[hb]);
+            for (int hb = 0; hb < HBM; ++hb) {
+                if (fl.cid == 0 && head_ok(hb)) {
+                    unsigned long long* e = tg.rec + (long long)s * kTeamRecW * kTeamRecHeads + hb * 4 + fl.hl;
+                    cst(e + 0 * kTeamRecHeads, tagw(tag, o.mf[hb]));
+                    cst(e + 1 * kTeamRecHeads, tagw(tag, o.lf[hb]));
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) cst(e + 64 * (2 + j), o.a[hb][j]);
+                    for (int j = 0; j < 8; ++j) cst(e + (2 + j) * kTeamRecHeads, tagw(tag, o.a[hb][j]));
+                    cst(e + 10 * kTeamRecHeads, tagw(tag, __int_as_float(C.err)));
                 }
-                // the re-read returns once every store before it has completed
-                const float last = cld(slot + (HBM - 1) * kSlotLane * 64 + 64 * 9 + lane);
-                asm volatile("" ::"v"(last) : "memory");
-                if (lane == 0)
-                    cst(P.team_tag + (long long)grp * kTeamRingG + s,
-                        stamp(P.epoch, (unsigned)(t + 1) | ((unsigned)C.err << 31)));
             }
         }
-        if (!haveN) break;
+        // keep the tile's partial until its decision
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            q0.m[hb] = o.mf[hb];
+            q0.l[hb] = o.lf[hb];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q0.a[hb][j] = o.a[hb][j];
+        }
+        t0 = t;
+        np = 1;
+        // the next tile's loads (after the hand-over: the record goes out
+        // early, and the tile's partial is no longer live across the issue)
+        const int tn = t + plan.W;
+        if (tn >= nt || tn >= bnd) break;
+        S::resolve_from(P, grp, n, tn, blkN, C);
+        if constexpr (!PRIMARY) load_glb();
+        st.template issue<0>(P, C, 0);
+        st.template issue<1>(P, C, 1);
+        blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
+        ++loaded;
+        rows += min(S::T, n - tn * S::T);
         t = tn;
         o1 += ostep;
-        C = N;
     }
+    // the last tile's decision
+    if (!gv) retire();
     // loads of a tile fetched past the stop may still be landing (in LDS too)
     __builtin_amdgcn_s_waitcnt(0);
     count_stats(P, loaded, rows);
     if (VSKIP && P.stats && lane == 0) atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 3), skipped);
 }
 
-// sum of squares of 8 values as a balanced tree (short dependency chain)
-__device__ __forceinline__ float sumsq8(const float (&v)[8]) {
-    const float a = fmaf(v[1], v[1], v[0] * v[0]), b = fmaf(v[3], v[3], v[2] * v[2]);
-    const float c = fmaf(v[5], v[5], v[4] * v[4]), d = fmaf(v[7], v[7], v[6] * v[6]);
-    return (a + b) + (c + d);
-}
-
-// Running state of the group's heads, in the decider (fold mapping).
-template <int HBM>
-struct DeciderState {
-    float M[HBM], L[HBM], A[HBM][8], prev[HBM][8], pn[HBM];
-    int streak[HBM], U[HBM], err[HBM];
-    int ug;  // largest tiles_used so far
-};
-
-// Folds tile f (this lane's m, l and 8 accumulator values per head block, and
-// the tile's error flag) into D; writes the output of each head that stops.
-// Returns true once every head has stopped.
-template <int HBM>
-__device__ __forceinline__ bool fold_tile(const Params& P, int grp, const FoldLanes& fl, DeciderState<HBM>& D, int f,
-                                          const float (&mt)[HBM], const float (&lt)[HBM], const float (&at)[HBM][8],
-                                          int et) {
-    const int lane = lane_id(), row0 = lane & ~15;
-    bool any = false;
-    static_for<0, HBM>([&](auto hbc) {
-        constexpr int hb = decltype(hbc)::value;
-        const int h = hb * 4 + fl.hl;
-        const bool act = D.U[hb] < 0;
-        bool pass = false;
-        if (act) {
-            const float Mn = fmaxf(D.M[hb], mt[hb]);
-            const float al = D.M[hb] == kNegInf ? 0.f : exp_fast(D.M[hb] - Mn);
-            const float be = mt[hb] == kNegInf ? 0.f : exp_fast(mt[hb] - Mn);
-            D.L[hb] = fmaf(al, D.L[hb], be * lt[hb]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) D.A[hb][j] = fmaf(al, D.A[hb][j], be * at[hb][j]);
-            D.M[hb] = Mn;
-            D.err[hb] |= et;
-            // probe: head dims 0..7 are this row's lane 16*hl (cid 0); the
-            // hardware reciprocal and square root (about 1 ulp) keep the
-            // per-tile chain short
-            const float invL = __builtin_amdgcn_rcpf(D.L[hb]);
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = D.A[hb][j] * invL;
-            const float xn = __builtin_amdgcn_sqrtf(sumsq8(x));
-            if (f >= 1) {
-                float ds, dd;
-                if (xn == 0.f || D.pn[hb] == 0.f) {
-                    ds = dd = INFINITY;
-                } else {
-                    const float ix = __builtin_amdgcn_rcpf(xn), ip = __builtin_amdgcn_rcpf(D.pn[hb]);
-                    ds = fabsf(xn - D.pn[hb]) * ip;
-                    // 1 - cos as half the squared distance of the unit vectors
-                    float dl2[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) dl2[j] = fmaf(x[j], ix, -(D.prev[hb][j] * ip));
-                    dd = 0.5f * sumsq8(dl2);
-                }
-                pass = ds < P.eps_scale && dd < P.eps_dir;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) D.prev[hb][j] = x[j];
-            D.pn[hb] = xn;
-        }
-        // the row's decision is that of its lane 16*hl
-        const bool pass_row = ((__ballot(pass && fl.cid == 0) >> row0) & 1ull) != 0ull;
-        if (act && f >= 1) {
-            D.streak[hb] = pass_row ? D.streak[hb] + 1 : 0;
-            if (D.streak[hb] >= P.patience) {
-                D.U[hb] = f + 1;
-                D.ug = max(D.ug, D.U[hb]);
-                write_head_out(P, grp, h, fl, D.A[hb], D.L[hb], D.err[hb], D.U[hb]);
-            }
-        }
-        any |= D.U[hb] < 0;
-    });
-    return __ballot(any) == 0ull;
-}
-
-// Folds tiles 0, 1, ... of the group in order: the primary's from LDS, the
-// helpers' from the global ring, a batch at a time.  A wait longer than
-// kWaitTicks (impossible unless a worker faulted) ends the group: its
-// unfinished heads get tiles_used = -2 and NaN.
-template <int HBM>
-__device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const TeamPlan& plan, const float* ring,
-                                             TeamShared* sh) {
-    constexpr int kBatch = 8 / HBM;  // helper tiles loaded at once
-    const int lane = lane_id();
+// Decides the group's tiles, block after block; at the end leaves each
+// head's tiles_used (or -2) in its decision word and its error flag in LDS.
+template <int HBM, int GMAX>
+__device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const TeamPlan& plan,
+                                             TeamShared<GMAX>* sh) {
+    const int lane = lane_id(), i = lane & 15, row0 = lane & ~15;
     const FoldLanes fl(P);
     const int G = P.G;
-    unsigned long long* gctl = P.team_ctl + 2 * grp;
-    const unsigned long long* gtag = P.team_tag + (long long)grp * kTeamRingG;
-    DeciderState<HBM> D;
+    const TeamGlobal tg(P, grp);
+    const bool glb = plan.nH > 0;
+    // committed state: after the tiles before the current block (replicated over the row)
+    float cM[HBM], cL[HBM], cP[HBM][8], cX[HBM][8], cXn[HBM];
+    int streak[HBM], U[HBM], err[HBM];
+    bool hv[HBM];
 #pragma unroll
     for (int hb = 0; hb < HBM; ++hb) {
-        const int h = hb * 4 + fl.hl;
-        D.M[hb] = kNegInf; D.L[hb] = 0.f; D.pn[hb] = 0.f; D.streak[hb] = 0; D.err[hb] = 0;
-        D.U[hb] = (hb < fl.HB && h < G) ? -1 : 0;
+        hv[hb] = hb < fl.HB && hb * 4 + fl.hl < G;
+        cM[hb] = kNegInf;
+        cL[hb] = 0.f;
+        cXn[hb] = 0.f;
+        streak[hb] = 0;
+        err[hb] = 0;
+        U[hb] = hv[hb] ? -1 : 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { D.A[hb][j] = 0.f; D.prev[hb][j] = 0.f; }
+        for (int j = 0; j < 8; ++j) {
+            cP[hb][j] = 0.f;
+            cX[hb][j] = 0.f;
+        }
     }
-    D.ug = 0;
+    int relA = 0, relH = 0;
     bool finished = false, gave_up = false;
-    // A primary tile's slot: the tag is read first and the data right after,
-    // without a wait in between.  A wave's LDS accesses execute in order and a
-    // worker stores the data before the tag, so when the tag shows the tile the
-    // data read after it is that tile's.  The next tile's slot is read while
-    // the current one is folded.
-    auto read_slot = [&](int s, int& tag, int& err, float (&mt)[HBM], float (&lt)[HBM], float (&at)[HBM][8]) {
-        tag = lds_ld(&sh->tag[s]);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        err = lds_ld(&sh->err[s]);
-        const float* slot = ring + s * (HBM * kSlotLane * 64);
+    for (int f0 = 0; f0 < nt && !finished && !gave_up; f0 += kBlock) {
+        const int kmax = min(kBlock, nt - f0);
+        const int t = f0 + i;
+        const bool inr = i < kmax;
+        const int kp = t % plan.W, per = t / plan.W;
+        const bool prim = kp < plan.nA;
+        const int ord = prim ? per * plan.nA + kp : per * plan.nH + (kp - plan.nA);
+        const int sA = ord & (kProbeRing - 1), sH = ord & (kTeamRingG - 1);
+        const unsigned rtag = rec_tag(P.epoch, ord);
+        // lane i's record of tile t (identity until it is there)
+        float rm[HBM], rl[HBM], rp[HBM][8];
+        int re[HBM];
 #pragma unroll
         for (int hb = 0; hb < HBM; ++hb) {
-            const float* e = slot + hb * kSlotLane * 64 + lane;
-            mt[hb] = e[0];
-            lt[hb] = e[64];
+            rm[hb] = kNegInf;
+            rl[hb] = 0.f;
+            re[hb] = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) at[hb][j] = e[64 * (2 + j)];
+            for (int j = 0; j < 8; ++j) rp[hb][j] = 0.f;
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    };
-    // tags of the helpers' tiles t0 .. t0 + cnt - 1 (helper ordinals h0 ..): lane i polls one
-    auto poll_tags = [&](int h0, int cnt) -> unsigned long long {
-        return lane < cnt ? cld(gtag + (h0 + lane) % kTeamRingG) : 0ull;
-    };
-    auto tags_ready = [&](unsigned long long tg, int t0, int cnt) {
-        const bool ok = lane >= cnt ||
-                        ((unsigned)(tg >> 32) == P.epoch && ((unsigned)tg & 0x7fffffffu) == (unsigned)(t0 + lane + 1));
-        return __ballot(!ok) == 0ull;
-    };
-    // position: tile f, f % W = pk, oA of the primary's and oH of the helpers' tiles folded
-    int f = 0, pk = 0, oA = 0, oH = 0;
-    int tagc = 0, errc = 0;
-    float mtc[HBM], ltc[HBM], atc[HBM][8];
-    read_slot(0, tagc, errc, mtc, ltc, atc);
-    // tags of the helpers' tiles of the current period, polled when the period starts
-    unsigned long long tgp = 0;
-    int hp0 = plan.nA, hpc = 0;
-    if (plan.nH) {
-        hpc = max(0, min(plan.nH, nt - hp0));
-        tgp = poll_tags(0, hpc);
-    }
-    while (f < nt) {
-        if (pk < plan.nA) {
-            const int s = oA % kTeamRing;
-            if (tagc != f + 1) {
-                // not there yet: poll the tag alone (the workers use LDS too), then read the slot
-                const Deadline dl;
-                while (lds_ld(&sh->tag[s]) != f + 1) {
-                    if (dl.passed()) {
-                        gave_up = true;
-                        break;
+        bool have = !inr;
+        int kdone = 0;
+        unsigned long long since = wall_clock64();
+        for (;;) {
+            if (!have) {
+                if (prim) {
+                    // a wave's LDS accesses execute in order and the worker stores
+                    // the data before the tag: data read after the tag is the tile's
+                    if (lds_ld(&sh->tag[sA]) == t + 1) {
+                        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+                        for (int hb = 0; hb < HBM; ++hb) {
+                            if (hv[hb]) {
+                                const float* e = sh->rec[sA][hb * 4 + fl.hl];
+                                const f4 x0 = *reinterpret_cast<const f4*>(e);
+                                const f4 x1 = *reinterpret_cast<const f4*>(e + 4);
+                                const f4 x2 = *reinterpret_cast<const f4*>(e + 8);
+                                rm[hb] = x0.x; rl[hb] = x0.y; rp[hb][0] = x0.z; rp[hb][1] = x0.w;
+                                rp[hb][2] = x1.x; rp[hb][3] = x1.y; rp[hb][4] = x1.z; rp[hb][5] = x1.w;
+                                rp[hb][6] = x2.x; rp[hb][7] = x2.y; re[hb] = __float_as_int(x2.z);
+                            }
+                        }
+                        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                        have = true;
                     }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                if (gave_up) break;
-                read_slot(s, tagc, errc, mtc, ltc, atc);
-            }
-            float mt[HBM], lt[HBM], at[HBM][8];
-            const int et = errc;
+                } else {
+                    bool ok = true;
+                    unsigned long long w[HBM][kTeamRecW];
 #pragma unroll
-            for (int hb = 0; hb < HBM; ++hb) {
-                mt[hb] = mtc[hb];
-                lt[hb] = ltc[hb];
+                    for (int hb = 0; hb < HBM; ++hb) {
+                        if (hv[hb]) {
+                            const unsigned long long* e =
+                                tg.rec + (long long)sH * kTeamRecW * kTeamRecHeads + hb * 4 + fl.hl;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) at[hb][j] = atc[hb][j];
-            }
-            // the next tile's slot, if it is the primary's too
-            if (f + 1 < nt && (pk + 1 < plan.nA || (pk + 1 == plan.W && plan.nA > 0)))
-                read_slot((oA + 1) % kTeamRing, tagc, errc, mtc, ltc, atc);
-            finished = fold_tile<HBM>(P, grp, fl, D, f, mt, lt, at, et);
-            ++f;
-            ++oA;
-            if (++pk == plan.W) pk = 0;
-            if (pk == 0 && plan.nH && f < nt) {
-                hp0 = f + plan.nA;
-                hpc = max(0, min(plan.nH, nt - hp0));
-                tgp = poll_tags(oH, hpc);
-            }
-        } else {
-            // the helpers' tiles of this period (from hp0, helper ordinals from
-            // oH - (f - hp0)), a batch of up to kBatch at a time
-            const int h0 = oH - (f - hp0);
-            const int bcnt = min(kBatch, hp0 + hpc - f);
-            if (!tags_ready(tgp, hp0, hpc)) {
-                const Deadline dl;
-                for (;;) {
-                    if (dl.passed()) {
-                        gave_up = true;
-                        break;
+                            for (int j = 0; j < kTeamRecW; ++j) w[hb][j] = cld(e + j * kTeamRecHeads);
+                        }
                     }
-                    __builtin_amdgcn_s_sleep(2);
-                    tgp = poll_tags(h0, hpc);
-                    if (tags_ready(tgp, hp0, hpc)) break;
-                }
-                if (gave_up) break;
-            }
-            const int errl = (int)((unsigned)tgp >> 31);
-            float mt[kBatch][HBM], lt[kBatch][HBM], at[kBatch][HBM][8];
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int si = (oH + i) % kTeamRingG;
-                const float* slot = P.team_ring + ((long long)grp * kTeamRingG + si) * (HBM * kSlotLane * 64);
+                    for (int hb = 0; hb < HBM; ++hb) {
+                        if (hv[hb]) {
+#pragma unroll
+                            for (int j = 0; j < kTeamRecW; ++j) ok &= (unsigned)(w[hb][j] >> 32) == rtag;
+                        }
+                    }
+                    if (ok) {
+#pragma unroll
+                        for (int hb = 0; hb < HBM; ++hb) {
+                            if (hv[hb]) {
+                                rm[hb] = untag(w[hb][0]);
+                                rl[hb] = untag(w[hb][1]);
+#pragma unroll
+                                for (int j = 0; j < 8; ++j) rp[hb][j] = untag(w[hb][2 + j]);
+                                re[hb] = (int)(unsigned)w[hb][10];
+                            }
+                        }
+                        have = true;
+                    }
+                }
+            }
+            // the tiles present for every head, from the block start
+            const unsigned long long hbits = __ballot(have);
+            const unsigned mask = (unsigned)(hbits & (hbits >> 16) & (hbits >> 32) & (hbits >> 48)) & 0xffffu;
+            const int kk = min(__builtin_ctz(~mask), kmax);
+            if (kk > kdone) {
+                since = wall_clock64();
+                bool any = false;
+                static_for<0, HBM>([&](auto hbc) {
+                    constexpr int hb = decltype(hbc)::value;
+                    const bool act = hv[hb] && U[hb] < 0;
+                    if (__ballot(act) == 0ull) return;
+                    // inclusive scan of the block's records along the row
+                    float m = rm[hb], l = rl[hb], p[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) p[j] = rp[hb][j];
+                    auto step = [&](auto dc) {
+                        constexpr int d = decltype(dc)::value;
+                        float om = row_shr<d>(kNegInf, m), ol = row_shr<d>(0.f, l), op[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) op[j] = row_shr<d>(0.f, p[j]);
+                        sm_merge_fast(om, ol, op, m, l, p);  // the earlier tiles first
+                        m = om;
+                        l = ol;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) p[j] = op[j];
+                    };
+                    step(std::integral_constant<int, 1>{});
+                    step(std::integral_constant<int, 2>{});
+                    step(std::integral_constant<int, 4>{});
+                    step(std::integral_constant<int, 8>{});
+                    // the running state after tile t: committed (+) scan
+                    float sM = cM[hb], sL = cL[hb], sP[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sP[j] = cP[hb][j];
+                    sm_merge_fast(sM, sL, sP, m, l, p);
+                    // probe: dims 0..7 of the normalised running output; the
+                    // hardware reciprocal and square root (about 1 ulp)
+                    const float invL = __builtin_amdgcn_rcpf(sL);
+                    float x[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[j] = sP[j] * invL;
+                    const float xn = __builtin_amdgcn_sqrtf(sumsq8(x));
+                    // the previous probe: lane i - 1's, the committed one for lane 0
+                    const float ppn = row_shr<1>(cXn[hb], xn);
+                    float pp[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) pp[j] = row_shr<1>(cX[hb][j], x[j]);
+                    bool pass = false;
+                    if (t >= 1) {
+                        float ds, dd;
+                        if (xn == 0.f || ppn == 0.f) {
+                            ds = dd = INFINITY;
+                        } else {
+                            const float ix = __builtin_amdgcn_rcpf(xn), ip = __builtin_amdgcn_rcpf(ppn);
+                            ds = fabsf(xn - ppn) * ip;
+                            // 1 - cos as half the squared distance of the unit vectors
+                            float dl2[8];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) dl2[j] = fmaf(x[j], ix, -(pp[j] * ip));
+                            dd = 0.5f * sumsq8(dl2);
+                        }
+                        pass = ds < P.eps_scale && dd < P.eps_dir;
+                    }
+                    const unsigned pbits = (unsigned)(__ballot(pass) >> row0) & 0xffffu;
+                    const unsigned ebits = (unsigned)(__ballot(re[hb] != 0) >> row0) & 0xffffu;
+                    // the streak from the block start (the same at every pass) to the first stop
+                    int sk;
+                    const int istop = first_stop(pbits, kk, streak[hb], P.patience, sk);
+                    if (act) {
+                        if (istop >= 0) {
+                            U[hb] = f0 + istop + 1;
+                            err[hb] |= (ebits & ((2u << istop) - 1u)) != 0u;
+                        } else if (kk == kmax) {
+                            // the block is complete: commit its last tile's state
+                            const int src = row0 | (kmax - 1);
+                            err[hb] |= (ebits & ((2u << (kmax - 1)) - 1u)) != 0u;
+                            streak[hb] = sk;
+                            cM[hb] = __shfl(sM, src);
+                            cL[hb] = __shfl(sL, src);
+                            cXn[hb] = __shfl(xn, src);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                cP[hb][j] = __shfl(sP[j], src);
+                                cX[hb][j] = __shfl(x[j], src);
+                            }
+                            if (f0 + kmax >= nt) U[hb] = nt;  // no stop: every tile is used
+                        }
+                    }
+                });
+                kdone = kk;
+                // publish each head's decision word, then the bound once every head is done
+                int ug = 0;
 #pragma unroll
                 for (int hb = 0; hb < HBM; ++hb) {
-                    const float* e = slot + hb * kSlotLane * 64 + lane;
-                    const bool v = i < bcnt;
-                    mt[i][hb] = v ? cld(e) : kNegInf;
-                    lt[i][hb] = v ? cld(e + 64) : 0.f;
+                    any |= hv[hb] && U[hb] < 0;
+                    if (hv[hb]) ug = max(ug, U[hb]);
+                }
+                finished = __ballot(any) == 0ull;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) at[i][hb][j] = v ? cld(e + 64 * (2 + j)) : 0.f;
+                for (int hb = 0; hb < HBM; ++hb) {
+                    if (i == 0 && hv[hb]) {
+                        const int h = hb * 4 + fl.hl;
+                        const int wd = U[hb] >= 0 ? (kHdStop | U[hb]) : (f0 + kdone);
+                        lds_st(&sh->word[h], wd);
+                        if (glb) cst(tg.ctl + 4 + h, stamp(P.epoch, (unsigned)wd));
+                    }
+                }
+                if (finished) {
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) ug = max(ug, __shfl_xor(ug, o));
+                    if (lane == 0) {
+                        lds_st(&sh->bound, ug);
+                        if (glb) cst(tg.ctl + 1, stamp(P.epoch, (unsigned)ug));
+                    }
+                    break;
                 }
             }
-            // the next period's first (primary) slot, read while this batch is folded
-            if (f + bcnt < nt && pk + bcnt == plan.W) read_slot(oA % kTeamRing, tagc, errc, mtc, ltc, atc);
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                if (i < bcnt && !finished) {
-                    finished = fold_tile<HBM>(P, grp, fl, D, f, mt[i], lt[i], at[i], __shfl(errl, f - hp0));
-                    ++f;
-                    ++oH;
-                    if (++pk == plan.W) pk = 0;
-                }
+            if (kdone == kmax) break;
+            if (wall_clock64() - since > kWaitTicks) {
+                gave_up = true;
+                break;
             }
-            if (pk == 0 && f < nt) {
-                hp0 = f + plan.nA;
-                hpc = max(0, min(plan.nH, nt - hp0));
-                tgp = poll_tags(oH, hpc);
-            }
+            __builtin_amdgcn_s_sleep(1);
         }
-        if (finished) break;
+        if (finished || gave_up) break;
+        // the block is decided: its slots may be reused
+        const int na = __builtin_popcountll(__ballot(inr && prim) & 0xffffull);
+        relA += na;
+        relH += kmax - na;
         if (lane == 0) {
-            lds_st(&sh->frontier, oA);
-            if (plan.nH) cst(gctl + 0, stamp(P.epoch, (unsigned)oH));
+            lds_st(&sh->released, relA);
+            if (glb) cst(tg.ctl + 0, stamp(P.epoch, (unsigned)relH));
         }
     }
-    // heads that never stopped used every tile (or the group gave up)
+    if (gave_up) {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            if (i == 0 && hv[hb] && U[hb] < 0) {
+                const int h = hb * 4 + fl.hl;
+                lds_st(&sh->word[h], kHdGaveUp);
+                if (glb) cst(tg.ctl + 4 + h, stamp(P.epoch, (unsigned)kHdGaveUp));
+            }
+        }
+        if (lane == 0) {
+            lds_st(&sh->bound, 0);
+            if (glb) cst(tg.ctl + 1, stamp(P.epoch, 0u));
+        }
+    }
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb)
+        if (i == 0 && hv[hb]) lds_st(&sh->err[hb * 4 + fl.hl], err[hb]);
+}
+
+// running states of waves w0 .. w1-1, each in its area of the LDS, merged in wave order
+template <int HBM>
+__device__ __forceinline__ void merge_areas(const float* lds, size_t wave_floats, int w0, int w1, Part<HBM>& out) {
+    const int lane = lane_id();
+    out.clear();
+    for (int w = w0; w < w1; ++w) {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            const float* e = lds + w * wave_floats + (hb * kTeamStateW) * 64 + lane;
+            float a2[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a2[j] = e[64 * (2 + j)];
+            sm_merge(out.m[hb], out.l[hb], out.a[hb], e[0], e[64], a2);
+        }
+    }
+}
+
+template <int HBM>
+__device__ __forceinline__ void store_area(float* mine, const Part<HBM>& ws) {
+    const int lane = lane_id();
 #pragma unroll
     for (int hb = 0; hb < HBM; ++hb) {
-        const int h = hb * 4 + fl.hl;
-        if (D.U[hb] < 0) {
-            if (gave_up) {
-                float nan8[8];
+        float* e = mine + (hb * kTeamStateW) * 64 + lane;
+        e[0] = ws.m[hb];
+        e[64] = ws.l[hb];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) nan8[j] = NAN;
-                write_head_out(P, grp, h, fl, nan8, 1.f, 0, -2);
-            } else {
-                write_head_out(P, grp, h, fl, D.A[hb], D.L[hb], D.err[hb], nt);
-            }
-        }
-    }
-    int ugw = finished ? D.ug : 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ugw = max(ugw, __shfl_xor(ugw, o));
-    const int bound = finished ? ugw : (gave_up ? 0 : nt);
-    if (lane == 0) {
-        lds_st(&sh->bound, bound);
-        if (plan.nH) cst(gctl + 1, stamp(P.epoch, (unsigned)bound));
+        for (int j = 0; j < 8; ++j) e[64 * (2 + j)] = ws.a[hb][j];
     }
 }
 
@@ -2098,8 +2312,9 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
 template <class S, bool VSKIP>
 __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     extern __shared__ float lds[];
-    constexpr int HBM = S::HBM, TEAM = S::TEAM;
+    constexpr int HBM = S::HBM, TEAM = S::TEAM, GMAX = S::HEADS;
     const int wv = wave_id(), lane = lane_id();
+    const FoldLanes fl(P);
     const int G = P.G;
     const int grp = blockIdx.x % P.NG, team = blockIdx.x / P.NG;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
@@ -2117,42 +2332,120 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     }
     const TeamPlan plan(TEAM - 1, P.helpers * TEAM);
     const size_t wave_floats = S::lds_floats(P);
+    const TeamGlobal tg(P, grp);
+    Part<HBM> ws;
     if (team > 0) {
-        S st;
-        st.init(lds + wv * wave_floats);
-        if constexpr (!VSKIP)
-            team_worker<S, false, false>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st, nullptr, nullptr);
+        // a helper: every wave is a worker; their states, merged in wave
+        // order, go to the primary as tagged words
+        if constexpr (!VSKIP) {
+            S st;
+            st.init(lds + wv * wave_floats);
+            team_worker<S, false, false>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st, nullptr, ws);
+        } else {
+            ws.clear();
+        }
+        __syncthreads();  // every wave is done with its tile buffers
+        store_area<HBM>(lds + wv * wave_floats, ws);
+        __syncthreads();
+        if (wv == 0) {
+            Part<HBM> hs;
+            merge_areas<HBM>(lds, wave_floats, 0, TEAM, hs);
+            const unsigned tag = rec_tag(P.epoch, 0);
+            unsigned long long* dst = tg.hstate + (long long)(team - 1) * HBM * kTeamStateW * 64 + lane;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                unsigned long long* e = dst + hb * kTeamStateW * 64;
+                cst(e, tagw(tag, hs.m[hb]));
+                cst(e + 64, tagw(tag, hs.l[hb]));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) cst(e + 64 * (2 + j), tagw(tag, hs.a[hb][j]));
+            }
+        }
         return;
     }
-    float* ring = lds + (TEAM - 1) * wave_floats;  // [kTeamRing][HBM][kSlotLane][64]
-    TeamShared* sh = reinterpret_cast<TeamShared*>(ring + kTeamRing * HBM * kSlotLane * 64);
+    TeamShared<GMAX>* sh = reinterpret_cast<TeamShared<GMAX>*>(lds + (TEAM - 1) * wave_floats);
     if (wv == 0) {
-        if (lane < kTeamRing) {
-            sh->tag[lane] = 0;
+        for (int k = lane; k < kProbeRing; k += 64) sh->tag[k] = 0;
+        if (lane < kChain) sh->ptag[lane] = 0;
+        if (lane < GMAX) {
+            sh->word[lane] = 0;
             sh->err[lane] = 0;
         }
         if (lane == 0) {
-            sh->frontier = 0;
+            sh->released = 0;
             sh->bound = nt;
         }
-        if (lane < kChain) sh->ptag[lane] = 0;
     }
     __syncthreads();
     if (wv == 0) {
-        // the decider's per-tile chain is latency-bound: let its SIMD issue it first
+        // the decider's chain is latency-bound: let its SIMD issue it first
         __builtin_amdgcn_s_setprio(3);
-        team_decider<HBM>(P, grp, nt, plan, ring, sh);
+        team_decider<HBM, GMAX>(P, grp, nt, plan, sh);
+        __builtin_amdgcn_s_setprio(0);
+        ws.clear();
     } else {
         S st;
         st.init(lds + (wv - 1) * wave_floats);
-        team_worker<S, true, VSKIP>(P, grp, n, nt, wv - 1, plan, st, ring, sh);
+        team_worker<S, true, VSKIP>(P, grp, n, nt, wv - 1, plan, st, sh, ws);
+    }
+    __syncthreads();  // every worker is done with its tile buffers, the decider with the words
+    if (wv > 0) store_area<HBM>(lds + (wv - 1) * wave_floats, ws);
+    __syncthreads();
+    if (wv != 0) return;
+    // the primary's workers in order, then the helpers in order
+    Part<HBM> tot;
+    merge_areas<HBM>(lds, wave_floats, 0, TEAM - 1, tot);
+    bool lost = false;  // a helper's state did not arrive within kWaitTicks
+    const unsigned htag = rec_tag(P.epoch, 0);
+    for (int r = 0; r < P.helpers; ++r) {
+        const unsigned long long* src = tg.hstate + (long long)r * HBM * kTeamStateW * 64 + lane;
+        unsigned long long w[HBM][kTeamStateW];
+        const Deadline dl;
+        for (;;) {
+            bool ok = true;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb)
+#pragma unroll
+                for (int j = 0; j < kTeamStateW; ++j) {
+                    w[hb][j] = cld(src + (hb * kTeamStateW + j) * 64);
+                    ok &= (unsigned)(w[hb][j] >> 32) == htag;
+                }
+            if (__ballot(!ok) == 0ull) break;
+            if (dl.passed()) {
+                lost = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (lost) break;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            float a2[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a2[j] = untag(w[hb][2 + j]);
+            sm_merge(tot.m[hb], tot.l[hb], tot.a[hb], untag(w[hb][0]), untag(w[hb][1]), a2);
+        }
+    }
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        if (hb >= fl.HB || h >= G) continue;
+        const int wd = lds_ld(&sh->word[h]);
+        if (lost || !(wd & kHdStop)) {
+            float nan8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) nan8[j] = NAN;
+            write_head_out(P, grp, h, fl, nan8, 1.f, 0, -2);
+        } else {
+            write_head_out(P, grp, h, fl, tot.a[hb], tot.l[hb], lds_ld(&sh->err[h]), wd & kHdCount);
+        }
     }
 }
 
 template <class S>
 size_t team_lds_bytes(const Params& p) {
-    const size_t primary = ((size_t)(S::TEAM - 1) * S::lds_floats(p) + (size_t)kTeamRing * S::HBM * kSlotLane * 64) *
-                               sizeof(float) + sizeof(TeamShared);
+    const size_t primary =
+        (size_t)(S::TEAM - 1) * S::lds_floats(p) * sizeof(float) + sizeof(TeamShared<S::HEADS>);
     const size_t helper = (size_t)S::TEAM * S::lds_floats(p) * sizeof(float);
     return primary > helper ? primary : helper;
 }
@@ -2451,7 +2744,7 @@ int launch_team(const Params& p0, hipStream_t s) {
     const size_t lds = team_lds_bytes<S>(p);
     p.helpers = 0;
     int dev = 0, cus = 0, per_cu = 0;
-    if (!VSKIP && p0.helpers > 0 && hipGetDevice(&dev) == hipSuccess &&
+    if (!VSKIP && p0.helpers > 0 && p.NG <= kTeamHelpGroups && hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_team_kernel<S, VSKIP>, S::TEAM * 64, lds) == hipSuccess &&
         per_cu > 0) {

@@ -148,16 +148,21 @@ def test_worker_count_does_not_change_results():
 
 @pytest.mark.parametrize("helpers", [1, 3])
 def test_helper_work_groups_do_not_change_results(helpers):
-    # helper work-groups on other CUs take some of each group's tiles; every
-    # tile's partial is computed alike and folded in the same order, so the
-    # results are those without helpers, bit for bit
+    # helper work-groups on other CUs take some of each group's tiles; the
+    # stop decisions come from per-tile records scanned in fixed blocks, so
+    # tiles_used is the one without helpers exactly, and the output differs
+    # only by the order in which the workers' partial sums are merged.  A
+    # launch shape is deterministic: a repeat gives the same bits.
     c = A.config(3, small=True)
     dev = to_device(c)
     o_art, u_art = run_gpu(c, dev)
     for kw in (dict(), dict(eps_scale=1e-30, eps_dir=1e-30)):
         o0, u0 = run_gpu(c, dev, **kw)
         o1, u1 = run_gpu(c, dev, team_helpers=helpers, **kw)
-        assert np.array_equal(u1, u0) and np.array_equal(o1, o0)
+        o1b, u1b = run_gpu(c, dev, team_helpers=helpers, **kw)
+        assert np.array_equal(u1, u0)
+        assert np.array_equal(u1b, u1) and np.array_equal(o1b, o1)
+        np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-5)
     o0, u0 = o_art, u_art
     # and with more groups than the chip can give further CUs: the helpers are dropped
     import dataclasses
