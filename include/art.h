@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define ART_ABI_VERSION 2
+#define ART_ABI_VERSION 3
 
 typedef enum {
     ART_OK = 0,
@@ -41,6 +41,19 @@ typedef enum {
 } art_status;
 
 typedef enum { ART_F32 = 0, ART_BF16 = 1, ART_I8 = 2 } art_dtype;
+
+/* How ART-mode work is spread over the GPU (results agree to rounding; tiles_used
+ * is the same whichever runs).  The choice applies to bf16/int8 caches with
+ * head_dim 128, bf16 queries, at most 8 query heads per KV head and 64-token
+ * tiles; other shapes always run the work-sharing engine. */
+typedef enum {
+    ART_ENGINE_AUTO = 0,    /* library default                                         */
+    ART_ENGINE_TEAM = 1,    /* one work-group per (row, KV head), plus team_helpers    */
+    ART_ENGINE_POOL = 2,    /* waves on every CU move to the groups with work left; no
+                               V skip (falls back to TEAM) and at most one group per
+                               resident work-group                                     */
+    ART_ENGINE_SHARED = 3   /* work-sharing engine: max_workers waves claim tiles      */
+} art_engine;
 
 /*
  * Shape and options of one call.  Layouts are row-major:
@@ -81,11 +94,13 @@ typedef struct {
                                     [3] (query head, position) pairs whose V row was
                                         skipped (v_skip_eps > 0; counted by the
                                         default engine for 64-token tiles only)       */
-    int32_t max_workers;         /* 0 = library default; > 0: work-sharing engine     */
+    int32_t max_workers;         /* 0 = library default; > 0 (engine AUTO or SHARED):
+                                    the work-sharing engine with this many waves      */
     int32_t team_helpers;        /* team engine (ART, streamed tiles): helper work-groups
                                     per group on other CUs, 0..3; 0 = none (default).
                                     Used only where every work-group of the launch can
                                     be resident at once; results do not depend on it  */
+    int32_t engine;              /* art_engine; ART_ENGINE_AUTO = 0                    */
 } art_desc;
 
 /*

@@ -50,10 +50,14 @@ class ArtDesc(ctypes.Structure):
         ("stats", ctypes.c_void_p),
         ("max_workers", ctypes.c_int32),
         ("team_helpers", ctypes.c_int32),
+        ("engine", ctypes.c_int32),
     ]
 
 
 _lib = None
+
+
+ABI_VERSION = 3  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
 
 
 def load():
@@ -80,6 +84,9 @@ def load():
     lib.art_last_error.restype = ctypes.c_char_p
     lib.art_abi_version.argtypes = []
     lib.art_abi_version.restype = ctypes.c_int32
+    if lib.art_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.art_abi_version()}, this binding expects "
+                           f"{ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -92,11 +99,11 @@ def _check(rc: int):
 def make_desc(*, batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, block_size=0,
               max_blocks_per_seq=0, num_blocks=0, max_ctx=0, patience=1, v_skip_eps=0.0,
               k_scale=0, v_scale=0, workspace=0, workspace_bytes=0, stats=0, max_workers=0,
-              team_helpers=0) -> ArtDesc:
+              team_helpers=0, engine=0) -> ArtDesc:
     return ArtDesc(batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, block_size,
                    max_blocks_per_seq, num_blocks, max_ctx, patience, v_skip_eps, k_scale or None,
                    v_scale or None, workspace or None, workspace_bytes, stats or None, max_workers,
-                   team_helpers)
+                   team_helpers, engine)
 
 
 def workspace_bytes(desc: ArtDesc, tile: int) -> int:
@@ -115,6 +122,7 @@ def _dtype_code(t):
 def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64, eps_scale=1e-3,
                      eps_dir=1e-4, patience=1, v_skip_eps=0.0, k_scale=None, v_scale=None,
                      out=None, tiles_used=None, workspace=None, stats=None, max_workers=0, team_helpers=0,
+                     engine=0,
                      stream=None):
     """ART decode attention on device tensors; returns (out fp32, tiles_used int32).
 
@@ -144,7 +152,7 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
                      k_scale=k_scale.data_ptr() if k_scale is not None else 0,
                      v_scale=v_scale.data_ptr() if v_scale is not None else 0,
                      stats=stats.data_ptr() if stats is not None else 0, max_workers=max_workers,
-                     team_helpers=team_helpers)
+                     team_helpers=team_helpers, engine=engine)
     need = workspace_bytes(desc, tile)
     if need == 0:
         _check(validate(desc, tile, eps_scale, eps_dir))

@@ -17,6 +17,9 @@ HIPCC_FLAGS = [
     # no implicit multiply-add fusion: the kernels write their fused
     # multiply-adds out, so every inlined copy of a computation rounds alike
     "-ffp-contract=off",
+    # a wave's atomics here are issued by one lane on purpose; the optimizer's
+    # wave-wide rewrite would read every result at once (a wait for all loads)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

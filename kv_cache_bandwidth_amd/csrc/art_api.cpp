@@ -79,6 +79,8 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     if (d->max_workers < 0) return fail(ART_E_PARAM, "max_workers %d < 0", d->max_workers);
     if (d->team_helpers < 0 || d->team_helpers > art::kMaxHelpers)
         return fail(ART_E_PARAM, "team_helpers %d not in 0..%d", d->team_helpers, art::kMaxHelpers);
+    if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_SHARED)
+        return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_SHARED);
 
     p = art::Params{};
     p.B = d->batch; p.Hq = d->num_q_heads; p.Hkv = d->num_kv_heads; p.G = G; p.D = d->head_dim; p.T = tile;
@@ -120,7 +122,7 @@ Layout workspace_layout(const Params& p) {
     L.vmax = o; o = align256(o + NG * (size_t)p.nt_max * 16 * sizeof(float));
     L.partials = o; o = align256(o + NG * (size_t)p.splits * p.slot * sizeof(float));
     const size_t NT = NG <= (size_t)kTeamHelpGroups ? NG : 0;  // groups that helpers may serve
-    L.team_ring = o; o = align256(o + NT * team_words(p.G) * sizeof(unsigned long long));
+    L.team_ring = o; o = align256(o + NT * group_words(p.G) * sizeof(unsigned long long));
     L.team_ctl = o; o = align256(o + NT * kTeamCtl * sizeof(unsigned long long));
     L.total = o;
     return L;
@@ -194,6 +196,7 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     if (workers > tiles) workers = tiles > 0 ? tiles : 1;
     p.workers = (int)workers;
     p.helpers = desc->team_helpers;
+    p.engine = desc->engine;
     const art::Layout L = art::workspace_layout(p);
     char* ws = static_cast<char*>(desc->workspace);
     p.abort_flag = reinterpret_cast<int*>(ws + L.abort_flag);

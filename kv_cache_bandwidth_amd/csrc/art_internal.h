@@ -20,7 +20,12 @@ constexpr int kTeamRecHeads = 8;  // heads per record slot (streamed tiles serve
 constexpr int kTeamStateW = 10;   // 64-bit words per lane per head block of a helper's final state: m, l, 8 dims
 constexpr int kMaxHelpers = 3;    // helper work-groups per group at most
 constexpr int kTeamCtl = 16;      // control words: [0] helper records released, [1] bound, [4..11] per-head decision
-constexpr int kTeamHelpGroups = 512;  // helpers serve launches of at most this many groups (workspace sized for them)
+constexpr int kTeamHelpGroups = 512;  // helpers and the pool engine serve launches of at most this many
+                                      // groups (the workspace holds their shared words only then)
+constexpr int kPoolRing = 128;    // pool engine: record slots per group, by tile index (a power of two)
+constexpr int kPoolContrib = 32;  // pool engine: workers per group at most (each leaves its running state)
+constexpr int kPoolCtl = 16;      // pool engine control words: [0] tiles released, [1] bound, [2] claim counter,
+                                  // [3] workers joined, [4..11] per-head decision, [12] workers active
 constexpr unsigned long long kWaitTicks = 50000000ull;  // 0.5 s of the 100 MHz device clock:
                                                       // longest any wait may last before the kernel gives up
 constexpr int kSlotHeader = 48;   // floats before the accumulator block of a partial:
@@ -70,12 +75,16 @@ struct Params {
     int* vmax_tag;      // [NG][nt_max]
     float* vmax;        // [NG][nt_max][16]
     float* partials;    // [NG][splits][slot]
-    unsigned long long* team_ring;  // [NG][team_words(G)]: the helpers' probe records
+    unsigned long long* team_ring;  // [NG][group_words(G)]: team engine: the helpers' probe records
                                     // [kTeamRingG][kTeamRecW][kTeamRecHeads], then their final running
-                                    // states [kMaxHelpers][HB][kTeamStateW][64]; (tag << 32) | value bits
+                                    // states [kMaxHelpers][HB][kTeamStateW][64]; pool engine: records
+                                    // [kPoolRing][..][..], then worker states [kPoolContrib][HB][..][64];
+                                    // (tag << 32) | value bits
     unsigned long long* team_ctl;   // [NG][kTeamCtl]: (epoch << 32) | value
     unsigned epoch;     // distinct per call: stale team words of earlier calls never match
     int helpers;        // helper work-groups per group (team kernel)
+    int pool_cap;       // pool kernel: workers that may join one group (<= kPoolContrib)
+    int engine;         // art_engine requested
     int slot;           // floats per partial: kSlotHeader + G*D
     // launch
     int deciders;       // decider waves of the persistent kernel (each owns whole groups)
@@ -84,10 +93,15 @@ struct Params {
     int tiles_per_split;
 };
 
-// 64-bit words of team_ring per group
+// 64-bit words per group: the team engine's helper records and states, or
+// the pool engine's records and worker states
 constexpr size_t team_words(int G) {
     return (size_t)kTeamRingG * kTeamRecW * kTeamRecHeads + (size_t)kMaxHelpers * ((G + 3) / 4) * kTeamStateW * 64;
 }
+constexpr size_t pool_words(int G) {
+    return (size_t)kPoolRing * kTeamRecW * kTeamRecHeads + (size_t)kPoolContrib * ((G + 3) / 4) * kTeamStateW * 64;
+}
+constexpr size_t group_words(int G) { return team_words(G) > pool_words(G) ? team_words(G) : pool_words(G); }
 
 // Workspace layout for a Params (offsets in bytes, all 256-byte aligned).
 struct Layout {

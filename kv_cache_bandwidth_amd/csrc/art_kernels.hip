@@ -73,6 +73,13 @@ template <class T>
 __device__ __forceinline__ void cst(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// a wave-uniform value in scalar registers
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ unsigned long long uni64(unsigned long long x) {
+    return ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+           (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)x);
+}
+
 __device__ __forceinline__ int faa(int* p, int v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -755,6 +762,23 @@ struct Stream {
         if (P.block_size && lane < PAGES && tokp < n)
             blk = P.block_table[(long long)b * P.mbps + (unsigned)tokp / (unsigned)P.block_size];
         return blk;
+    }
+
+    // fetch_blocks() into LDS (dst[p] = page p's entry) with LDS-direct loads,
+    // so that the ids hold no register while they are in flight; read them
+    // (resolve_lds) once the wave's loads have landed
+    __device__ __forceinline__ static void fetch_blocks_lds(const Params& P, int grp, int n, int t, int* dst) {
+        const int lane = lane_id(), b = grp / P.Hkv;
+        const int tokp = t * T + 16 * lane;
+        if (P.block_size && lane < PAGES && tokp < n)
+            __builtin_amdgcn_global_load_lds(P.block_table + (long long)b * P.mbps + (unsigned)tokp / (unsigned)P.block_size,
+                                             (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
+    __device__ __forceinline__ static void resolve_lds(const Params& P, int grp, int n, int t, const int* src,
+                                                       TileRef& r) {
+        const int lane = lane_id();
+        const int blkv = lane < PAGES ? src[lane] : 0;
+        resolve_from(P, grp, n, t, blkv, r);
     }
 
     // resolve() from the block ids fetch_blocks() returned for tile t
@@ -1711,11 +1735,12 @@ __device__ __forceinline__ unsigned long long tagw(unsigned tag, float v) {
     return ((unsigned long long)tag << 32) | (unsigned)__float_as_int(v);
 }
 __device__ __forceinline__ float untag(unsigned long long w) { return __int_as_float((int)(unsigned)w); }
-// tag of helper record ordinal o: the call and the lap of its slot (a slot is
+// tag of record ordinal o in a ring of RING slots: the call and the lap of its slot (a slot is
 // rewritten only after the decider has taken the previous lap, so a word is
 // either of this lap or of the one before)
+template <int RING>
 __device__ __forceinline__ unsigned rec_tag(unsigned epoch, int o) {
-    return epoch * 2u + (unsigned)((o / kTeamRingG) & 1);
+    return epoch * 2u + (unsigned)((o / RING) & 1);
 }
 
 // row_shr:D within 16-lane rows; lanes i < D of a row get `old`
@@ -1779,7 +1804,7 @@ struct TeamGlobal {
     unsigned long long* hstate;  // [kMaxHelpers][HB][kTeamStateW][64]
     unsigned long long* ctl;     // [kTeamCtl]
     __device__ TeamGlobal(const Params& P, int grp) {
-        rec = P.team_ring + (long long)grp * team_words(P.G);
+        rec = P.team_ring + (long long)grp * group_words(P.G);
         hstate = rec + kTeamRingG * kTeamRecW * kTeamRecHeads;
         ctl = P.team_ctl + (long long)grp * kTeamCtl;
     }
@@ -1829,8 +1854,8 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     auto read_lds = [&]() {
 #pragma unroll
         for (int hb = 0; hb < HBM; ++hb) hw[hb] = head_ok(hb) ? lds_ld(&sh->word[hb * 4 + fl.hl]) : (kHdStop | 0);
-        bnd = lds_ld(&sh->bound);
-        rel = lds_ld(&sh->released);
+        bnd = uni(lds_ld(&sh->bound));
+        rel = uni(lds_ld(&sh->released));
     };
     auto load_glb = [&]() {
 #pragma unroll
@@ -1841,8 +1866,8 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     auto take_glb = [&]() {
 #pragma unroll
         for (int hb = 0; hb < HBM; ++hb) hw[hb] = head_ok(hb) ? unstamp(qw[hb], P.epoch, 0) : (kHdStop | 0);
-        bnd = unstamp(qb, P.epoch, nt);
-        rel = unstamp(qr, P.epoch, 0);
+        bnd = uni(unstamp(qb, P.epoch, nt));
+        rel = uni(unstamp(qr, P.epoch, 0));
     };
     auto refresh = [&]() {
         if constexpr (PRIMARY) {
@@ -1868,7 +1893,7 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
         if (__ballot(und) != 0ull) return false;
 #pragma unroll
         for (int hb = 0; hb < HBM; ++hb)
-            if (fate[hb] > 0) sm_merge(ws.m[hb], ws.l[hb], ws.a[hb], q0.m[hb], q0.l[hb], q0.a[hb]);
+            if (fate[hb] > 0) sm_merge_fast(ws.m[hb], ws.l[hb], ws.a[hb], q0.m[hb], q0.l[hb], q0.a[hb]);
         np = 0;
         return true;
     };
@@ -1930,6 +1955,19 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
         if constexpr (PRIMARY) read_lds();
         else take_glb();
         if (t >= bnd) break;  // past the group's stop: no head uses the tile
+        // the next tile's loads first, then the hand-over of this one
+        const int tn = t + plan.W;
+        const bool haveN = tn < nt && tn < bnd;
+        const int cerr = C.err;
+        if (haveN) {
+            S::resolve_from(P, grp, n, tn, blkN, C);
+            if constexpr (!PRIMARY) load_glb();
+            st.template issue<0>(P, C, 0);
+            st.template issue<1>(P, C, 1);
+            blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
+            ++loaded;
+            rows += min(S::T, n - tn * S::T);
+        }
         // the previous tile's decision (by now, as a rule, known)
         retire();
         if (gv) break;
@@ -1940,11 +1978,11 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
             for (;;) {
                 __builtin_amdgcn_s_sleep(PRIMARY ? 1 : 4);
                 if constexpr (PRIMARY) {
-                    rel = lds_ld(&sh->released);
-                    bnd = lds_ld(&sh->bound);
+                    rel = uni(lds_ld(&sh->released));
+                    bnd = uni(lds_ld(&sh->bound));
                 } else {
-                    rel = unstamp(cld(tg.ctl + 0), P.epoch, 0);
-                    bnd = unstamp(cld(tg.ctl + 1), P.epoch, nt);
+                    rel = uni(unstamp(cld(tg.ctl + 0), P.epoch, 0));
+                    bnd = uni(unstamp(cld(tg.ctl + 1), P.epoch, nt));
                 }
                 if (o1 - ring < rel || t >= bnd) break;
                 if (dl.passed()) {
@@ -1963,13 +2001,13 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
                     float* e = sh->rec[s][hb * 4 + fl.hl];
                     *reinterpret_cast<f4*>(e) = f4{o.mf[hb], o.lf[hb], o.a[hb][0], o.a[hb][1]};
                     *reinterpret_cast<f4*>(e + 4) = f4{o.a[hb][2], o.a[hb][3], o.a[hb][4], o.a[hb][5]};
-                    *reinterpret_cast<f4*>(e + 8) = f4{o.a[hb][6], o.a[hb][7], __int_as_float(C.err), 0.f};
+                    *reinterpret_cast<f4*>(e + 8) = f4{o.a[hb][6], o.a[hb][7], __int_as_float(cerr), 0.f};
                 }
             }
             wait_lds();  // the records are written before their tag
             if (lane == 0) lds_st(&sh->tag[s], t + 1);
         } else {
-            const unsigned tag = rec_tag(P.epoch, o1);
+            const unsigned tag = rec_tag<kTeamRingG>(P.epoch, o1);
 #pragma unroll
             for (int hb = 0; hb < HBM; ++hb) {
                 if (fl.cid == 0 && head_ok(hb)) {
@@ -1978,7 +2016,7 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
                     cst(e + 1 * kTeamRecHeads, tagw(tag, o.lf[hb]));
 #pragma unroll
                     for (int j = 0; j < 8; ++j) cst(e + (2 + j) * kTeamRecHeads, tagw(tag, o.a[hb][j]));
-                    cst(e + 10 * kTeamRecHeads, tagw(tag, __int_as_float(C.err)));
+                    cst(e + 10 * kTeamRecHeads, tagw(tag, __int_as_float(cerr)));
                 }
             }
         }
@@ -1992,17 +2030,7 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
         }
         t0 = t;
         np = 1;
-        // the next tile's loads (after the hand-over: the record goes out
-        // early, and the tile's partial is no longer live across the issue)
-        const int tn = t + plan.W;
-        if (tn >= nt || tn >= bnd) break;
-        S::resolve_from(P, grp, n, tn, blkN, C);
-        if constexpr (!PRIMARY) load_glb();
-        st.template issue<0>(P, C, 0);
-        st.template issue<1>(P, C, 1);
-        blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
-        ++loaded;
-        rows += min(S::T, n - tn * S::T);
+        if (!haveN) break;
         t = tn;
         o1 += ostep;
     }
@@ -2014,37 +2042,228 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     if (VSKIP && P.stats && lane == 0) atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 3), skipped);
 }
 
+// The decider's state for a group's heads: the running (max, sum, probe dims)
+// committed after the tiles before the current block, the probe after the
+// last committed tile, the streak, and per head tiles_used (-1 while active)
+// and the error flag; one head per 16-lane row, replicated over the row.
+template <int HBM>
+struct ProbeState {
+    float M[HBM], L[HBM], Pd[HBM][8], X[HBM][8], Xn[HBM];
+    int streak[HBM], U[HBM], err[HBM];
+    bool hv[HBM];
+    __device__ __forceinline__ void init(const FoldLanes& fl, int G) {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            hv[hb] = hb < fl.HB && hb * 4 + fl.hl < G;
+            M[hb] = kNegInf;
+            L[hb] = 0.f;
+            Xn[hb] = 0.f;
+            streak[hb] = 0;
+            err[hb] = 0;
+            U[hb] = hv[hb] ? -1 : 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                Pd[hb][j] = 0.f;
+                X[hb][j] = 0.f;
+            }
+        }
+    }
+    // no head left undecided
+    __device__ __forceinline__ bool finished() const {
+        bool any = false;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) any |= hv[hb] && U[hb] < 0;
+        return __ballot(any) == 0ull;
+    }
+    // the largest tiles_used over the group's heads
+    __device__ __forceinline__ int bound() const {
+        int ug = 0;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (hv[hb]) ug = max(ug, U[hb]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ug = max(ug, __shfl_xor(ug, o));
+        return ug;
+    }
+    // decision word of head block hb (this lane's row): tiles_used once
+    // stopped, else the tiles decided
+    __device__ __forceinline__ int word(int hb, int decided) const {
+        return U[hb] >= 0 ? (kHdStop | U[hb]) : decided;
+    }
+};
+
+// Lane i's probe record: tile f0 + i of the current block (identity until present).
+template <int HBM>
+struct BlockRecs {
+    float m[HBM], l[HBM], p[HBM][8];
+    int e[HBM];
+    __device__ __forceinline__ void clear() {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            m[hb] = kNegInf;
+            l[hb] = 0.f;
+            e[hb] = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[hb][j] = 0.f;
+        }
+    }
+    // from tagged 64-bit words of a record ([word][kTeamRecHeads] apart); false
+    // unless every word carries `tag`
+    __device__ __forceinline__ bool load_tagged(const unsigned long long* rec, const bool (&hv)[HBM], int hl,
+                                                unsigned tag) {
+        unsigned long long w[HBM][kTeamRecW];
+        bool ok = true;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (hv[hb])
+#pragma unroll
+                for (int j = 0; j < kTeamRecW; ++j) w[hb][j] = cld(rec + j * kTeamRecHeads + hb * 4 + hl);
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (hv[hb])
+#pragma unroll
+                for (int j = 0; j < kTeamRecW; ++j) ok &= (unsigned)(w[hb][j] >> 32) == tag;
+        if (ok) {
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                if (hv[hb]) {
+                    m[hb] = untag(w[hb][0]);
+                    l[hb] = untag(w[hb][1]);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) p[hb][j] = untag(w[hb][2 + j]);
+                    e[hb] = (int)(unsigned)w[hb][10];
+                }
+            }
+        }
+        return ok;
+    }
+};
+
+// One pass over block f0 (kmax tiles) whose first kk tiles are present
+// (more than at the previous pass): an inclusive online-softmax scan of the
+// records along each row, merged with the committed state, gives the probe
+// after every tile; both metrics, the streaks and the first stop follow.  A
+// head that stops gets tiles_used; when the block is complete (kk == kmax)
+// the state after its last tile is committed.  Lane i's values depend on
+// tiles f0 .. f0 + i only, so every pass over a block agrees with the others.
+template <int HBM>
+__device__ __forceinline__ void decide_pass(const Params& P, ProbeState<HBM>& D, const BlockRecs<HBM>& R, int f0,
+                                            int kk, int kmax, int nt) {
+    const int lane = lane_id(), i = lane & 15, row0 = lane & ~15;
+    const int t = f0 + i;
+    static_for<0, HBM>([&](auto hbc) {
+        constexpr int hb = decltype(hbc)::value;
+        const bool act = D.hv[hb] && D.U[hb] < 0;
+        if (__ballot(act) == 0ull) return;
+        float m = R.m[hb], l = R.l[hb], p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = R.p[hb][j];
+        auto step = [&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            float om = row_shr<d>(kNegInf, m), ol = row_shr<d>(0.f, l), op[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) op[j] = row_shr<d>(0.f, p[j]);
+            sm_merge_fast(om, ol, op, m, l, p);  // the earlier tiles first
+            m = om;
+            l = ol;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = op[j];
+        };
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 4>{});
+        step(std::integral_constant<int, 8>{});
+        // the running state after tile t: committed (+) scan
+        float sM = D.M[hb], sL = D.L[hb], sP[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sP[j] = D.Pd[hb][j];
+        sm_merge_fast(sM, sL, sP, m, l, p);
+        // probe: dims 0..7 of the normalised running output; the hardware
+        // reciprocal and square root (about 1 ulp)
+        const float invL = __builtin_amdgcn_rcpf(sL);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = sP[j] * invL;
+        const float xn = __builtin_amdgcn_sqrtf(sumsq8(x));
+        // the previous probe: lane i - 1's, the committed one for lane 0
+        const float ppn = row_shr<1>(D.Xn[hb], xn);
+        float pp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pp[j] = row_shr<1>(D.X[hb][j], x[j]);
+        bool pass = false;
+        if (t >= 1) {
+            float ds, dd;
+            if (xn == 0.f || ppn == 0.f) {
+                ds = dd = INFINITY;
+            } else {
+                const float ix = __builtin_amdgcn_rcpf(xn), ip = __builtin_amdgcn_rcpf(ppn);
+                ds = fabsf(xn - ppn) * ip;
+                // 1 - cos as half the squared distance of the unit vectors
+                float dl2[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dl2[j] = fmaf(x[j], ix, -(pp[j] * ip));
+                dd = 0.5f * sumsq8(dl2);
+            }
+            pass = ds < P.eps_scale && dd < P.eps_dir;
+        }
+        const unsigned pbits = (unsigned)(__ballot(pass) >> row0) & 0xffffu;
+        const unsigned ebits = (unsigned)(__ballot(R.e[hb] != 0) >> row0) & 0xffffu;
+        // the streak from the block start (the same at every pass) to the first stop
+        int sk;
+        const int istop = first_stop(pbits, kk, D.streak[hb], P.patience, sk);
+        if (act) {
+            if (istop >= 0) {
+                D.U[hb] = f0 + istop + 1;
+                D.err[hb] |= (ebits & ((2u << istop) - 1u)) != 0u;
+            } else if (kk == kmax) {
+                // the block is complete: commit its last tile's state
+                const int src = row0 | (kmax - 1);
+                D.err[hb] |= (ebits & ((2u << (kmax - 1)) - 1u)) != 0u;
+                D.streak[hb] = sk;
+                D.M[hb] = __shfl(sM, src);
+                D.L[hb] = __shfl(sL, src);
+                D.Xn[hb] = __shfl(xn, src);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    D.Pd[hb][j] = __shfl(sP[j], src);
+                    D.X[hb][j] = __shfl(x[j], src);
+                }
+                if (f0 + kmax >= nt) D.U[hb] = nt;  // no stop: every tile is used
+            }
+        }
+    });
+}
+
+// The present prefix of the block: tiles whose records every head's row holds.
+__device__ __forceinline__ int present_prefix(bool have, int kmax) {
+    const unsigned long long b = __ballot(have);
+    const unsigned mask = (unsigned)(b & (b >> 16) & (b >> 32) & (b >> 48)) & 0xffffu;
+    return min(__builtin_ctz(~mask), kmax);
+}
+
 // Decides the group's tiles, block after block; at the end leaves each
 // head's tiles_used (or -2) in its decision word and its error flag in LDS.
 template <int HBM, int GMAX>
 __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const TeamPlan& plan,
                                              TeamShared<GMAX>* sh) {
-    const int lane = lane_id(), i = lane & 15, row0 = lane & ~15;
+    const int lane = lane_id(), i = lane & 15;
     const FoldLanes fl(P);
-    const int G = P.G;
     const TeamGlobal tg(P, grp);
     const bool glb = plan.nH > 0;
-    // committed state: after the tiles before the current block (replicated over the row)
-    float cM[HBM], cL[HBM], cP[HBM][8], cX[HBM][8], cXn[HBM];
-    int streak[HBM], U[HBM], err[HBM];
-    bool hv[HBM];
-#pragma unroll
-    for (int hb = 0; hb < HBM; ++hb) {
-        hv[hb] = hb < fl.HB && hb * 4 + fl.hl < G;
-        cM[hb] = kNegInf;
-        cL[hb] = 0.f;
-        cXn[hb] = 0.f;
-        streak[hb] = 0;
-        err[hb] = 0;
-        U[hb] = hv[hb] ? -1 : 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            cP[hb][j] = 0.f;
-            cX[hb][j] = 0.f;
-        }
-    }
+    ProbeState<HBM> D;
+    D.init(fl, P.G);
     int relA = 0, relH = 0;
     bool finished = false, gave_up = false;
+    auto publish = [&](int decided) {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            if (i == 0 && D.hv[hb]) {
+                const int h = hb * 4 + fl.hl, wd = D.word(hb, decided);
+                lds_st(&sh->word[h], wd);
+                if (glb) cst(tg.ctl + 4 + h, stamp(P.epoch, (unsigned)wd));
+            }
+        }
+    };
     for (int f0 = 0; f0 < nt && !finished && !gave_up; f0 += kBlock) {
         const int kmax = min(kBlock, nt - f0);
         const int t = f0 + i;
@@ -2053,18 +2272,9 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
         const bool prim = kp < plan.nA;
         const int ord = prim ? per * plan.nA + kp : per * plan.nH + (kp - plan.nA);
         const int sA = ord & (kProbeRing - 1), sH = ord & (kTeamRingG - 1);
-        const unsigned rtag = rec_tag(P.epoch, ord);
-        // lane i's record of tile t (identity until it is there)
-        float rm[HBM], rl[HBM], rp[HBM][8];
-        int re[HBM];
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            rm[hb] = kNegInf;
-            rl[hb] = 0.f;
-            re[hb] = 0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) rp[hb][j] = 0.f;
-        }
+        const unsigned rtag = rec_tag<kTeamRingG>(P.epoch, ord);
+        BlockRecs<HBM> R;
+        R.clear();
         bool have = !inr;
         int kdone = 0;
         unsigned long long since = wall_clock64();
@@ -2077,163 +2287,32 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                         __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
                         for (int hb = 0; hb < HBM; ++hb) {
-                            if (hv[hb]) {
+                            if (D.hv[hb]) {
                                 const float* e = sh->rec[sA][hb * 4 + fl.hl];
                                 const f4 x0 = *reinterpret_cast<const f4*>(e);
                                 const f4 x1 = *reinterpret_cast<const f4*>(e + 4);
                                 const f4 x2 = *reinterpret_cast<const f4*>(e + 8);
-                                rm[hb] = x0.x; rl[hb] = x0.y; rp[hb][0] = x0.z; rp[hb][1] = x0.w;
-                                rp[hb][2] = x1.x; rp[hb][3] = x1.y; rp[hb][4] = x1.z; rp[hb][5] = x1.w;
-                                rp[hb][6] = x2.x; rp[hb][7] = x2.y; re[hb] = __float_as_int(x2.z);
+                                R.m[hb] = x0.x; R.l[hb] = x0.y; R.p[hb][0] = x0.z; R.p[hb][1] = x0.w;
+                                R.p[hb][2] = x1.x; R.p[hb][3] = x1.y; R.p[hb][4] = x1.z; R.p[hb][5] = x1.w;
+                                R.p[hb][6] = x2.x; R.p[hb][7] = x2.y; R.e[hb] = __float_as_int(x2.z);
                             }
                         }
                         __atomic_signal_fence(__ATOMIC_SEQ_CST);
                         have = true;
                     }
                 } else {
-                    bool ok = true;
-                    unsigned long long w[HBM][kTeamRecW];
-#pragma unroll
-                    for (int hb = 0; hb < HBM; ++hb) {
-                        if (hv[hb]) {
-                            const unsigned long long* e =
-                                tg.rec + (long long)sH * kTeamRecW * kTeamRecHeads + hb * 4 + fl.hl;
-#pragma unroll
-                            for (int j = 0; j < kTeamRecW; ++j) w[hb][j] = cld(e + j * kTeamRecHeads);
-                        }
-                    }
-#pragma unroll
-                    for (int hb = 0; hb < HBM; ++hb) {
-                        if (hv[hb]) {
-#pragma unroll
-                            for (int j = 0; j < kTeamRecW; ++j) ok &= (unsigned)(w[hb][j] >> 32) == rtag;
-                        }
-                    }
-                    if (ok) {
-#pragma unroll
-                        for (int hb = 0; hb < HBM; ++hb) {
-                            if (hv[hb]) {
-                                rm[hb] = untag(w[hb][0]);
-                                rl[hb] = untag(w[hb][1]);
-#pragma unroll
-                                for (int j = 0; j < 8; ++j) rp[hb][j] = untag(w[hb][2 + j]);
-                                re[hb] = (int)(unsigned)w[hb][10];
-                            }
-                        }
-                        have = true;
-                    }
+                    have = R.load_tagged(tg.rec + (long long)sH * kTeamRecW * kTeamRecHeads, D.hv, fl.hl, rtag);
                 }
             }
-            // the tiles present for every head, from the block start
-            const unsigned long long hbits = __ballot(have);
-            const unsigned mask = (unsigned)(hbits & (hbits >> 16) & (hbits >> 32) & (hbits >> 48)) & 0xffffu;
-            const int kk = min(__builtin_ctz(~mask), kmax);
+            const int kk = present_prefix(have, kmax);
             if (kk > kdone) {
                 since = wall_clock64();
-                bool any = false;
-                static_for<0, HBM>([&](auto hbc) {
-                    constexpr int hb = decltype(hbc)::value;
-                    const bool act = hv[hb] && U[hb] < 0;
-                    if (__ballot(act) == 0ull) return;
-                    // inclusive scan of the block's records along the row
-                    float m = rm[hb], l = rl[hb], p[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) p[j] = rp[hb][j];
-                    auto step = [&](auto dc) {
-                        constexpr int d = decltype(dc)::value;
-                        float om = row_shr<d>(kNegInf, m), ol = row_shr<d>(0.f, l), op[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) op[j] = row_shr<d>(0.f, p[j]);
-                        sm_merge_fast(om, ol, op, m, l, p);  // the earlier tiles first
-                        m = om;
-                        l = ol;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) p[j] = op[j];
-                    };
-                    step(std::integral_constant<int, 1>{});
-                    step(std::integral_constant<int, 2>{});
-                    step(std::integral_constant<int, 4>{});
-                    step(std::integral_constant<int, 8>{});
-                    // the running state after tile t: committed (+) scan
-                    float sM = cM[hb], sL = cL[hb], sP[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) sP[j] = cP[hb][j];
-                    sm_merge_fast(sM, sL, sP, m, l, p);
-                    // probe: dims 0..7 of the normalised running output; the
-                    // hardware reciprocal and square root (about 1 ulp)
-                    const float invL = __builtin_amdgcn_rcpf(sL);
-                    float x[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) x[j] = sP[j] * invL;
-                    const float xn = __builtin_amdgcn_sqrtf(sumsq8(x));
-                    // the previous probe: lane i - 1's, the committed one for lane 0
-                    const float ppn = row_shr<1>(cXn[hb], xn);
-                    float pp[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) pp[j] = row_shr<1>(cX[hb][j], x[j]);
-                    bool pass = false;
-                    if (t >= 1) {
-                        float ds, dd;
-                        if (xn == 0.f || ppn == 0.f) {
-                            ds = dd = INFINITY;
-                        } else {
-                            const float ix = __builtin_amdgcn_rcpf(xn), ip = __builtin_amdgcn_rcpf(ppn);
-                            ds = fabsf(xn - ppn) * ip;
-                            // 1 - cos as half the squared distance of the unit vectors
-                            float dl2[8];
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) dl2[j] = fmaf(x[j], ix, -(pp[j] * ip));
-                            dd = 0.5f * sumsq8(dl2);
-                        }
-                        pass = ds < P.eps_scale && dd < P.eps_dir;
-                    }
-                    const unsigned pbits = (unsigned)(__ballot(pass) >> row0) & 0xffffu;
-                    const unsigned ebits = (unsigned)(__ballot(re[hb] != 0) >> row0) & 0xffffu;
-                    // the streak from the block start (the same at every pass) to the first stop
-                    int sk;
-                    const int istop = first_stop(pbits, kk, streak[hb], P.patience, sk);
-                    if (act) {
-                        if (istop >= 0) {
-                            U[hb] = f0 + istop + 1;
-                            err[hb] |= (ebits & ((2u << istop) - 1u)) != 0u;
-                        } else if (kk == kmax) {
-                            // the block is complete: commit its last tile's state
-                            const int src = row0 | (kmax - 1);
-                            err[hb] |= (ebits & ((2u << (kmax - 1)) - 1u)) != 0u;
-                            streak[hb] = sk;
-                            cM[hb] = __shfl(sM, src);
-                            cL[hb] = __shfl(sL, src);
-                            cXn[hb] = __shfl(xn, src);
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) {
-                                cP[hb][j] = __shfl(sP[j], src);
-                                cX[hb][j] = __shfl(x[j], src);
-                            }
-                            if (f0 + kmax >= nt) U[hb] = nt;  // no stop: every tile is used
-                        }
-                    }
-                });
+                decide_pass<HBM>(P, D, R, f0, kk, kmax, nt);
                 kdone = kk;
-                // publish each head's decision word, then the bound once every head is done
-                int ug = 0;
-#pragma unroll
-                for (int hb = 0; hb < HBM; ++hb) {
-                    any |= hv[hb] && U[hb] < 0;
-                    if (hv[hb]) ug = max(ug, U[hb]);
-                }
-                finished = __ballot(any) == 0ull;
-#pragma unroll
-                for (int hb = 0; hb < HBM; ++hb) {
-                    if (i == 0 && hv[hb]) {
-                        const int h = hb * 4 + fl.hl;
-                        const int wd = U[hb] >= 0 ? (kHdStop | U[hb]) : (f0 + kdone);
-                        lds_st(&sh->word[h], wd);
-                        if (glb) cst(tg.ctl + 4 + h, stamp(P.epoch, (unsigned)wd));
-                    }
-                }
+                finished = D.finished();
+                publish(f0 + kdone);
                 if (finished) {
-#pragma unroll
-                    for (int o = 32; o > 0; o >>= 1) ug = max(ug, __shfl_xor(ug, o));
+                    const int ug = D.bound();
                     if (lane == 0) {
                         lds_st(&sh->bound, ug);
                         if (glb) cst(tg.ctl + 1, stamp(P.epoch, (unsigned)ug));
@@ -2261,7 +2340,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
     if (gave_up) {
 #pragma unroll
         for (int hb = 0; hb < HBM; ++hb) {
-            if (i == 0 && hv[hb] && U[hb] < 0) {
+            if (i == 0 && D.hv[hb] && D.U[hb] < 0) {
                 const int h = hb * 4 + fl.hl;
                 lds_st(&sh->word[h], kHdGaveUp);
                 if (glb) cst(tg.ctl + 4 + h, stamp(P.epoch, (unsigned)kHdGaveUp));
@@ -2274,7 +2353,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
     }
 #pragma unroll
     for (int hb = 0; hb < HBM; ++hb)
-        if (i == 0 && hv[hb]) lds_st(&sh->err[hb * 4 + fl.hl], err[hb]);
+        if (i == 0 && D.hv[hb]) lds_st(&sh->err[hb * 4 + fl.hl], D.err[hb]);
 }
 
 // running states of waves w0 .. w1-1, each in its area of the LDS, merged in wave order
@@ -2350,7 +2429,7 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
         if (wv == 0) {
             Part<HBM> hs;
             merge_areas<HBM>(lds, wave_floats, 0, TEAM, hs);
-            const unsigned tag = rec_tag(P.epoch, 0);
+            const unsigned tag = rec_tag<kTeamRingG>(P.epoch, 0);
             unsigned long long* dst = tg.hstate + (long long)(team - 1) * HBM * kTeamStateW * 64 + lane;
 #pragma unroll
             for (int hb = 0; hb < HBM; ++hb) {
@@ -2396,7 +2475,7 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     Part<HBM> tot;
     merge_areas<HBM>(lds, wave_floats, 0, TEAM - 1, tot);
     bool lost = false;  // a helper's state did not arrive within kWaitTicks
-    const unsigned htag = rec_tag(P.epoch, 0);
+    const unsigned htag = rec_tag<kTeamRingG>(P.epoch, 0);
     for (int r = 0; r < P.helpers; ++r) {
         const unsigned long long* src = tg.hstate + (long long)r * HBM * kTeamStateW * 64 + lane;
         unsigned long long w[HBM][kTeamStateW];
@@ -2448,6 +2527,505 @@ size_t team_lds_bytes(const Params& p) {
         (size_t)(S::TEAM - 1) * S::lds_floats(p) * sizeof(float) + sizeof(TeamShared<S::HEADS>);
     const size_t helper = (size_t)S::TEAM * S::lds_floats(p) * sizeof(float);
     return primary > helper ? primary : helper;
+}
+
+// ------------------------------------------------------------------ pool kernel (workers shared by the groups)
+constexpr int kPoolAutoGroups = 64;  // library default: the pool for at most this many groups ...
+constexpr int kPoolAutoTiles = 1024; // ... of at least this many tiles
+//
+// Every CU runs one persistent work-group.  Wave 0 of work-group g < NG
+// decides group g; every other wave is a tile worker that serves whichever
+// group needs it.  A worker joins a group (it takes a running-state slot,
+// so at most pool_cap workers serve a group), claims the group's tiles one at
+// a time from a counter in global memory (a few tiles ahead, so that the
+// claim and the block-id lookup of a tile are done before its loads are
+// issued), and for each tile publishes a probe record as tagged 64-bit words
+// (the same records as the team kernel's helpers, in a ring indexed by tile).
+// It merges each of its tiles into its running state once the decider has
+// decided the tile, and when the group has no tile left to claim (or has
+// stopped) it leaves its running state in its slot and moves to the group
+// that has the fewest workers among those with tiles left, so the CUs of
+// groups that stop early speed up those that run long.  The decider scans
+// the records in aligned blocks like the team kernel's, publishes per-head
+// decisions and the bound, and at the end merges the workers' states in slot
+// order and writes the output.  Every shared word carries the call's epoch:
+// the decider resets each counter to (epoch, 0), and a worker adds to a
+// counter only once it has seen it so (the order of stores to different words
+// is not relied on).
+__device__ __forceinline__ unsigned state_tag(unsigned epoch) { return epoch * 2u; }
+
+// one atomic add for the whole wave (lane 0's), its old value in every lane
+__device__ __forceinline__ unsigned long long faa64(unsigned long long* p, unsigned long long v) {
+    unsigned long long r = 0;
+    if (lane_id() == 0) r = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return uni64(r);
+}
+// the same without waiting for it: the low word of the old value in lane 0
+// only (read it with uni() once the wave's loads issued before it have landed)
+__device__ __forceinline__ int faa64_async(unsigned long long* p, unsigned long long v) {
+    int r = 0;
+    if (lane_id() == 0) r = (int)(unsigned)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return r;
+}
+// an atomic add whose old value is not needed
+__device__ __forceinline__ void add64(unsigned long long* p, unsigned long long v) {
+    if (lane_id() == 0) __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A group's words in global memory (pool kernel).
+struct PoolGlobal {
+    unsigned long long* rec;     // [kPoolRing][kTeamRecW][kTeamRecHeads]
+    unsigned long long* state;   // [kPoolContrib][HB][kTeamStateW][64]
+    unsigned long long* ctl;     // [kPoolCtl]
+    __device__ PoolGlobal(const Params& P, int grp) {
+        rec = P.team_ring + (long long)grp * group_words(P.G);
+        state = rec + kPoolRing * kTeamRecW * kTeamRecHeads;
+        ctl = P.team_ctl + (long long)grp * kTeamCtl;
+    }
+};
+
+// tiles of group grp (0 for an empty or invalid row)
+__device__ __forceinline__ int group_tiles(const Params& P, int grp, int T) {
+    const int n = P.ctx_lens[grp / P.Hkv];
+    return (n <= 0 || n > P.cap) ? 0 : (n + T - 1) / T;
+}
+
+template <int HBM>
+__device__ __forceinline__ void pool_decider(const Params& P, int grp, int T) {
+    const int lane = lane_id(), i = lane & 15;
+    const FoldLanes fl(P);
+    const int G = P.G;
+    const unsigned e = P.epoch;
+    const PoolGlobal pg(P, grp);
+    const int b = grp / P.Hkv, g = grp % P.Hkv;
+    const int n = P.ctx_lens[b];
+    const bool bad = n < 0 || n > P.cap;
+    const int nt = (bad || n == 0) ? 0 : (n + T - 1) / T;
+    // reset the counters (the claim counter last: workers join once they see it reset)
+    if (lane == 0) {
+        cst(pg.ctl + 0, stamp(e, 0u));
+        cst(pg.ctl + 1, stamp(e, (unsigned)nt));
+        cst(pg.ctl + 3, stamp(e, 0u));
+        cst(pg.ctl + 12, stamp(e, 0u));
+        cst(pg.ctl + 2, stamp(e, 0u));
+    }
+    if (nt == 0) {
+        // empty row: zero output, no tiles; invalid length: NaN, -1
+        const long long row0 = (long long)b * P.Hq + (long long)g * G;
+        for (int k = lane; k < G * P.D; k += 64) P.out[row0 * P.D + k] = bad ? NAN : 0.f;
+        for (int h = lane; h < G; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
+        return;
+    }
+    ProbeState<HBM> D;
+    D.init(fl, G);
+    bool finished = false, gave_up = false;
+    auto publish = [&](int decided) {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (i == 0 && D.hv[hb]) cst(pg.ctl + 4 + hb * 4 + fl.hl, stamp(e, (unsigned)D.word(hb, decided)));
+    };
+    for (int f0 = 0; f0 < nt && !finished && !gave_up; f0 += kBlock) {
+        const int kmax = min(kBlock, nt - f0);
+        const int t = f0 + i;
+        const unsigned tag = rec_tag<kPoolRing>(e, t);
+        const unsigned long long* rec = pg.rec + (long long)(t & (kPoolRing - 1)) * kTeamRecW * kTeamRecHeads;
+        BlockRecs<HBM> R;
+        R.clear();
+        bool have = i >= kmax;
+        int kdone = 0;
+        unsigned long long since = wall_clock64();
+        for (;;) {
+            if (!have) have = R.load_tagged(rec, D.hv, fl.hl, tag);
+            const int kk = present_prefix(have, kmax);
+            if (kk > kdone) {
+                since = wall_clock64();
+                decide_pass<HBM>(P, D, R, f0, kk, kmax, nt);
+                kdone = kk;
+                finished = D.finished();
+                publish(f0 + kdone);
+                if (finished) {
+                    const int ug = D.bound();
+                    if (lane == 0) cst(pg.ctl + 1, stamp(e, (unsigned)ug));
+                    break;
+                }
+            }
+            if (kdone == kmax) break;
+            if (wall_clock64() - since > kWaitTicks) {
+                gave_up = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (finished || gave_up) break;
+        if (lane == 0) cst(pg.ctl + 0, stamp(e, (unsigned)(f0 + kmax)));  // the block's slots may be reused
+    }
+    if (gave_up) {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (i == 0 && D.hv[hb] && D.U[hb] < 0) cst(pg.ctl + 4 + hb * 4 + fl.hl, stamp(e, (unsigned)kHdGaveUp));
+        if (lane == 0) cst(pg.ctl + 1, stamp(e, 0u));
+    }
+    // the workers' running states, in slot order.  Every worker that claimed a
+    // tile joined before it claimed, so the count read now covers them all; a
+    // later one finds no tile and its slot is not read.
+    const int J = min(unstamp(uni64(cld(pg.ctl + 3)), e, 0), P.pool_cap);
+    const unsigned stg = state_tag(e);
+    Part<HBM> tot;
+    tot.clear();
+    bool lost = false;
+    constexpr int kB = 4 / HBM;  // states loaded at once
+    for (int c0 = 0; c0 < J && !lost; c0 += kB) {
+        unsigned long long w[kB][HBM][kTeamStateW];
+        const Deadline dl;
+        for (;;) {
+            bool ok = true;
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                if (c0 + k < J) {
+                    const unsigned long long* src = pg.state + (long long)(c0 + k) * HBM * kTeamStateW * 64 + lane;
+#pragma unroll
+                    for (int hb = 0; hb < HBM; ++hb)
+#pragma unroll
+                        for (int j = 0; j < kTeamStateW; ++j) {
+                            w[k][hb][j] = cld(src + (hb * kTeamStateW + j) * 64);
+                            ok &= (unsigned)(w[k][hb][j] >> 32) == stg;
+                        }
+                }
+            }
+            if (__ballot(!ok) == 0ull) break;
+            if (dl.passed()) {
+                lost = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+        }
+        if (lost) break;
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+            if (c0 + k < J) {
+#pragma unroll
+                for (int hb = 0; hb < HBM; ++hb) {
+                    float a2[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) a2[j] = untag(w[k][hb][2 + j]);
+                    sm_merge(tot.m[hb], tot.l[hb], tot.a[hb], untag(w[k][hb][0]), untag(w[k][hb][1]), a2);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        if (!D.hv[hb]) continue;
+        if (lost || D.U[hb] < 0) {
+            float nan8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) nan8[j] = NAN;
+            write_head_out(P, grp, h, fl, nan8, 1.f, 0, -2);
+        } else {
+            write_head_out(P, grp, h, fl, tot.a[hb], tot.l[hb], D.err[hb], D.U[hb]);
+        }
+    }
+}
+
+// The group a worker moves to after `cur`: among those with tiles left to
+// claim and room for a worker, the one with the fewest workers (ties: the
+// nearest after cur, so that workers spread); -1 if none is left.
+__device__ __forceinline__ int pool_pick(const Params& P, int cur, int T) {
+    const int lane = lane_id();
+    const unsigned e = P.epoch;
+    unsigned long long best = ~0ull;
+    for (int g0 = 0; g0 < P.NG; g0 += 64) {
+        const int g = g0 + lane;
+        if (g < P.NG) {
+            const unsigned long long* ctl = P.team_ctl + (long long)g * kTeamCtl;
+            const unsigned long long cw = cld(ctl + 2), bw = cld(ctl + 1), jw = cld(ctl + 3), aw = cld(ctl + 12);
+            const int nt = group_tiles(P, g, T);
+            bool cand;
+            int act = 0;
+            if ((unsigned)(cw >> 32) != e) {
+                cand = nt > 0;  // not open yet
+            } else {
+                const int lim = min(nt, unstamp(bw, e, nt));
+                cand = (int)(unsigned)cw < lim && unstamp(jw, e, 0) < P.pool_cap;
+                act = unstamp(aw, e, 0);
+            }
+            const unsigned dist = (unsigned)((g - cur - 1 + P.NG) % P.NG);
+            const unsigned long long key = ((unsigned long long)act << 32) | dist;
+            if (cand && key < best) best = key;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long other = __shfl_xor(best, o);
+        best = other < best ? other : best;
+    }
+    if (best == ~0ull) return -1;
+    return (int)(((unsigned)best + cur + 1) % (unsigned)P.NG);
+}
+
+// A running state kept in LDS ([head block][m, l, 8 dims][lane]), so that it
+// does not hold registers across the tile loop.
+template <int HBM>
+struct LdsPart {
+    float* base;
+    __device__ __forceinline__ float& at(int hb, int j) const { return base[(hb * kTeamStateW + j) * 64 + lane_id()]; }
+    __device__ __forceinline__ void clear() const {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            at(hb, 0) = kNegInf;
+#pragma unroll
+            for (int j = 1; j < kTeamStateW; ++j) at(hb, j) = 0.f;
+        }
+    }
+    // state (+) q for head block hb
+    __device__ __forceinline__ void merge(int hb, float qm, float ql, const float (&qa)[8]) const {
+        float m = at(hb, 0), l = at(hb, 1), a[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = at(hb, 2 + j);
+        sm_merge_fast(m, l, a, qm, ql, qa);
+        at(hb, 0) = m;
+        at(hb, 1) = l;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) at(hb, 2 + j) = a[j];
+    }
+};
+
+// One worker: joins groups and processes their tiles until none is left;
+// its running state lives in `wsl` (HBM * kTeamStateW * 64 floats of LDS),
+// the next tile's block ids in `blk` (S::PAGES ints of LDS).
+template <class S>
+__device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, float* wsl, int* blk) {
+    constexpr int HBM = S::HBM, T = S::T;
+    const int lane = lane_id();
+    const FoldLanes fl(P);
+    const unsigned e = P.epoch;
+    unsigned long long loaded = 0, rows = 0;
+    auto head_ok = [&](int hb) { return hb < fl.HB && hb * 4 + fl.hl < P.G; };
+    int grp = widx % P.NG;
+    for (int round = 0;; ++round) {
+        if (round > 0) {
+            grp = uni(pool_pick(P, grp, T));
+            if (grp < 0) break;
+        }
+        const PoolGlobal pg(P, grp);
+        const int n = P.ctx_lens[grp / P.Hkv];
+        const int nt = group_tiles(P, grp, T);
+        if (nt == 0) continue;
+        // join: once the group's counters are reset, take a state slot
+        unsigned long long cw, jw, aw, bw;
+        {
+            const Deadline dl;
+            for (;;) {
+                cw = uni64(cld(pg.ctl + 2));
+                jw = uni64(cld(pg.ctl + 3));
+                aw = uni64(cld(pg.ctl + 12));
+                bw = uni64(cld(pg.ctl + 1));
+                if ((unsigned)(cw >> 32) == e && (unsigned)(jw >> 32) == e && (unsigned)(aw >> 32) == e) break;
+                if (dl.passed()) break;
+                __builtin_amdgcn_s_sleep(8);
+            }
+        }
+        if ((unsigned)(cw >> 32) != e || (unsigned)(jw >> 32) != e || (unsigned)(aw >> 32) != e)
+            break;  // the group's decider never opened it: give up (the decider reports its heads)
+        const int lim0 = min(nt, unstamp(bw, e, nt));
+        if ((int)(unsigned)cw >= lim0) continue;  // nothing left to claim
+        const int slot = (int)(unsigned)faa64(pg.ctl + 3, 1ull);
+        if (slot >= P.pool_cap) continue;  // the group has as many workers as it may have
+        add64(pg.ctl + 12, 1ull);
+        // the decisions as last seen, loaded before a tile's loads and taken
+        // once those have landed; the released tiles are read when needed
+        int hw[HBM];
+        int bnd = nt, rel = 0;
+        unsigned long long qw[HBM], qb = 0;
+        auto load_glb = [&]() {
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) qw[hb] = cld(pg.ctl + 4 + min(hb * 4 + fl.hl, kTeamRecHeads - 1));
+            qb = cld(pg.ctl + 1);
+        };
+        auto take_glb = [&]() {
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) hw[hb] = head_ok(hb) ? unstamp(qw[hb], e, 0) : (kHdStop | 0);
+            bnd = uni(unstamp(qb, e, nt));
+        };
+        const LdsPart<HBM> ws{wsl};
+        // the tiles awaiting their decision, oldest first (two: a decision
+        // takes about a tile's time to come back through global memory)
+        Part<HBM> q0, q1;
+        int t0 = 0, t1 = 0, np = 0;
+        ws.clear();
+        bool gv = false;
+        // merges (or drops) the oldest pending tile once every head has decided it
+        auto try_front = [&]() -> bool {
+            int fate[HBM];
+            bool und = false;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                fate[hb] = tile_fate(hw[hb], t0);
+                und |= fate[hb] < 0;
+            }
+            if (__ballot(und) != 0ull) return false;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb)
+                if (fate[hb] > 0) ws.merge(hb, q0.m[hb], q0.l[hb], q0.a[hb]);
+            q0 = q1;
+            t0 = t1;
+            --np;
+            return true;
+        };
+        // merges what is decided; then waits until at most `keep` tiles are pending
+        auto retire = [&](int keep) {
+            while (np > 0 && try_front()) {
+            }
+            if (np <= keep) return;
+            const Deadline dl;
+            for (;;) {
+                __builtin_amdgcn_s_sleep(4);
+                load_glb();
+                take_glb();
+                while (np > 0 && try_front()) {
+                }
+                if (np <= keep) return;
+                if (dl.passed()) {
+                    gv = true;
+                    np = 0;
+                    return;
+                }
+            }
+        };
+        auto claim = [&]() { return (int)(unsigned)faa64(pg.ctl + 2, 1ull); };
+        auto claim_async = [&]() { return faa64_async(pg.ctl + 2, 1ull); };
+        // the first tile: claim it and look up its blocks now
+        load_glb();
+        st.load_q(P, grp);
+        int t = claim();
+        if (t >= lim0) t = nt;  // nothing needed left
+        typename S::TileRef C;
+        if (t < nt) {
+            const int blk = S::fetch_blocks(P, grp, n, t);
+            S::resolve_from(P, grp, n, t, blk, C);
+            st.template issue<0>(P, C, 0);
+            st.template issue<1>(P, C, 1);
+            ++loaded;
+            rows += min(T, n - t * T);
+        }
+        // the next one claimed, its blocks in flight; the one after, claimed in flight
+        int tN = t < nt ? claim() : nt;
+        if (tN < nt) S::fetch_blocks_lds(P, grp, n, tN, blk);
+        int tXr = tN < nt ? claim_async() : nt;  // (lane 0)
+        while (t < nt) {
+            st.template consume<0>(P, C, 0, true);
+            st.template consume<1>(P, C, 1, false);
+            typename S::Out o;
+            st.flush(P, o);
+            take_glb();
+            const int tX = uni(tXr);  // landed with the tile
+            if (t >= bnd) break;  // past the group's stop: no head uses the tile
+            retire(0);  // the previous tile first (two pending partials would not fit in registers)
+            if (gv) break;
+            // the record's slot must have been released (none is, once the
+            // group is done: then the tile is past the bound)
+            if (t - kPoolRing >= rel) {
+                const Deadline dl;
+                for (;;) {
+                    rel = uni(unstamp(cld(pg.ctl + 0), e, 0));
+                    bnd = uni(unstamp(cld(pg.ctl + 1), e, nt));
+                    if (t - kPoolRing < rel || t >= bnd) break;
+                    if (dl.passed()) {
+                        gv = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(4);
+                }
+                if (gv || t >= bnd) break;
+            }
+            {
+                const unsigned tag = rec_tag<kPoolRing>(e, t);
+                unsigned long long* rb = pg.rec + (long long)(t & (kPoolRing - 1)) * kTeamRecW * kTeamRecHeads;
+#pragma unroll
+                for (int hb = 0; hb < HBM; ++hb) {
+                    if (fl.cid == 0 && head_ok(hb)) {
+                        unsigned long long* r = rb + hb * 4 + fl.hl;
+                        cst(r + 0 * kTeamRecHeads, tagw(tag, o.mf[hb]));
+                        cst(r + 1 * kTeamRecHeads, tagw(tag, o.lf[hb]));
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) cst(r + (2 + j) * kTeamRecHeads, tagw(tag, o.a[hb][j]));
+                        cst(r + 10 * kTeamRecHeads, tagw(tag, __int_as_float(C.err)));
+                    }
+                }
+            }
+            {
+                Part<HBM> qn;
+#pragma unroll
+                for (int hb = 0; hb < HBM; ++hb) {
+                    qn.m[hb] = o.mf[hb];
+                    qn.l[hb] = o.lf[hb];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) qn.a[hb][j] = o.a[hb][j];
+                }
+                if (np == 0) {
+                    q0 = qn;
+                    t0 = t;
+                } else {
+                    q1 = qn;
+                    t1 = t;
+                }
+                ++np;
+            }
+            // the next tile's loads
+            if (tN >= min(nt, bnd)) break;  // (tX > tN: none of this worker's claims is needed)
+            S::resolve_lds(P, grp, n, tN, blk, C);  // (the ids landed with the last tile's loads)
+            load_glb();
+            st.template issue<0>(P, C, 0);
+            st.template issue<1>(P, C, 1);
+            ++loaded;
+            rows += min(T, n - tN * T);
+            t = tN;
+            tN = tX;
+            if (tN < nt) S::fetch_blocks_lds(P, grp, n, tN, blk);
+            tXr = tN < nt ? claim_async() : nt;
+        }
+        if (!gv) retire(0);
+        __builtin_amdgcn_s_waitcnt(0);  // loads of a dropped tile may still be landing (in LDS too)
+        // leave the running state in the slot, then leave the group
+        const unsigned stg = state_tag(e);
+        unsigned long long* dst = pg.state + (long long)slot * HBM * kTeamStateW * 64 + lane;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            unsigned long long* w = dst + hb * kTeamStateW * 64;
+#pragma unroll
+            for (int j = 0; j < kTeamStateW; ++j) cst(w + 64 * j, tagw(stg, ws.at(hb, j)));
+        }
+        add64(pg.ctl + 12, ~0ull);  // one worker less
+        if (gv) break;
+    }
+    count_stats(P, loaded, rows);
+}
+
+// Grid: one work-group per CU, all resident (cooperative launch).
+template <class S>
+__global__ __launch_bounds__(S::TEAM * 64) void art_pool_kernel(Params P) {
+    extern __shared__ float lds[];
+    constexpr int TEAM = S::TEAM;
+    const int wv = wave_id(), wg = blockIdx.x;
+    if (wg < P.NG && wv == 0) {
+        // the decider's chain is latency-bound: let its SIMD issue it first
+        __builtin_amdgcn_s_setprio(3);
+        pool_decider<S::HBM>(P, wg, S::T);
+        return;
+    }
+    // workers numbered so that consecutive ones start on consecutive groups
+    const int widx = wg < P.NG ? wg * (TEAM - 1) + wv - 1 : P.NG * (TEAM - 1) + (wg - P.NG) * TEAM + wv;
+    S st;
+    st.init(lds + wv * S::lds_floats(P));
+    float* mine = lds + TEAM * S::lds_floats(P) + wv * (S::HBM * kTeamStateW * 64 + 16);
+    pool_worker<S>(P, st, widx, mine, reinterpret_cast<int*>(mine + S::HBM * kTeamStateW * 64));
+}
+
+// per wave: tile buffers, then (after all waves' buffers) a running state and 16 words for block ids
+template <class S>
+size_t pool_lds_bytes(const Params& p) {
+    return (size_t)S::TEAM * (S::lds_floats(p) + S::HBM * kTeamStateW * 64 + 16) * sizeof(float);
 }
 
 // Full mode, one tile at a time: split sp of group grp covers a fixed tile range.
@@ -2722,11 +3300,14 @@ bool fast_path(const Params& p) {
     return p.D == 128 && p.q_dtype == ART_BF16 && (p.kv_dtype == ART_BF16 || p.kv_dtype == ART_I8) &&
            p.G <= 8 && (p.T == 16 || p.T == 32 || p.T == 64);
 }
-// Streamed 64-token tiles: the team engine (ART, with or without the V
-// skip), the ring engine (ART without the V skip, when a worker count is
-// requested) and full mode.
+// the work-sharing engine serves ART mode
+bool sharing(const Params& p) {
+    return p.engine == ART_ENGINE_SHARED || (p.engine == ART_ENGINE_AUTO && p.workers > 0);
+}
+// Streamed 64-token tiles: the team and pool engines (ART; the V skip on the
+// team engine), the work-sharing engine (ART without the V skip) and full mode.
 bool stream_path(const Params& p, bool art) {
-    return fast_path(p) && p.T == 64 && (!p.vskip || (art && p.workers == 0));
+    return fast_path(p) && p.T == 64 && (!p.vskip || (art && !sharing(p)));
 }
 
 template <class Tile>
@@ -2767,12 +3348,43 @@ int launch_team(const Params& p0, hipStream_t s) {
     return (int)hipGetLastError();
 }
 
+// One work-group per resident slot, all resident (cooperative launch), as
+// long as each group's decider has a work-group; returns 1 when it did not
+// launch (too many groups), so that the team engine runs instead.
+template <class S>
+int launch_pool(const Params& p0, hipStream_t s) {
+    Params p = p0;
+    const size_t lds = pool_lds_bytes<S>(p);
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_pool_kernel<S>, S::TEAM * 64, lds) != hipSuccess ||
+        per_cu < 1) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    const long long grid = (long long)per_cu * cus;
+    if (p.NG > grid || p.NG > kTeamHelpGroups) return 1;
+    p.pool_cap = kPoolContrib;
+    void* args[] = {&p};
+    const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&art_pool_kernel<S>), dim3((unsigned)grid),
+                                                    dim3(S::TEAM * 64), args, (unsigned)lds, s);
+    if (e == hipSuccess) return 0;
+    (void)hipGetLastError();
+    return 1;
+}
+
 template <class S>
 int run_stream(const Params& p, hipStream_t s, bool art) {
-    // a requested worker count selects the work-sharing engine
-    if (art && p.workers == 0) return p.vskip ? launch_team<S, true>(p, s) : launch_team<S, false>(p, s);
-    if (art) return launch_persistent<decltype(&art_stream_kernel<S>), S>(p, s, &art_stream_kernel<S>);
-    return launch_split<decltype(&art_full_stream_kernel<S>), S>(p, s, &art_full_stream_kernel<S>);
+    if (!art) return launch_split<decltype(&art_full_stream_kernel<S>), S>(p, s, &art_full_stream_kernel<S>);
+    if (sharing(p)) return launch_persistent<decltype(&art_stream_kernel<S>), S>(p, s, &art_stream_kernel<S>);
+    if (p.vskip) return launch_team<S, true>(p, s);
+    // by default the pool serves few, long groups (where one CU per group
+    // would leave most of the chip idle)
+    const bool pool = p.engine == ART_ENGINE_POOL ||
+                      (p.engine == ART_ENGINE_AUTO && p.NG <= kPoolAutoGroups && p.nt_max >= kPoolAutoTiles);
+    if (pool && launch_pool<S>(p, s) == 0) return 0;
+    return launch_team<S, false>(p, s);
 }
 
 template <int KV, int GMAX>

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = art.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.art_abi_version() == 2
+    assert lib.art_abi_version() == 3
 
 
 def desc(**kw):
@@ -72,6 +72,8 @@ def test_valid_desc_passes():
     (dict(max_workers=-3), -5),
     (dict(team_helpers=-1), -5),
     (dict(team_helpers=4), -5),
+    (dict(engine=-1), -5),
+    (dict(engine=4), -5),
 ])
 def test_bad_desc_rejected(kw, code):
     assert B.validate(desc(**kw), 64, 1e-3, 1e-4) == code

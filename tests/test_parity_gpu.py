@@ -17,7 +17,8 @@ def _run_and_check(case, label, **kw):
     log(f"[parity] {label}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} d={case.d} "
         f"ctx={case.ctx_lens.tolist()[:4]} kv={case.kv_dtype} T={case.tile} {kw}")
     out, used = run_gpu(case, **kw)
-    r = check_parity(case, out, used, **{k: v for k, v in kw.items() if k not in ("max_workers", "team_helpers")})
+    r = check_parity(case, out, used,
+                     **{k: v for k, v in kw.items() if k not in ("max_workers", "team_helpers", "engine")})
     log(f"[parity] {label}: max_abs={r['max_abs']:.3e} near={r['near']} "
         f"mean tiles_used={np.mean(r['tiles_used']):.1f}")
     return out, used, r
@@ -182,6 +183,40 @@ def test_helper_work_groups_parity():
     _run_and_check(c, "config2 art, 3 helper work-groups per group", team_helpers=3)
     c = A.config(4, small=True)
     _run_and_check(c, "config4-small art, 1 helper work-group per group", team_helpers=1)
+
+
+ENGINE_TEAM, ENGINE_POOL = 1, 2
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_pool_engine_parity(n):
+    # waves on every CU serve whichever groups have tiles left
+    c = A.config(n, small=n != 2)
+    _run_and_check(c, f"config{n} pool art", engine=ENGINE_POOL, v_skip_eps=0.0)
+
+
+def test_pool_engine_matches_team_engine():
+    # the same probe records and block scan decide: tiles_used is identical,
+    # and the outputs differ only by the order of the partial-sum merges
+    c = A.config(3, small=True)
+    dev = to_device(c)
+    for kw in (dict(), dict(eps_scale=1e-30, eps_dir=1e-30), dict(patience=3)):
+        o1, u1 = run_gpu(c, dev, engine=ENGINE_TEAM, **kw)
+        o2, u2 = run_gpu(c, dev, engine=ENGINE_POOL, **kw)
+        assert np.array_equal(u1, u2)
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-5)
+
+
+def test_pool_engine_ragged_empty_and_invalid_rows():
+    c = A.config(3, small=True, batch=5)
+    c.ctx_lens[1] = 0                                   # empty row
+    c.ctx_lens[2] = 1                                   # one token
+    c.ctx_lens[3] = 64 * 3 + 17                         # ragged tail
+    c.ctx_lens[4] = c.block_table.shape[1] * 16 + 1     # longer than its table
+    out, used = run_gpu(c, engine=ENGINE_POOL)
+    assert (used[1] == 0).all() and (out[1] == 0).all()
+    assert (used[4] == -1).all() and np.isnan(out[4]).all()
+    check_parity(c, out, used, rows=[0, 1, 2, 3])
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
