@@ -685,7 +685,8 @@ struct Stream {
     using Out = TileOutT<HBM>;
     typedef typename std::conditional<KV == ART_I8, u2, u4>::type vvec;
 
-    __host__ __device__ static size_t lds_floats(const Params&) { return (2 * UP * PAGEB) / 4 + 64 * GMAX; }
+    static constexpr int LDS_FLOATS = (2 * UP * PAGEB) / 4 + 64 * GMAX;
+    __host__ __device__ static size_t lds_floats(const Params&) { return LDS_FLOATS; }
 
     struct TileRef {             // one tile of one group (wave-uniform)
         int grp, t, n;
@@ -2792,8 +2793,8 @@ struct LdsPart {
 };
 
 // One worker: joins groups and processes their tiles until none is left;
-// its running state lives in `wsl` (HBM * kTeamStateW * 64 floats of LDS),
-// the next tile's block ids in `blk` (S::PAGES ints of LDS).
+// its running state and a pending tile live in `wsl` (2 * HBM * kTeamStateW
+// * 64 floats of LDS), the next tile's block ids in `blk` (S::PAGES ints).
 template <class S>
 __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, float* wsl, int* blk) {
     constexpr int HBM = S::HBM, T = S::T;
@@ -2849,9 +2850,11 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
             bnd = uni(unstamp(qb, e, nt));
         };
         const LdsPart<HBM> ws{wsl};
-        // the tiles awaiting their decision, oldest first (two: a decision
-        // takes about a tile's time to come back through global memory)
-        Part<HBM> q0, q1;
+        // the tiles awaiting their decision, oldest first: two, as a decision
+        // takes about a tile's time to come back through global memory (the
+        // second one in LDS, next to the running state)
+        const LdsPart<HBM> q1{wsl + HBM * kTeamStateW * 64};
+        Part<HBM> q0;
         int t0 = 0, t1 = 0, np = 0;
         ws.clear();
         bool gv = false;
@@ -2868,7 +2871,15 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
 #pragma unroll
             for (int hb = 0; hb < HBM; ++hb)
                 if (fate[hb] > 0) ws.merge(hb, q0.m[hb], q0.l[hb], q0.a[hb]);
-            q0 = q1;
+            if (np == 2) {
+#pragma unroll
+                for (int hb = 0; hb < HBM; ++hb) {
+                    q0.m[hb] = q1.at(hb, 0);
+                    q0.l[hb] = q1.at(hb, 1);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) q0.a[hb][j] = q1.at(hb, 2 + j);
+                }
+            }
             t0 = t1;
             --np;
             return true;
@@ -2921,7 +2932,7 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
             take_glb();
             const int tX = uni(tXr);  // landed with the tile
             if (t >= bnd) break;  // past the group's stop: no head uses the tile
-            retire(0);  // the previous tile first (two pending partials would not fit in registers)
+            retire(1);  // room for this tile
             if (gv) break;
             // the record's slot must have been released (none is, once the
             // group is done: then the tile is past the bound)
@@ -2967,7 +2978,13 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
                     q0 = qn;
                     t0 = t;
                 } else {
-                    q1 = qn;
+#pragma unroll
+                    for (int hb = 0; hb < HBM; ++hb) {
+                        q1.at(hb, 0) = qn.m[hb];
+                        q1.at(hb, 1) = qn.l[hb];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) q1.at(hb, 2 + j) = qn.a[hb][j];
+                    }
                     t1 = t;
                 }
                 ++np;
@@ -3002,11 +3019,20 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
     count_stats(P, loaded, rows);
 }
 
+// Waves of a pool work-group: as many as are resident on a CU, as long as
+// their LDS (tile buffers, running state, a pending tile, block ids) fits.
+template <class S>
+struct PoolShape {
+    static constexpr int WAVE_FLOATS = S::LDS_FLOATS + 2 * S::HBM * kTeamStateW * 64 + 16;
+    static constexpr int FIT = (160 * 1024 / 4) / WAVE_FLOATS;
+    static constexpr int WAVES = FIT < S::TEAM ? FIT : S::TEAM;
+};
+
 // Grid: one work-group per CU, all resident (cooperative launch).
 template <class S>
-__global__ __launch_bounds__(S::TEAM * 64) void art_pool_kernel(Params P) {
+__global__ __launch_bounds__(PoolShape<S>::WAVES * 64) void art_pool_kernel(Params P) {
     extern __shared__ float lds[];
-    constexpr int TEAM = S::TEAM;
+    constexpr int TEAM = PoolShape<S>::WAVES;
     const int wv = wave_id(), wg = blockIdx.x;
     if (wg < P.NG && wv == 0) {
         // the decider's chain is latency-bound: let its SIMD issue it first
@@ -3017,15 +3043,16 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_pool_kernel(Params P) {
     // workers numbered so that consecutive ones start on consecutive groups
     const int widx = wg < P.NG ? wg * (TEAM - 1) + wv - 1 : P.NG * (TEAM - 1) + (wg - P.NG) * TEAM + wv;
     S st;
-    st.init(lds + wv * S::lds_floats(P));
-    float* mine = lds + TEAM * S::lds_floats(P) + wv * (S::HBM * kTeamStateW * 64 + 16);
-    pool_worker<S>(P, st, widx, mine, reinterpret_cast<int*>(mine + S::HBM * kTeamStateW * 64));
+    st.init(lds + wv * S::LDS_FLOATS);
+    float* mine = lds + TEAM * S::LDS_FLOATS + wv * (2 * S::HBM * kTeamStateW * 64 + 16);
+    pool_worker<S>(P, st, widx, mine, reinterpret_cast<int*>(mine + 2 * S::HBM * kTeamStateW * 64));
 }
 
-// per wave: tile buffers, then (after all waves' buffers) a running state and 16 words for block ids
+// per wave: tile buffers, then (after all waves' buffers) a running state, a
+// pending tile and 16 words for block ids
 template <class S>
-size_t pool_lds_bytes(const Params& p) {
-    return (size_t)S::TEAM * (S::lds_floats(p) + S::HBM * kTeamStateW * 64 + 16) * sizeof(float);
+size_t pool_lds_bytes(const Params&) {
+    return (size_t)PoolShape<S>::WAVES * PoolShape<S>::WAVE_FLOATS * sizeof(float);
 }
 
 // Full mode, one tile at a time: split sp of group grp covers a fixed tile range.
@@ -3358,7 +3385,8 @@ int launch_pool(const Params& p0, hipStream_t s) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_pool_kernel<S>, S::TEAM * 64, lds) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_pool_kernel<S>, PoolShape<S>::WAVES * 64, lds) !=
+            hipSuccess ||
         per_cu < 1) {
         (void)hipGetLastError();
         return 1;
@@ -3368,7 +3396,7 @@ int launch_pool(const Params& p0, hipStream_t s) {
     p.pool_cap = kPoolContrib;
     void* args[] = {&p};
     const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&art_pool_kernel<S>), dim3((unsigned)grid),
-                                                    dim3(S::TEAM * 64), args, (unsigned)lds, s);
+                                                    dim3(PoolShape<S>::WAVES * 64), args, (unsigned)lds, s);
     if (e == hipSuccess) return 0;
     (void)hipGetLastError();
     return 1;
