@@ -1658,15 +1658,17 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P)
 // tiles, the loads of the next one issued before the current one is handed
 // over.
 //
-// For every tile a worker hands over, per head, a probe record: the tile's
-// softmax max and sum, its accumulator on head dims 0..7 (the probe dims)
-// and its error flag.  Primary workers write records to LDS (data, a wait
-// for LDS, then the slot's tag); helpers write them to global memory as
-// 64-bit words whose upper half names the call (epoch) and the lap of the
-// ring slot, so the decider recognises a record word by word and no store
-// has to wait for another.  A worker keeps each tile's whole partial until
-// the tile is decided, then merges it into its own running state for every
-// head that uses the tile.
+// A primary worker hands each tile's whole partial (per head: the tile's
+// softmax max and sum and its accumulator, in the fold mapping) to the
+// decider through a ring of LDS slots (data, a wait for LDS, then the slot's
+// tag) and never waits for a decision.  A helper hands over only a probe
+// record per head (the tile's max and sum, its accumulator on head dims 0..7
+// -- the probe dims -- and its error flag) through global memory, as 64-bit
+// words whose upper half names the call (epoch) and the lap of the ring slot,
+// so that the decider recognises a record word by word and no store has to
+// wait for another; a helper keeps each tile's partial until the decider has
+// decided the tile, then merges it into its own running state for every head
+// that uses it.
 //
 // The decider takes the tiles in aligned blocks of kBlock: lane i of a
 // 16-lane row (one row per head) holds tile f0 + i's record, and an
@@ -1675,16 +1677,16 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P)
 // tile of the block.  Lane i's value depends on tiles f0 .. f0 + i only, so
 // the tiles of a block are decided as soon as their prefix is complete, with
 // the same values however the records trickled in.  Both stability metrics,
-// the streak and the stop then follow for every tile in order.  Per head the
-// decider publishes how many tiles are decided, or tiles_used once the head
-// stops; once every head has stopped the bound drops and no worker loads a
-// further tile.  At the end the workers' running states are merged in a
-// fixed order (the primary's workers, then the helpers'), so the output does
-// not depend on timing.
-constexpr int kProbeRing = 64;  // LDS record slots, by ordinal among the primary's tiles (a power of two)
+// the streak and the stop then follow for every tile in order.  The decider
+// merges each primary tile, once decided, into the group's output for the
+// heads that use it (in tile order, freeing its slot), publishes per head how
+// many tiles are decided -- or tiles_used once the head stops -- for the
+// helpers, and once every head has stopped drops the bound, so that no worker
+// loads a further tile.  The helpers' running states are merged last, in
+// helper order, so the output does not depend on timing.
+constexpr int kTeamSlots = 8;   // LDS slots of whole partials, by ordinal among the primary's tiles (a power of two)
 constexpr int kBlock = 16;      // tiles the decider scans together
 constexpr int kChain = 8;       // LDS slots of the running-max chain (V skip)
-constexpr int kRecF = 12;       // floats per LDS record: max, sum, probe dims 0..7, error flag, pad
 
 // decision word of a head
 constexpr int kHdStop = 1 << 30;         // the head stopped; the count is its tiles_used
@@ -1698,14 +1700,13 @@ __device__ __forceinline__ int tile_fate(int w, int q) {
     return q < (w & kHdCount) ? 1 : -1;
 }
 
-template <int GMAX>
+template <int HBM>
 struct TeamShared {
-    int tag[kProbeRing];                  // t + 1 once the slot holds tile t's records
-    float rec[kProbeRing][GMAX][kRecF];   // probe records of the primary's tiles
-    int released;                         // the primary's ordinals whose slots may be reused
-    int bound;                            // tiles that may still be loaded
-    int word[GMAX];                       // decision word per head
-    int err[GMAX];                        // final: a used tile met an invalid block id
+    int tag[kTeamSlots];  // t + 1 once the slot holds tile t's partial
+    int err[kTeamSlots];  // the tile met an invalid block id
+    float part[kTeamSlots][HBM * kTeamStateW * 64];  // [head block][max, sum, 8 dims][lane]
+    int released;         // the primary's ordinals merged by the decider (their slots may be reused)
+    int bound;            // tiles that may still be loaded
     // V skip: the running max through tile t, per head, in slot t % kChain (its tag t + 1 once written)
     int ptag[kChain];
     float pmax[kChain][16];
@@ -1827,12 +1828,11 @@ struct Part {
     }
 };
 
-// One tile worker: tiles first, first + W, ... of the group, merged into ws.
-// PRIMARY: records and decisions through LDS; else through global memory.
-template <class S, bool PRIMARY, bool VSKIP>
-__device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int nt, int first, const TeamPlan& plan,
-                                            S& st, TeamShared<S::HEADS>* sh, Part<S::HBM>& ws) {
-    static_assert(PRIMARY || !VSKIP, "the V skip's running-max chain lives in the primary's LDS");
+// A helper worker: tiles first, first + W, ... of the group, merged into ws
+// as they are decided; records and decisions through global memory.
+template <class S>
+__device__ __forceinline__ void team_helper_worker(const Params& P, int grp, int n, int nt, int first,
+                                                   const TeamPlan& plan, S& st, Part<S::HBM>& ws) {
     constexpr int HBM = S::HBM;
     const int lane = lane_id();
     const FoldLanes fl(P);
@@ -1840,24 +1840,16 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     ws.clear();
     int t = first;
     if (t >= nt) return;
-    // ordinal of tile t among the primary's (or the helpers') tiles; its slot
-    // may be written once the decider has released the ordinal a ring before
-    int o1 = PRIMARY ? first : first - plan.nA;
-    const int ostep = PRIMARY ? plan.nA : plan.nH;
-    constexpr int ring = PRIMARY ? kProbeRing : kTeamRingG;
+    // ordinal of tile t among the helpers' tiles; its record slot may be
+    // written once the decider has released the ordinal a ring before
+    int o1 = first - plan.nA;
     // the decisions as last seen: this lane's head's word per head block, the
-    // bound and the released ordinals.  Helpers load the global words before a
-    // tile's loads and take them once those have landed.
+    // bound and the released ordinals, loaded before a tile's loads and taken
+    // once those have landed
     int hw[HBM];
     int bnd = nt, rel = 0;
     unsigned long long qw[HBM], qb = 0, qr = 0;
     auto head_ok = [&](int hb) { return hb < fl.HB && hb * 4 + fl.hl < P.G; };
-    auto read_lds = [&]() {
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) hw[hb] = head_ok(hb) ? lds_ld(&sh->word[hb * 4 + fl.hl]) : (kHdStop | 0);
-        bnd = uni(lds_ld(&sh->bound));
-        rel = uni(lds_ld(&sh->released));
-    };
     auto load_glb = [&]() {
 #pragma unroll
         for (int hb = 0; hb < HBM; ++hb) qw[hb] = cld(tg.ctl + 4 + min(hb * 4 + fl.hl, kTeamRecHeads - 1));
@@ -1869,14 +1861,6 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
         for (int hb = 0; hb < HBM; ++hb) hw[hb] = head_ok(hb) ? unstamp(qw[hb], P.epoch, 0) : (kHdStop | 0);
         bnd = uni(unstamp(qb, P.epoch, nt));
         rel = uni(unstamp(qr, P.epoch, 0));
-    };
-    auto refresh = [&]() {
-        if constexpr (PRIMARY) {
-            read_lds();
-        } else {
-            load_glb();
-            take_glb();
-        }
     };
     // the tile awaiting its decision
     Part<HBM> q0;
@@ -1903,8 +1887,9 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
         if (np == 0 || try_front()) return;
         const Deadline dl;
         for (;;) {
-            __builtin_amdgcn_s_sleep(PRIMARY ? 1 : 4);
-            refresh();
+            __builtin_amdgcn_s_sleep(4);
+            load_glb();
+            take_glb();
             if (try_front()) return;
             if (dl.passed()) {
                 gv = true;
@@ -1915,7 +1900,103 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
     };
 
     typename S::TileRef C;
-    if constexpr (!PRIMARY) load_glb();
+    load_glb();
+    st.load_q(P, grp);  // before the tile's loads: consume() counts those in issue order
+    S::resolve(P, grp, t, C);
+    st.template issue<0>(P, C, 0);
+    st.template issue<1>(P, C, 1);
+    int blkN = S::fetch_blocks(P, grp, n, t + plan.W);  // block ids of the next tile
+    // tiles (and rows) loaded, counted when their loads are issued
+    unsigned long long loaded = 1, rows = min(S::T, n - t * S::T);
+    for (;;) {
+        st.template consume<0>(P, C, 0, true);
+        st.template consume<1>(P, C, 1, false);
+        typename S::Out o;
+        st.flush(P, o);
+        take_glb();
+        if (t >= bnd) break;  // past the group's stop: no head uses the tile
+        // the next tile's loads first, then the hand-over of this one
+        const int tn = t + plan.W;
+        const bool haveN = tn < nt && tn < bnd;
+        const int cerr = C.err;
+        if (haveN) {
+            S::resolve_from(P, grp, n, tn, blkN, C);
+            load_glb();
+            st.template issue<0>(P, C, 0);
+            st.template issue<1>(P, C, 1);
+            blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
+            ++loaded;
+            rows += min(S::T, n - tn * S::T);
+        }
+        // the previous tile's decision (by now, as a rule, known)
+        retire();
+        if (gv) break;
+        // its record slot must have been released (the decider releases no
+        // further slot once the group is done: then the tile is past the bound)
+        if (o1 - kTeamRingG >= rel) {
+            const Deadline dl;
+            for (;;) {
+                __builtin_amdgcn_s_sleep(4);
+                rel = uni(unstamp(cld(tg.ctl + 0), P.epoch, 0));
+                bnd = uni(unstamp(cld(tg.ctl + 1), P.epoch, nt));
+                if (o1 - kTeamRingG < rel || t >= bnd) break;
+                if (dl.passed()) {
+                    gv = true;
+                    break;
+                }
+            }
+            if (gv || t >= bnd) break;
+        }
+        // the record: lane 16*hl (cid 0) holds head 4hb + hl's probe dims
+        {
+            const int s = o1 & (kTeamRingG - 1);
+            const unsigned tag = rec_tag<kTeamRingG>(P.epoch, o1);
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                if (fl.cid == 0 && head_ok(hb)) {
+                    unsigned long long* e = tg.rec + (long long)s * kTeamRecW * kTeamRecHeads + hb * 4 + fl.hl;
+                    cst(e + 0 * kTeamRecHeads, tagw(tag, o.mf[hb]));
+                    cst(e + 1 * kTeamRecHeads, tagw(tag, o.lf[hb]));
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) cst(e + (2 + j) * kTeamRecHeads, tagw(tag, o.a[hb][j]));
+                    cst(e + 10 * kTeamRecHeads, tagw(tag, __int_as_float(cerr)));
+                }
+            }
+        }
+        // keep the tile's partial until its decision
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            q0.m[hb] = o.mf[hb];
+            q0.l[hb] = o.lf[hb];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q0.a[hb][j] = o.a[hb][j];
+        }
+        t0 = t;
+        np = 1;
+        if (!haveN) break;
+        t = tn;
+        o1 += plan.nH;
+    }
+    // the last tile's decision
+    if (!gv) retire();
+    // loads of a tile fetched past the stop may still be landing (in LDS too)
+    __builtin_amdgcn_s_waitcnt(0);
+    count_stats(P, loaded, rows);
+}
+
+// A primary worker: tiles first, first + W, ... of the group, each handed
+// over whole to the decider through the LDS slots.
+template <class S, bool VSKIP>
+__device__ __forceinline__ void team_primary_worker(const Params& P, int grp, int n, int nt, int first,
+                                                    const TeamPlan& plan, S& st, TeamShared<S::HBM>* sh) {
+    constexpr int HBM = S::HBM;
+    const int lane = lane_id();
+    int t = first;
+    if (t >= nt) return;
+    int o1 = first;  // ordinal of tile t among the primary's tiles
+    int bnd = nt, rel = 0;
+    bool gv = false;  // a wait outlasted kWaitTicks
+    typename S::TileRef C;
     st.load_q(P, grp);  // before the tile's loads: consume() counts those in issue order
     S::resolve(P, grp, t, C);
     st.template issue<0>(P, C, 0);
@@ -1953,8 +2034,7 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
         }
         typename S::Out o;
         st.flush(P, o);
-        if constexpr (PRIMARY) read_lds();
-        else take_glb();
+        bnd = uni(lds_ld(&sh->bound));
         if (t >= bnd) break;  // past the group's stop: no head uses the tile
         // the next tile's loads first, then the hand-over of this one
         const int tn = t + plan.W;
@@ -1962,30 +2042,22 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
         const int cerr = C.err;
         if (haveN) {
             S::resolve_from(P, grp, n, tn, blkN, C);
-            if constexpr (!PRIMARY) load_glb();
             st.template issue<0>(P, C, 0);
             st.template issue<1>(P, C, 1);
             blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
             ++loaded;
             rows += min(S::T, n - tn * S::T);
         }
-        // the previous tile's decision (by now, as a rule, known)
-        retire();
-        if (gv) break;
-        // its record slot must have been released (the decider releases no
-        // further slot once the group is done: then the tile is past the bound)
-        if (o1 - ring >= rel) {
+        // the slot must have been released (the decider releases no further
+        // slot once the group is done: then the tile is past the bound)
+        rel = uni(lds_ld(&sh->released));
+        if (o1 - kTeamSlots >= rel) {
             const Deadline dl;
             for (;;) {
-                __builtin_amdgcn_s_sleep(PRIMARY ? 1 : 4);
-                if constexpr (PRIMARY) {
-                    rel = uni(lds_ld(&sh->released));
-                    bnd = uni(lds_ld(&sh->bound));
-                } else {
-                    rel = uni(unstamp(cld(tg.ctl + 0), P.epoch, 0));
-                    bnd = uni(unstamp(cld(tg.ctl + 1), P.epoch, nt));
-                }
-                if (o1 - ring < rel || t >= bnd) break;
+                __builtin_amdgcn_s_sleep(1);
+                rel = uni(lds_ld(&sh->released));
+                bnd = uni(lds_ld(&sh->bound));
+                if (o1 - kTeamSlots < rel || t >= bnd) break;
                 if (dl.passed()) {
                     gv = true;
                     break;
@@ -1993,50 +2065,24 @@ __device__ __forceinline__ void team_worker(const Params& P, int grp, int n, int
             }
             if (gv || t >= bnd) break;
         }
-        // the record: lane 16*hl (cid 0) holds head 4hb + hl's probe dims
-        const int s = o1 & (ring - 1);
-        if constexpr (PRIMARY) {
+        {
+            const int s = o1 & (kTeamSlots - 1);
+            float* e = sh->part[s] + lane;
 #pragma unroll
             for (int hb = 0; hb < HBM; ++hb) {
-                if (fl.cid == 0 && head_ok(hb)) {
-                    float* e = sh->rec[s][hb * 4 + fl.hl];
-                    *reinterpret_cast<f4*>(e) = f4{o.mf[hb], o.lf[hb], o.a[hb][0], o.a[hb][1]};
-                    *reinterpret_cast<f4*>(e + 4) = f4{o.a[hb][2], o.a[hb][3], o.a[hb][4], o.a[hb][5]};
-                    *reinterpret_cast<f4*>(e + 8) = f4{o.a[hb][6], o.a[hb][7], __int_as_float(cerr), 0.f};
-                }
+                e[(hb * kTeamStateW + 0) * 64] = o.mf[hb];
+                e[(hb * kTeamStateW + 1) * 64] = o.lf[hb];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) e[(hb * kTeamStateW + 2 + j) * 64] = o.a[hb][j];
             }
-            wait_lds();  // the records are written before their tag
+            if (lane == 0) lds_st(&sh->err[s], cerr);
+            wait_lds();  // the partial is written before its tag
             if (lane == 0) lds_st(&sh->tag[s], t + 1);
-        } else {
-            const unsigned tag = rec_tag<kTeamRingG>(P.epoch, o1);
-#pragma unroll
-            for (int hb = 0; hb < HBM; ++hb) {
-                if (fl.cid == 0 && head_ok(hb)) {
-                    unsigned long long* e = tg.rec + (long long)s * kTeamRecW * kTeamRecHeads + hb * 4 + fl.hl;
-                    cst(e + 0 * kTeamRecHeads, tagw(tag, o.mf[hb]));
-                    cst(e + 1 * kTeamRecHeads, tagw(tag, o.lf[hb]));
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) cst(e + (2 + j) * kTeamRecHeads, tagw(tag, o.a[hb][j]));
-                    cst(e + 10 * kTeamRecHeads, tagw(tag, __int_as_float(cerr)));
-                }
-            }
         }
-        // keep the tile's partial until its decision
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            q0.m[hb] = o.mf[hb];
-            q0.l[hb] = o.lf[hb];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) q0.a[hb][j] = o.a[hb][j];
-        }
-        t0 = t;
-        np = 1;
         if (!haveN) break;
         t = tn;
-        o1 += ostep;
+        o1 += plan.nA;
     }
-    // the last tile's decision
-    if (!gv) retire();
     // loads of a tile fetched past the stop may still be landing (in LDS too)
     __builtin_amdgcn_s_waitcnt(0);
     count_stats(P, loaded, rows);
@@ -2242,28 +2288,50 @@ __device__ __forceinline__ int present_prefix(bool have, int kmax) {
     return min(__builtin_ctz(~mask), kmax);
 }
 
-// Decides the group's tiles, block after block; at the end leaves each
-// head's tiles_used (or -2) in its decision word and its error flag in LDS.
-template <int HBM, int GMAX>
+// Decides the group's tiles, block after block, and merges the primary's
+// tiles into acc as they are decided; D holds each head's tiles_used (-1 if
+// undecided: the wait for a tile outlasted kWaitTicks) and error flag.
+template <int HBM>
 __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const TeamPlan& plan,
-                                             TeamShared<GMAX>* sh) {
+                                             TeamShared<HBM>* sh, ProbeState<HBM>& D, Part<HBM>& acc) {
     const int lane = lane_id(), i = lane & 15;
     const FoldLanes fl(P);
     const TeamGlobal tg(P, grp);
     const bool glb = plan.nH > 0;
-    ProbeState<HBM> D;
     D.init(fl, P.G);
+    acc.clear();
     int relA = 0, relH = 0;
     bool finished = false, gave_up = false;
+    // the decisions, for the helpers
     auto publish = [&](int decided) {
+        if (!glb) return;
 #pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            if (i == 0 && D.hv[hb]) {
-                const int h = hb * 4 + fl.hl, wd = D.word(hb, decided);
-                lds_st(&sh->word[h], wd);
-                if (glb) cst(tg.ctl + 4 + h, stamp(P.epoch, (unsigned)wd));
+        for (int hb = 0; hb < HBM; ++hb)
+            if (i == 0 && D.hv[hb]) cst(tg.ctl + 4 + hb * 4 + fl.hl, stamp(P.epoch, (unsigned)D.word(hb, decided)));
+    };
+    // merges the decided primary tiles among f0 + q0 .. f0 + q1 - 1, in order
+    auto merge_primary = [&](int f0, int q0, int q1) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the slots are read after their tags
+        for (int q = q0; q < q1; ++q) {
+            const int tq = f0 + q, kq = tq % plan.W;
+            if (kq >= plan.nA) continue;  // a helper's tile: it merges its own
+            const int oq = (tq / plan.W) * plan.nA + kq;
+            const float* e = sh->part[oq & (kTeamSlots - 1)] + lane;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                if (D.hv[hb] && (D.U[hb] < 0 || tq < D.U[hb])) {
+                    float a2[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) a2[j] = e[(hb * kTeamStateW + 2 + j) * 64];
+                    sm_merge_fast(acc.m[hb], acc.l[hb], acc.a[hb], e[(hb * kTeamStateW) * 64],
+                                  e[(hb * kTeamStateW + 1) * 64], a2);
+                }
             }
+            relA = oq + 1;
         }
+        // (a wave's LDS accesses execute in order: the slots are read before they are released)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) lds_st(&sh->released, relA);
     };
     for (int f0 = 0; f0 < nt && !finished && !gave_up; f0 += kBlock) {
         const int kmax = min(kBlock, nt - f0);
@@ -2272,7 +2340,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
         const int kp = t % plan.W, per = t / plan.W;
         const bool prim = kp < plan.nA;
         const int ord = prim ? per * plan.nA + kp : per * plan.nH + (kp - plan.nA);
-        const int sA = ord & (kProbeRing - 1), sH = ord & (kTeamRingG - 1);
+        const int sA = ord & (kTeamSlots - 1), sH = ord & (kTeamRingG - 1);
         const unsigned rtag = rec_tag<kTeamRingG>(P.epoch, ord);
         BlockRecs<HBM> R;
         R.clear();
@@ -2286,16 +2354,16 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                     // the data before the tag: data read after the tag is the tile's
                     if (lds_ld(&sh->tag[sA]) == t + 1) {
                         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                        const float* e = sh->part[sA] + 16 * fl.hl;  // lane 16*hl holds the probe dims
+                        const int ev = lds_ld(&sh->err[sA]);
 #pragma unroll
                         for (int hb = 0; hb < HBM; ++hb) {
                             if (D.hv[hb]) {
-                                const float* e = sh->rec[sA][hb * 4 + fl.hl];
-                                const f4 x0 = *reinterpret_cast<const f4*>(e);
-                                const f4 x1 = *reinterpret_cast<const f4*>(e + 4);
-                                const f4 x2 = *reinterpret_cast<const f4*>(e + 8);
-                                R.m[hb] = x0.x; R.l[hb] = x0.y; R.p[hb][0] = x0.z; R.p[hb][1] = x0.w;
-                                R.p[hb][2] = x1.x; R.p[hb][3] = x1.y; R.p[hb][4] = x1.z; R.p[hb][5] = x1.w;
-                                R.p[hb][6] = x2.x; R.p[hb][7] = x2.y; R.e[hb] = __float_as_int(x2.z);
+                                R.m[hb] = e[(hb * kTeamStateW) * 64];
+                                R.l[hb] = e[(hb * kTeamStateW + 1) * 64];
+#pragma unroll
+                                for (int j = 0; j < 8; ++j) R.p[hb][j] = e[(hb * kTeamStateW + 2 + j) * 64];
+                                R.e[hb] = ev;
                             }
                         }
                         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -2309,6 +2377,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
             if (kk > kdone) {
                 since = wall_clock64();
                 decide_pass<HBM>(P, D, R, f0, kk, kmax, nt);
+                merge_primary(f0, kdone, kk);
                 kdone = kk;
                 finished = D.finished();
                 publish(f0 + kdone);
@@ -2329,32 +2398,22 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
             __builtin_amdgcn_s_sleep(1);
         }
         if (finished || gave_up) break;
-        // the block is decided: its slots may be reused
-        const int na = __builtin_popcountll(__ballot(inr && prim) & 0xffffull);
-        relA += na;
-        relH += kmax - na;
-        if (lane == 0) {
-            lds_st(&sh->released, relA);
-            if (glb) cst(tg.ctl + 0, stamp(P.epoch, (unsigned)relH));
-        }
+        // the helpers' record slots of the block may be reused
+        relH += kmax - __builtin_popcountll(__ballot(inr && prim) & 0xffffull);
+        if (glb && lane == 0) cst(tg.ctl + 0, stamp(P.epoch, (unsigned)relH));
     }
     if (gave_up) {
+        if (glb) {
 #pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            if (i == 0 && D.hv[hb] && D.U[hb] < 0) {
-                const int h = hb * 4 + fl.hl;
-                lds_st(&sh->word[h], kHdGaveUp);
-                if (glb) cst(tg.ctl + 4 + h, stamp(P.epoch, (unsigned)kHdGaveUp));
-            }
+            for (int hb = 0; hb < HBM; ++hb)
+                if (i == 0 && D.hv[hb] && D.U[hb] < 0)
+                    cst(tg.ctl + 4 + hb * 4 + fl.hl, stamp(P.epoch, (unsigned)kHdGaveUp));
         }
         if (lane == 0) {
             lds_st(&sh->bound, 0);
             if (glb) cst(tg.ctl + 1, stamp(P.epoch, 0u));
         }
     }
-#pragma unroll
-    for (int hb = 0; hb < HBM; ++hb)
-        if (i == 0 && D.hv[hb]) lds_st(&sh->err[hb * 4 + fl.hl], D.err[hb]);
 }
 
 // running states of waves w0 .. w1-1, each in its area of the LDS, merged in wave order
@@ -2392,7 +2451,7 @@ __device__ __forceinline__ void store_area(float* mine, const Part<HBM>& ws) {
 template <class S, bool VSKIP>
 __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     extern __shared__ float lds[];
-    constexpr int HBM = S::HBM, TEAM = S::TEAM, GMAX = S::HEADS;
+    constexpr int HBM = S::HBM, TEAM = S::TEAM;
     const int wv = wave_id(), lane = lane_id();
     const FoldLanes fl(P);
     const int G = P.G;
@@ -2420,7 +2479,7 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
         if constexpr (!VSKIP) {
             S st;
             st.init(lds + wv * wave_floats);
-            team_worker<S, false, false>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st, nullptr, ws);
+            team_helper_worker<S>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st, ws);
         } else {
             ws.clear();
         }
@@ -2443,38 +2502,29 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
         }
         return;
     }
-    TeamShared<GMAX>* sh = reinterpret_cast<TeamShared<GMAX>*>(lds + (TEAM - 1) * wave_floats);
+    TeamShared<HBM>* sh = reinterpret_cast<TeamShared<HBM>*>(lds + (TEAM - 1) * wave_floats);
     if (wv == 0) {
-        for (int k = lane; k < kProbeRing; k += 64) sh->tag[k] = 0;
+        if (lane < kTeamSlots) sh->tag[lane] = 0;
         if (lane < kChain) sh->ptag[lane] = 0;
-        if (lane < GMAX) {
-            sh->word[lane] = 0;
-            sh->err[lane] = 0;
-        }
         if (lane == 0) {
             sh->released = 0;
             sh->bound = nt;
         }
     }
     __syncthreads();
-    if (wv == 0) {
-        // the decider's chain is latency-bound: let its SIMD issue it first
-        __builtin_amdgcn_s_setprio(3);
-        team_decider<HBM, GMAX>(P, grp, nt, plan, sh);
-        __builtin_amdgcn_s_setprio(0);
-        ws.clear();
-    } else {
+    if (wv != 0) {
         S st;
         st.init(lds + (wv - 1) * wave_floats);
-        team_worker<S, true, VSKIP>(P, grp, n, nt, wv - 1, plan, st, sh, ws);
+        team_primary_worker<S, VSKIP>(P, grp, n, nt, wv - 1, plan, st, sh);
+        return;
     }
-    __syncthreads();  // every worker is done with its tile buffers, the decider with the words
-    if (wv > 0) store_area<HBM>(lds + (wv - 1) * wave_floats, ws);
-    __syncthreads();
-    if (wv != 0) return;
-    // the primary's workers in order, then the helpers in order
+    // the decider's chain is latency-bound: let its SIMD issue it first
+    __builtin_amdgcn_s_setprio(3);
+    ProbeState<HBM> D;
     Part<HBM> tot;
-    merge_areas<HBM>(lds, wave_floats, 0, TEAM - 1, tot);
+    team_decider<HBM>(P, grp, nt, plan, sh, D, tot);
+    __builtin_amdgcn_s_setprio(0);
+    // then the helpers' states, in helper order
     bool lost = false;  // a helper's state did not arrive within kWaitTicks
     const unsigned htag = rec_tag<kTeamRingG>(P.epoch, 0);
     for (int r = 0; r < P.helpers; ++r) {
@@ -2509,15 +2559,14 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
 #pragma unroll
     for (int hb = 0; hb < HBM; ++hb) {
         const int h = hb * 4 + fl.hl;
-        if (hb >= fl.HB || h >= G) continue;
-        const int wd = lds_ld(&sh->word[h]);
-        if (lost || !(wd & kHdStop)) {
+        if (!D.hv[hb]) continue;
+        if (lost || D.U[hb] < 0) {
             float nan8[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) nan8[j] = NAN;
             write_head_out(P, grp, h, fl, nan8, 1.f, 0, -2);
         } else {
-            write_head_out(P, grp, h, fl, tot.a[hb], tot.l[hb], lds_ld(&sh->err[h]), wd & kHdCount);
+            write_head_out(P, grp, h, fl, tot.a[hb], tot.l[hb], D.err[hb], D.U[hb]);
         }
     }
 }
@@ -2525,14 +2574,14 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
 template <class S>
 size_t team_lds_bytes(const Params& p) {
     const size_t primary =
-        (size_t)(S::TEAM - 1) * S::lds_floats(p) * sizeof(float) + sizeof(TeamShared<S::HEADS>);
+        (size_t)(S::TEAM - 1) * S::lds_floats(p) * sizeof(float) + sizeof(TeamShared<S::HBM>);
     const size_t helper = (size_t)S::TEAM * S::lds_floats(p) * sizeof(float);
     return primary > helper ? primary : helper;
 }
 
 // ------------------------------------------------------------------ pool kernel (workers shared by the groups)
 constexpr int kPoolAutoGroups = 64;  // library default: the pool for at most this many groups ...
-constexpr int kPoolAutoTiles = 1024; // ... of at least this many tiles
+constexpr int kPoolAutoTiles = 512;  // ... of at least this many tiles
 //
 // Every CU runs one persistent work-group.  Wave 0 of work-group g < NG
 // decides group g; every other wave is a tile worker that serves whichever
