@@ -14,12 +14,13 @@ constexpr int kMaxG = 16;         // query heads per KV head
 constexpr int kWavesPerWG = 4;    // independent waves per work-group
 constexpr int kMaxDeciders = 512; // decider waves at most (one per group up to this many groups)
 // team engine, words shared through the workspace (per group)
-constexpr int kTeamRingG = 64;    // probe-record slots for the helpers' tiles (a power of two)
+constexpr int kTeamRingG = 16;    // slots of the helpers' tile partials per group (a power of two)
 constexpr int kTeamRecW = 11;     // 64-bit words per (tile, head) record: max, sum, probe dims 0..7, error flag
 constexpr int kTeamRecHeads = 8;  // heads per record slot (streamed tiles serve up to 8 query heads per KV head)
-constexpr int kTeamStateW = 10;   // 64-bit words per lane per head block of a helper's final state: m, l, 8 dims
+constexpr int kTeamStateW = 10;   // values per lane per head block of a partial or running state: m, l, 8 dims
+constexpr int kTeamPartW = 11;    // 64-bit words per lane per head block of a helper's tile partial: m, l, 8 dims, error flag
 constexpr int kMaxHelpers = 3;    // helper work-groups per group at most
-constexpr int kTeamCtl = 16;      // control words: [0] helper records released, [1] bound, [4..11] per-head decision
+constexpr int kTeamCtl = 16;      // control words: [0] helper slots released, [1] bound
 constexpr int kTeamHelpGroups = 512;  // helpers and the pool engine serve launches of at most this many
                                       // groups (the workspace holds their shared words only then)
 constexpr int kPoolRing = 128;    // pool engine: record slots per group, by tile index (a power of two)
@@ -75,11 +76,10 @@ struct Params {
     int* vmax_tag;      // [NG][nt_max]
     float* vmax;        // [NG][nt_max][16]
     float* partials;    // [NG][splits][slot]
-    unsigned long long* team_ring;  // [NG][group_words(G)]: team engine: the helpers' probe records
-                                    // [kTeamRingG][kTeamRecW][kTeamRecHeads], then their final running
-                                    // states [kMaxHelpers][HB][kTeamStateW][64]; pool engine: records
-                                    // [kPoolRing][..][..], then worker states [kPoolContrib][HB][..][64];
-                                    // (tag << 32) | value bits
+    unsigned long long* team_ring;  // [NG][group_words(G)]: team engine: the helpers' tile partials
+                                    // [kTeamRingG][HB][kTeamPartW][64]; pool engine: records
+                                    // [kPoolRing][kTeamRecW][kTeamRecHeads], then worker states
+                                    // [kPoolContrib][HB][kTeamStateW][64]; (tag << 32) | value bits
     unsigned long long* team_ctl;   // [NG][kTeamCtl]: (epoch << 32) | value
     unsigned epoch;     // distinct per call: stale team words of earlier calls never match
     int helpers;        // helper work-groups per group (team kernel)
@@ -93,11 +93,9 @@ struct Params {
     int tiles_per_split;
 };
 
-// 64-bit words per group: the team engine's helper records and states, or
-// the pool engine's records and worker states
-constexpr size_t team_words(int G) {
-    return (size_t)kTeamRingG * kTeamRecW * kTeamRecHeads + (size_t)kMaxHelpers * ((G + 3) / 4) * kTeamStateW * 64;
-}
+// 64-bit words per group: the team engine's helper tile partials, or the
+// pool engine's records and worker states
+constexpr size_t team_words(int G) { return (size_t)kTeamRingG * ((G + 3) / 4) * kTeamPartW * 64; }
 constexpr size_t pool_words(int G) {
     return (size_t)kPoolRing * kTeamRecW * kTeamRecHeads + (size_t)kPoolContrib * ((G + 3) / 4) * kTeamStateW * 64;
 }

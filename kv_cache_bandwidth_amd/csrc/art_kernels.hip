@@ -1800,15 +1800,15 @@ struct TeamPlan {
     __device__ TeamPlan(int nA_, int nH_) : nA(nA_), nH(nH_), W(nA_ + nH_) {}
 };
 
-// A group's words in global memory.
+// A group's words in global memory (team kernel with helpers).
 struct TeamGlobal {
-    unsigned long long* rec;     // [kTeamRingG][kTeamRecW][kTeamRecHeads]
-    unsigned long long* hstate;  // [kMaxHelpers][HB][kTeamStateW][64]
-    unsigned long long* ctl;     // [kTeamCtl]
+    unsigned long long* part;  // [kTeamRingG][HB][kTeamPartW][64]: the helpers' tile partials, tagged
+    unsigned long long* ctl;   // [kTeamCtl]
+    int slot_words;            // HB * kTeamPartW * 64
     __device__ TeamGlobal(const Params& P, int grp) {
-        rec = P.team_ring + (long long)grp * group_words(P.G);
-        hstate = rec + kTeamRingG * kTeamRecW * kTeamRecHeads;
+        part = P.team_ring + (long long)grp * group_words(P.G);
         ctl = P.team_ctl + (long long)grp * kTeamCtl;
+        slot_words = ((P.G + 3) / 4) * kTeamPartW * 64;
     }
 };
 
@@ -1828,77 +1828,34 @@ struct Part {
     }
 };
 
-// A helper worker: tiles first, first + W, ... of the group, merged into ws
-// as they are decided; records and decisions through global memory.
+// A helper worker: tiles first, first + W, ... of the group.  Each tile's
+// whole partial goes to the group's ring in global memory as tagged 64-bit
+// words (so no store waits for another), and the primary's decider merges
+// it: a helper never waits for a decision, only for a free slot.
 template <class S>
 __device__ __forceinline__ void team_helper_worker(const Params& P, int grp, int n, int nt, int first,
-                                                   const TeamPlan& plan, S& st, Part<S::HBM>& ws) {
+                                                   const TeamPlan& plan, S& st) {
     constexpr int HBM = S::HBM;
     const int lane = lane_id();
-    const FoldLanes fl(P);
     const TeamGlobal tg(P, grp);
-    ws.clear();
     int t = first;
     if (t >= nt) return;
-    // ordinal of tile t among the helpers' tiles; its record slot may be
-    // written once the decider has released the ordinal a ring before
+    // ordinal of tile t among the helpers' tiles; its slot may be written
+    // once the decider has released the ordinal a ring before
     int o1 = first - plan.nA;
-    // the decisions as last seen: this lane's head's word per head block, the
-    // bound and the released ordinals, loaded before a tile's loads and taken
-    // once those have landed
-    int hw[HBM];
+    // the bound and the released ordinals as last seen, loaded before a
+    // tile's loads and taken once those have landed
     int bnd = nt, rel = 0;
-    unsigned long long qw[HBM], qb = 0, qr = 0;
-    auto head_ok = [&](int hb) { return hb < fl.HB && hb * 4 + fl.hl < P.G; };
+    unsigned long long qb = 0, qr = 0;
     auto load_glb = [&]() {
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) qw[hb] = cld(tg.ctl + 4 + min(hb * 4 + fl.hl, kTeamRecHeads - 1));
         qb = cld(tg.ctl + 1);
         qr = cld(tg.ctl + 0);
     };
     auto take_glb = [&]() {
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) hw[hb] = head_ok(hb) ? unstamp(qw[hb], P.epoch, 0) : (kHdStop | 0);
         bnd = uni(unstamp(qb, P.epoch, nt));
         rel = uni(unstamp(qr, P.epoch, 0));
     };
-    // the tile awaiting its decision
-    Part<HBM> q0;
-    int t0 = 0, np = 0;
     bool gv = false;  // a wait outlasted kWaitTicks
-    // merges (or drops) the pending tile once every head has decided it
-    auto try_front = [&]() -> bool {
-        int fate[HBM];
-        bool und = false;
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            fate[hb] = tile_fate(hw[hb], t0);
-            und |= fate[hb] < 0;
-        }
-        if (__ballot(und) != 0ull) return false;
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb)
-            if (fate[hb] > 0) sm_merge_fast(ws.m[hb], ws.l[hb], ws.a[hb], q0.m[hb], q0.l[hb], q0.a[hb]);
-        np = 0;
-        return true;
-    };
-    // waits until the pending tile is decided, and merges it
-    auto retire = [&]() {
-        if (np == 0 || try_front()) return;
-        const Deadline dl;
-        for (;;) {
-            __builtin_amdgcn_s_sleep(4);
-            load_glb();
-            take_glb();
-            if (try_front()) return;
-            if (dl.passed()) {
-                gv = true;
-                np = 0;
-                return;
-            }
-        }
-    };
-
     typename S::TileRef C;
     load_glb();
     st.load_q(P, grp);  // before the tile's loads: consume() counts those in issue order
@@ -1928,11 +1885,8 @@ __device__ __forceinline__ void team_helper_worker(const Params& P, int grp, int
             ++loaded;
             rows += min(S::T, n - tn * S::T);
         }
-        // the previous tile's decision (by now, as a rule, known)
-        retire();
-        if (gv) break;
-        // its record slot must have been released (the decider releases no
-        // further slot once the group is done: then the tile is past the bound)
+        // the slot must have been released (the decider releases no further
+        // slot once the group is done: then the tile is past the bound)
         if (o1 - kTeamRingG >= rel) {
             const Deadline dl;
             for (;;) {
@@ -1947,38 +1901,23 @@ __device__ __forceinline__ void team_helper_worker(const Params& P, int grp, int
             }
             if (gv || t >= bnd) break;
         }
-        // the record: lane 16*hl (cid 0) holds head 4hb + hl's probe dims
         {
-            const int s = o1 & (kTeamRingG - 1);
             const unsigned tag = rec_tag<kTeamRingG>(P.epoch, o1);
+            unsigned long long* e = tg.part + (long long)(o1 & (kTeamRingG - 1)) * tg.slot_words + lane;
 #pragma unroll
             for (int hb = 0; hb < HBM; ++hb) {
-                if (fl.cid == 0 && head_ok(hb)) {
-                    unsigned long long* e = tg.rec + (long long)s * kTeamRecW * kTeamRecHeads + hb * 4 + fl.hl;
-                    cst(e + 0 * kTeamRecHeads, tagw(tag, o.mf[hb]));
-                    cst(e + 1 * kTeamRecHeads, tagw(tag, o.lf[hb]));
+                unsigned long long* w = e + hb * kTeamPartW * 64;
+                cst(w, tagw(tag, o.mf[hb]));
+                cst(w + 64, tagw(tag, o.lf[hb]));
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) cst(e + (2 + j) * kTeamRecHeads, tagw(tag, o.a[hb][j]));
-                    cst(e + 10 * kTeamRecHeads, tagw(tag, __int_as_float(cerr)));
-                }
+                for (int j = 0; j < 8; ++j) cst(w + 64 * (2 + j), tagw(tag, o.a[hb][j]));
+                cst(w + 64 * 10, tagw(tag, __int_as_float(cerr)));
             }
         }
-        // keep the tile's partial until its decision
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            q0.m[hb] = o.mf[hb];
-            q0.l[hb] = o.lf[hb];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) q0.a[hb][j] = o.a[hb][j];
-        }
-        t0 = t;
-        np = 1;
         if (!haveN) break;
         t = tn;
         o1 += plan.nH;
     }
-    // the last tile's decision
-    if (!gv) retire();
     // loads of a tile fetched past the stop may still be landing (in LDS too)
     __builtin_amdgcn_s_waitcnt(0);
     count_stats(P, loaded, rows);
@@ -2154,6 +2093,36 @@ struct BlockRecs {
             for (int j = 0; j < 8; ++j) p[hb][j] = 0.f;
         }
     }
+    // from the tagged 64-bit words of a helper's partial ([head block][word][lane],
+    // `src` at this row's lane 16*hl); false unless every word carries `tag`
+    __device__ __forceinline__ bool load_tagged_part(const unsigned long long* src, const bool (&hv)[HBM],
+                                                     unsigned tag) {
+        unsigned long long w[HBM][kTeamPartW];
+        bool ok = true;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (hv[hb])
+#pragma unroll
+                for (int j = 0; j < kTeamPartW; ++j) w[hb][j] = cld(src + (hb * kTeamPartW + j) * 64);
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (hv[hb])
+#pragma unroll
+                for (int j = 0; j < kTeamPartW; ++j) ok &= (unsigned)(w[hb][j] >> 32) == tag;
+        if (ok) {
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                if (hv[hb]) {
+                    m[hb] = untag(w[hb][0]);
+                    l[hb] = untag(w[hb][1]);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) p[hb][j] = untag(w[hb][2 + j]);
+                    e[hb] = __float_as_int(untag(w[hb][10]));
+                }
+            }
+        }
+        return ok;
+    }
     // from tagged 64-bit words of a record ([word][kTeamRecHeads] apart); false
     // unless every word carries `tag`
     __device__ __forceinline__ bool load_tagged(const unsigned long long* rec, const bool (&hv)[HBM], int hl,
@@ -2291,23 +2260,80 @@ __device__ __forceinline__ int present_prefix(bool have, int kmax) {
 // Decides the group's tiles, block after block, and merges the primary's
 // tiles into acc as they are decided; D holds each head's tiles_used (-1 if
 // undecided: the wait for a tile outlasted kWaitTicks) and error flag.
-template <int HBM>
+template <int HBM, bool HELPERS>
 __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const TeamPlan& plan,
-                                             TeamShared<HBM>* sh, ProbeState<HBM>& D, Part<HBM>& acc) {
+                                             TeamShared<HBM>* sh, ProbeState<HBM>& D, Part<HBM>& acc,
+                                             Part<HBM>& accH) {
     const int lane = lane_id(), i = lane & 15;
     const FoldLanes fl(P);
     const TeamGlobal tg(P, grp);
     const bool glb = plan.nH > 0;
     D.init(fl, P.G);
     acc.clear();
+    accH.clear();
     int relA = 0, relH = 0;
     bool finished = false, gave_up = false;
-    // the decisions, for the helpers
-    auto publish = [&](int decided) {
-        if (!glb) return;
+    // merges the decided helper tiles among f0 + qa .. f0 + qb - 1, in order,
+    // kHB at a time (their words loaded together); false if a partial did not
+    // arrive whole within kWaitTicks
+    constexpr int kHB = 4 / HBM;
+    auto merge_helpers = [&](int f0, int qa, int qb) -> bool {
+        int q = qa;
+        for (;;) {
+            int tl[kHB];
+            int cnt = 0;
+            static_for<0, kHB>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                while (q < qb && (f0 + q) % plan.W < plan.nA) ++q;
+                tl[k] = -1;
+                if (q < qb) {
+                    tl[k] = f0 + q;
+                    ++q;
+                    ++cnt;
+                }
+            });
+            if (cnt == 0) return true;
+            unsigned long long w[kHB][HBM][kTeamStateW];
+            const Deadline dl;
+            for (;;) {
+                bool ok = true;
+                static_for<0, kHB>([&](auto kc) {
+                    constexpr int k = decltype(kc)::value;
+                    if (tl[k] >= 0) {
+                        const int o = (tl[k] / plan.W) * plan.nH + tl[k] % plan.W - plan.nA;
+                        const unsigned tag = rec_tag<kTeamRingG>(P.epoch, o);
+                        const unsigned long long* e = tg.part + (long long)(o & (kTeamRingG - 1)) * tg.slot_words + lane;
 #pragma unroll
-        for (int hb = 0; hb < HBM; ++hb)
-            if (i == 0 && D.hv[hb]) cst(tg.ctl + 4 + hb * 4 + fl.hl, stamp(P.epoch, (unsigned)D.word(hb, decided)));
+                        for (int hb = 0; hb < HBM; ++hb)
+#pragma unroll
+                            for (int j = 0; j < kTeamStateW; ++j) {
+                                w[k][hb][j] = cld(e + (hb * kTeamPartW + j) * 64);
+                                ok &= (unsigned)(w[k][hb][j] >> 32) == tag;
+                            }
+                    }
+                });
+                if (__ballot(!ok) == 0ull) break;
+                if (dl.passed()) return false;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            static_for<0, kHB>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if (tl[k] >= 0) {
+#pragma unroll
+                    for (int hb = 0; hb < HBM; ++hb) {
+                        if (D.hv[hb] && (D.U[hb] < 0 || tl[k] < D.U[hb])) {
+                            float a2[8];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) a2[j] = untag(w[k][hb][2 + j]);
+                            sm_merge_fast(accH.m[hb], accH.l[hb], accH.a[hb], untag(w[k][hb][0]),
+                                          untag(w[k][hb][1]), a2);
+                        }
+                    }
+                    relH = (tl[k] / plan.W) * plan.nH + tl[k] % plan.W - plan.nA + 1;
+                }
+            });
+            if (lane == 0) cst(tg.ctl + 0, stamp(P.epoch, (unsigned)relH));  // their slots may be reused
+        }
     };
     // merges the decided primary tiles among f0 + q0 .. f0 + q1 - 1, in order
     auto merge_primary = [&](int f0, int q0, int q1) {
@@ -2369,8 +2395,9 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                         __atomic_signal_fence(__ATOMIC_SEQ_CST);
                         have = true;
                     }
-                } else {
-                    have = R.load_tagged(tg.rec + (long long)sH * kTeamRecW * kTeamRecHeads, D.hv, fl.hl, rtag);
+                } else if constexpr (HELPERS) {
+                    // the probe record: the words of lane 16*hl of the helper's partial
+                    have = R.load_tagged_part(tg.part + (long long)sH * tg.slot_words + 16 * fl.hl, D.hv, rtag);
                 }
             }
             const int kk = present_prefix(have, kmax);
@@ -2378,9 +2405,14 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                 since = wall_clock64();
                 decide_pass<HBM>(P, D, R, f0, kk, kmax, nt);
                 merge_primary(f0, kdone, kk);
+                if constexpr (HELPERS) {
+                    if (glb && !merge_helpers(f0, kdone, kk)) {
+                        gave_up = true;
+                        break;
+                    }
+                }
                 kdone = kk;
                 finished = D.finished();
-                publish(f0 + kdone);
                 if (finished) {
                     const int ug = D.bound();
                     if (lane == 0) {
@@ -2398,51 +2430,15 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
             __builtin_amdgcn_s_sleep(1);
         }
         if (finished || gave_up) break;
-        // the helpers' record slots of the block may be reused
-        relH += kmax - __builtin_popcountll(__ballot(inr && prim) & 0xffffull);
-        if (glb && lane == 0) cst(tg.ctl + 0, stamp(P.epoch, (unsigned)relH));
     }
     if (gave_up) {
-        if (glb) {
+        // every head reports -2 (a helper's partial may be missing from any of them)
 #pragma unroll
-            for (int hb = 0; hb < HBM; ++hb)
-                if (i == 0 && D.hv[hb] && D.U[hb] < 0)
-                    cst(tg.ctl + 4 + hb * 4 + fl.hl, stamp(P.epoch, (unsigned)kHdGaveUp));
-        }
+        for (int hb = 0; hb < HBM; ++hb) D.U[hb] = D.hv[hb] ? -1 : 0;
         if (lane == 0) {
             lds_st(&sh->bound, 0);
             if (glb) cst(tg.ctl + 1, stamp(P.epoch, 0u));
         }
-    }
-}
-
-// running states of waves w0 .. w1-1, each in its area of the LDS, merged in wave order
-template <int HBM>
-__device__ __forceinline__ void merge_areas(const float* lds, size_t wave_floats, int w0, int w1, Part<HBM>& out) {
-    const int lane = lane_id();
-    out.clear();
-    for (int w = w0; w < w1; ++w) {
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            const float* e = lds + w * wave_floats + (hb * kTeamStateW) * 64 + lane;
-            float a2[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a2[j] = e[64 * (2 + j)];
-            sm_merge(out.m[hb], out.l[hb], out.a[hb], e[0], e[64], a2);
-        }
-    }
-}
-
-template <int HBM>
-__device__ __forceinline__ void store_area(float* mine, const Part<HBM>& ws) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int hb = 0; hb < HBM; ++hb) {
-        float* e = mine + (hb * kTeamStateW) * 64 + lane;
-        e[0] = ws.m[hb];
-        e[64] = ws.l[hb];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[64 * (2 + j)] = ws.a[hb][j];
     }
 }
 
@@ -2471,34 +2467,12 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     }
     const TeamPlan plan(TEAM - 1, P.helpers * TEAM);
     const size_t wave_floats = S::lds_floats(P);
-    const TeamGlobal tg(P, grp);
-    Part<HBM> ws;
     if (team > 0) {
-        // a helper: every wave is a worker; their states, merged in wave
-        // order, go to the primary as tagged words
+        // a helper: every wave is a worker
         if constexpr (!VSKIP) {
             S st;
             st.init(lds + wv * wave_floats);
-            team_helper_worker<S>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st, ws);
-        } else {
-            ws.clear();
-        }
-        __syncthreads();  // every wave is done with its tile buffers
-        store_area<HBM>(lds + wv * wave_floats, ws);
-        __syncthreads();
-        if (wv == 0) {
-            Part<HBM> hs;
-            merge_areas<HBM>(lds, wave_floats, 0, TEAM, hs);
-            const unsigned tag = rec_tag<kTeamRingG>(P.epoch, 0);
-            unsigned long long* dst = tg.hstate + (long long)(team - 1) * HBM * kTeamStateW * 64 + lane;
-#pragma unroll
-            for (int hb = 0; hb < HBM; ++hb) {
-                unsigned long long* e = dst + hb * kTeamStateW * 64;
-                cst(e, tagw(tag, hs.m[hb]));
-                cst(e + 64, tagw(tag, hs.l[hb]));
-#pragma unroll
-                for (int j = 0; j < 8; ++j) cst(e + 64 * (2 + j), tagw(tag, hs.a[hb][j]));
-            }
+            team_helper_worker<S>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st);
         }
         return;
     }
@@ -2521,51 +2495,21 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     // the decider's chain is latency-bound: let its SIMD issue it first
     __builtin_amdgcn_s_setprio(3);
     ProbeState<HBM> D;
-    Part<HBM> tot;
-    team_decider<HBM>(P, grp, nt, plan, sh, D, tot);
+    Part<HBM> tot, toth;
+    team_decider<HBM, !VSKIP>(P, grp, nt, plan, sh, D, tot, toth);  // (the V skip runs without helpers)
     __builtin_amdgcn_s_setprio(0);
-    // then the helpers' states, in helper order
-    bool lost = false;  // a helper's state did not arrive within kWaitTicks
-    const unsigned htag = rec_tag<kTeamRingG>(P.epoch, 0);
-    for (int r = 0; r < P.helpers; ++r) {
-        const unsigned long long* src = tg.hstate + (long long)r * HBM * kTeamStateW * 64 + lane;
-        unsigned long long w[HBM][kTeamStateW];
-        const Deadline dl;
-        for (;;) {
-            bool ok = true;
-#pragma unroll
-            for (int hb = 0; hb < HBM; ++hb)
-#pragma unroll
-                for (int j = 0; j < kTeamStateW; ++j) {
-                    w[hb][j] = cld(src + (hb * kTeamStateW + j) * 64);
-                    ok &= (unsigned)(w[hb][j] >> 32) == htag;
-                }
-            if (__ballot(!ok) == 0ull) break;
-            if (dl.passed()) {
-                lost = true;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(8);
-        }
-        if (lost) break;
-#pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            float a2[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a2[j] = untag(w[hb][2 + j]);
-            sm_merge(tot.m[hb], tot.l[hb], tot.a[hb], untag(w[hb][0]), untag(w[hb][1]), a2);
-        }
-    }
 #pragma unroll
     for (int hb = 0; hb < HBM; ++hb) {
         const int h = hb * 4 + fl.hl;
         if (!D.hv[hb]) continue;
-        if (lost || D.U[hb] < 0) {
+        if (D.U[hb] < 0) {
             float nan8[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) nan8[j] = NAN;
             write_head_out(P, grp, h, fl, nan8, 1.f, 0, -2);
         } else {
+            // the primary's tiles, then the helpers' (each merged in tile order)
+            sm_merge(tot.m[hb], tot.l[hb], tot.a[hb], toth.m[hb], toth.l[hb], toth.a[hb]);
             write_head_out(P, grp, h, fl, tot.a[hb], tot.l[hb], D.err[hb], D.U[hb]);
         }
     }
