@@ -20,7 +20,7 @@ constexpr int kTeamRecHeads = 8;  // heads per record slot (streamed tiles serve
 constexpr int kTeamStateW = 10;   // values per lane per head block of a partial or running state: m, l, 8 dims
 constexpr int kTeamPartW = 11;    // 64-bit words per lane per head block of a helper's tile partial: m, l, 8 dims, error flag
 constexpr int kMaxHelpers = 3;    // helper work-groups per group at most
-constexpr int kTeamCtl = 16;      // control words: [0] helper slots released, [1] bound
+constexpr int kTeamCtl = 16;      // control words: [0] helper slots released, [1] bound, [2] tiles decided
 constexpr int kTeamHelpGroups = 512;  // helpers and the pool engine serve launches of at most this many
                                       // groups (the workspace holds their shared words only then)
 constexpr int kPoolRing = 128;    // pool engine: record slots per group, by tile index (a power of two)

@@ -1795,10 +1795,25 @@ __device__ __forceinline__ int first_stop(unsigned p, int kk, int s0, int patien
 }
 
 // Static assignment of a group's tiles to the workers of its teams.
+// Tiles below S0 go to the primary's workers alone, in turn; from S0 on,
+// over every W = nA + nH consecutive tiles, the first nA go to the primary's
+// workers and the rest to the helpers' (S0 is a multiple of nA, so a primary
+// worker's tiles step by nA below S0 and by W above, and its ordinals among
+// the primary's tiles by nA throughout).
 struct TeamPlan {
-    int nA, nH, W;  // primary workers, helper workers (all helpers), period
-    __device__ TeamPlan(int nA_, int nH_) : nA(nA_), nH(nH_), W(nA_ + nH_) {}
+    int nA, nH, W, S0;  // primary workers, helper workers (all helpers), period, first shared tile
+    __device__ TeamPlan(int nA_, int nH_, int from)
+        : nA(nA_), nH(nH_), W(nA_ + nH_), S0(nH_ > 0 ? (from + nA_ - 1) / nA_ * nA_ : 0) {}
+    __device__ bool primary(int t) const { return t < S0 || (t - S0) % W < nA; }
+    // ordinal of primary tile t among the primary's tiles
+    __device__ int ordA(int t) const { return t < S0 ? t : S0 + (t - S0) / W * nA + (t - S0) % W; }
+    // ordinal of helper tile t among the helpers' tiles
+    __device__ int ordH(int t) const { return (t - S0) / W * nH + (t - S0) % W - nA; }
+    // the primary worker's tile after t
+    __device__ int nextA(int t) const { return t + (t < S0 ? nA : W); }
 };
+constexpr int kTeamHelpFrom = 96;  // helpers take no tile below this one (most groups stop before)
+constexpr int kTeamHelpLead = 16;  // a helper starts once the decided tiles reach its first tile less this
 
 // A group's words in global memory (team kernel with helpers).
 struct TeamGlobal {
@@ -1842,7 +1857,20 @@ __device__ __forceinline__ void team_helper_worker(const Params& P, int grp, int
     if (t >= nt) return;
     // ordinal of tile t among the helpers' tiles; its slot may be written
     // once the decider has released the ordinal a ring before
-    int o1 = first - plan.nA;
+    int o1 = plan.ordH(first);
+    // start once the decided tiles come near this worker's first tile (the
+    // group may stop before: then load nothing)
+    {
+        const Deadline dl;
+        for (;;) {
+            const int dec = uni(unstamp(cld(tg.ctl + 2), P.epoch, 0));
+            const int b0 = uni(unstamp(cld(tg.ctl + 1), P.epoch, nt));
+            if (t >= b0) return;
+            if (dec >= plan.S0 - kTeamHelpLead) break;
+            if (dl.passed()) return;
+            __builtin_amdgcn_s_sleep(16);
+        }
+    }
     // the bound and the released ordinals as last seen, loaded before a
     // tile's loads and taken once those have landed
     int bnd = nt, rel = 0;
@@ -1940,7 +1968,7 @@ __device__ __forceinline__ void team_primary_worker(const Params& P, int grp, in
     S::resolve(P, grp, t, C);
     st.template issue<0>(P, C, 0);
     st.template issue<1>(P, C, 1);
-    int blkN = S::fetch_blocks(P, grp, n, t + plan.W);  // block ids of the next tile
+    int blkN = S::fetch_blocks(P, grp, n, plan.nextA(t));  // block ids of the next tile
     // tiles (and rows) loaded, counted when their loads are issued
     unsigned long long loaded = 1, rows = min(S::T, n - t * S::T), skipped = 0;
     for (;;) {
@@ -1976,14 +2004,14 @@ __device__ __forceinline__ void team_primary_worker(const Params& P, int grp, in
         bnd = uni(lds_ld(&sh->bound));
         if (t >= bnd) break;  // past the group's stop: no head uses the tile
         // the next tile's loads first, then the hand-over of this one
-        const int tn = t + plan.W;
+        const int tn = plan.nextA(t);
         const bool haveN = tn < nt && tn < bnd;
         const int cerr = C.err;
         if (haveN) {
             S::resolve_from(P, grp, n, tn, blkN, C);
             st.template issue<0>(P, C, 0);
             st.template issue<1>(P, C, 1);
-            blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
+            blkN = S::fetch_blocks(P, grp, n, plan.nextA(tn));
             ++loaded;
             rows += min(S::T, n - tn * S::T);
         }
@@ -2276,7 +2304,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
     // merges the decided helper tiles among f0 + qa .. f0 + qb - 1, in order,
     // kHB at a time (their words loaded together); false if a partial did not
     // arrive whole within kWaitTicks
-    constexpr int kHB = 4 / HBM;
+    constexpr int kHB = HBM == 1 ? 4 : 1;
     auto merge_helpers = [&](int f0, int qa, int qb) -> bool {
         int q = qa;
         for (;;) {
@@ -2284,7 +2312,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
             int cnt = 0;
             static_for<0, kHB>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
-                while (q < qb && (f0 + q) % plan.W < plan.nA) ++q;
+                while (q < qb && plan.primary(f0 + q)) ++q;
                 tl[k] = -1;
                 if (q < qb) {
                     tl[k] = f0 + q;
@@ -2300,7 +2328,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                 static_for<0, kHB>([&](auto kc) {
                     constexpr int k = decltype(kc)::value;
                     if (tl[k] >= 0) {
-                        const int o = (tl[k] / plan.W) * plan.nH + tl[k] % plan.W - plan.nA;
+                        const int o = plan.ordH(tl[k]);
                         const unsigned tag = rec_tag<kTeamRingG>(P.epoch, o);
                         const unsigned long long* e = tg.part + (long long)(o & (kTeamRingG - 1)) * tg.slot_words + lane;
 #pragma unroll
@@ -2329,7 +2357,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                                           untag(w[k][hb][1]), a2);
                         }
                     }
-                    relH = (tl[k] / plan.W) * plan.nH + tl[k] % plan.W - plan.nA + 1;
+                    relH = plan.ordH(tl[k]) + 1;
                 }
             });
             if (lane == 0) cst(tg.ctl + 0, stamp(P.epoch, (unsigned)relH));  // their slots may be reused
@@ -2339,9 +2367,9 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
     auto merge_primary = [&](int f0, int q0, int q1) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the slots are read after their tags
         for (int q = q0; q < q1; ++q) {
-            const int tq = f0 + q, kq = tq % plan.W;
-            if (kq >= plan.nA) continue;  // a helper's tile: it merges its own
-            const int oq = (tq / plan.W) * plan.nA + kq;
+            const int tq = f0 + q;
+            if (!plan.primary(tq)) continue;  // a helper's tile: merged from global memory
+            const int oq = plan.ordA(tq);
             const float* e = sh->part[oq & (kTeamSlots - 1)] + lane;
 #pragma unroll
             for (int hb = 0; hb < HBM; ++hb) {
@@ -2363,9 +2391,8 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
         const int kmax = min(kBlock, nt - f0);
         const int t = f0 + i;
         const bool inr = i < kmax;
-        const int kp = t % plan.W, per = t / plan.W;
-        const bool prim = kp < plan.nA;
-        const int ord = prim ? per * plan.nA + kp : per * plan.nH + (kp - plan.nA);
+        const bool prim = plan.primary(t);
+        const int ord = prim ? plan.ordA(t) : plan.ordH(t);
         const int sA = ord & (kTeamSlots - 1), sH = ord & (kTeamRingG - 1);
         const unsigned rtag = rec_tag<kTeamRingG>(P.epoch, ord);
         BlockRecs<HBM> R;
@@ -2413,6 +2440,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                 }
                 kdone = kk;
                 finished = D.finished();
+                if (glb && lane == 0) cst(tg.ctl + 2, stamp(P.epoch, (unsigned)(f0 + kdone)));  // progress, for helpers
                 if (finished) {
                     const int ug = D.bound();
                     if (lane == 0) {
@@ -2465,14 +2493,14 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
         }
         return;
     }
-    const TeamPlan plan(TEAM - 1, P.helpers * TEAM);
+    const TeamPlan plan(TEAM - 1, P.helpers * TEAM, kTeamHelpFrom);
     const size_t wave_floats = S::lds_floats(P);
     if (team > 0) {
         // a helper: every wave is a worker
         if constexpr (!VSKIP) {
             S st;
             st.init(lds + wv * wave_floats);
-            team_helper_worker<S>(P, grp, n, nt, plan.nA + (team - 1) * TEAM + wv, plan, st);
+            team_helper_worker<S>(P, grp, n, nt, plan.S0 + plan.nA + (team - 1) * TEAM + wv, plan, st);
         }
         return;
     }
