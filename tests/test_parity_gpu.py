@@ -178,6 +178,23 @@ def test_helper_work_groups_do_not_change_results(helpers):
     assert (u2[c.B:] == 0).all() and (o2[c.B:] == 0).all()
 
 
+@pytest.mark.parametrize("helpers", [1, 3])
+def test_helpers_join_long_groups(helpers):
+    # helpers take tiles only from tile 96 on: contexts of 256 tiles, thresholds
+    # that never pass (every tile used) and the configuration's own thresholds;
+    # tiles_used as without helpers, outputs to rounding, and against the oracle
+    c = A.config(3, small=True, ctx=16384)
+    dev = to_device(c)
+    for kw in (dict(eps_scale=1e-30, eps_dir=1e-30), dict()):
+        o0, u0 = run_gpu(c, dev, **kw)
+        o1, u1 = run_gpu(c, dev, team_helpers=helpers, **kw)
+        assert np.array_equal(u1, u0)
+        np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-5)
+        r = check_parity(c, o1, u1, **kw)
+        log(f"[parity] config3 ctx16384 helpers={helpers} {kw}: max_abs={r['max_abs']:.3e} "
+            f"mean tiles_used={np.mean(r['tiles_used']):.1f}")
+
+
 def test_helper_work_groups_parity():
     c = A.config(2, sink_mode="sqrt_d")
     _run_and_check(c, "config2 art, 3 helper work-groups per group", team_helpers=3)
