@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-full", action="store_true", help="skip the full-attention comparison")
     ap.add_argument("--flush-mb", type=int, default=1024)
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the context timings of the other workloads (2, 4, 5)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (a known-size "
                          "reference for hardware byte counters) and exit")
@@ -249,7 +251,54 @@ def main():
             "tiles_used_equal": int((used.cpu().numpy() == r.tiles_used).sum()),
             "heads": int(r.tiles_used.size),
             "max_abs_out": float(np.abs(out.cpu().numpy().astype(np.float64) - r.out).max())}
+    if not args.no_others:
+        res["other_workloads"] = other_workloads(args, flush_buf)
     print(json.dumps(res), flush=True)
+
+
+def other_workloads(args, flush_buf, steps=7):
+    """Context, not the metric: ART (library default engine, each workload's
+    own thresholds and V-skip setting) and full attention on workloads 2, 4
+    and 5 at full size, median µs per call, same timing method."""
+    import torch
+    import art_inputs as A
+    import kv_cache_bandwidth_amd as art
+    from tests.gpu_util import to_device
+    stream = torch.cuda.current_stream()
+    res = {}
+    for n in (2, 4, 5):
+        if n == args.config:
+            continue
+        log(f"context timing: workload {n}")
+        case = A.config(n, seed=args.seed)
+        dev = to_device(case)
+
+        def med(**kw):
+            a = dict(block_table=dev["bt"], tile=case.tile, eps_scale=case.eps_scale, eps_dir=case.eps_dir,
+                     patience=case.patience, v_skip_eps=case.v_skip_eps, k_scale=dev["ks"], v_scale=dev["vs"])
+            a.update(kw)
+            out, used = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], **a)
+            ms = []
+            for _ in range(steps + 2):
+                flush_buf.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], out=out, tiles_used=used, **a)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            return statistics.median(ms[2:]) * 1e3, used.cpu().numpy()
+
+        t_art, used = med()
+        t_full, _ = med(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
+        nt = -(-case.ctx_lens // case.tile)
+        entry = {"workload": A.WORKLOADS[n], "art_us": round(t_art, 1), "full_us": round(t_full, 1),
+                 "kv_tiles_skipped_head_level": round(float(1.0 - used.sum() / (nt[:, None] * case.Hq).sum()), 4)}
+        if case.v_skip_eps > 0:
+            entry["art_no_vskip_us"] = round(med(v_skip_eps=0.0)[0], 1)
+        res[f"workload{n}"] = entry
+        del dev
+    return res
 
 
 if __name__ == "__main__":
