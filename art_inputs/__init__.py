@@ -51,6 +51,21 @@ def f16_bits(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
+def sink_first_orders(ctx_lens, tile: int, stride: int | None = None, seed: int = 0) -> np.ndarray:
+    """Random caller-side tile orders: row b lists its ceil(ctx_lens[b] / tile)
+    tiles with tile 0 first and the others shuffled; entries past them are -1."""
+    ctx_lens = np.asarray(ctx_lens)
+    nts = [-(-int(n) // tile) for n in ctx_lens]
+    stride = max([1] + nts) if stride is None else stride
+    rng = np.random.default_rng(seed)
+    perm = np.full((len(nts), stride), -1, np.int32)
+    for b, nt in enumerate(nts):
+        if nt:
+            perm[b, 0] = 0
+            perm[b, 1:nt] = 1 + rng.permutation(nt - 1)
+    return perm
+
+
 def quantize_int8(x):
     """Symmetric per-row int8: scale = fp16(max|x| / 127); code = rint(x/scale).
 
@@ -89,6 +104,8 @@ class Case:
     eps_dir: float = 1e-4
     patience: int = 1
     v_skip_eps: float = 0.0
+    order: int = 0                # tile order: 0 ascending, 1 tile 0 then most recent first, 2 tile_perm
+    tile_perm: np.ndarray | None = None    # int32 [B, stride]: row b's tiles in visiting order (order 2)
     meta: dict = field(default_factory=dict)
 
     @property

@@ -12,9 +12,11 @@
  *
  *   For every batch row b and query head h, one decode query attends over the
  *   first n = ctx_lens[b] cached positions of KV head g = h / (Hq/Hkv).  The
- *   positions are visited in tiles of T consecutive tokens, tile 0 first
- *   (ART summary, section 2.1: tile-wise incremental attention that exposes
- *   the running output).  After each tile the running softmax output
+ *   positions are visited in tiles of T consecutive tokens (ART summary,
+ *   section 2.1: tile-wise incremental attention that exposes the running
+ *   output), tile 0 first and by default in ascending order; section 2.4
+ *   lets the tile sequence be reordered (recency-first, importance-first:
+ *   see visit_tile below).  After each tile the running softmax output
  *   O(t) = acc / l is formed and its first min(8, d) dimensions are the probe
  *   x(t) (section 2.2: a cheap probe vector of the partial output).
  *   From tile 1 on, two changes against the previous probe are measured
@@ -23,10 +25,10 @@
  *       d_dir   = max(0, 1 - cos(x(t), x(t-1)))
  *   A tile passes when both are strictly below their thresholds (section
  *   2.2: both must fall below simultaneously).  After `patience` consecutive
- *   passing tiles (section 2.3) the traversal stops: tiles_used = t + 1 and
- *   the remaining tiles are never visited.  Tile 0 is always evaluated
- *   before any stop (section 2.4, attention sinks).  Without a stop,
- *   tiles_used = ceil(n / T).
+ *   passing tiles (section 2.3) the traversal stops: tiles_used = t + 1 (t
+ *   counts visiting steps) and the remaining tiles are never visited.  Tile
+ *   0 is always evaluated before any stop (section 2.4, attention sinks):
+ *   every order visits it first.  Without a stop, tiles_used = ceil(n / T).
  *
  *   Optional V skip (puntofijo.es: flash attention forms the softmax weights
  *   before touching V, so V rows whose weight is negligible need not be
@@ -43,7 +45,8 @@
  * Pins: see tests/test_oracle.py (brute-force softmax attention, prefix
  * identity, convexity, constant-V closed form, designed probe sequences,
  * paged-layout permutation, GQA replication, int8 dequant identity, V-skip
- * limits and error bound, output awareness).
+ * limits and error bound, output awareness, tile orders against physically
+ * permuted caches and permutation invariance of full attention).
  */
 #include <math.h>
 #include <pthread.h>
@@ -70,6 +73,9 @@ typedef struct {
     int32_t *tiles_used;
     double *trace;
     int trace_tiles;
+    int order;             /* tile order: see visit_tile */
+    const int32_t *perm;   /* order 2: [B][perm_stride] */
+    int perm_stride;
     int next_item; /* work counter, protected by mu */
     pthread_mutex_t mu;
 } job_t;
@@ -103,6 +109,24 @@ static long row_index(const job_t *J, int b, int g, int j) {
     int blk = J->block_table[(long)b * J->max_blocks_per_seq + j / J->block_size];
     if (blk < 0 || blk >= J->num_blocks) return -1;
     return ((long)blk * J->Hkv + g) * J->block_size + (j % J->block_size);
+}
+
+/* Tile visited at step t (0-based) of row b, which has nt tiles.  Section
+   2.4 of the ART summary lets the sequence of tiles be reordered, e.g.
+   recency-first or importance-first, with no approximation error since
+   attention does not depend on the order, and has block 0 (the attention
+   sink) evaluated before any termination.  Orders:
+     0  ascending: 0, 1, ..., nt-1
+     1  the sink, then the most recent first: 0, nt-1, nt-2, ..., 1
+     2  the caller's list perm[b][0..nt-1]: step 0 must name tile 0 and
+        every later step a tile in 1..nt-1
+   Returns -1 for a list entry that breaks those rules. */
+static int visit_tile(const job_t *J, int b, int nt, int t) {
+    if (J->order == 0) return t;
+    if (J->order == 1) return t == 0 ? 0 : nt - t;
+    const int e = J->perm[(long)b * J->perm_stride + t];
+    if (t == 0) return e == 0 ? 0 : -1;
+    return (e >= 1 && e < nt) ? e : -1;
 }
 
 static void load_row(const job_t *J, const void *base, const uint16_t *scale, long row, double *dst) {
@@ -150,7 +174,9 @@ static int run_item(job_t *J, int b, int h, double *scratch) {
     int streak = 0, U = nt;
 
     for (int t = 0; t < nt; ++t) {
-        const int j0 = t * T, j1 = (j0 + T < n) ? j0 + T : n;
+        const int pt = visit_tile(J, b, nt, t); /* the tile of step t */
+        if (pt < 0) return -1;
+        const int j0 = pt * T, j1 = (j0 + T < n) ? j0 + T : n;
         /* scores of the tile, s_j = q.k_j / sqrt(d) */
         double tmax = -INFINITY;
         for (int j = j0; j < j1; ++j) {
@@ -229,7 +255,8 @@ static void *worker(void *arg) {
 }
 
 /* Returns 0 on success, negative on a malformed argument, -100 if a block id
-   read from the table lies outside [0, num_blocks). */
+   read from the table lies outside [0, num_blocks) or an entry of a caller's
+   tile order breaks the rules of visit_tile. */
 int art_oracle_decode(int B, int Hq, int Hkv, int d, int q_dtype, int kv_dtype,
                       int block_size, int max_blocks_per_seq, int max_ctx, int num_blocks,
                       const void *q, const void *k, const void *v,
@@ -237,16 +264,20 @@ int art_oracle_decode(int B, int Hq, int Hkv, int d, int q_dtype, int kv_dtype,
                       const int32_t *block_table, const int32_t *ctx_lens,
                       int tile, double eps_scale, double eps_dir, int patience, double v_skip_eps,
                       double *out, int32_t *tiles_used,
-                      double *trace, int trace_tiles, int nthreads) {
+                      double *trace, int trace_tiles, int nthreads,
+                      int order, const int32_t *perm, int perm_stride) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return -2;
     if (!q || !k || !v || !ctx_lens || !out || !tiles_used) return -1;
     if (q_dtype != ODT_F32 && q_dtype != ODT_BF16) return -3;
     if (kv_dtype < ODT_F32 || kv_dtype > ODT_I8) return -3;
     if (kv_dtype == ODT_I8 && (!k_scale || !v_scale)) return -1;
     if (tile <= 0 || patience < 1) return -5;
+    if (order < 0 || order > 2) return -5;
+    if (order == 2 && !perm) return -1;
     for (int b = 0; b < B; ++b) {
         long cap = block_size ? (long)max_blocks_per_seq * block_size : max_ctx;
         if (ctx_lens[b] < 0 || ctx_lens[b] > cap) return -2;
+        if (order == 2 && (ctx_lens[b] + tile - 1) / tile > perm_stride) return -2;
     }
     if (block_size && !block_table) return -1;
     job_t J;
@@ -257,6 +288,7 @@ int art_oracle_decode(int B, int Hq, int Hkv, int d, int q_dtype, int kv_dtype,
     J.block_table = block_table; J.ctx_lens = ctx_lens; J.tile = tile; J.patience = patience;
     J.eps_scale = eps_scale; J.eps_dir = eps_dir; J.v_skip_eps = v_skip_eps;
     J.out = out; J.tiles_used = tiles_used; J.trace = trace; J.trace_tiles = trace ? trace_tiles : 0;
+    J.order = order; J.perm = perm; J.perm_stride = perm_stride;
     pthread_mutex_init(&J.mu, NULL);
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;

@@ -61,3 +61,17 @@ def attention(case, b: int, h: int, n: int) -> np.ndarray:
     G = case.Hq // case.Hkv
     V = logical_rows(case, "v", b, h // G, n)
     return attention_weights(case, b, h, n) @ V
+
+
+def attention_at(case, b: int, h: int, positions) -> np.ndarray:
+    """Softmax attention over an explicit set of positions (float64 [d])."""
+    positions = np.asarray(sorted(positions), dtype=np.int64)
+    if positions.size == 0:
+        return np.zeros(case.d)
+    n = int(positions.max()) + 1
+    G = case.Hq // case.Hkv
+    K = logical_rows(case, "k", b, h // G, n)[positions]
+    V = logical_rows(case, "v", b, h // G, n)[positions]
+    s = K @ query(case, b, h) / np.sqrt(case.d)
+    w = np.exp(s - s.max())
+    return (w / w.sum()) @ V

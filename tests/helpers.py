@@ -44,7 +44,8 @@ def to_paged(case: Case, block_size: int, seed: int, extra_blocks: int = 0) -> C
                 k_scale=None if case.k_scale is None else pack(case.k_scale, ()),
                 v_scale=None if case.v_scale is None else pack(case.v_scale, ()),
                 tile=case.tile, eps_scale=case.eps_scale, eps_dir=case.eps_dir,
-                patience=case.patience, v_skip_eps=case.v_skip_eps, meta=dict(case.meta))
+                patience=case.patience, v_skip_eps=case.v_skip_eps, order=case.order,
+                tile_perm=case.tile_perm, meta=dict(case.meta))
 
 
 def designed_case(fx, seed=0):
@@ -71,6 +72,7 @@ def run_oracle(case, **kw):
     args = dict(tile=case.tile, eps_scale=case.eps_scale, eps_dir=case.eps_dir,
                 patience=case.patience, v_skip_eps=case.v_skip_eps,
                 block_table=case.block_table, block_size=case.block_size,
-                k_scale=case.k_scale, v_scale=case.v_scale)
+                k_scale=case.k_scale, v_scale=case.v_scale, order=case.order,
+                tile_perm=case.tile_perm)
     args.update(kw)
     return oracle.decode(case.q, case.k, case.v, case.ctx_lens, **args)

@@ -318,3 +318,156 @@ def test_vskip_uses_running_max_through_the_tile():
     assert w[4] == 0.0          # top of tile 1, but exp(-15 - 5) < 1e-6
     assert w[0] > 0.0           # top of tile 0 when it was read
     assert w[8] > 0.0
+
+
+# ---------------------------------------------------------------- P-order: tile orders (section 2.4)
+#
+# Section 2.4 of the ART summary lets the tile sequence be reordered
+# (recency-first, importance-first) with no approximation error, block 0 (the
+# attention sink) being evaluated first.  A tile order is an index remap: ART
+# over a cache in order pi must equal ART in ascending order over the cache
+# whose tile s physically holds tile pi(s).
+
+def visiting_order(order, nt, perm_row=None):
+    if order == 0:
+        return list(range(nt))
+    if order == 1:
+        return [0] + list(range(nt - 1, 0, -1))
+    return [int(x) for x in perm_row[:nt]]
+
+
+def permuted_tiles(case, orders):
+    """Contiguous case whose row b holds, as tile s, the tile orders[b][s] of `case`."""
+    import copy
+    T = case.tile
+    c = copy.copy(case)
+    c.k = case.k.copy()
+    c.v = case.v.copy()
+    for b, seq in enumerate(orders):
+        for s, src in enumerate(seq):
+            c.k[b, :, s * T:(s + 1) * T] = case.k[b, :, src * T:(src + 1) * T]
+            c.v[b, :, s * T:(s + 1) * T] = case.v[b, :, src * T:(src + 1) * T]
+    c.order, c.tile_perm = 0, None
+    return c
+
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+def test_order_full_mode_is_plain_attention(order, kv):
+    c = rand_case(B=3, Hq=6, Hkv=2, d=32, n=200, seed=41 + order, kv=kv, qd=kv, tile=16,
+                  eps_scale=0.0, eps_dir=0.0)
+    c.ctx_lens[:] = [200, 17, 129]
+    c.order = order
+    c.tile_perm = A.sink_first_orders(c.ctx_lens, 16, seed=5) if order == 2 else None
+    r = run_oracle(c)
+    for b in range(3):
+        n = int(c.ctx_lens[b])
+        assert (r.tiles_used[b] == ntiles(n, 16)).all()
+        for h in range(6):
+            assert np.allclose(r.out[b, h], BF.attention(c, b, h, n), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("seed", range(4))
+def test_order_equals_physically_permuted_cache(order, seed):
+    T = 8
+    c = rand_case(B=3, Hq=4, Hkv=2, d=16, n=320, seed=200 + seed, tile=T,
+                  eps_scale=0.05, eps_dir=0.02, patience=1 + seed % 2)
+    c.ctx_lens[:] = [320, 160 - 8 * seed, 24]
+    c.order = order
+    c.tile_perm = A.sink_first_orders(c.ctx_lens, T, stride=50, seed=seed) if order == 2 else None
+    seqs = [visiting_order(order, ntiles(int(n), T), None if c.tile_perm is None else c.tile_perm[b])
+            for b, n in enumerate(c.ctx_lens)]
+    r = run_oracle(c, trace=True)
+    ref = run_oracle(permuted_tiles(c, seqs), trace=True)
+    assert np.array_equal(r.tiles_used, ref.tiles_used)
+    assert np.array_equal(r.out, ref.out)
+    assert np.array_equal(np.isnan(r.trace), np.isnan(ref.trace))
+    assert np.array_equal(np.nan_to_num(r.trace), np.nan_to_num(ref.trace))
+    U = r.tiles_used[0]
+    assert (U < ntiles(320, T)).any() and (U > 2).any()  # stops, and not all at once
+    # the order changes the outcome (else this would not test the remap)
+    asc = run_oracle(c, order=0, tile_perm=None)
+    assert not np.array_equal(asc.tiles_used, r.tiles_used)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_recent_first_ragged_tile_and_stop(seed):
+    # the partial last tile is visited second; the output of a stopped head is
+    # attention over the tiles it visited
+    T = 8
+    c = rand_case(B=2, Hq=4, Hkv=2, d=16, n=300, seed=300 + seed, tile=T,
+                  eps_scale=0.05, eps_dir=0.02, patience=1 + seed % 2)
+    c.ctx_lens[:] = [300, 211 - 9 * seed]
+    c.order = 1
+    r = run_oracle(c)
+    stopped = 0
+    for b in range(2):
+        n = int(c.ctx_lens[b])
+        nt = ntiles(n, T)
+        seq = visiting_order(1, nt)
+        for h in range(4):
+            U = int(r.tiles_used[b, h])
+            stopped += U < nt
+            pos = [j for s in seq[:U] for j in range(s * T, min(n, (s + 1) * T))]
+            assert np.allclose(r.out[b, h], BF.attention_at(c, b, h, pos), rtol=1e-12, atol=1e-13)
+    assert stopped > 0
+
+
+def test_recent_first_stops_early_where_recent_tokens_dominate():
+    # scores high on the last tile only: ascending order meets the dominant
+    # tile last and runs to the end; sink + recency-first meets it second and
+    # stops right after, with an output close to full attention
+    T, nt, d = 16, 40, 32
+    n = T * nt
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 1, d))
+    K = rng.standard_normal((1, 1, n, d)) * 0.05
+    K[0, 0, -T:] += 9.0 * q[0, 0] / np.linalg.norm(q[0, 0])
+    V = rng.standard_normal((1, 1, n, d))
+    c = contiguous_case(q, K, V, tile=T, eps_scale=1e-3, eps_dir=1e-4, patience=2)
+    asc = run_oracle(c)
+    c.order = 1
+    rec = run_oracle(c)
+    full = BF.attention(c, 0, 0, n)
+    assert int(asc.tiles_used[0, 0]) == nt
+    assert int(rec.tiles_used[0, 0]) <= 5
+    assert np.abs(rec.out[0, 0] - full).max() < 1e-2
+
+
+def test_invalid_tile_orders_rejected():
+    T = 16
+    c = rand_case(B=2, Hq=2, Hkv=1, d=16, n=160, seed=17, tile=T, eps_scale=0.0, eps_dir=0.0)
+    c.order = 2
+    good = A.sink_first_orders(c.ctx_lens, T, seed=1)
+    c.tile_perm = good
+    run_oracle(c)
+    for b, s, val in [(0, 0, 3), (1, 4, 0), (1, 9, 10), (0, 2, -1)]:
+        bad = good.copy()
+        bad[b, s] = val
+        c.tile_perm = bad
+        with pytest.raises(ValueError):
+            run_oracle(c)
+    c.tile_perm = good[:, :5]  # shorter than a row's tiles
+    with pytest.raises(ValueError):
+        run_oracle(c)
+
+
+def test_order_entries_past_the_stop_are_not_read():
+    # constant V: the probe is the same after every tile, so every head stops
+    # after tile 1 (patience 1) and later entries are never visited
+    T, nt, d = 16, 10, 16
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 2, d))
+    K = rng.standard_normal((1, 1, T * nt, d))
+    V = np.repeat(rng.standard_normal((1, 1, 1, d)), T * nt, axis=2)
+    c = contiguous_case(q, K, V, tile=T, eps_scale=1e-3, eps_dir=1e-4, patience=1)
+    c.order = 2
+    perm = A.sink_first_orders(c.ctx_lens, T, seed=2)
+    perm[0, 2:] = 99
+    c.tile_perm = perm
+    r = run_oracle(c)
+    assert (r.tiles_used == 2).all()
+    perm[0, 1] = 99
+    with pytest.raises(ValueError):
+        run_oracle(c)

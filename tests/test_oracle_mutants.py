@@ -44,8 +44,14 @@ MUTANTS = {
                              "if (J->v_skip_eps > 0.0 && exp(s[j - j0] - tmax) < J->v_skip_eps) continue;"),
     "paged_offset_wrong": ("return ((long)blk * J->Hkv + g) * J->block_size + (j % J->block_size);",
                            "return ((long)blk * J->Hkv + g) * J->block_size + (j / J->block_size) % J->block_size;"),
-    "last_tile_not_masked": ("const int j0 = t * T, j1 = (j0 + T < n) ? j0 + T : n;",
-                             "const int j0 = t * T, j1 = (j0 + T < n) ? j0 + T : ((nt * T <= J->max_ctx) ? nt * T : n);"),
+    "last_tile_not_masked": ("const int j0 = pt * T, j1 = (j0 + T < n) ? j0 + T : n;",
+                             "const int j0 = pt * T, j1 = (j0 + T < n) ? j0 + T : ((nt * T <= J->max_ctx) ? nt * T : n);"),
+    "order_ignored": ("if (J->order == 0) return t;", "return t;"),
+    "recent_order_shifted": ("return t == 0 ? 0 : nt - t;", "return t == 0 ? 0 : nt - 1 - t + (t == nt - 1);"),
+    "recent_order_oldest_first": ("return t == 0 ? 0 : nt - t;", "return t;"),
+    "perm_row_ignored": ("J->perm[(long)b * J->perm_stride + t]", "J->perm[t]"),
+    "perm_sink_not_forced": ("if (t == 0) return e == 0 ? 0 : -1;", "if (t == 0) return (e >= 0 && e < nt) ? e : -1;"),
+    "positions_from_step": ("const int j0 = pt * T, j1", "const int j0 = t * T, j1"),
     "int8_scale_ignored": ("double s = widen_f16(scale[row]);", "double s = 1.0;"),
     "direction_not_clamped_half": ("dd = 1.0 - dot / (xn * prev_norm);", "dd = 0.5 * (1.0 - dot / (xn * prev_norm));"),
 }
@@ -69,6 +75,12 @@ PINS = [
     P.test_vskip_error_bound,
     P.test_vskip_uses_running_max_through_the_tile,
     P.test_low_weight_large_value_row_delays_the_stop,
+    lambda: [P.test_order_full_mode_is_plain_attention(o, "f32") for o in (1, 2)],
+    lambda: [P.test_order_equals_physically_permuted_cache(o, s) for o in (1, 2) for s in range(2)],
+    lambda: [P.test_recent_first_ragged_tile_and_stop(s) for s in range(2)],
+    P.test_recent_first_stops_early_where_recent_tokens_dominate,
+    P.test_invalid_tile_orders_rejected,
+    P.test_order_entries_past_the_stop_are_not_read,
 ]
 
 
@@ -98,7 +110,7 @@ def test_mutant_is_caught(name, monkeypatch):
         for pin in PINS:
             try:
                 pin()
-            except (AssertionError, ValueError):
+            except (AssertionError, ValueError, pytest.fail.Exception):
                 caught.append(getattr(pin, "__name__", "lambda"))
         assert caught, f"no pin detects mutant {name}"
     finally:
