@@ -252,8 +252,43 @@ def main():
             "heads": int(r.tiles_used.size),
             "max_abs_out": float(np.abs(out.cpu().numpy().astype(np.float64) - r.out).max())}
     if not args.no_others:
+        res["tile_orders"] = tile_orders(case, dev, flush_buf)
         res["other_workloads"] = other_workloads(args, flush_buf)
     print(json.dumps(res), flush=True)
+
+
+def tile_orders(case, dev, flush_buf, steps=7):
+    """Context, not the metric: the same workload and thresholds with the tiles
+    visited sink first then most recent first, and in a random sink-first list
+    (median us per call, head-level share of tiles skipped)."""
+    import torch
+    import art_inputs as A
+    import kv_cache_bandwidth_amd as art
+    stream = torch.cuda.current_stream()
+    stride = -(-case.max_ctx // case.tile)
+    perm = torch.from_numpy(A.sink_first_orders(case.ctx_lens, case.tile, stride=stride, seed=1)).cuda()
+    nt = -(-case.ctx_lens // case.tile)
+    res = {}
+    for name, kw in (("recent_first", dict(tile_order=art.ORDER_RECENT)),
+                     ("random_list", dict(tile_order=art.ORDER_LIST, tile_perm=perm))):
+        log(f"context timing: tile order {name}")
+        a = dict(block_table=dev["bt"], tile=case.tile, eps_scale=case.eps_scale, eps_dir=case.eps_dir,
+                 patience=case.patience, v_skip_eps=case.v_skip_eps, k_scale=dev["ks"], v_scale=dev["vs"],
+                 **kw)
+        out, used = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], **a)
+        ms = []
+        for _ in range(steps + 2):
+            flush_buf.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], out=out, tiles_used=used, **a)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        u = used.cpu().numpy()
+        res[name] = {"art_us": round(statistics.median(ms[2:]) * 1e3, 1),
+                     "kv_tiles_skipped_head_level": round(float(1.0 - u.sum() / (nt[:, None] * case.Hq).sum()), 4)}
+    return res
 
 
 def other_workloads(args, flush_buf, steps=7):

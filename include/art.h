@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define ART_ABI_VERSION 3
+#define ART_ABI_VERSION 4
 
 typedef enum {
     ART_OK = 0,
@@ -54,6 +54,20 @@ typedef enum {
                                resident work-group                                     */
     ART_ENGINE_SHARED = 3   /* work-sharing engine: max_workers waves claim tiles      */
 } art_engine;
+
+/* Order in which a row's tiles are visited (ART summary, section 2.4: the tile
+ * sequence may be reordered, e.g. recency- or importance-first, without
+ * approximation error; block 0, the attention sink, is evaluated first).  The
+ * probe sequence, the patience streak, tiles_used and the V-skip running max
+ * follow the visiting steps; every order visits tile 0 first. */
+typedef enum {
+    ART_ORDER_ASCENDING = 0,  /* tiles 0, 1, ..., n_t - 1                                */
+    ART_ORDER_RECENT = 1,     /* tile 0, then the most recent first: n_t - 1, n_t - 2, ..., 1 */
+    ART_ORDER_LIST = 2        /* the caller's tile_perm: row b's step s visits tile
+                                 tile_perm[b][s]; step 0 must name tile 0 and steps
+                                 1..n_t-1 tiles in 1..n_t-1 (a permutation of them;
+                                 repeats are not detected)                          */
+} art_order;
 
 /*
  * Shape and options of one call.  Layouts are row-major:
@@ -101,14 +115,20 @@ typedef struct {
                                     Used only where every work-group of the launch can
                                     be resident at once; results do not depend on it  */
     int32_t engine;              /* art_engine; ART_ENGINE_AUTO = 0                    */
+    int32_t tile_order;          /* art_order; ART_ORDER_ASCENDING = 0                 */
+    int32_t tile_perm_stride;    /* ART_ORDER_LIST: row stride of tile_perm, at least
+                                    ceil(row capacity / tile)                         */
+    const int32_t* tile_perm;    /* ART_ORDER_LIST: device int32 [batch][tile_perm_stride],
+                                    caller-owned, read only; else ignored            */
 } art_desc;
 
 /*
  * art_decode_attention -- ART-terminated decode attention over a KV cache.
  *
  * For every (b, h): the query attends over positions 0..ctx_lens[b]-1 of its
- * KV head in tiles of `tile` tokens, tile 0 first, with an online softmax
- * (ART summary, section 2.1).  After each tile t the probe is dims 0..7 of the
+ * KV head in tiles of `tile` tokens, tile 0 first and then in desc->tile_order,
+ * with an online softmax (ART summary, section 2.1).  After each visiting step
+ * t the probe is dims 0..7 of the
  * normalised running output; from t = 1 on, d_scale = | |x_t| - |x_{t-1}| | /
  * |x_{t-1}| and d_dir = 1 - cos(x_t, x_{t-1}) (section 2.2).  A tile passes
  * when d_scale < eps_scale and d_dir < eps_dir; after `patience` consecutive
@@ -122,8 +142,9 @@ typedef struct {
  * ctx_lens[b] = 0 gives out = 0 and tiles_used = 0.
  *
  * Errors detected on the device, per batch row: ctx_lens[b] < 0 or larger than
- * the cache row capacity, or a block id outside [0, num_blocks) inside a
- * visited tile -> tiles_used = -1 and out = NaN for the affected heads; no
+ * the cache row capacity, a block id outside [0, num_blocks) inside a
+ * visited tile, or a tile_perm entry at a visited step that breaks the rules
+ * of ART_ORDER_LIST -> tiles_used = -1 and out = NaN for the affected heads; no
  * out-of-range address is ever dereferenced.  Should a wait between the
  * cooperating waves of a call outlast half a second (the GPU was shared with
  * a starving workload), the heads not yet decided report tiles_used = -2 and

@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libart.so")
 
 ART_F32, ART_BF16, ART_I8 = 0, 1, 2
+ORDER_ASCENDING, ORDER_RECENT, ORDER_LIST = 0, 1, 2
 
 STATUS = {0: "ART_OK", -1: "ART_E_NULL", -2: "ART_E_SHAPE", -3: "ART_E_DTYPE", -4: "ART_E_TILE",
           -5: "ART_E_PARAM", -6: "ART_E_WORKSPACE", -7: "ART_E_HIP"}
@@ -51,13 +52,16 @@ class ArtDesc(ctypes.Structure):
         ("max_workers", ctypes.c_int32),
         ("team_helpers", ctypes.c_int32),
         ("engine", ctypes.c_int32),
+        ("tile_order", ctypes.c_int32),
+        ("tile_perm_stride", ctypes.c_int32),
+        ("tile_perm", ctypes.c_void_p),
     ]
 
 
 _lib = None
 
 
-ABI_VERSION = 3  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
+ABI_VERSION = 4  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
 
 
 def load():
@@ -99,11 +103,11 @@ def _check(rc: int):
 def make_desc(*, batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, block_size=0,
               max_blocks_per_seq=0, num_blocks=0, max_ctx=0, patience=1, v_skip_eps=0.0,
               k_scale=0, v_scale=0, workspace=0, workspace_bytes=0, stats=0, max_workers=0,
-              team_helpers=0, engine=0) -> ArtDesc:
+              team_helpers=0, engine=0, tile_order=0, tile_perm_stride=0, tile_perm=0) -> ArtDesc:
     return ArtDesc(batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, block_size,
                    max_blocks_per_seq, num_blocks, max_ctx, patience, v_skip_eps, k_scale or None,
                    v_scale or None, workspace or None, workspace_bytes, stats or None, max_workers,
-                   team_helpers, engine)
+                   team_helpers, engine, tile_order, tile_perm_stride, tile_perm or None)
 
 
 def workspace_bytes(desc: ArtDesc, tile: int) -> int:
@@ -122,7 +126,7 @@ def _dtype_code(t):
 def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64, eps_scale=1e-3,
                      eps_dir=1e-4, patience=1, v_skip_eps=0.0, k_scale=None, v_scale=None,
                      out=None, tiles_used=None, workspace=None, stats=None, max_workers=0, team_helpers=0,
-                     engine=0,
+                     engine=0, tile_order=0, tile_perm=None,
                      stream=None):
     """ART decode attention on device tensors; returns (out fp32, tiles_used int32).
 
@@ -130,6 +134,8 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
     block_table is given, else contiguous [B, Hkv, max_ctx, d]; fp32/bf16/int8
     (int8 needs k_scale/v_scale fp16 shaped like the cache without d).
     ctx_lens int32 [B]; block_table int32 [B, max_blocks_per_seq].
+    tile_order: ORDER_ASCENDING, ORDER_RECENT or ORDER_LIST (then tile_perm is
+    an int32 device tensor [B, stride], row b listing its tiles in visiting order).
     """
     import torch
     lib = load()
@@ -142,7 +148,8 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
         _, Hkv, max_ctx, _ = k_cache.shape
         nb = bs = mbps = 0
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("ctx_lens", ctx_lens),
-                    ("block_table", block_table), ("k_scale", k_scale), ("v_scale", v_scale)):
+                    ("block_table", block_table), ("k_scale", k_scale), ("v_scale", v_scale),
+                    ("tile_perm", tile_perm)):
         if t is not None and not (t.is_cuda and t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous device tensor")
     desc = make_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
@@ -152,7 +159,9 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
                      k_scale=k_scale.data_ptr() if k_scale is not None else 0,
                      v_scale=v_scale.data_ptr() if v_scale is not None else 0,
                      stats=stats.data_ptr() if stats is not None else 0, max_workers=max_workers,
-                     team_helpers=team_helpers, engine=engine)
+                     team_helpers=team_helpers, engine=engine, tile_order=tile_order,
+                     tile_perm_stride=tile_perm.shape[1] if tile_perm is not None else 0,
+                     tile_perm=tile_perm.data_ptr() if tile_perm is not None else 0)
     need = workspace_bytes(desc, tile)
     if need == 0:
         _check(validate(desc, tile, eps_scale, eps_dir))

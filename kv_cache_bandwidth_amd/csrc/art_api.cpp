@@ -81,6 +81,14 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
         return fail(ART_E_PARAM, "team_helpers %d not in 0..%d", d->team_helpers, art::kMaxHelpers);
     if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_SHARED)
         return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_SHARED);
+    if (d->tile_order < ART_ORDER_ASCENDING || d->tile_order > ART_ORDER_LIST)
+        return fail(ART_E_PARAM, "tile_order %d not in %d..%d", d->tile_order, ART_ORDER_ASCENDING, ART_ORDER_LIST);
+    if (d->tile_order == ART_ORDER_LIST) {
+        if (!d->tile_perm) return fail(ART_E_NULL, "ART_ORDER_LIST needs tile_perm");
+        const long long need = (cap + tile - 1) / tile;
+        if (d->tile_perm_stride < need)
+            return fail(ART_E_SHAPE, "tile_perm_stride %d < %lld tiles a row can hold", d->tile_perm_stride, need);
+    }
 
     p = art::Params{};
     p.B = d->batch; p.Hq = d->num_q_heads; p.Hkv = d->num_kv_heads; p.G = G; p.D = d->head_dim; p.T = tile;
@@ -91,6 +99,9 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     p.nt_max = (int)((cap + tile - 1) / tile);
     p.NG = d->batch * d->num_kv_heads;
     p.patience = d->patience;
+    p.order = d->tile_order;
+    p.tile_perm = d->tile_order == ART_ORDER_LIST ? d->tile_perm : nullptr;
+    p.perm_stride = d->tile_order == ART_ORDER_LIST ? d->tile_perm_stride : 0;
     p.art = eps_scale > 0.f && eps_dir > 0.f;
     p.vskip = d->v_skip_eps > 0.f;
     p.eps_scale = eps_scale; p.eps_dir = eps_dir; p.v_skip_eps = d->v_skip_eps;
@@ -124,6 +135,8 @@ Layout workspace_layout(const Params& p) {
     const size_t NT = NG <= (size_t)kTeamHelpGroups ? NG : 0;  // groups that helpers may serve
     L.team_ring = o; o = align256(o + NT * group_words(p.G) * sizeof(unsigned long long));
     L.team_ctl = o; o = align256(o + NT * kTeamCtl * sizeof(unsigned long long));
+    const size_t NS = p.order == ART_ORDER_LIST ? (size_t)p.B * p.nt_max : 0;  // step-table records
+    L.steps = o; o = align256(o + NS * kStepW * sizeof(int));
     L.total = o;
     return L;
 }
@@ -208,6 +221,7 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     p.partials = reinterpret_cast<float*>(ws + L.partials);
     p.team_ring = reinterpret_cast<unsigned long long*>(ws + L.team_ring);
     p.team_ctl = reinterpret_cast<unsigned long long*>(ws + L.team_ctl);
+    p.steps = reinterpret_cast<int*>(ws + L.steps);
     p.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
     if (p.epoch == 0) p.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;  // 0 never stamps
     const int rc = (p.art || p.vskip) ? art::launch_art(p, stream) : art::launch_full(p, stream);

@@ -29,6 +29,8 @@ constexpr int kPoolCtl = 16;      // pool engine control words: [0] tiles releas
                                   // [3] workers joined, [4..11] per-head decision, [12] workers active
 constexpr unsigned long long kWaitTicks = 50000000ull;  // 0.5 s of the 100 MHz device clock:
                                                       // longest any wait may last before the kernel gives up
+constexpr int kStepPages = 4;     // 16-token pages of a 64-token tile (entries of a step-table record)
+constexpr int kStepW = 8;         // ints per step-table record: kStepPages block ids, the tile, padding
 constexpr int kSlotHeader = 48;   // floats before the accumulator block of a partial:
                                   // [0,16) tile max per head, [16,32) tile sum per head,
                                   // [32] error flag (as int), [33] V rows kept (as int)
@@ -54,6 +56,9 @@ struct Params {
     int NG;             // B * Hkv groups
     // method
     int patience;
+    int order;          // art_order: tile i of a row's visiting sequence is tile_at(i)
+    const int* tile_perm;  // ART_ORDER_LIST: [B][perm_stride]
+    int perm_stride;
     int art;            // stop rule active
     int vskip;          // V-row skip active
     float eps_scale, eps_dir, v_skip_eps, inv_sqrt_d;
@@ -81,6 +86,7 @@ struct Params {
                                     // [kPoolRing][kTeamRecW][kTeamRecHeads], then worker states
                                     // [kPoolContrib][HB][kTeamStateW][64]; (tag << 32) | value bits
     unsigned long long* team_ctl;   // [NG][kTeamCtl]: (epoch << 32) | value
+    int* steps;         // ART_ORDER_LIST: [B][nt_max][kStepW] step table (see art_steps_kernel)
     unsigned epoch;     // distinct per call: stale team words of earlier calls never match
     int helpers;        // helper work-groups per group (team kernel)
     int pool_cap;       // pool kernel: workers that may join one group (<= kPoolContrib)
@@ -103,7 +109,7 @@ constexpr size_t group_words(int G) { return team_words(G) > pool_words(G) ? tea
 
 // Workspace layout for a Params (offsets in bytes, all 256-byte aligned).
 struct Layout {
-    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, team_ring, team_ctl, total;
+    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, team_ring, team_ctl, steps, total;
 };
 Layout workspace_layout(const Params& p);
 

@@ -208,6 +208,21 @@ __device__ __forceinline__ long long row_index(const Params& P, int b, int g, in
     return ((long long)blk * P.Hkv + g) * P.block_size + (j % P.block_size);
 }
 
+// The tile visited at step t of row b, which has nt tiles.  The tile sequence
+// may be reordered (ART summary, section 2.4: recency- or importance-first;
+// the result does not depend on the order, and block 0, the attention sink,
+// is evaluated first): ascending; tile 0 then the most recent first; or the
+// caller's list, whose step 0 must name tile 0 and later steps tiles
+// 1..nt-1 -- any other entry gives -1 and the tile reports an error.  Steps
+// past the row's tiles map to themselves (no position of them exists).
+__device__ __forceinline__ int tile_at(const Params& P, int b, int nt, int t) {
+    if (P.order == ART_ORDER_ASCENDING || t < 0 || t >= nt) return t;
+    if (P.order == ART_ORDER_RECENT) return t == 0 ? 0 : nt - t;
+    const int e = P.tile_perm[(long long)b * P.perm_stride + t];
+    if (t == 0) return e == 0 ? 0 : -1;
+    return (e >= 1 && e < nt) ? e : -1;
+}
+
 // ------------------------------------------------------------------ tile output
 //
 // "Fold mapping", shared by every consumer of partials: lane l serves head
@@ -270,15 +285,16 @@ struct GenericTile {
     __device__ __forceinline__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
         const int lane = lane_id();
         const int G = P.G, T = P.T;
-        const int j0 = t * T;
+        const int pt = tile_at(P, b, (n + T - 1) / T, t);  // the tile of step t
+        const int j0 = pt * T;
         float s[2][kMaxG];
         bool valid[2];
-        int bad = 0;
+        int bad = pt < 0;
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
             const int jj = ps * 64 + lane;
             const int j = j0 + jj;
-            valid[ps] = jj < T && j < n;
+            valid[ps] = pt >= 0 && jj < T && j < n;
 #pragma unroll
             for (int h = 0; h < kMaxG; ++h) s[ps][h] = 0.f;
             if (valid[ps]) {
@@ -442,15 +458,16 @@ struct FastTile {
     __device__ __forceinline__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         const int G = P.G;
-        const int tok0 = t * T;
+        const int pt = tile_at(P, b, (n + T - 1) / T, t);  // the tile of step t
+        const int tok0 = pt * T;
         // pages of the tile: first row index and validity (wave-uniform)
         long long prow[PAGES];
         bool pval[PAGES];
-        int bad = 0;
+        int bad = pt < 0;
 #pragma unroll
         for (int p = 0; p < PAGES; ++p) {
             const int tokp = tok0 + 16 * p;
-            pval[p] = tokp < n;
+            pval[p] = pt >= 0 && tokp < n;
             prow[p] = 0;
             if (pval[p]) {
                 bool ok = true;
@@ -665,10 +682,14 @@ struct FastTile {
 // accumulates head dims 8(l&15)..+7 over rows 4v + (l>>4) of each page, with
 // the weights of its rows read from LDS.  Units of one tile (ART mode) or of
 // a whole split range (full mode) accumulate into one running (max, sum,
-// accumulator) state that flush() reduces into the fold mapping.
-template <int KV, int GMAX>
+// accumulator) state that flush() reduces into the fold mapping.  ORD: the
+// art_order the call visits the tiles in (tile_at), fixed at compile time so
+// that each instance carries only its own remap (none for ascending).
+template <int KV, int GMAX, int ORD = ART_ORDER_ASCENDING>
 struct Stream {
     static constexpr int D = 128, UP = 2, T = 64, PAGES = 4;
+    static constexpr int ORDER = ORD;
+    static_assert(PAGES == kStepPages, "step-table records hold one block id per page");
     static constexpr int EB = KV == ART_I8 ? 1 : 2;
     static constexpr int HBM = GMAX / 4;
     static constexpr int HEADS = GMAX;           // query heads per KV head at most
@@ -733,18 +754,42 @@ struct Stream {
         }
     }
 
+    // the tile visited at step t (tile_at) of group grp's row of n positions
+    __device__ __forceinline__ static int phys(const Params& P, int grp, int n, int t) {
+        if constexpr (ORD == ART_ORDER_ASCENDING) {
+            return t;
+        } else if constexpr (ORD == ART_ORDER_RECENT) {
+            const int nt = (n + T - 1) / T;
+            return (t <= 0 || t >= nt) ? t : nt - t;
+        } else {
+            return tile_at(P, grp / P.Hkv, (n + T - 1) / T, t);
+        }
+    }
+    // whether tile index pt names a tile: a bad list entry gives -1
+    __device__ __forceinline__ static bool named(int pt) { return ORD != ART_ORDER_LIST || pt >= 0; }
+    // positions of a resolved tile
+    __device__ __forceinline__ static int rows_in(const TileRef& r) {
+        return named(r.t) ? max(0, min(T, r.n - r.t * T)) : 0;
+    }
+
+    // r: the tile visited at step t of group grp (r.t is the tile itself)
     __device__ __forceinline__ static void resolve(const Params& P, int grp, int t, TileRef& r) {
         const int b = grp / P.Hkv, g = grp % P.Hkv;
+        if constexpr (ORD == ART_ORDER_LIST) {
+            const int n = P.ctx_lens[b];
+            resolve_from(P, grp, n, t, fetch_blocks(P, grp, n, t), r);
+            return;
+        }
         r.grp = grp;
-        r.t = t;
         r.n = P.ctx_lens[b];
+        r.t = phys(P, grp, r.n, t);
         r.pmask = 0;
-        r.err = 0;
+        r.err = !named(r.t);
 #pragma unroll
         for (int p = 0; p < PAGES; ++p) {
-            const int tokp = t * T + 16 * p;
+            const int tokp = r.t * T + 16 * p;
             r.prow[p] = 0;
-            if (tokp < r.n) {
+            if (named(r.t) && tokp < r.n) {
                 bool ok = true;
                 r.prow[p] = row_index(P, b, g, tokp, ok);
                 if (ok) r.pmask |= 1 << p;
@@ -756,11 +801,21 @@ struct Stream {
     // The block ids of tile t (paged caches): lane p < PAGES loads page p's
     // entry with a vector load, so that it can be issued well before the tile
     // is resolved, and complete with the tile loads issued before it.
+    //
+    // A caller's tile list (ORD == ART_ORDER_LIST) reads the step table
+    // instead: lanes 0..PAGES-1 the pages' block ids, lane PAGES the tile; for
+    // a step past the row's tiles lane PAGES holds the step itself.
     __device__ __forceinline__ static int fetch_blocks(const Params& P, int grp, int n, int t) {
         const int lane = lane_id(), b = grp / P.Hkv;
-        const int tokp = t * T + 16 * lane;
+        if constexpr (ORD == ART_ORDER_LIST) {
+            int v = lane == PAGES ? t : 0;
+            if (lane <= PAGES && t < (n + T - 1) / T) v = P.steps[((long long)b * P.nt_max + t) * kStepW + lane];
+            return v;
+        }
+        const int pt = phys(P, grp, n, t);
+        const int tokp = pt * T + 16 * lane;
         int blk = 0;
-        if (P.block_size && lane < PAGES && tokp < n)
+        if (P.block_size && lane < PAGES && named(pt) && tokp < n)
             blk = P.block_table[(long long)b * P.mbps + (unsigned)tokp / (unsigned)P.block_size];
         return blk;
     }
@@ -770,15 +825,22 @@ struct Stream {
     // (resolve_lds) once the wave's loads have landed
     __device__ __forceinline__ static void fetch_blocks_lds(const Params& P, int grp, int n, int t, int* dst) {
         const int lane = lane_id(), b = grp / P.Hkv;
-        const int tokp = t * T + 16 * lane;
-        if (P.block_size && lane < PAGES && tokp < n)
+        if constexpr (ORD == ART_ORDER_LIST) {
+            if (lane <= PAGES && t < (n + T - 1) / T)
+                __builtin_amdgcn_global_load_lds(P.steps + ((long long)b * P.nt_max + t) * kStepW + lane,
+                                                 (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+            return;
+        }
+        const int pt = phys(P, grp, n, t);
+        const int tokp = pt * T + 16 * lane;
+        if (P.block_size && lane < PAGES && named(pt) && tokp < n)
             __builtin_amdgcn_global_load_lds(P.block_table + (long long)b * P.mbps + (unsigned)tokp / (unsigned)P.block_size,
                                              (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
     }
     __device__ __forceinline__ static void resolve_lds(const Params& P, int grp, int n, int t, const int* src,
                                                        TileRef& r) {
         const int lane = lane_id();
-        const int blkv = lane < PAGES ? src[lane] : 0;
+        const int blkv = lane < PAGES || (ORD == ART_ORDER_LIST && lane == PAGES) ? src[lane] : 0;
         resolve_from(P, grp, n, t, blkv, r);
     }
 
@@ -786,15 +848,18 @@ struct Stream {
     __device__ __forceinline__ static void resolve_from(const Params& P, int grp, int n, int t, int blkv, TileRef& r) {
         const int b = grp / P.Hkv, g = grp % P.Hkv;
         r.grp = grp;
-        r.t = t;
+        if constexpr (ORD == ART_ORDER_LIST)
+            r.t = t < (n + T - 1) / T ? __builtin_amdgcn_readlane(blkv, PAGES) : t;
+        else
+            r.t = phys(P, grp, n, t);
         r.n = n;
         r.pmask = 0;
-        r.err = 0;
+        r.err = !named(r.t);
 #pragma unroll
         for (int p = 0; p < PAGES; ++p) {
-            const int tokp = t * T + 16 * p;
+            const int tokp = r.t * T + 16 * p;
             r.prow[p] = 0;
-            if (tokp < n) {
+            if (named(r.t) && tokp < n) {
                 if (P.block_size == 0) {
                     r.prow[p] = ((long long)b * P.Hkv + g) * P.max_ctx + tokp;
                     r.pmask |= 1 << p;
@@ -1530,6 +1595,33 @@ __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
     for (int h = tid; h < P.G; h += blockDim.x) P.tiles_used[row0 + h] = nt > 0 ? -2 : (bad ? -1 : 0);
 }
 
+// A caller's tile list (ART_ORDER_LIST) turned into a step table for the
+// streamed kernels: record (b, s) holds, for the tile visited at step s of
+// row b (tile_at: -1 for a bad list entry), the block id of each of its
+// 16-token pages (paged caches) and, last, the tile itself, so that a worker
+// finds a step's tile and blocks with one load that it issues a tile ahead,
+// as for the ascending order.  Records past a row's tiles are never read.
+static_assert(kStepW == 8 && kStepPages == 4, "a step-table record is two 16-byte stores");
+__global__ __launch_bounds__(256) void art_steps_kernel(Params P) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long long)P.B * P.nt_max) return;
+    const int b = (int)(i / P.nt_max), s = (int)(i % P.nt_max);
+    const int n = P.ctx_lens[b];
+    if (n < 0 || n > P.cap) return;  // the row reports -1 and no worker reads its records
+    const int nt = (n + P.T - 1) / P.T;
+    if (s >= nt) return;
+    const int pt = tile_at(P, b, nt, s);
+    int rec[kStepW] = {};
+    for (int p = 0; p < kStepPages; ++p) {
+        const int tok = pt * P.T + 16 * p;
+        if (P.block_size && pt >= 0 && tok < n) rec[p] = P.block_table[(long long)b * P.mbps + tok / P.block_size];
+    }
+    rec[kStepPages] = pt;
+    int4* dst = reinterpret_cast<int4*>(P.steps + i * kStepW);
+    dst[0] = make_int4(rec[0], rec[1], rec[2], rec[3]);
+    dst[1] = make_int4(rec[4], rec[5], rec[6], rec[7]);
+}
+
 __device__ __forceinline__ void count_stats(const Params& P, unsigned long long tiles, unsigned long long rows) {
     if (P.stats && lane_id() == 0) {
         atomicAdd(reinterpret_cast<unsigned long long*>(P.stats + 0), tiles);
@@ -1639,10 +1731,10 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_stream_kernel(Params P)
         typename S::Out o;
         st.flush(P, o);
         o.err = C.err;
-        const int rows = min(S::T, max(0, C.n - C.t * S::T));
+        const int rows = S::named(C.t) ? min(S::T, max(0, C.n - C.t * S::T)) : 0;
         o.kept = rows;
-        const int token = publish_data(P, C.grp, C.t, o);
-        publish_flag(P, C.grp, C.t, token);
+        const int token = publish_data(P, C.grp, t, o);
+        publish_flag(P, C.grp, t, token);
         count_stats(P, 1ull, (unsigned long long)rows);
     }
 }
@@ -1892,7 +1984,7 @@ __device__ __forceinline__ void team_helper_worker(const Params& P, int grp, int
     st.template issue<1>(P, C, 1);
     int blkN = S::fetch_blocks(P, grp, n, t + plan.W);  // block ids of the next tile
     // tiles (and rows) loaded, counted when their loads are issued
-    unsigned long long loaded = 1, rows = min(S::T, n - t * S::T);
+    unsigned long long loaded = 1, rows = S::rows_in(C);
     for (;;) {
         st.template consume<0>(P, C, 0, true);
         st.template consume<1>(P, C, 1, false);
@@ -1911,7 +2003,7 @@ __device__ __forceinline__ void team_helper_worker(const Params& P, int grp, int
             st.template issue<1>(P, C, 1);
             blkN = S::fetch_blocks(P, grp, n, tn + plan.W);
             ++loaded;
-            rows += min(S::T, n - tn * S::T);
+            rows += S::rows_in(C);
         }
         // the slot must have been released (the decider releases no further
         // slot once the group is done: then the tile is past the bound)
@@ -1970,7 +2062,7 @@ __device__ __forceinline__ void team_primary_worker(const Params& P, int grp, in
     st.template issue<1>(P, C, 1);
     int blkN = S::fetch_blocks(P, grp, n, plan.nextA(t));  // block ids of the next tile
     // tiles (and rows) loaded, counted when their loads are issued
-    unsigned long long loaded = 1, rows = min(S::T, n - t * S::T), skipped = 0;
+    unsigned long long loaded = 1, rows = S::rows_in(C), skipped = 0;
     for (;;) {
         if constexpr (VSKIP) {
             // the running max through tile t: that through tile t - 1 (from its
@@ -2013,7 +2105,7 @@ __device__ __forceinline__ void team_primary_worker(const Params& P, int grp, in
             st.template issue<1>(P, C, 1);
             blkN = S::fetch_blocks(P, grp, n, plan.nextA(tn));
             ++loaded;
-            rows += min(S::T, n - tn * S::T);
+            rows += S::rows_in(C);
         }
         // the slot must have been released (the decider releases no further
         // slot once the group is done: then the tile is past the bound)
@@ -2939,7 +3031,7 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
             st.template issue<0>(P, C, 0);
             st.template issue<1>(P, C, 1);
             ++loaded;
-            rows += min(T, n - t * T);
+            rows += S::rows_in(C);
         }
         // the next one claimed, its blocks in flight; the one after, claimed in flight
         int tN = t < nt ? claim() : nt;
@@ -3017,7 +3109,7 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
             st.template issue<0>(P, C, 0);
             st.template issue<1>(P, C, 1);
             ++loaded;
-            rows += min(T, n - tN * T);
+            rows += S::rows_in(C);
             t = tN;
             tN = tX;
             if (tN < nt) S::fetch_blocks_lds(P, grp, n, tN, blk);
@@ -3174,7 +3266,7 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_full_stream_kernel(Para
     const int t1 = min(t0 + P.tiles_per_split, nt);
     S st;
     st.init(lds + wv * S::lds_floats(P));
-    int err = 0;
+    int err = 0, rows = 0;
     typename S::Out o;
     if (t0 < t1) {
         st.load_q(P, grp);
@@ -3186,6 +3278,7 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_full_stream_kernel(Para
             const bool more = t + 1 < t1;
             if (more) S::resolve(P, grp, t + 1, N);
             err |= C.err;
+            rows += S::named(C.t) ? min(S::T, n - C.t * S::T) : 0;
             st.template consume<0>(P, C, 0, true);
             if (more) st.template issue<0>(P, N, 0);
             st.template consume<1>(P, C, 1, more);
@@ -3212,7 +3305,6 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_full_stream_kernel(Para
                 slot[16 + h] = o.l[h];
             }
         }
-        const int rows = t1 > t0 ? min(n, t1 * S::T) - t0 * S::T : 0;
         reinterpret_cast<int*>(slot)[32] = err;
         reinterpret_cast<int*>(slot)[33] = rows;
         if (t1 > t0 && P.stats) {
@@ -3425,6 +3517,14 @@ int launch_pool(const Params& p0, hipStream_t s) {
 
 template <class S>
 int run_stream(const Params& p, hipStream_t s, bool art) {
+    if constexpr (S::ORDER == ART_ORDER_LIST) {
+        const long long recs = (long long)p.B * p.nt_max;
+        if (recs > 0) {
+            hipLaunchKernelGGL(art_steps_kernel, dim3((unsigned)((recs + 255) / 256)), dim3(256), 0, s, p);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
     if (!art) return launch_split<decltype(&art_full_stream_kernel<S>), S>(p, s, &art_full_stream_kernel<S>);
     if (sharing(p)) return launch_persistent<decltype(&art_stream_kernel<S>), S>(p, s, &art_stream_kernel<S>);
     if (p.vskip) return launch_team<S, true>(p, s);
@@ -3438,7 +3538,10 @@ int run_stream(const Params& p, hipStream_t s, bool art) {
 
 template <int KV, int GMAX>
 int run_fast(const Params& p, hipStream_t s, bool art) {
-    if (stream_path(p, art)) return run_stream<Stream<KV, GMAX>>(p, s, art);
+    if (stream_path(p, art))
+        return p.order == ART_ORDER_ASCENDING ? run_stream<Stream<KV, GMAX, ART_ORDER_ASCENDING>>(p, s, art)
+               : p.order == ART_ORDER_RECENT  ? run_stream<Stream<KV, GMAX, ART_ORDER_RECENT>>(p, s, art)
+                                              : run_stream<Stream<KV, GMAX, ART_ORDER_LIST>>(p, s, art);
     if (p.T == 64) return run_tile<FastTile<KV, 4, GMAX>>(p, s, art);
     if (p.T == 32) return run_tile<FastTile<KV, 2, GMAX>>(p, s, art);
     return run_tile<FastTile<KV, 1, GMAX>>(p, s, art);

@@ -32,7 +32,8 @@ def to_device(case):
 
     return dict(q=t(case.q), k=t(case.k), v=t(case.v), ctx=t(case.ctx_lens.astype(np.int32)),
                 bt=t(case.block_table), ks=t(case.k_scale, as_f16=True),
-                vs=t(case.v_scale, as_f16=True))
+                vs=t(case.v_scale, as_f16=True),
+                perm=t(None if case.tile_perm is None else case.tile_perm.astype(np.int32)))
 
 
 def run_gpu(case, dev=None, **kw):
@@ -41,7 +42,8 @@ def run_gpu(case, dev=None, **kw):
     dev = dev or to_device(case)
     args = dict(block_table=dev["bt"], tile=case.tile, eps_scale=case.eps_scale,
                 eps_dir=case.eps_dir, patience=case.patience, v_skip_eps=case.v_skip_eps,
-                k_scale=dev["ks"], v_scale=dev["vs"])
+                k_scale=dev["ks"], v_scale=dev["vs"], tile_order=case.order,
+                tile_perm=dev["perm"] if case.order == 2 else None)
     args.update(kw)
     out, used = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], **args)
     torch.cuda.synchronize()
@@ -83,8 +85,7 @@ def check_parity(case, out, used, *, eps_scale=None, eps_dir=None, patience=None
                                  f"gpu {g_used[bi, h]} oracle {ora.tiles_used[bi, h]}")
             near.append((rows[bi], int(h), int(g_used[bi, h]), int(ora.tiles_used[bi, h])))
             if vk == 0 and g_used[bi, h] > 0:
-                n = min(int(g_used[bi, h]) * case.tile, int(sub.ctx_lens[bi]))
-                ref = BF.attention(sub, bi, int(h), n)
+                ref = BF.attention_at(sub, bi, int(h), visited_positions(sub, bi, int(g_used[bi, h])))
                 assert np.abs(g_out[bi, h] - ref).max() <= tol
     same = g_used == ora.tiles_used
     err = np.abs(g_out - ora.out).max(axis=-1)
@@ -95,6 +96,19 @@ def check_parity(case, out, used, *, eps_scale=None, eps_dir=None, patience=None
     return dict(max_abs=maxerr, near=near, heads=int(same.size), tiles_used=ora.tiles_used)
 
 
+def visited_positions(case, b, steps):
+    """Positions of the tiles row b visits in its first `steps` steps."""
+    T, n = case.tile, int(case.ctx_lens[b])
+    nt = -(-n // T)
+    if case.order == 0:
+        seq = list(range(nt))
+    elif case.order == 1:
+        seq = [0] + list(range(nt - 1, 0, -1))
+    else:
+        seq = [int(x) for x in case.tile_perm[b, :nt]]
+    return [j for s in seq[:steps] for j in range(s * T, min(n, (s + 1) * T))]
+
+
 def _subset(case, rows):
     if rows == list(range(case.B)):
         return case
@@ -103,6 +117,8 @@ def _subset(case, rows):
     c.B = len(rows)
     c.q = np.ascontiguousarray(case.q[rows])
     c.ctx_lens = np.ascontiguousarray(case.ctx_lens[rows])
+    if case.tile_perm is not None:
+        c.tile_perm = np.ascontiguousarray(case.tile_perm[rows])
     if case.block_size:
         c.block_table = np.ascontiguousarray(case.block_table[rows])
     else:

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = art.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.art_abi_version() == 3
+    assert lib.art_abi_version() == 4
 
 
 def desc(**kw):
@@ -50,6 +50,12 @@ def ok_desc(**kw):
 def test_valid_desc_passes():
     assert B.validate(ok_desc(), 64, 1e-3, 1e-4) == 0
     assert B.validate(ok_desc(block_size=0, max_ctx=64), 64, 0.0, 0.0) == 0
+    assert B.validate(ok_desc(tile_order=1), 64, 1e-3, 1e-4) == 0
+    # a caller's order: one entry per tile a row can hold (8 blocks of 16 -> 2 tiles of 64)
+    assert B.validate(ok_desc(max_blocks_per_seq=8, tile_order=2, tile_perm=1 << 20, tile_perm_stride=2),
+                      64, 1e-3, 1e-4) == 0
+    assert B.validate(desc(max_blocks_per_seq=8, tile_order=2, tile_perm=1 << 20, tile_perm_stride=1),
+                      64, 1e-3, 1e-4) == -2
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -74,6 +80,10 @@ def test_valid_desc_passes():
     (dict(team_helpers=4), -5),
     (dict(engine=-1), -5),
     (dict(engine=4), -5),
+    (dict(tile_order=-1), -5),
+    (dict(tile_order=3), -5),
+    (dict(tile_order=2), -1),                  # a caller's order without tile_perm
+    (dict(tile_order=2, tile_perm=1 << 20, tile_perm_stride=0), -2),  # 4 blocks of 16 = 1 tile
 ])
 def test_bad_desc_rejected(kw, code):
     assert B.validate(desc(**kw), 64, 1e-3, 1e-4) == code
