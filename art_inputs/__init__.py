@@ -55,7 +55,7 @@ def sink_first_orders(ctx_lens, tile: int, stride: int | None = None, seed: int 
     """Random caller-side tile orders: row b lists its ceil(ctx_lens[b] / tile)
     tiles with tile 0 first and the others shuffled; entries past them are -1."""
     ctx_lens = np.asarray(ctx_lens)
-    nts = [-(-int(n) // tile) for n in ctx_lens]
+    nts = [-(-int(n) // tile) for n in ctx_lens.ravel()]
     stride = max([1] + nts) if stride is None else stride
     rng = np.random.default_rng(seed)
     perm = np.full((len(nts), stride), -1, np.int32)
@@ -63,7 +63,42 @@ def sink_first_orders(ctx_lens, tile: int, stride: int | None = None, seed: int 
         if nt:
             perm[b, 0] = 0
             perm[b, 1:nt] = 1 + rng.permutation(nt - 1)
-    return perm
+    return perm.reshape(ctx_lens.shape + (stride,))
+
+
+def retained_tables(case: "Case", *, sink_blocks: int, recent_blocks: int, keep_frac: float,
+                    seed: int = 0) -> "Case":
+    """The same paged cache seen through per-(row, KV head) block tables after a
+    block-granular retention policy: every KV head keeps its row's first
+    `sink_blocks` and last `recent_blocks` blocks plus a uniformly random
+    `keep_frac` share of the blocks between them, drawn per head (0: sinks and
+    a recent window only).  The kept blocks are listed in order; a head's
+    length counts their tokens (the row's last block may be partial)."""
+    assert case.block_size and not case.per_head_tables
+    bs = case.block_size
+    B, mbps = case.block_table.shape
+    rng = np.random.default_rng(seed)
+    table = np.zeros((B, case.Hkv, mbps), np.int32)
+    lens = np.zeros((B, case.Hkv), np.int32)
+    for b in range(B):
+        n = int(case.ctx_lens[b])
+        nblk = -(-n // bs)
+        for g in range(case.Hkv):
+            if nblk == 0:
+                continue
+            head = list(range(min(sink_blocks, nblk)))
+            tail = list(range(max(len(head), nblk - recent_blocks), nblk))
+            mid = np.arange(len(head), nblk - len(tail))
+            kept = head + [int(i) for i in mid[rng.random(mid.size) < keep_frac]] + tail
+            table[b, g, :len(kept)] = case.block_table[b, kept]
+            last = n - (nblk - 1) * bs if kept[-1] == nblk - 1 else bs
+            lens[b, g] = (len(kept) - 1) * bs + last
+    return Case(name=case.name + "-retained", B=B, Hq=case.Hq, Hkv=case.Hkv, d=case.d, q=case.q,
+                k=case.k, v=case.v, ctx_lens=lens, block_size=bs, block_table=table,
+                k_scale=case.k_scale, v_scale=case.v_scale, tile=case.tile,
+                eps_scale=case.eps_scale, eps_dir=case.eps_dir, patience=case.patience,
+                v_skip_eps=case.v_skip_eps, per_head_tables=True,
+                meta=dict(case.meta, kept_blocks=(sink_blocks, recent_blocks, keep_frac)))
 
 
 def quantize_int8(x):
@@ -104,6 +139,7 @@ class Case:
     eps_dir: float = 1e-4
     patience: int = 1
     v_skip_eps: float = 0.0
+    per_head_tables: bool = False  # ctx_lens [B, Hkv], block_table [B, Hkv, mbps], tile_perm [B, Hkv, stride]
     order: int = 0                # tile order: 0 ascending, 1 tile 0 then most recent first, 2 tile_perm
     tile_perm: np.ndarray | None = None    # int32 [B, stride]: row b's tiles in visiting order (order 2)
     meta: dict = field(default_factory=dict)
@@ -120,7 +156,7 @@ class Case:
     @property
     def max_ctx(self) -> int:
         if self.block_size:
-            return self.block_table.shape[1] * self.block_size
+            return self.block_table.shape[-1] * self.block_size
         return self.k.shape[2]
 
     @property

@@ -52,7 +52,7 @@ def _load():
     f = lib.art_oracle_decode
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     f.argtypes = [i32] * 10 + [vp] * 7 + [i32, ctypes.c_double, ctypes.c_double, i32,
-                                         ctypes.c_double, vp, vp, vp, i32, i32, i32, vp, i32]
+                                         ctypes.c_double, vp, vp, vp, i32, i32, i32, vp, i32, i32]
     f.restype = i32
     _lib = lib
     return lib
@@ -79,7 +79,7 @@ def _ptr(a):
 def decode(q, k, v, ctx_lens, *, tile=64, eps_scale=1e-3, eps_dir=1e-4, patience=1,
            v_skip_eps=0.0, block_table=None, block_size=0, k_scale=None, v_scale=None,
            q_dtype=None, kv_dtype=None, trace=False, threads=None, order=0,
-           tile_perm=None) -> OracleResult:
+           tile_perm=None, per_head_tables=False) -> OracleResult:
     """Run the oracle.
 
     q: [B, Hq, d] float32, or uint16 bf16 bit patterns.
@@ -91,6 +91,8 @@ def decode(q, k, v, ctx_lens, *, tile=64, eps_scale=1e-3, eps_dir=1e-4, patience
     order: 0 ascending tiles, 1 tile 0 then the most recent first, 2 the
           caller's tile_perm (int32 [B, stride]: row b lists its tiles in
           visiting order, tile 0 first).
+    per_head_tables: ctx_lens is [B, Hkv], block_table [B, Hkv, mbps] and
+          tile_perm [B, Hkv, stride]: every (row, KV head) has its own sequence.
     """
     lib = _load()
     q = np.ascontiguousarray(q)
@@ -107,20 +109,24 @@ def decode(q, k, v, ctx_lens, *, tile=64, eps_scale=1e-3, eps_dir=1e-4, patience
         num_blocks, Hkv, bs, _ = k.shape
         assert bs == block_size
         block_table = np.ascontiguousarray(block_table, dtype=np.int32)
-        mbps = block_table.shape[1]
+        mbps = block_table.shape[-1]
         max_ctx = 0
     else:
         _, Hkv, max_ctx, _ = k.shape
         num_blocks, mbps = 0, 0
         block_table = None
+    seqs = (B, Hkv) if per_head_tables else (B,)
+    assert ctx_lens.shape == seqs, (ctx_lens.shape, seqs)
+    if block_size:
+        assert block_table.shape[:-1] == seqs, (block_table.shape, seqs)
     if kv_dtype == I8:
         k_scale = np.ascontiguousarray(k_scale, dtype=np.uint16)
         v_scale = np.ascontiguousarray(v_scale, dtype=np.uint16)
     stride = 0
     if order == 2:
         tile_perm = np.ascontiguousarray(tile_perm, dtype=np.int32)
-        assert tile_perm.ndim == 2 and tile_perm.shape[0] == B
-        stride = tile_perm.shape[1]
+        assert tile_perm.shape[:-1] == ((B, Hkv) if per_head_tables else (B,))
+        stride = tile_perm.shape[-1]
     else:
         tile_perm = None
     out = np.zeros((B, Hq, d), np.float64)
@@ -135,7 +141,8 @@ def decode(q, k, v, ctx_lens, *, tile=64, eps_scale=1e-3, eps_dir=1e-4, patience
                                _ptr(v_scale), _ptr(block_table), _ptr(ctx_lens), tile,
                                float(eps_scale), float(eps_dir), int(patience),
                                float(v_skip_eps), _ptr(out), _ptr(U), _ptr(tr), ntr,
-                               threads or default_threads(), int(order), _ptr(tile_perm), stride)
+                               threads or default_threads(), int(order), _ptr(tile_perm), stride,
+                               int(bool(per_head_tables)))
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return OracleResult(out, U, tr)

@@ -11,7 +11,10 @@
  * the puntofijo.es article on skipping V dequantisation in llama.cpp):
  *
  *   For every batch row b and query head h, one decode query attends over the
- *   first n = ctx_lens[b] cached positions of KV head g = h / (Hq/Hkv).  The
+ *   first n = ctx_lens[b] cached positions of KV head g = h / (Hq/Hkv).  With
+ *   per-head tables each (b, g) has its own length and block table: the
+ *   positions a per-head retention or eviction policy kept, in order (ART
+ *   summary, section 2.4: ART runs on top of such policies unchanged).  The
  *   positions are visited in tiles of T consecutive tokens (ART summary,
  *   section 2.1: tile-wise incremental attention that exposes the running
  *   output), tile 0 first and by default in ascending order; section 2.4
@@ -73,6 +76,7 @@ typedef struct {
     int32_t *tiles_used;
     double *trace;
     int trace_tiles;
+    int per_head;          /* ctx_lens [B][Hkv], block_table [B][Hkv][mbps], perm [B][Hkv][stride] */
     int order;             /* tile order: see visit_tile */
     const int32_t *perm;   /* order 2: [B][perm_stride] */
     int perm_stride;
@@ -101,30 +105,35 @@ static double widen_f16(uint16_t h) {
     return sign ? -v : v;
 }
 
+/* the sequence (b, KV head g) reads: its own with per-head tables, else row b's */
+static long seq_of(const job_t *J, int b, int g) {
+    return J->per_head ? (long)b * J->Hkv + g : b;
+}
+
 /* index of cached row (b, kv head g, position j): returns -1 if the block id
    read from the table is out of range */
 static long row_index(const job_t *J, int b, int g, int j) {
     if (J->block_size == 0)
         return ((long)b * J->Hkv + g) * J->max_ctx + j;
-    int blk = J->block_table[(long)b * J->max_blocks_per_seq + j / J->block_size];
+    int blk = J->block_table[seq_of(J, b, g) * J->max_blocks_per_seq + j / J->block_size];
     if (blk < 0 || blk >= J->num_blocks) return -1;
     return ((long)blk * J->Hkv + g) * J->block_size + (j % J->block_size);
 }
 
-/* Tile visited at step t (0-based) of row b, which has nt tiles.  Section
+/* Tile visited at step t (0-based) of sequence sq, which has nt tiles.  Section
    2.4 of the ART summary lets the sequence of tiles be reordered, e.g.
    recency-first or importance-first, with no approximation error since
    attention does not depend on the order, and has block 0 (the attention
    sink) evaluated before any termination.  Orders:
      0  ascending: 0, 1, ..., nt-1
      1  the sink, then the most recent first: 0, nt-1, nt-2, ..., 1
-     2  the caller's list perm[b][0..nt-1]: step 0 must name tile 0 and
+     2  the caller's list perm[sq][0..nt-1]: step 0 must name tile 0 and
         every later step a tile in 1..nt-1
    Returns -1 for a list entry that breaks those rules. */
-static int visit_tile(const job_t *J, int b, int nt, int t) {
+static int visit_tile(const job_t *J, long sq, int nt, int t) {
     if (J->order == 0) return t;
     if (J->order == 1) return t == 0 ? 0 : nt - t;
-    const int e = J->perm[(long)b * J->perm_stride + t];
+    const int e = J->perm[sq * J->perm_stride + t];
     if (t == 0) return e == 0 ? 0 : -1;
     return (e >= 1 && e < nt) ? e : -1;
 }
@@ -158,7 +167,8 @@ static int run_item(job_t *J, int b, int h, double *scratch) {
            *prev = x + 8, *s = prev + 8; /* s holds T scores */
     double *out = J->out + ((long)b * J->Hq + h) * d;
     int32_t *U_out = J->tiles_used + (long)b * J->Hq + h;
-    const int n = J->ctx_lens[b];
+    const long sq = seq_of(J, b, g);
+    const int n = J->ctx_lens[sq];
     const int nt = (n + T - 1) / T;
 
     /* widen the query */
@@ -174,7 +184,7 @@ static int run_item(job_t *J, int b, int h, double *scratch) {
     int streak = 0, U = nt;
 
     for (int t = 0; t < nt; ++t) {
-        const int pt = visit_tile(J, b, nt, t); /* the tile of step t */
+        const int pt = visit_tile(J, sq, nt, t); /* the tile of step t */
         if (pt < 0) return -1;
         const int j0 = pt * T, j1 = (j0 + T < n) ? j0 + T : n;
         /* scores of the tile, s_j = q.k_j / sqrt(d) */
@@ -265,7 +275,7 @@ int art_oracle_decode(int B, int Hq, int Hkv, int d, int q_dtype, int kv_dtype,
                       int tile, double eps_scale, double eps_dir, int patience, double v_skip_eps,
                       double *out, int32_t *tiles_used,
                       double *trace, int trace_tiles, int nthreads,
-                      int order, const int32_t *perm, int perm_stride) {
+                      int order, const int32_t *perm, int perm_stride, int per_head) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return -2;
     if (!q || !k || !v || !ctx_lens || !out || !tiles_used) return -1;
     if (q_dtype != ODT_F32 && q_dtype != ODT_BF16) return -3;
@@ -274,10 +284,11 @@ int art_oracle_decode(int B, int Hq, int Hkv, int d, int q_dtype, int kv_dtype,
     if (tile <= 0 || patience < 1) return -5;
     if (order < 0 || order > 2) return -5;
     if (order == 2 && !perm) return -1;
-    for (int b = 0; b < B; ++b) {
+    const long nseq = per_head ? (long)B * Hkv : B;
+    for (long sq = 0; sq < nseq; ++sq) {
         long cap = block_size ? (long)max_blocks_per_seq * block_size : max_ctx;
-        if (ctx_lens[b] < 0 || ctx_lens[b] > cap) return -2;
-        if (order == 2 && (ctx_lens[b] + tile - 1) / tile > perm_stride) return -2;
+        if (ctx_lens[sq] < 0 || ctx_lens[sq] > cap) return -2;
+        if (order == 2 && (ctx_lens[sq] + tile - 1) / tile > perm_stride) return -2;
     }
     if (block_size && !block_table) return -1;
     job_t J;
@@ -288,7 +299,7 @@ int art_oracle_decode(int B, int Hq, int Hkv, int d, int q_dtype, int kv_dtype,
     J.block_table = block_table; J.ctx_lens = ctx_lens; J.tile = tile; J.patience = patience;
     J.eps_scale = eps_scale; J.eps_dir = eps_dir; J.v_skip_eps = v_skip_eps;
     J.out = out; J.tiles_used = tiles_used; J.trace = trace; J.trace_tiles = trace ? trace_tiles : 0;
-    J.order = order; J.perm = perm; J.perm_stride = perm_stride;
+    J.order = order; J.perm = perm; J.perm_stride = perm_stride; J.per_head = per_head != 0;
     pthread_mutex_init(&J.mu, NULL);
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;

@@ -28,7 +28,8 @@ def logical_rows(case, which: str, b: int, g: int, n: int) -> np.ndarray:
     scale = case.k_scale if which == "k" else case.v_scale
     idx = np.arange(n)
     if case.block_size:
-        blk = case.block_table[b, idx // case.block_size]
+        table = case.block_table[b, g] if case.per_head_tables else case.block_table[b]
+        blk = table[idx // case.block_size]
         off = idx % case.block_size
         raw = arr[blk, g, off]
         sc = None if scale is None else scale[blk, g, off]

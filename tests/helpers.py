@@ -23,7 +23,7 @@ def contiguous_case(q, K, V, ctx_lens=None, *, kv="f32", qd="f32", name="custom"
 
 def to_paged(case: Case, block_size: int, seed: int, extra_blocks: int = 0) -> Case:
     """Same logical cache as a contiguous case, laid out in randomly permuted pages."""
-    assert case.block_size == 0
+    assert case.block_size == 0 and not case.per_head_tables
     B, Hkv, n, d = case.k.shape
     nbs = -(-n // block_size)
     nb = B * nbs + extra_blocks
@@ -73,6 +73,6 @@ def run_oracle(case, **kw):
                 patience=case.patience, v_skip_eps=case.v_skip_eps,
                 block_table=case.block_table, block_size=case.block_size,
                 k_scale=case.k_scale, v_scale=case.v_scale, order=case.order,
-                tile_perm=case.tile_perm)
+                tile_perm=case.tile_perm, per_head_tables=case.per_head_tables)
     args.update(kw)
     return oracle.decode(case.q, case.k, case.v, case.ctx_lens, **args)

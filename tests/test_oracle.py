@@ -471,3 +471,92 @@ def test_order_entries_past_the_stop_are_not_read():
     perm[0, 1] = 99
     with pytest.raises(ValueError):
         run_oracle(c)
+
+
+# ---------------------------------------------------------------- per-head tables (composition with retention)
+#
+# ART runs unchanged on top of a per-head retention or eviction policy (ART
+# summary, section 2.4: an orthogonal control layer).  With per-head tables
+# every (row, KV head) is its own sequence; the pins tie that to calls with
+# shared tables and to plain attention over the positions a policy kept.
+
+def paged_case(B=3, Hq=8, Hkv=2, d=16, n=640, seed=0, T=16, **params):
+    c = rand_case(B=B, Hq=Hq, Hkv=Hkv, d=d, n=n, seed=seed, tile=T, **params)
+    return to_paged(c, 16, seed=seed + 1, extra_blocks=5)
+
+
+def per_head_slice(c, g):
+    """The KV head g of a per-head case as a call of its own with shared tables."""
+    import copy
+    G = c.Hq // c.Hkv
+    s = copy.copy(c)
+    s.Hq, s.Hkv = G, 1
+    s.q = np.ascontiguousarray(c.q[:, g * G:(g + 1) * G])
+    s.k = np.ascontiguousarray(c.k[:, g:g + 1])
+    s.v = np.ascontiguousarray(c.v[:, g:g + 1])
+    s.ctx_lens = np.ascontiguousarray(c.ctx_lens[:, g])
+    s.block_table = np.ascontiguousarray(c.block_table[:, g])
+    s.tile_perm = None if c.tile_perm is None else np.ascontiguousarray(c.tile_perm[:, g])
+    s.per_head_tables = False
+    return s
+
+
+@pytest.mark.parametrize("order", [0, 1, 2])
+def test_per_head_identical_tables_equal_shared_tables(order):
+    c = paged_case(seed=31, eps_scale=0.05, eps_dir=0.02)
+    c.ctx_lens[:] = [640, 401, 77]
+    c.order = order
+    c.tile_perm = A.sink_first_orders(c.ctx_lens, 16, stride=40, seed=2) if order == 2 else None
+    ref = run_oracle(c)
+    import copy
+    p = copy.copy(c)
+    p.per_head_tables = True
+    p.ctx_lens = np.repeat(c.ctx_lens[:, None], c.Hkv, axis=1)
+    p.block_table = np.repeat(c.block_table[:, None], c.Hkv, axis=1)
+    p.tile_perm = None if order != 2 else np.repeat(c.tile_perm[:, None], c.Hkv, axis=1)
+    r = run_oracle(p)
+    assert np.array_equal(r.tiles_used, ref.tiles_used) and np.array_equal(r.out, ref.out)
+
+
+@pytest.mark.parametrize("order", [0, 1, 2])
+@pytest.mark.parametrize("keep", [0.0, 0.5])
+def test_per_head_tables_equal_separate_calls(order, keep):
+    c = paged_case(B=3, Hq=8, Hkv=2, n=960, seed=40, eps_scale=0.05, eps_dir=0.02)
+    c.ctx_lens[:] = [960, 611, 203]
+    p = A.retained_tables(c, sink_blocks=2, recent_blocks=24, keep_frac=keep, seed=7)
+    assert (p.ctx_lens[:, 0] != p.ctx_lens[:, 1]).any() or keep == 0.0
+    p.order = order
+    p.tile_perm = A.sink_first_orders(p.ctx_lens, 16, stride=60, seed=4) if order == 2 else None
+    r = run_oracle(p)
+    G = c.Hq // c.Hkv
+    for g in range(c.Hkv):
+        s = run_oracle(per_head_slice(p, g))
+        assert np.array_equal(r.tiles_used[:, g * G:(g + 1) * G], s.tiles_used)
+        assert np.array_equal(r.out[:, g * G:(g + 1) * G], s.out)
+    assert (r.tiles_used < -(-p.ctx_lens.repeat(G, axis=1) // 16)).any()  # some heads stop
+
+
+def test_retained_full_mode_is_attention_over_kept_positions():
+    c = paged_case(B=2, Hq=4, Hkv=2, n=700, seed=50, eps_scale=0.0, eps_dir=0.0)
+    c.ctx_lens[:] = [700, 333]
+    p = A.retained_tables(c, sink_blocks=1, recent_blocks=5, keep_frac=0.4, seed=3)
+    r = run_oracle(p)
+    G = c.Hq // c.Hkv
+    for b in range(2):
+        n = int(c.ctx_lens[b])
+        for g in range(2):
+            k = -(-int(p.ctx_lens[b, g]) // 16)
+            blocks = [int(np.flatnonzero(c.block_table[b] == blk)[0]) for blk in p.block_table[b, g, :k]]
+            pos = [j for i in blocks for j in range(16 * i, min(n, 16 * (i + 1)))]
+            assert len(pos) == p.ctx_lens[b, g]
+            for h in range(g * G, (g + 1) * G):
+                assert r.tiles_used[b, h] == -(-len(pos) // 16)
+                assert np.allclose(r.out[b, h], BF.attention_at(c, b, h, pos), rtol=1e-12, atol=1e-13)
+
+
+def test_per_head_lengths_checked():
+    c = paged_case(B=2, Hq=4, Hkv=2, n=320, seed=60)
+    p = A.retained_tables(c, sink_blocks=1, recent_blocks=4, keep_frac=1.0, seed=1)
+    p.ctx_lens[1, 1] = p.block_table.shape[-1] * 16 + 1
+    with pytest.raises(ValueError):
+        run_oracle(p)

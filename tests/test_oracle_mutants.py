@@ -49,9 +49,13 @@ MUTANTS = {
     "order_ignored": ("if (J->order == 0) return t;", "return t;"),
     "recent_order_shifted": ("return t == 0 ? 0 : nt - t;", "return t == 0 ? 0 : nt - 1 - t + (t == nt - 1);"),
     "recent_order_oldest_first": ("return t == 0 ? 0 : nt - t;", "return t;"),
-    "perm_row_ignored": ("J->perm[(long)b * J->perm_stride + t]", "J->perm[t]"),
+    "perm_row_ignored": ("J->perm[sq * J->perm_stride + t]", "J->perm[t]"),
     "perm_sink_not_forced": ("if (t == 0) return e == 0 ? 0 : -1;", "if (t == 0) return (e >= 0 && e < nt) ? e : -1;"),
     "positions_from_step": ("const int j0 = pt * T, j1", "const int j0 = t * T, j1"),
+    "per_head_sequence_ignored": ("return J->per_head ? (long)b * J->Hkv + g : b;", "return b;"),
+    "per_head_table_row_shared": ("J->block_table[seq_of(J, b, g) * J->max_blocks_per_seq",
+                                  "J->block_table[(long)b * J->max_blocks_per_seq"),
+    "per_head_list_row_shared": ("const int pt = visit_tile(J, sq, nt, t);", "const int pt = visit_tile(J, b, nt, t);"),
     "int8_scale_ignored": ("double s = widen_f16(scale[row]);", "double s = 1.0;"),
     "direction_not_clamped_half": ("dd = 1.0 - dot / (xn * prev_norm);", "dd = 0.5 * (1.0 - dot / (xn * prev_norm));"),
 }
@@ -81,6 +85,8 @@ PINS = [
     P.test_recent_first_stops_early_where_recent_tokens_dominate,
     P.test_invalid_tile_orders_rejected,
     P.test_order_entries_past_the_stop_are_not_read,
+    lambda: [P.test_per_head_tables_equal_separate_calls(o, k) for o in (0, 2) for k in (0.0, 0.5)],
+    P.test_retained_full_mode_is_attention_over_kept_positions,
 ]
 
 
