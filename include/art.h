@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define ART_ABI_VERSION 4
+#define ART_ABI_VERSION 5
 
 typedef enum {
     ART_OK = 0,
@@ -80,6 +80,11 @@ typedef enum {
  *   block_table int32 [batch][max_blocks_per_seq] (paged only): logical page p
  *               of row b lives in physical block block_table[b][p]
  *   ctx_lens    int32 [batch]: cached positions of each row (0 allowed)
+ *   with per_head_tables = 1 every (row b, KV head g) is a sequence of its own:
+ *               ctx_lens [batch][num_kv_heads], block_table
+ *               [batch][num_kv_heads][max_blocks_per_seq] (KV head g reads its
+ *               slice of the blocks its row lists) and tile_perm
+ *               [batch][num_kv_heads][tile_perm_stride]
  *   out         fp32 [batch][num_q_heads][head_dim]
  *   tiles_used  int32 [batch][num_q_heads]
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
@@ -120,12 +125,17 @@ typedef struct {
                                     ceil(row capacity / tile)                         */
     const int32_t* tile_perm;    /* ART_ORDER_LIST: device int32 [batch][tile_perm_stride],
                                     caller-owned, read only; else ignored            */
+    int32_t per_head_tables;     /* 0: lengths, block tables and tile lists per row;
+                                    1: per (row, KV head) -- the positions a per-head
+                                    retention or eviction policy kept, in order (ART
+                                    summary, section 2.4: ART runs unchanged on top) */
 } art_desc;
 
 /*
  * art_decode_attention -- ART-terminated decode attention over a KV cache.
  *
- * For every (b, h): the query attends over positions 0..ctx_lens[b]-1 of its
+ * For every (b, h): the query attends over positions 0..ctx_lens[b]-1 (per-head
+ * tables: ctx_lens[b][g]) of its
  * KV head in tiles of `tile` tokens, tile 0 first and then in desc->tile_order,
  * with an online softmax (ART summary, section 2.1).  After each visiting step
  * t the probe is dims 0..7 of the

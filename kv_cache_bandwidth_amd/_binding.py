@@ -55,13 +55,14 @@ class ArtDesc(ctypes.Structure):
         ("tile_order", ctypes.c_int32),
         ("tile_perm_stride", ctypes.c_int32),
         ("tile_perm", ctypes.c_void_p),
+        ("per_head_tables", ctypes.c_int32),
     ]
 
 
 _lib = None
 
 
-ABI_VERSION = 4  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
+ABI_VERSION = 5  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
 
 
 def load():
@@ -103,11 +104,13 @@ def _check(rc: int):
 def make_desc(*, batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, block_size=0,
               max_blocks_per_seq=0, num_blocks=0, max_ctx=0, patience=1, v_skip_eps=0.0,
               k_scale=0, v_scale=0, workspace=0, workspace_bytes=0, stats=0, max_workers=0,
-              team_helpers=0, engine=0, tile_order=0, tile_perm_stride=0, tile_perm=0) -> ArtDesc:
+              team_helpers=0, engine=0, tile_order=0, tile_perm_stride=0, tile_perm=0,
+              per_head_tables=0) -> ArtDesc:
     return ArtDesc(batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, block_size,
                    max_blocks_per_seq, num_blocks, max_ctx, patience, v_skip_eps, k_scale or None,
                    v_scale or None, workspace or None, workspace_bytes, stats or None, max_workers,
-                   team_helpers, engine, tile_order, tile_perm_stride, tile_perm or None)
+                   team_helpers, engine, tile_order, tile_perm_stride, tile_perm or None,
+                   int(per_head_tables))
 
 
 def workspace_bytes(desc: ArtDesc, tile: int) -> int:
@@ -126,7 +129,7 @@ def _dtype_code(t):
 def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64, eps_scale=1e-3,
                      eps_dir=1e-4, patience=1, v_skip_eps=0.0, k_scale=None, v_scale=None,
                      out=None, tiles_used=None, workspace=None, stats=None, max_workers=0, team_helpers=0,
-                     engine=0, tile_order=0, tile_perm=None,
+                     engine=0, tile_order=0, tile_perm=None, per_head_tables=False,
                      stream=None):
     """ART decode attention on device tensors; returns (out fp32, tiles_used int32).
 
@@ -136,17 +139,23 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
     ctx_lens int32 [B]; block_table int32 [B, max_blocks_per_seq].
     tile_order: ORDER_ASCENDING, ORDER_RECENT or ORDER_LIST (then tile_perm is
     an int32 device tensor [B, stride], row b listing its tiles in visiting order).
+    per_head_tables: ctx_lens [B, Hkv], block_table [B, Hkv, mbps] and tile_perm
+    [B, Hkv, stride]: every (row, KV head) has its own sequence.
     """
     import torch
     lib = load()
     B, Hq, d = q.shape
     if block_table is not None:
         nb, Hkv, bs, _ = k_cache.shape
-        mbps = block_table.shape[1]
+        mbps = block_table.shape[-1]
         max_ctx = 0
     else:
         _, Hkv, max_ctx, _ = k_cache.shape
         nb = bs = mbps = 0
+    seqs = (B, Hkv) if per_head_tables else (B,)
+    if tuple(ctx_lens.shape) != seqs or (block_table is not None and tuple(block_table.shape[:-1]) != seqs) \
+            or (tile_perm is not None and tuple(tile_perm.shape[:-1]) != seqs):
+        raise ValueError(f"ctx_lens, block_table and tile_perm must lead with {seqs}")
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("ctx_lens", ctx_lens),
                     ("block_table", block_table), ("k_scale", k_scale), ("v_scale", v_scale),
                     ("tile_perm", tile_perm)):
@@ -160,8 +169,9 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
                      v_scale=v_scale.data_ptr() if v_scale is not None else 0,
                      stats=stats.data_ptr() if stats is not None else 0, max_workers=max_workers,
                      team_helpers=team_helpers, engine=engine, tile_order=tile_order,
-                     tile_perm_stride=tile_perm.shape[1] if tile_perm is not None else 0,
-                     tile_perm=tile_perm.data_ptr() if tile_perm is not None else 0)
+                     tile_perm_stride=tile_perm.shape[-1] if tile_perm is not None else 0,
+                     tile_perm=tile_perm.data_ptr() if tile_perm is not None else 0,
+                     per_head_tables=per_head_tables)
     need = workspace_bytes(desc, tile)
     if need == 0:
         _check(validate(desc, tile, eps_scale, eps_dir))

@@ -81,6 +81,8 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
         return fail(ART_E_PARAM, "team_helpers %d not in 0..%d", d->team_helpers, art::kMaxHelpers);
     if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_SHARED)
         return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_SHARED);
+    if (d->per_head_tables != 0 && d->per_head_tables != 1)
+        return fail(ART_E_PARAM, "per_head_tables %d not 0 or 1", d->per_head_tables);
     if (d->tile_order < ART_ORDER_ASCENDING || d->tile_order > ART_ORDER_LIST)
         return fail(ART_E_PARAM, "tile_order %d not in %d..%d", d->tile_order, ART_ORDER_ASCENDING, ART_ORDER_LIST);
     if (d->tile_order == ART_ORDER_LIST) {
@@ -98,6 +100,18 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     p.cap = (int)cap;
     p.nt_max = (int)((cap + tile - 1) / tile);
     p.NG = d->batch * d->num_kv_heads;
+    p.seq_div = d->per_head_tables ? 1 : d->num_kv_heads;
+    {
+        // multiply-high constants for grp / seq_div (round-up method): with
+        // s = ceil(log2 seq_div), m = ceil(2^(31+s) / seq_div) < 2^32 and
+        // m * seq_div - 2^(31+s) < seq_div <= 2^s, the error term stays below
+        // 1 / seq_div for every grp < 2^31
+        int sh = 0;
+        while ((1LL << sh) < p.seq_div) ++sh;
+        const unsigned long long num = 1ULL << (31 + sh);
+        p.seq_m = (unsigned)((num + p.seq_div - 1) / p.seq_div);
+        p.seq_sh = 31 + sh;
+    }
     p.patience = d->patience;
     p.order = d->tile_order;
     p.tile_perm = d->tile_order == ART_ORDER_LIST ? d->tile_perm : nullptr;
@@ -135,7 +149,7 @@ Layout workspace_layout(const Params& p) {
     const size_t NT = NG <= (size_t)kTeamHelpGroups ? NG : 0;  // groups that helpers may serve
     L.team_ring = o; o = align256(o + NT * group_words(p.G) * sizeof(unsigned long long));
     L.team_ctl = o; o = align256(o + NT * kTeamCtl * sizeof(unsigned long long));
-    const size_t NS = p.order == ART_ORDER_LIST ? (size_t)p.B * p.nt_max : 0;  // step-table records
+    const size_t NS = p.order == ART_ORDER_LIST ? (size_t)(p.NG / p.seq_div) * p.nt_max : 0;  // step-table records
     L.steps = o; o = align256(o + NS * kStepW * sizeof(int));
     L.total = o;
     return L;

@@ -54,6 +54,9 @@ struct Params {
     int cap;            // tokens a row can hold
     int nt_max;         // ceil(cap / T)
     int NG;             // B * Hkv groups
+    int seq_div;        // group grp reads sequence grp / seq_div: Hkv (one per row), or 1 (per-head tables)
+    unsigned seq_m;     // grp / seq_div == (grp * seq_m) >> seq_sh for 0 <= grp < 2^31
+    int seq_sh;
     // method
     int patience;
     int order;          // art_order: tile i of a row's visiting sequence is tile_at(i)
@@ -86,7 +89,7 @@ struct Params {
                                     // [kPoolRing][kTeamRecW][kTeamRecHeads], then worker states
                                     // [kPoolContrib][HB][kTeamStateW][64]; (tag << 32) | value bits
     unsigned long long* team_ctl;   // [NG][kTeamCtl]: (epoch << 32) | value
-    int* steps;         // ART_ORDER_LIST: [B][nt_max][kStepW] step table (see art_steps_kernel)
+    int* steps;         // ART_ORDER_LIST: [sequences][nt_max][kStepW] step table (see art_steps_kernel)
     unsigned epoch;     // distinct per call: stale team words of earlier calls never match
     int helpers;        // helper work-groups per group (team kernel)
     int pool_cap;       // pool kernel: workers that may join one group (<= kPoolContrib)

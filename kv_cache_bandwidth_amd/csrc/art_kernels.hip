@@ -197,10 +197,19 @@ __device__ __forceinline__ void load_small(const void* base, long long off, floa
     }
 }
 
+// The sequence group grp = (b, kv head g) reads -- its length, block-table
+// row and tile list: row b's, or with per-head tables its own, i.e.
+// grp / seq_div with seq_div = Hkv or 1.  The quotient is taken by a
+// multiply-high and shift with the host's constants (exact for grp < 2^31),
+// cheap enough to recompute wherever a tile needs it.
+__device__ __forceinline__ int seq_of(const Params& P, int grp) {
+    return (int)(((unsigned long long)(unsigned)grp * P.seq_m) >> P.seq_sh);
+}
+
 // Row index of cached position j of (b, kv head g); ok=false on an invalid block id.
 __device__ __forceinline__ long long row_index(const Params& P, int b, int g, int j, bool& ok) {
     if (P.block_size == 0) return ((long long)b * P.Hkv + g) * P.max_ctx + j;
-    const int blk = P.block_table[(long long)b * P.mbps + j / P.block_size];
+    const int blk = P.block_table[(long long)seq_of(P, b * P.Hkv + g) * P.mbps + j / P.block_size];
     if (blk < 0 || blk >= P.num_blocks) {
         ok = false;
         return 0;
@@ -208,17 +217,17 @@ __device__ __forceinline__ long long row_index(const Params& P, int b, int g, in
     return ((long long)blk * P.Hkv + g) * P.block_size + (j % P.block_size);
 }
 
-// The tile visited at step t of row b, which has nt tiles.  The tile sequence
+// The tile visited at step t of sequence sq (seq_of), which has nt tiles.  The tile sequence
 // may be reordered (ART summary, section 2.4: recency- or importance-first;
 // the result does not depend on the order, and block 0, the attention sink,
 // is evaluated first): ascending; tile 0 then the most recent first; or the
 // caller's list, whose step 0 must name tile 0 and later steps tiles
 // 1..nt-1 -- any other entry gives -1 and the tile reports an error.  Steps
 // past the row's tiles map to themselves (no position of them exists).
-__device__ __forceinline__ int tile_at(const Params& P, int b, int nt, int t) {
+__device__ __forceinline__ int tile_at(const Params& P, int sq, int nt, int t) {
     if (P.order == ART_ORDER_ASCENDING || t < 0 || t >= nt) return t;
     if (P.order == ART_ORDER_RECENT) return t == 0 ? 0 : nt - t;
-    const int e = P.tile_perm[(long long)b * P.perm_stride + t];
+    const int e = P.tile_perm[(long long)sq * P.perm_stride + t];
     if (t == 0) return e == 0 ? 0 : -1;
     return (e >= 1 && e < nt) ? e : -1;
 }
@@ -285,7 +294,7 @@ struct GenericTile {
     __device__ __forceinline__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
         const int lane = lane_id();
         const int G = P.G, T = P.T;
-        const int pt = tile_at(P, b, (n + T - 1) / T, t);  // the tile of step t
+        const int pt = tile_at(P, seq_of(P, b * P.Hkv + g), (n + T - 1) / T, t);  // the tile of step t
         const int j0 = pt * T;
         float s[2][kMaxG];
         bool valid[2];
@@ -458,7 +467,7 @@ struct FastTile {
     __device__ __forceinline__ bool compute(const Params& P, int b, int g, int n, int t, Hook&& hook, Out& o) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         const int G = P.G;
-        const int pt = tile_at(P, b, (n + T - 1) / T, t);  // the tile of step t
+        const int pt = tile_at(P, seq_of(P, b * P.Hkv + g), (n + T - 1) / T, t);  // the tile of step t
         const int tok0 = pt * T;
         // pages of the tile: first row index and validity (wave-uniform)
         long long prow[PAGES];
@@ -762,7 +771,7 @@ struct Stream {
             const int nt = (n + T - 1) / T;
             return (t <= 0 || t >= nt) ? t : nt - t;
         } else {
-            return tile_at(P, grp / P.Hkv, (n + T - 1) / T, t);
+            return tile_at(P, seq_of(P, grp), (n + T - 1) / T, t);
         }
     }
     // whether tile index pt names a tile: a bad list entry gives -1
@@ -776,12 +785,12 @@ struct Stream {
     __device__ __forceinline__ static void resolve(const Params& P, int grp, int t, TileRef& r) {
         const int b = grp / P.Hkv, g = grp % P.Hkv;
         if constexpr (ORD == ART_ORDER_LIST) {
-            const int n = P.ctx_lens[b];
+            const int n = P.ctx_lens[seq_of(P, grp)];
             resolve_from(P, grp, n, t, fetch_blocks(P, grp, n, t), r);
             return;
         }
         r.grp = grp;
-        r.n = P.ctx_lens[b];
+        r.n = P.ctx_lens[seq_of(P, grp)];
         r.t = phys(P, grp, r.n, t);
         r.pmask = 0;
         r.err = !named(r.t);
@@ -806,17 +815,17 @@ struct Stream {
     // instead: lanes 0..PAGES-1 the pages' block ids, lane PAGES the tile; for
     // a step past the row's tiles lane PAGES holds the step itself.
     __device__ __forceinline__ static int fetch_blocks(const Params& P, int grp, int n, int t) {
-        const int lane = lane_id(), b = grp / P.Hkv;
+        const int lane = lane_id(), sq = seq_of(P, grp);
         if constexpr (ORD == ART_ORDER_LIST) {
             int v = lane == PAGES ? t : 0;
-            if (lane <= PAGES && t < (n + T - 1) / T) v = P.steps[((long long)b * P.nt_max + t) * kStepW + lane];
+            if (lane <= PAGES && t < (n + T - 1) / T) v = P.steps[((long long)sq * P.nt_max + t) * kStepW + lane];
             return v;
         }
         const int pt = phys(P, grp, n, t);
         const int tokp = pt * T + 16 * lane;
         int blk = 0;
         if (P.block_size && lane < PAGES && named(pt) && tokp < n)
-            blk = P.block_table[(long long)b * P.mbps + (unsigned)tokp / (unsigned)P.block_size];
+            blk = P.block_table[(long long)sq * P.mbps + (unsigned)tokp / (unsigned)P.block_size];
         return blk;
     }
 
@@ -824,17 +833,17 @@ struct Stream {
     // so that the ids hold no register while they are in flight; read them
     // (resolve_lds) once the wave's loads have landed
     __device__ __forceinline__ static void fetch_blocks_lds(const Params& P, int grp, int n, int t, int* dst) {
-        const int lane = lane_id(), b = grp / P.Hkv;
+        const int lane = lane_id(), sq = seq_of(P, grp);
         if constexpr (ORD == ART_ORDER_LIST) {
             if (lane <= PAGES && t < (n + T - 1) / T)
-                __builtin_amdgcn_global_load_lds(P.steps + ((long long)b * P.nt_max + t) * kStepW + lane,
+                __builtin_amdgcn_global_load_lds(P.steps + ((long long)sq * P.nt_max + t) * kStepW + lane,
                                                  (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
             return;
         }
         const int pt = phys(P, grp, n, t);
         const int tokp = pt * T + 16 * lane;
         if (P.block_size && lane < PAGES && named(pt) && tokp < n)
-            __builtin_amdgcn_global_load_lds(P.block_table + (long long)b * P.mbps + (unsigned)tokp / (unsigned)P.block_size,
+            __builtin_amdgcn_global_load_lds(P.block_table + (long long)sq * P.mbps + (unsigned)tokp / (unsigned)P.block_size,
                                              (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
     }
     __device__ __forceinline__ static void resolve_lds(const Params& P, int grp, int n, int t, const int* src,
@@ -1576,7 +1585,7 @@ __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
     const int grp = blockIdx.x;
     const int tid = threadIdx.x;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
-    const int n = P.ctx_lens[b];
+    const int n = P.ctx_lens[seq_of(P, grp)];
     const bool bad = n < 0 || n > P.cap;
     const int nt = (bad || n == 0) ? 0 : (n + P.T - 1) / P.T;
     GroupCtl* C = P.ctl + grp;
@@ -1596,25 +1605,25 @@ __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
 }
 
 // A caller's tile list (ART_ORDER_LIST) turned into a step table for the
-// streamed kernels: record (b, s) holds, for the tile visited at step s of
-// row b (tile_at: -1 for a bad list entry), the block id of each of its
+// streamed kernels: record (sq, s) holds, for the tile visited at step s of
+// sequence sq (tile_at: -1 for a bad list entry), the block id of each of its
 // 16-token pages (paged caches) and, last, the tile itself, so that a worker
 // finds a step's tile and blocks with one load that it issues a tile ahead,
 // as for the ascending order.  Records past a row's tiles are never read.
 static_assert(kStepW == 8 && kStepPages == 4, "a step-table record is two 16-byte stores");
 __global__ __launch_bounds__(256) void art_steps_kernel(Params P) {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (long long)P.B * P.nt_max) return;
-    const int b = (int)(i / P.nt_max), s = (int)(i % P.nt_max);
-    const int n = P.ctx_lens[b];
+    if (i >= (long long)(P.NG / P.seq_div) * P.nt_max) return;
+    const int sq = (int)(i / P.nt_max), s = (int)(i % P.nt_max);
+    const int n = P.ctx_lens[sq];
     if (n < 0 || n > P.cap) return;  // the row reports -1 and no worker reads its records
     const int nt = (n + P.T - 1) / P.T;
     if (s >= nt) return;
-    const int pt = tile_at(P, b, nt, s);
+    const int pt = tile_at(P, sq, nt, s);
     int rec[kStepW] = {};
     for (int p = 0; p < kStepPages; ++p) {
         const int tok = pt * P.T + 16 * p;
-        if (P.block_size && pt >= 0 && tok < n) rec[p] = P.block_table[(long long)b * P.mbps + tok / P.block_size];
+        if (P.block_size && pt >= 0 && tok < n) rec[p] = P.block_table[(long long)sq * P.mbps + tok / P.block_size];
     }
     rec[kStepPages] = pt;
     int4* dst = reinterpret_cast<int4*>(P.steps + i * kStepW);
@@ -1653,7 +1662,7 @@ __global__ __launch_bounds__(256) void art_persistent_kernel(Params P) {
             qgrp = grp;
         }
         GroupCtl* C = P.ctl + grp;
-        const int n = P.ctx_lens[b];
+        const int n = P.ctx_lens[seq_of(P, grp)];
         const int vbase = grp * P.nt_max;
         auto hook = [&](const float (&ml)[kMaxG], float (&Mt)[kMaxG]) -> bool {
 #pragma unroll
@@ -2573,7 +2582,7 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     const int G = P.G;
     const int grp = blockIdx.x % P.NG, team = blockIdx.x / P.NG;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
-    const int n = P.ctx_lens[b];
+    const int n = P.ctx_lens[seq_of(P, grp)];
     const bool bad = n < 0 || n > P.cap;
     const int nt = (bad || n == 0) ? 0 : (n + S::T - 1) / S::T;
     if (nt == 0) {
@@ -2700,7 +2709,7 @@ struct PoolGlobal {
 
 // tiles of group grp (0 for an empty or invalid row)
 __device__ __forceinline__ int group_tiles(const Params& P, int grp, int T) {
-    const int n = P.ctx_lens[grp / P.Hkv];
+    const int n = P.ctx_lens[seq_of(P, grp)];
     return (n <= 0 || n > P.cap) ? 0 : (n + T - 1) / T;
 }
 
@@ -2712,7 +2721,7 @@ __device__ __forceinline__ void pool_decider(const Params& P, int grp, int T) {
     const unsigned e = P.epoch;
     const PoolGlobal pg(P, grp);
     const int b = grp / P.Hkv, g = grp % P.Hkv;
-    const int n = P.ctx_lens[b];
+    const int n = P.ctx_lens[seq_of(P, grp)];
     const bool bad = n < 0 || n > P.cap;
     const int nt = (bad || n == 0) ? 0 : (n + T - 1) / T;
     // reset the counters (the claim counter last: workers join once they see it reset)
@@ -2923,7 +2932,7 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
             if (grp < 0) break;
         }
         const PoolGlobal pg(P, grp);
-        const int n = P.ctx_lens[grp / P.Hkv];
+        const int n = P.ctx_lens[seq_of(P, grp)];
         const int nt = group_tiles(P, grp, T);
         if (nt == 0) continue;
         // join: once the group's counters are reset, take a state slot
@@ -3179,7 +3188,7 @@ __global__ __launch_bounds__(256) void art_full_kernel(Params P) {
     const FoldLanes fl(P);
     const int grp = worker / P.splits, sp = worker % P.splits;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
-    const int n = P.ctx_lens[b];
+    const int n = P.ctx_lens[seq_of(P, grp)];
     const bool bad = n < 0 || n > P.cap;
     const int nt = bad ? 0 : (n + P.T - 1) / P.T;
     const int t0 = sp * P.tiles_per_split;
@@ -3258,8 +3267,7 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_full_stream_kernel(Para
     if (worker >= P.NG * P.splits) return;
     const FoldLanes fl(P);
     const int grp = worker / P.splits, sp = worker % P.splits;
-    const int b = grp / P.Hkv;
-    const int n = P.ctx_lens[b];
+    const int n = P.ctx_lens[seq_of(P, grp)];
     const bool bad = n < 0 || n > P.cap;
     const int nt = bad ? 0 : (n + S::T - 1) / S::T;
     const int t0 = sp * P.tiles_per_split;
@@ -3330,7 +3338,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void art_combine_kernel(Params 
     const FoldLanes fl(P);
     const int G = P.G, D = P.D;
     const int b = grp / P.Hkv, g = grp % P.Hkv;
-    const int n = P.ctx_lens[b];
+    const int n = P.ctx_lens[seq_of(P, grp)];
     const bool bad = n < 0 || n > P.cap;
     const int nt = bad ? 0 : (n + P.T - 1) / P.T;
     const float* base = P.partials + (long long)grp * P.splits * P.slot;
@@ -3518,7 +3526,7 @@ int launch_pool(const Params& p0, hipStream_t s) {
 template <class S>
 int run_stream(const Params& p, hipStream_t s, bool art) {
     if constexpr (S::ORDER == ART_ORDER_LIST) {
-        const long long recs = (long long)p.B * p.nt_max;
+        const long long recs = (long long)(p.NG / p.seq_div) * p.nt_max;
         if (recs > 0) {
             hipLaunchKernelGGL(art_steps_kernel, dim3((unsigned)((recs + 255) / 256)), dim3(256), 0, s, p);
             const hipError_t e = hipGetLastError();

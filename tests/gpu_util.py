@@ -43,7 +43,8 @@ def run_gpu(case, dev=None, **kw):
     args = dict(block_table=dev["bt"], tile=case.tile, eps_scale=case.eps_scale,
                 eps_dir=case.eps_dir, patience=case.patience, v_skip_eps=case.v_skip_eps,
                 k_scale=dev["ks"], v_scale=dev["vs"], tile_order=case.order,
-                tile_perm=dev["perm"] if case.order == 2 else None)
+                tile_perm=dev["perm"] if case.order == 2 else None,
+                per_head_tables=case.per_head_tables)
     args.update(kw)
     out, used = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], **args)
     torch.cuda.synchronize()
@@ -85,7 +86,7 @@ def check_parity(case, out, used, *, eps_scale=None, eps_dir=None, patience=None
                                  f"gpu {g_used[bi, h]} oracle {ora.tiles_used[bi, h]}")
             near.append((rows[bi], int(h), int(g_used[bi, h]), int(ora.tiles_used[bi, h])))
             if vk == 0 and g_used[bi, h] > 0:
-                ref = BF.attention_at(sub, bi, int(h), visited_positions(sub, bi, int(g_used[bi, h])))
+                ref = BF.attention_at(sub, bi, int(h), visited_positions(sub, bi, int(h), int(g_used[bi, h])))
                 assert np.abs(g_out[bi, h] - ref).max() <= tol
     same = g_used == ora.tiles_used
     err = np.abs(g_out - ora.out).max(axis=-1)
@@ -96,16 +97,18 @@ def check_parity(case, out, used, *, eps_scale=None, eps_dir=None, patience=None
     return dict(max_abs=maxerr, near=near, heads=int(same.size), tiles_used=ora.tiles_used)
 
 
-def visited_positions(case, b, steps):
-    """Positions of the tiles row b visits in its first `steps` steps."""
-    T, n = case.tile, int(case.ctx_lens[b])
+def visited_positions(case, b, h, steps):
+    """Positions of the tiles head h of row b visits in its first `steps` steps."""
+    g = h // (case.Hq // case.Hkv)
+    sq = (b, g) if case.per_head_tables else (b,)
+    T, n = case.tile, int(case.ctx_lens[sq])
     nt = -(-n // T)
     if case.order == 0:
         seq = list(range(nt))
     elif case.order == 1:
         seq = [0] + list(range(nt - 1, 0, -1))
     else:
-        seq = [int(x) for x in case.tile_perm[b, :nt]]
+        seq = [int(x) for x in case.tile_perm[sq][:nt]]
     return [j for s in seq[:steps] for j in range(s * T, min(n, (s + 1) * T))]
 
 

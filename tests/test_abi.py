@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = art.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.art_abi_version() == 4
+    assert lib.art_abi_version() == 5
 
 
 def desc(**kw):
@@ -51,6 +51,7 @@ def test_valid_desc_passes():
     assert B.validate(ok_desc(), 64, 1e-3, 1e-4) == 0
     assert B.validate(ok_desc(block_size=0, max_ctx=64), 64, 0.0, 0.0) == 0
     assert B.validate(ok_desc(tile_order=1), 64, 1e-3, 1e-4) == 0
+    assert B.validate(ok_desc(per_head_tables=1), 64, 1e-3, 1e-4) == 0
     # a caller's order: one entry per tile a row can hold (8 blocks of 16 -> 2 tiles of 64)
     assert B.validate(ok_desc(max_blocks_per_seq=8, tile_order=2, tile_perm=1 << 20, tile_perm_stride=2),
                       64, 1e-3, 1e-4) == 0
@@ -83,6 +84,7 @@ def test_valid_desc_passes():
     (dict(tile_order=-1), -5),
     (dict(tile_order=3), -5),
     (dict(tile_order=2), -1),                  # a caller's order without tile_perm
+    (dict(per_head_tables=2), -5),
     (dict(tile_order=2, tile_perm=1 << 20, tile_perm_stride=0), -2),  # 4 blocks of 16 = 1 tile
 ])
 def test_bad_desc_rejected(kw, code):
