@@ -253,8 +253,72 @@ def main():
             "max_abs_out": float(np.abs(out.cpu().numpy().astype(np.float64) - r.out).max())}
     if not args.no_others:
         res["tile_orders"] = tile_orders(case, dev, flush_buf)
+        res["per_head_retention"] = per_head_retention(case, flush_buf)
+        res["vskip_bf16"] = vskip_bf16(case, dev, flush_buf)
         res["other_workloads"] = other_workloads(args, flush_buf)
     print(json.dumps(res), flush=True)
+
+
+def _median_call(dev, a, flush_buf, steps):
+    import torch
+    import kv_cache_bandwidth_amd as art
+    stream = torch.cuda.current_stream()
+    out, used = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], **a)
+    ms = []
+    for _ in range(steps + 2):
+        flush_buf.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], out=out, tiles_used=used, **a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return statistics.median(ms[2:]) * 1e3, used.cpu().numpy()
+
+
+def per_head_retention(case, flush_buf, steps=7):
+    """Context, not the metric: ART on top of per-head block tables -- each KV
+    head keeps its row's first 4 blocks, the last 512 (8K tokens) and a random
+    quarter of the blocks between, drawn per head -- against full attention
+    over the same retained tables (median us per call)."""
+    import art_inputs as A
+    from tests.gpu_util import to_device
+    log("context timing: per-head retention tables")
+    kept = A.retained_tables(case, sink_blocks=4, recent_blocks=512, keep_frac=0.25, seed=1)
+    dev = to_device(kept)
+    a = dict(block_table=dev["bt"], tile=kept.tile, eps_scale=kept.eps_scale, eps_dir=kept.eps_dir,
+             patience=kept.patience, v_skip_eps=kept.v_skip_eps, k_scale=dev["ks"], v_scale=dev["vs"],
+             per_head_tables=True)
+    t_art, used = _median_call(dev, a, flush_buf, steps)
+    t_full, _ = _median_call(dev, dict(a, eps_scale=0.0, eps_dir=0.0), flush_buf, steps)
+    G = kept.Hq // kept.Hkv
+    nt = -(-kept.ctx_lens // kept.tile)
+    return {"policy": "per KV head: first 4 + last 512 blocks of 16, a random 25% of the rest",
+            "kept_tokens_share": round(float(kept.ctx_lens.sum() / (case.ctx_lens.sum() * case.Hkv)), 4),
+            "art_us": round(t_art, 1), "full_us": round(t_full, 1),
+            "kv_tiles_skipped_head_level": round(float(1.0 - used.sum() / (np.repeat(nt, G, axis=1)).sum()), 4)}
+
+
+def vskip_bf16(case, dev, flush_buf, steps=7):
+    """Context, not the metric: the V skip on this bf16 workload (same
+    thresholds), median us per call and the share of (query head, V row)
+    pairs of the tiles read that were skipped."""
+    import torch
+    res = {}
+    for eps in (1e-6, 1e-4):
+        log(f"context timing: V skip {eps:g} on bf16")
+        a = dict(block_table=dev["bt"], tile=case.tile, eps_scale=case.eps_scale, eps_dir=case.eps_dir,
+                 patience=case.patience, v_skip_eps=eps, k_scale=dev["ks"], v_scale=dev["vs"])
+        stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+        import kv_cache_bandwidth_amd as art
+        art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], stats=stats, **a)
+        torch.cuda.synchronize()
+        st = stats.cpu().numpy()
+        t, _ = _median_call(dev, a, flush_buf, steps)
+        G = case.Hq // case.Hkv
+        res[f"eps_{eps:g}"] = {"art_us": round(t, 1),
+                               "pairs_skipped_share": round(float(st[3]) / max(1.0, float(st[0]) * case.tile * G), 4)}
+    return res
 
 
 def tile_orders(case, dev, flush_buf, steps=7):

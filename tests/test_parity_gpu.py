@@ -18,7 +18,7 @@ def _run_and_check(case, label, **kw):
         f"ctx={case.ctx_lens.tolist()[:4]} kv={case.kv_dtype} T={case.tile} {kw}")
     out, used = run_gpu(case, **kw)
     r = check_parity(case, out, used,
-                     **{k: v for k, v in kw.items() if k not in ("max_workers", "team_helpers", "engine")})
+                     **{k: v for k, v in kw.items() if k not in ("max_workers", "team_helpers", "engine", "stats")})
     log(f"[parity] {label}: max_abs={r['max_abs']:.3e} near={r['near']} "
         f"mean tiles_used={np.mean(r['tiles_used']):.1f}")
     return out, used, r
@@ -274,3 +274,20 @@ def test_full_size_sampled_rows(n):
         log(f"[parity] config{n} full size {kw}: max_abs={r['max_abs']:.3e} near={r['near']} "
             f"mean tiles_used (sampled)={np.mean(r['tiles_used']):.1f}")
         assert (used <= -(-c.ctx_lens[:, None] // c.tile)).all() and (used >= 1).all()
+
+
+# ---------------------------------------------------------------- V skip on bf16 caches
+
+@pytest.mark.parametrize("n", [3, 4])
+def test_vskip_bf16_cache(n):
+    # the V-skip predicate does not depend on the cache format: bf16 caches
+    # take the same skip path as int8 ones (team kernel, work-sharing engine,
+    # one-tile-at-a-time kernel for fp32 queries)
+    import torch
+    c = A.config(n, small=True, v_skip_eps=1e-4)
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    _run_and_check(c, f"config{n} bf16 art+vskip", stats=stats)
+    assert int(stats[3].item()) > 0  # some (head, row) pairs were skipped
+    _run_and_check(c, f"config{n} bf16 full+vskip", eps_scale=0.0, eps_dir=0.0)
+    _run_and_check(c, f"config{n} bf16 art+vskip work-sharing", max_workers=96)
+    _run_and_check(c, f"config{n} bf16 art+vskip patience 3", patience=3)
