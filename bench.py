@@ -92,6 +92,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (a known-size "
                          "reference for hardware byte counters) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the threshold / patience sweep (stops, error against full "
+                         "attention, premature stops, time) on workloads 3, 4 and 3 with drifting "
+                         "values, print one JSON line and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode-attention path is single-GPU "
@@ -107,6 +111,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.sweep:
+        print(json.dumps(threshold_sweep(args)), flush=True)
         return
     import art_inputs as A
     import kv_cache_bandwidth_amd as art
@@ -297,6 +304,61 @@ def per_head_retention(case, flush_buf, steps=7):
             "kept_tokens_share": round(float(kept.ctx_lens.sum() / (case.ctx_lens.sum() * case.Hkv)), 4),
             "art_us": round(t_art, 1), "full_us": round(t_full, 1),
             "kv_tiles_skipped_head_level": round(float(1.0 - used.sum() / (np.repeat(nt, G, axis=1)).sum()), 4)}
+
+
+SWEEP_SCALE = (1e-4, 1e-3, 1e-2)
+SWEEP_DIR = (1e-5, 1e-4, 1e-3)
+SWEEP_PATIENCE = (1, 2, 4)
+
+
+def threshold_sweep(args, steps=5):
+    """The stop rule against its parameters (ART summary, sections 2.2-2.3):
+    for every (eps_scale, eps_dir, patience) of the grid, on workload 3, on
+    workload 4 (rows of large value at low weight) and on workload 3 with
+    values drifting around a common mean: the share of (head, tile) pairs
+    skipped, the error of each head's output against full attention (relative
+    L2), the share of stopped heads whose error exceeds 1e-2 and 1e-3
+    (premature stops), and the median time per call."""
+    import torch
+    import art_inputs as A
+    import kv_cache_bandwidth_amd as art
+    from tests.gpu_util import to_device
+    flush_buf = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device="cuda")
+    res = {"grid": {"eps_scale": SWEEP_SCALE, "eps_dir": SWEEP_DIR, "patience": SWEEP_PATIENCE},
+           "workloads": {}}
+    for name, case in (("workload3", lambda: A.config(3, seed=args.seed)),
+                       ("workload4", lambda: A.config(4, seed=args.seed)),
+                       ("workload3_drift", lambda: A.config(3, seed=args.seed, v_mean=3.0))):
+        log(f"sweep: generating {name}")
+        case = case()
+        dev = to_device(case)
+        base = dict(block_table=dev["bt"], tile=case.tile, v_skip_eps=0.0, k_scale=dev["ks"],
+                    v_scale=dev["vs"])
+        full, _ = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], eps_scale=0.0,
+                                       eps_dir=0.0, **base)
+        full = full.double()
+        fn = full.norm(dim=-1)
+        nt = torch.from_numpy(-(-case.ctx_lens // case.tile)).cuda()[:, None]
+        rows = []
+        for es in SWEEP_SCALE:
+            for ed in SWEEP_DIR:
+                for p in SWEEP_PATIENCE:
+                    a = dict(base, eps_scale=es, eps_dir=ed, patience=p)
+                    out, used = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], **a)
+                    err = (out.double() - full).norm(dim=-1) / fn
+                    stopped = used < nt
+                    ns = int(stopped.sum())
+                    t, _ = _median_call(dev, a, flush_buf, steps)
+                    rows.append({"eps_scale": es, "eps_dir": ed, "patience": p,
+                                 "skipped": round(1.0 - float(used.sum()) / float((nt * case.Hq).sum()), 4),
+                                 "err_max": float(err.max()), "err_mean": float(err.mean()),
+                                 "premature_1e-2": round(float((stopped & (err > 1e-2)).sum()) / max(1, ns), 4),
+                                 "premature_1e-3": round(float((stopped & (err > 1e-3)).sum()) / max(1, ns), 4),
+                                 "us": round(t, 1)})
+        res["workloads"][name] = {"workload": A.WORKLOADS[3 if "3" in name else 4]
+                                  + (", values N(3, 1)" if "drift" in name else ""), "rows": rows}
+        del dev
+    return res
 
 
 def vskip_bf16(case, dev, flush_buf, steps=7):
