@@ -116,6 +116,25 @@ def quantize_int8(x):
     return codes, scale.view(np.uint16)
 
 
+def quantize_int4(x):
+    """Symmetric per-row int4: scale = fp16(max|x| / 7); code = rint(x/scale)
+    clipped to [-7, 7]; codes packed two per byte, element 2i in the low nibble
+    of byte i (two's complement nibbles).
+
+    Returns (uint8 array shaped like x with the last dim halved, uint16 fp16-bit
+    scales shaped x.shape[:-1]).  Rows of zeros get scale 1 and codes 0.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    assert x.shape[-1] % 2 == 0
+    amax = np.abs(x).max(axis=-1)
+    scale = (amax / np.float32(7.0)).astype(np.float16)
+    scale = np.where(scale == 0, np.float16(1.0), scale)
+    s32 = scale.astype(np.float32)[..., None]
+    codes = np.clip(np.rint(x / s32), -7, 7).astype(np.int8)
+    nib = (codes.astype(np.int16) & 0xF).astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8), scale.view(np.uint16)
+
+
 # ---------------------------------------------------------------- container
 
 @dataclass
@@ -151,7 +170,7 @@ class Case:
     @property
     def kv_dtype(self) -> str:
         return {np.dtype(np.float32): "f32", np.dtype(np.uint16): "bf16",
-                np.dtype(np.int8): "i8"}[self.k.dtype]
+                np.dtype(np.int8): "i8", np.dtype(np.uint8): "i4"}[self.k.dtype]
 
     @property
     def max_ctx(self) -> int:
@@ -165,7 +184,7 @@ class Case:
 
     def kv_bytes_full(self) -> int:
         """Bytes of K+V (+ scales) covering every position 0..ctx_len-1."""
-        per = self.d * self.k.dtype.itemsize * 2 + (4 if self.kv_dtype == "i8" else 0)
+        per = self.k.shape[-1] * self.k.dtype.itemsize * 2 + (4 if self.kv_dtype in ("i8", "i4") else 0)
         return int(self.ctx_lens.astype(np.int64).sum()) * self.Hkv * per
 
 
@@ -178,6 +197,8 @@ def _store(x, kv_dtype):
         return bf16_bits(x), None
     if kv_dtype == "i8":
         return quantize_int8(x)
+    if kv_dtype == "i4":
+        return quantize_int4(x)
     raise ValueError(kv_dtype)
 
 
@@ -262,10 +283,10 @@ def make_case(name, *, B, Hq, Hkv, d, ctx_lens, seed=0, kv_dtype="bf16", q_dtype
         assert nb >= B * nb_seq
         perm = rng.permutation(nb)[:B * nb_seq].astype(np.int32)
         block_table = perm.reshape(B, nb_seq)
-        shape = (nb, Hkv, block_size, d)
+        shape = (nb, Hkv, block_size, d // 2 if kv_dtype == "i4" else d)
         k_arr = np.zeros(shape, _storage_np(kv_dtype))
         v_arr = np.zeros(shape, _storage_np(kv_dtype))
-        if kv_dtype == "i8":
+        if kv_dtype in ("i8", "i4"):
             k_scale = np.zeros(shape[:-1], np.uint16)
             v_scale = np.zeros(shape[:-1], np.uint16)
         for b in range(B):
@@ -273,17 +294,17 @@ def make_case(name, *, B, Hq, Hkv, d, ctx_lens, seed=0, kv_dtype="bf16", q_dtype
             for g in range(Hkv):
                 for src, dst, sc in ((k_log, k_arr, k_scale), (v_log, v_arr, v_scale)):
                     data, scale = _store(src[b][g], kv_dtype)
-                    dst[rows, g] = data.reshape(nb_seq, block_size, d)
+                    dst[rows, g] = data.reshape(nb_seq, block_size, shape[-1])
                     if sc is not None:
                         sc[rows, g] = scale.reshape(nb_seq, block_size)
                 src = None
             k_log[b] = v_log[b] = None  # free as we go
     else:
         block_table = None
-        shape = (B, Hkv, max_ctx, d)
+        shape = (B, Hkv, max_ctx, d // 2 if kv_dtype == "i4" else d)
         k_arr = np.zeros(shape, _storage_np(kv_dtype))
         v_arr = np.zeros(shape, _storage_np(kv_dtype))
-        if kv_dtype == "i8":
+        if kv_dtype in ("i8", "i4"):
             k_scale = np.zeros(shape[:-1], np.uint16)
             v_scale = np.zeros(shape[:-1], np.uint16)
         for b in range(B):
@@ -300,7 +321,7 @@ def make_case(name, *, B, Hq, Hkv, d, ctx_lens, seed=0, kv_dtype="bf16", q_dtype
 
 
 def _storage_np(kv_dtype):
-    return {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[kv_dtype]
+    return {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "i4": np.uint8}[kv_dtype]
 
 
 # ---------------------------------------------------------------- named workloads
@@ -343,5 +364,6 @@ def config(n: int, seed: int = 0, *, small: bool = False, batch=None, ctx=None,
         B = batch
     if ctx is not None:
         n_ctx = ctx
+    kw.update(params)  # a caller's setting (e.g. kv_dtype) overrides the workload's
     return make_case(f"config{n}{'-small' if small else ''}", B=B, Hq=Hq, Hkv=Hkv, d=d,
-                     ctx_lens=[n_ctx] * B, seed=seed, **kw, **params)
+                     ctx_lens=[n_ctx] * B, seed=seed, **kw)

@@ -25,7 +25,7 @@ _SRC = os.path.join(_HERE, "art_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # dtype codes of the oracle's C interface
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, I4 = 0, 1, 2, 3
 
 # fields of one trace record (per batch row, query head, tile)
 TRACE_FIELDS = ("m", "l", "d_scale", "d_dir", "streak", "kept", "probe_norm", "evaluated")
@@ -84,7 +84,8 @@ def decode(q, k, v, ctx_lens, *, tile=64, eps_scale=1e-3, eps_dir=1e-4, patience
 
     q: [B, Hq, d] float32, or uint16 bf16 bit patterns.
     k, v: contiguous [B, Hkv, max_ctx, d] when block_size == 0, else paged
-          [num_blocks, Hkv, block_size, d]; float32, uint16 (bf16 bits) or int8.
+          [num_blocks, Hkv, block_size, d]; float32, uint16 (bf16 bits), int8,
+          or uint8 holding int4 codes two per byte (last dim d / 2).
     k_scale, v_scale: uint16 fp16 bit patterns shaped like k/v without the last
           dim (int8 caches only).
     block_table: int32 [B, max_blocks_per_seq] (paged only).
@@ -104,7 +105,7 @@ def decode(q, k, v, ctx_lens, *, tile=64, eps_scale=1e-3, eps_dir=1e-4, patience
         q_dtype = F32 if q.dtype == np.float32 else BF16
     if kv_dtype is None:
         kv_dtype = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16,
-                    np.dtype(np.int8): I8}[k.dtype]
+                    np.dtype(np.int8): I8, np.dtype(np.uint8): I4}[k.dtype]
     if block_size:
         num_blocks, Hkv, bs, _ = k.shape
         assert bs == block_size
@@ -119,7 +120,7 @@ def decode(q, k, v, ctx_lens, *, tile=64, eps_scale=1e-3, eps_dir=1e-4, patience
     assert ctx_lens.shape == seqs, (ctx_lens.shape, seqs)
     if block_size:
         assert block_table.shape[:-1] == seqs, (block_table.shape, seqs)
-    if kv_dtype == I8:
+    if kv_dtype in (I8, I4):
         k_scale = np.ascontiguousarray(k_scale, dtype=np.uint16)
         v_scale = np.ascontiguousarray(v_scale, dtype=np.uint16)
     stride = 0

@@ -43,7 +43,9 @@
  * ones this file depends on: scores are q.k / sqrt(d); a probe of norm zero
  * makes both metrics +infinity (never passes); ctx_len 0 gives out = 0 and
  * tiles_used = 0; int8 values are dequantised as int8 * fp16 scale per
- * (token, KV head).
+ * (token, KV head); int4 values likewise, as signed 4-bit codes stored two
+ * per byte, element 2i in the low nibble of byte i (a format of this
+ * library: the pages name lower-bit caches but do not specify a codec).
  *
  * Pins: see tests/test_oracle.py (brute-force softmax attention, prefix
  * identity, convexity, constant-V closed form, designed probe sequences,
@@ -57,7 +59,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_I8 = 2 };
+enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_I8 = 2, ODT_I4 = 3 };
 
 /* trace record per (b, h, tile): see ORACLE_TRACE_FIELDS in oracle/__init__.py */
 #define TRACE_FIELDS 8
@@ -146,10 +148,18 @@ static void load_row(const job_t *J, const void *base, const uint16_t *scale, lo
     } else if (J->kv_dtype == ODT_BF16) {
         const uint16_t *p = (const uint16_t *)base + row * d;
         for (int i = 0; i < d; ++i) dst[i] = widen_bf16(p[i]);
-    } else {
+    } else if (J->kv_dtype == ODT_I8) {
         const int8_t *p = (const int8_t *)base + row * d;
         double s = widen_f16(scale[row]);
         for (int i = 0; i < d; ++i) dst[i] = (double)p[i] * s;
+    } else {
+        const uint8_t *p = (const uint8_t *)base + row * (d / 2);
+        double s = widen_f16(scale[row]);
+        for (int i = 0; i < d; ++i) {
+            int nib = (i % 2 == 0) ? (p[i / 2] & 0x0f) : (p[i / 2] >> 4);
+            int code = nib >= 8 ? nib - 16 : nib; /* two's complement, 4 bits */
+            dst[i] = (double)code * s;
+        }
     }
 }
 
@@ -279,8 +289,9 @@ int art_oracle_decode(int B, int Hq, int Hkv, int d, int q_dtype, int kv_dtype,
     if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return -2;
     if (!q || !k || !v || !ctx_lens || !out || !tiles_used) return -1;
     if (q_dtype != ODT_F32 && q_dtype != ODT_BF16) return -3;
-    if (kv_dtype < ODT_F32 || kv_dtype > ODT_I8) return -3;
-    if (kv_dtype == ODT_I8 && (!k_scale || !v_scale)) return -1;
+    if (kv_dtype < ODT_F32 || kv_dtype > ODT_I4) return -3;
+    if ((kv_dtype == ODT_I8 || kv_dtype == ODT_I4) && (!k_scale || !v_scale)) return -1;
+    if (kv_dtype == ODT_I4 && d % 2) return -2;
     if (tile <= 0 || patience < 1) return -5;
     if (order < 0 || order > 2) return -5;
     if (order == 2 && !perm) return -1;

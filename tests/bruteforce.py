@@ -39,6 +39,11 @@ def logical_rows(case, which: str, b: int, g: int, n: int) -> np.ndarray:
     if raw.dtype == np.int8:
         s = sc.view(np.float16).astype(np.float64)
         return raw.astype(np.float64) * s[:, None]
+    if raw.dtype == np.uint8:  # int4 codes, element 2i in the low nibble of byte i
+        nib = np.stack([raw & 0x0F, raw >> 4], axis=-1).reshape(raw.shape[0], -1).astype(np.int64)
+        codes = np.where(nib >= 8, nib - 16, nib)
+        s = sc.view(np.float16).astype(np.float64)
+        return codes.astype(np.float64) * s[:, None]
     return widen(raw)
 
 

@@ -226,6 +226,51 @@ def test_int8_equals_dequantised_fp32():
         assert np.array_equal(a.out, b.out) and np.array_equal(a.tiles_used, b.tiles_used)
 
 
+def int4_reference_decode(packed, sc):
+    """The int4 codec decoded by hand: byte i holds element 2i in bits 0-3 and
+    element 2i+1 in bits 4-7, each a two's complement 4-bit code."""
+    out = np.zeros(packed.shape[:-1] + (2 * packed.shape[-1],), np.float32)
+    for e in range(out.shape[-1]):
+        byte = packed[..., e // 2].astype(np.int32)
+        nib = (byte >> (4 * (e % 2))) & 15
+        out[..., e] = np.where(nib > 7, nib - 16, nib)
+    return out * sc.view(np.float16).astype(np.float32)[..., None]
+
+
+def test_int4_codec_round_trip():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 3, 64)).astype(np.float32)
+    x[0, 0] = 0.0
+    packed, sc = A.quantize_int4(x)
+    assert packed.shape == (5, 3, 32) and packed.dtype == np.uint8
+    y = int4_reference_decode(packed, sc)
+    step = sc.view(np.float16).astype(np.float32)[..., None]
+    assert (np.abs(y - x) <= 0.5 * step + 1e-6).all()   # rounding to the nearest code
+    assert (y[0, 0] == 0).all()
+    # codes span -7..7 and the largest magnitude of each row maps to +-7
+    codes = np.rint(y / step)
+    assert codes.min() >= -7 and codes.max() <= 7
+    assert (np.abs(codes).max(axis=-1)[1:] == 7).all()
+
+
+def test_int4_equals_dequantised_fp32():
+    c = A.config(5, small=True, seed=3, batch=1, ctx=512, kv_dtype="i4")
+    assert c.kv_dtype == "i4" and c.k.shape[-1] == c.d // 2
+    f = A.Case(name="deq", B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, q=c.q,
+               k=int4_reference_decode(c.k, c.k_scale), v=int4_reference_decode(c.v, c.v_scale),
+               ctx_lens=c.ctx_lens, block_size=c.block_size, block_table=c.block_table, tile=c.tile)
+    for kw in (dict(v_skip_eps=0.0), dict(v_skip_eps=1e-4),
+               dict(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)):
+        a = run_oracle(c, **kw)
+        b = run_oracle(f, **kw)
+        assert np.array_equal(a.out, b.out) and np.array_equal(a.tiles_used, b.tiles_used)
+    # and full mode is plain attention over the decoded cache
+    r = run_oracle(c, eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
+    n = int(c.ctx_lens[0])
+    for h in (0, c.Hq - 1):
+        assert np.allclose(r.out[0, h], BF.attention(c, 0, h, n), rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- P10: V skip
 
 def test_vskip_limits():

@@ -52,6 +52,9 @@ MUTANTS = {
     "perm_row_ignored": ("J->perm[sq * J->perm_stride + t]", "J->perm[t]"),
     "perm_sink_not_forced": ("if (t == 0) return e == 0 ? 0 : -1;", "if (t == 0) return (e >= 0 && e < nt) ? e : -1;"),
     "positions_from_step": ("const int j0 = pt * T, j1", "const int j0 = t * T, j1"),
+    "int4_nibbles_swapped": ("int nib = (i % 2 == 0) ? (p[i / 2] & 0x0f) : (p[i / 2] >> 4);",
+                             "int nib = (i % 2 == 1) ? (p[i / 2] & 0x0f) : (p[i / 2] >> 4);"),
+    "int4_unsigned_codes": ("int code = nib >= 8 ? nib - 16 : nib;", "int code = nib;"),
     "per_head_sequence_ignored": ("return J->per_head ? (long)b * J->Hkv + g : b;", "return b;"),
     "per_head_table_row_shared": ("J->block_table[seq_of(J, b, g) * J->max_blocks_per_seq",
                                   "J->block_table[(long)b * J->max_blocks_per_seq"),
@@ -87,6 +90,7 @@ PINS = [
     P.test_order_entries_past_the_stop_are_not_read,
     lambda: [P.test_per_head_tables_equal_separate_calls(o, k) for o in (0, 2) for k in (0.0, 0.5)],
     P.test_retained_full_mode_is_attention_over_kept_positions,
+    P.test_int4_equals_dequantised_fp32,
 ]
 
 
