@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define ART_ABI_VERSION 5
+#define ART_ABI_VERSION 6
 
 typedef enum {
     ART_OK = 0,
@@ -40,7 +40,12 @@ typedef enum {
     ART_E_HIP = -7          /* a HIP runtime call (launch) failed                  */
 } art_status;
 
-typedef enum { ART_F32 = 0, ART_BF16 = 1, ART_I8 = 2 } art_dtype;
+/* ART_I4: signed 4-bit codes, two per byte -- element 2i in the low nibble of
+ * byte i, element 2i + 1 in the high nibble -- with the same per-(token, KV
+ * head) fp16 scale as ART_I8; a cache row is head_dim / 2 bytes.  This
+ * library's own lower-bit format (the pages name quantised caches without
+ * specifying their codecs). */
+typedef enum { ART_F32 = 0, ART_BF16 = 1, ART_I8 = 2, ART_I4 = 3 } art_dtype;
 
 /* How ART-mode work is spread over the GPU (results agree to rounding; tiles_used
  * is the same whichever runs).  The choice applies to bf16/int8 caches with
@@ -74,9 +79,10 @@ typedef enum {
  *   q           [batch][num_q_heads][head_dim]           q_dtype (F32 or BF16)
  *   k/v cache   paged:      [num_blocks][num_kv_heads][block_size][head_dim]
  *               contiguous: [batch][num_kv_heads][max_ctx][head_dim]
- *               kv_dtype F32, BF16, or I8 (then k_scale/v_scale are required)
+ *               kv_dtype F32, BF16, I8 or I4 (then k_scale/v_scale are required;
+ *               I4 rows hold head_dim / 2 bytes)
  *   k/v scale   fp16 bit patterns, the cache layout without head_dim: one scale
- *               per (token, KV head); the value of an I8 entry is code * scale
+ *               per (token, KV head); the value of an I8 or I4 entry is code * scale
  *   block_table int32 [batch][max_blocks_per_seq] (paged only): logical page p
  *               of row b lives in physical block block_table[b][p]
  *   ctx_lens    int32 [batch]: cached positions of each row (0 allowed)

@@ -13,7 +13,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libart.so")
 
-ART_F32, ART_BF16, ART_I8 = 0, 1, 2
+ART_F32, ART_BF16, ART_I8, ART_I4 = 0, 1, 2, 3
 ORDER_ASCENDING, ORDER_RECENT, ORDER_LIST = 0, 1, 2
 
 STATUS = {0: "ART_OK", -1: "ART_E_NULL", -2: "ART_E_SHAPE", -3: "ART_E_DTYPE", -4: "ART_E_TILE",
@@ -62,7 +62,7 @@ class ArtDesc(ctypes.Structure):
 _lib = None
 
 
-ABI_VERSION = 5  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
+ABI_VERSION = 6  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
 
 
 def load():
@@ -123,7 +123,8 @@ def validate(desc: ArtDesc, tile: int, eps_scale: float, eps_dir: float) -> int:
 
 def _dtype_code(t):
     import torch
-    return {torch.float32: ART_F32, torch.bfloat16: ART_BF16, torch.int8: ART_I8}[t.dtype]
+    # uint8 caches hold packed int4 codes (two per byte)
+    return {torch.float32: ART_F32, torch.bfloat16: ART_BF16, torch.int8: ART_I8, torch.uint8: ART_I4}[t.dtype]
 
 
 def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64, eps_scale=1e-3,
@@ -135,7 +136,8 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
 
     q [B, Hq, d] fp32/bf16; k_cache/v_cache paged [num_blocks, Hkv, bs, d] when
     block_table is given, else contiguous [B, Hkv, max_ctx, d]; fp32/bf16/int8
-    (int8 needs k_scale/v_scale fp16 shaped like the cache without d).
+    (int8 needs k_scale/v_scale fp16 shaped like the cache without d); a uint8
+    cache holds int4 codes, two per byte (last dim d / 2), with the same scales.
     ctx_lens int32 [B]; block_table int32 [B, max_blocks_per_seq].
     tile_order: ORDER_ASCENDING, ORDER_RECENT or ORDER_LIST (then tile_perm is
     an int32 device tensor [B, stride], row b listing its tiles in visiting order).

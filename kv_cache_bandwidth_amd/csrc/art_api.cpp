@@ -52,10 +52,10 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
         return fail(ART_E_SHAPE, "head_dim %d; supported: 64, 128", d->head_dim);
     if (d->q_dtype != ART_F32 && d->q_dtype != ART_BF16)
         return fail(ART_E_DTYPE, "q_dtype %d; supported: ART_F32, ART_BF16", d->q_dtype);
-    if (d->kv_dtype != ART_F32 && d->kv_dtype != ART_BF16 && d->kv_dtype != ART_I8)
+    if (d->kv_dtype != ART_F32 && d->kv_dtype != ART_BF16 && d->kv_dtype != ART_I8 && d->kv_dtype != ART_I4)
         return fail(ART_E_DTYPE, "kv_dtype %d unknown", d->kv_dtype);
-    if (d->kv_dtype == ART_I8 && (!d->k_scale || !d->v_scale))
-        return fail(ART_E_NULL, "int8 cache needs k_scale and v_scale");
+    if ((d->kv_dtype == ART_I8 || d->kv_dtype == ART_I4) && (!d->k_scale || !d->v_scale))
+        return fail(ART_E_NULL, "int8 and int4 caches need k_scale and v_scale");
     if (tile != 16 && tile != 32 && tile != 64 && tile != 128)
         return fail(ART_E_TILE, "tile %d; supported: 16, 32, 64, 128", tile);
     long long cap;

@@ -138,6 +138,8 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 __device__ __forceinline__ float sbyte(uint32_t w, int k) { return (float)(int)(int8_t)(w >> (8 * k)); }
+// signed 4-bit code k of a 32-bit word (code k in bits 4k..4k+3), sign-extended
+__device__ __forceinline__ float snib(uint32_t w, int k) { return (float)((int)(w << (28 - 4 * k)) >> 28); }
 // two small integers (|x| <= 127) as a packed bf16 pair: exact, since they need at most 8 bits
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
     return (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
@@ -156,7 +158,7 @@ __device__ __forceinline__ void load8(const void* base, long long off, float (&o
         u4 a = __builtin_nontemporal_load(p);
         o[0] = bf16lo(a.x); o[1] = bf16hi(a.x); o[2] = bf16lo(a.y); o[3] = bf16hi(a.y);
         o[4] = bf16lo(a.z); o[5] = bf16hi(a.z); o[6] = bf16lo(a.w); o[7] = bf16hi(a.w);
-    } else {
+    } else if constexpr (KV == ART_I8) {
         const u2* p = reinterpret_cast<const u2*>(static_cast<const int8_t*>(base) + off);
         u2 a = __builtin_nontemporal_load(p);
 #pragma unroll
@@ -164,6 +166,12 @@ __device__ __forceinline__ void load8(const void* base, long long off, float (&o
             o[i] = sbyte(a.x, i);
             o[4 + i] = sbyte(a.y, i);
         }
+    } else {
+        // int4: element e in the low (even e) or high (odd e) nibble of byte e / 2
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(base) + off / 2);
+        const uint32_t a = __builtin_nontemporal_load(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = snib(a, i);
     }
 }
 
@@ -186,13 +194,20 @@ __device__ __forceinline__ void load_small(const void* base, long long off, floa
         } else {
             o[0] = bf16lo(__builtin_nontemporal_load(p));
         }
-    } else {
+    } else if constexpr (KV == ART_I8) {
         const int8_t* p = static_cast<const int8_t*>(base) + off;
         if constexpr (APL == 2) {
             uint16_t w = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
             o[0] = sbyte(w, 0); o[1] = sbyte(w, 1);
         } else {
             o[0] = (float)__builtin_nontemporal_load(p);
+        }
+    } else {
+        const uint32_t w = __builtin_nontemporal_load(static_cast<const uint8_t*>(base) + off / 2);
+        if constexpr (APL == 2) {  // off is even: both nibbles of one byte
+            o[0] = snib(w, 0); o[1] = snib(w, 1);
+        } else {
+            o[0] = snib(w, (int)(off & 1));
         }
     }
 }
@@ -313,7 +328,7 @@ struct GenericTile {
                     bad = 1;
                     valid[ps] = false;
                 } else {
-                    const float sc = (KV == ART_I8 ? f16_to_f32(P.ks[r]) : 1.f) * P.inv_sqrt_d;
+                    const float sc = (KV == ART_I8 || KV == ART_I4 ? f16_to_f32(P.ks[r]) : 1.f) * P.inv_sqrt_d;
                     for (int c = 0; c < D; c += 8) {
                         float kk[8];
                         load8<KV>(P.k, r * D + c, kk);
@@ -381,7 +396,7 @@ struct GenericTile {
                 m &= m - 1;
                 bool ok = true;
                 const long long r = row_index(P, b, g, j0 + jj, ok);
-                const float vsc = KV == ART_I8 ? f16_to_f32(P.vs[r]) : 1.f;
+                const float vsc = KV == ART_I8 || KV == ART_I4 ? f16_to_f32(P.vs[r]) : 1.f;
                 float vv[APL];
                 load_small<KV, APL>(P.v, r * D + lane * APL, vv);
 #pragma unroll
@@ -3563,11 +3578,13 @@ int run(const Params& p, hipStream_t s, bool art) {
     if (p.D == 64) {
         if (p.kv_dtype == ART_F32) return run_tile<GenericTile<64, ART_F32>>(p, s, art);
         if (p.kv_dtype == ART_BF16) return run_tile<GenericTile<64, ART_BF16>>(p, s, art);
-        return run_tile<GenericTile<64, ART_I8>>(p, s, art);
+        if (p.kv_dtype == ART_I8) return run_tile<GenericTile<64, ART_I8>>(p, s, art);
+        return run_tile<GenericTile<64, ART_I4>>(p, s, art);
     }
     if (p.kv_dtype == ART_F32) return run_tile<GenericTile<128, ART_F32>>(p, s, art);
     if (p.kv_dtype == ART_BF16) return run_tile<GenericTile<128, ART_BF16>>(p, s, art);
-    return run_tile<GenericTile<128, ART_I8>>(p, s, art);
+    if (p.kv_dtype == ART_I8) return run_tile<GenericTile<128, ART_I8>>(p, s, art);
+    return run_tile<GenericTile<128, ART_I4>>(p, s, art);
 }
 
 }  // namespace

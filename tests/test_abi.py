@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = art.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.art_abi_version() == 5
+    assert lib.art_abi_version() == 6
 
 
 def desc(**kw):
@@ -68,6 +68,7 @@ def test_valid_desc_passes():
     (dict(q_dtype=B.ART_I8), -3),
     (dict(kv_dtype=7), -3),
     (dict(kv_dtype=B.ART_I8), -1),             # int8 without scales
+    (dict(kv_dtype=B.ART_I4), -1),             # int4 without scales
     (dict(block_size=8), -2),
     (dict(block_size=24), -2),
     (dict(max_blocks_per_seq=0), -2),

@@ -291,3 +291,22 @@ def test_vskip_bf16_cache(n):
     _run_and_check(c, f"config{n} bf16 full+vskip", eps_scale=0.0, eps_dir=0.0)
     _run_and_check(c, f"config{n} bf16 art+vskip work-sharing", max_workers=96)
     _run_and_check(c, f"config{n} bf16 art+vskip patience 3", patience=3)
+
+
+# ---------------------------------------------------------------- int4 caches
+
+@pytest.mark.parametrize("d,paged", [(128, True), (64, True), (128, False)])
+def test_int4_cache(d, paged):
+    # int4 codes two per byte with fp16 scales: the one-tile-at-a-time kernels
+    c = A.make_case("i4", B=3, Hq=8, Hkv=2, d=d, ctx_lens=[1500, 700, 0], kv_dtype="i4",
+                    block_size=16 if paged else 0, q_mode="temperature", seed=31)
+    _run_and_check(c, f"int4 d{d} paged={paged} art")
+    _run_and_check(c, f"int4 d{d} paged={paged} art+vskip", v_skip_eps=1e-4)
+    _run_and_check(c, f"int4 d{d} paged={paged} full", eps_scale=0.0, eps_dir=0.0)
+    _run_and_check(c, f"int4 d{d} paged={paged} full+vskip", eps_scale=0.0, eps_dir=0.0, v_skip_eps=1e-4)
+
+
+def test_int4_config5_small():
+    c = A.config(5, small=True, kv_dtype="i4")
+    _run_and_check(c, "config5-small int4 art+vskip")
+    _run_and_check(c, "config5-small int4 full", eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
