@@ -420,18 +420,19 @@ def tile_orders(case, dev, flush_buf, steps=7):
 def other_workloads(args, flush_buf, steps=7):
     """Context, not the metric: ART (library default engine, each workload's
     own thresholds and V-skip setting) and full attention on workloads 2, 4
-    and 5 at full size, median µs per call, same timing method."""
+    and 5 at full size, and workload 5 with an int4 cache, median µs per
+    call, same timing method."""
     import torch
     import art_inputs as A
     import kv_cache_bandwidth_amd as art
     from tests.gpu_util import to_device
     stream = torch.cuda.current_stream()
     res = {}
-    for n in (2, 4, 5):
+    for n in (2, 4, 5, "5i4"):
         if n == args.config:
             continue
         log(f"context timing: workload {n}")
-        case = A.config(n, seed=args.seed)
+        case = A.config(5, seed=args.seed, kv_dtype="i4") if n == "5i4" else A.config(n, seed=args.seed)
         dev = to_device(case)
 
         def med(**kw):
@@ -453,7 +454,8 @@ def other_workloads(args, flush_buf, steps=7):
         t_art, used = med()
         t_full, _ = med(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
         nt = -(-case.ctx_lens // case.tile)
-        entry = {"workload": A.WORKLOADS[n], "art_us": round(t_art, 1), "full_us": round(t_full, 1),
+        name = A.WORKLOADS[5].replace("int8", "int4 (two codes per byte)") if n == "5i4" else A.WORKLOADS[n]
+        entry = {"workload": name, "art_us": round(t_art, 1), "full_us": round(t_full, 1),
                  "kv_tiles_skipped_head_level": round(float(1.0 - used.sum() / (nt[:, None] * case.Hq).sum()), 4)}
         if case.v_skip_eps > 0:
             entry["art_no_vskip_us"] = round(med(v_skip_eps=0.0)[0], 1)
