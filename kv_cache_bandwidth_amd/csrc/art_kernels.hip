@@ -714,21 +714,23 @@ struct Stream {
     static constexpr int D = 128, UP = 2, T = 64, PAGES = 4;
     static constexpr int ORDER = ORD;
     static_assert(PAGES == kStepPages, "step-table records hold one block id per page");
-    static constexpr int EB = KV == ART_I8 ? 1 : 2;
+    static constexpr bool SCALED = KV == ART_I8 || KV == ART_I4;  // codes times per-row fp16 scales
     static constexpr int HBM = GMAX / 4;
     static constexpr int HEADS = GMAX;           // query heads per KV head at most
-    static constexpr int ROWB = D * EB;          // bytes of one cache row
+    static constexpr int ROWB = KV == ART_I4 ? D / 2 : KV == ART_I8 ? D : 2 * D;  // bytes of one cache row
     static constexpr int PAGEB = 16 * ROWB;      // bytes of one 16-row page
     static constexpr int KDMA = PAGEB / 1024;    // LDS-direct loads per page
     static constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
     // vector-memory instructions one issue() emits (all unconditional)
-    static constexpr int OPS = UP * (4 + KDMA + (KV == ART_I8 ? 5 : 0));
+    static constexpr int OPS = UP * (4 + KDMA + (SCALED ? 5 : 0));
     // resident waves per SIMD the register budget is cut for (two when it fits without heavy spills)
     static constexpr int MIN_WAVES = GMAX == 4 ? 2 : 1;
     // waves of a team (one work-group, one CU): as many as are resident on a CU
     static constexpr int TEAM = 4 * MIN_WAVES;
     using Out = TileOutT<HBM>;
-    typedef typename std::conditional<KV == ART_I8, u2, u4>::type vvec;
+    // 8 elements of a V row
+    typedef typename std::conditional<KV == ART_I4, uint32_t,
+                                      typename std::conditional<KV == ART_I8, u2, u4>::type>::type vvec;
 
     static constexpr int LDS_FLOATS = (2 * UP * PAGEB) / 4 + 64 * GMAX;
     __host__ __device__ static size_t lds_floats(const Params&) { return LDS_FLOATS; }
@@ -919,9 +921,9 @@ struct Stream {
             for (int v = 0; v < 4; ++v) {
                 const int row = 4 * v + rg;
                 vb[BUF][pp][v] = __builtin_nontemporal_load(
-                    reinterpret_cast<const vvec*>(vbase + row * ROWB + 8 * EB * r16));
+                    reinterpret_cast<const vvec*>(vbase + row * ROWB + (ROWB / 16) * r16));
             }
-            if constexpr (KV == ART_I8) {
+            if constexpr (SCALED) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) vsc[BUF][pp][v] = f16_to_f32(P.vs[pr + 4 * v + rg]);
                 const u2 w = *reinterpret_cast<const u2*>(P.ks + pr + 4 * rg);
@@ -976,6 +978,16 @@ struct Stream {
                     cv.z = bf16_pair(sbyte(w.y, 0), sbyte(w.y, 1));
                     cv.w = bf16_pair(sbyte(w.y, 2), sbyte(w.y, 3));
                     a = __builtin_bit_cast(bf16x8, cv);
+                } else if constexpr (KV == ART_I4) {
+                    // 4 bytes: head dims 32st + 8rg .. +7 of row r16 (two codes per byte)
+                    const int c = st ^ (r16 % CPR);
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(kp + r16 * ROWB + 16 * c + 4 * rg);
+                    u4 cv;
+                    cv.x = bf16_pair(snib(w, 0), snib(w, 1));
+                    cv.y = bf16_pair(snib(w, 2), snib(w, 3));
+                    cv.z = bf16_pair(snib(w, 4), snib(w, 5));
+                    cv.w = bf16_pair(snib(w, 6), snib(w, 7));
+                    a = __builtin_bit_cast(bf16x8, cv);
                 } else {
                     const int c = (4 * st + rg) ^ r16;
                     a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u4*>(kp + r16 * ROWB + 16 * c));
@@ -985,7 +997,7 @@ struct Stream {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool valid = ((r.pmask >> p) & 1) && r.t * T + 16 * p + 4 * rg + i < r.n;
-                const float sc = KV == ART_I8 ? ksc[BUF][pp][i] : P.inv_sqrt_d;
+                const float sc = SCALED ? ksc[BUF][pp][i] : P.inv_sqrt_d;
                 s[pp][i] = valid ? a4[i] * sc : kNegInf;
                 mu = fmaxf(mu, s[pp][i]);
             }
@@ -1119,6 +1131,12 @@ struct Stream {
                         vf[k] = sbyte(w.x, k);
                         vf[4 + k] = sbyte(w.y, k);
                     }
+                } else if constexpr (KV == ART_I4) {
+#pragma unroll
+                    for (int h = 0; h < GMAX; ++h) pw[h] *= vsc[BUF][pp][v];
+                    const uint32_t w = vb[BUF][pp][v];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) vf[k] = snib(w, k);
                 } else {
                     const u4 w = vb[BUF][pp][v];
                     vf[0] = bf16lo(w.x); vf[1] = bf16hi(w.x); vf[2] = bf16lo(w.y); vf[3] = bf16hi(w.y);
@@ -3460,8 +3478,9 @@ int launch_split(const Params& p, hipStream_t s, K kernel) {
 // at most 8 query heads per KV head and tiles of 16, 32 or 64 tokens; 64-token
 // tiles without the V skip are streamed.
 bool fast_path(const Params& p) {
-    return p.D == 128 && p.q_dtype == ART_BF16 && (p.kv_dtype == ART_BF16 || p.kv_dtype == ART_I8) &&
-           p.G <= 8 && (p.T == 16 || p.T == 32 || p.T == 64);
+    return p.D == 128 && p.q_dtype == ART_BF16 && p.G <= 8 &&
+           (((p.kv_dtype == ART_BF16 || p.kv_dtype == ART_I8) && (p.T == 16 || p.T == 32 || p.T == 64)) ||
+            (p.kv_dtype == ART_I4 && p.T == 64));
 }
 // the work-sharing engine serves ART mode
 bool sharing(const Params& p) {
@@ -3565,15 +3584,21 @@ int run_fast(const Params& p, hipStream_t s, bool art) {
         return p.order == ART_ORDER_ASCENDING ? run_stream<Stream<KV, GMAX, ART_ORDER_ASCENDING>>(p, s, art)
                : p.order == ART_ORDER_RECENT  ? run_stream<Stream<KV, GMAX, ART_ORDER_RECENT>>(p, s, art)
                                               : run_stream<Stream<KV, GMAX, ART_ORDER_LIST>>(p, s, art);
-    if (p.T == 64) return run_tile<FastTile<KV, 4, GMAX>>(p, s, art);
-    if (p.T == 32) return run_tile<FastTile<KV, 2, GMAX>>(p, s, art);
-    return run_tile<FastTile<KV, 1, GMAX>>(p, s, art);
+    if constexpr (KV == ART_I4) {
+        // int4 has only the streamed 64-token tile; the rest runs on the generic tile
+        return run_tile<GenericTile<128, ART_I4>>(p, s, art);
+    } else {
+        if (p.T == 64) return run_tile<FastTile<KV, 4, GMAX>>(p, s, art);
+        if (p.T == 32) return run_tile<FastTile<KV, 2, GMAX>>(p, s, art);
+        return run_tile<FastTile<KV, 1, GMAX>>(p, s, art);
+    }
 }
 
 int run(const Params& p, hipStream_t s, bool art) {
     if (fast_path(p)) {
         if (p.kv_dtype == ART_BF16) return p.G <= 4 ? run_fast<ART_BF16, 4>(p, s, art) : run_fast<ART_BF16, 8>(p, s, art);
-        return p.G <= 4 ? run_fast<ART_I8, 4>(p, s, art) : run_fast<ART_I8, 8>(p, s, art);
+        if (p.kv_dtype == ART_I8) return p.G <= 4 ? run_fast<ART_I8, 4>(p, s, art) : run_fast<ART_I8, 8>(p, s, art);
+        return p.G <= 4 ? run_fast<ART_I4, 4>(p, s, art) : run_fast<ART_I4, 8>(p, s, art);
     }
     if (p.D == 64) {
         if (p.kv_dtype == ART_F32) return run_tile<GenericTile<64, ART_F32>>(p, s, art);

@@ -307,6 +307,19 @@ def test_int4_cache(d, paged):
 
 
 def test_int4_config5_small():
+    # the streamed 64-token tile (codes widened to bf16 for the matrix cores)
     c = A.config(5, small=True, kv_dtype="i4")
     _run_and_check(c, "config5-small int4 art+vskip")
+    _run_and_check(c, "config5-small int4 art", v_skip_eps=0.0)
+    _run_and_check(c, "config5-small int4 art pool", engine=ENGINE_POOL, v_skip_eps=0.0)
+    _run_and_check(c, "config5-small int4 art work-sharing", max_workers=96, v_skip_eps=0.0)
     _run_and_check(c, "config5-small int4 full", eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
+
+
+@pytest.mark.parametrize("G", [1, 5, 8])
+def test_int4_group_sizes(G):
+    c = A.make_case(f"i4-G{G}", B=2, Hq=2 * G, Hkv=2, d=128, ctx_lens=[1700, 513], kv_dtype="i4",
+                    block_size=16, q_mode="temperature", seed=40 + G)
+    _run_and_check(c, f"int4 G={G} art")
+    _run_and_check(c, f"int4 G={G} art+vskip", v_skip_eps=1e-4)
+    _run_and_check(c, f"int4 G={G} full", eps_scale=0.0, eps_dir=0.0)
