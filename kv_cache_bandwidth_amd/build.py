@@ -8,7 +8,6 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libart.so")
-SOURCES = ["art_api.cpp", "art_kernels.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -23,15 +22,43 @@ HIPCC_FLAGS = [
 ]
 
 
+# art_kernels.hip is compiled once per launch part (ART_PART, see the end of
+# that file) so that the parts build in parallel; the objects and art_api.cpp
+# are then linked into the shared library.
+PARTS = (0, 1, 2, 3)
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+    out = os.path.join(ROOT, "_build")
+    os.makedirs(out, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for part in PARTS:
+        obj = os.path.join(out, f"art_kernels_part{part}.o")
+        jobs.append((obj, [hipcc, *flags, *inc, f"-DART_PART={part}", "-c",
+                           os.path.join(CSRC, "art_kernels.hip"), "-o", obj]))
+    api = os.path.join(out, "art_api.o")
+    jobs.append((api, [hipcc, *flags, *inc, "-c", os.path.join(CSRC, "art_api.cpp"), "-o", api]))
+    procs = []
+    for obj, cmd in jobs:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    errors = []
+    for cmd, pr in procs:
+        _, err = pr.communicate()
+        if pr.returncode != 0:
+            errors.append(f"{' '.join(cmd[-4:])}: {err[-3000:]}")
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+    link = [hipcc, *HIPCC_FLAGS, *[obj for obj, _ in jobs], "-o", LIB + ".tmp"]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-4000:]}")
+        raise RuntimeError(f"link failed ({r.returncode}):\n{r.stderr[-4000:]}")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -3594,12 +3594,36 @@ int run_fast(const Params& p, hipStream_t s, bool art) {
     }
 }
 
-int run(const Params& p, hipStream_t s, bool art) {
-    if (fast_path(p)) {
-        if (p.kv_dtype == ART_BF16) return p.G <= 4 ? run_fast<ART_BF16, 4>(p, s, art) : run_fast<ART_BF16, 8>(p, s, art);
-        if (p.kv_dtype == ART_I8) return p.G <= 4 ? run_fast<ART_I8, 4>(p, s, art) : run_fast<ART_I8, 8>(p, s, art);
-        return p.G <= 4 ? run_fast<ART_I4, 4>(p, s, art) : run_fast<ART_I4, 8>(p, s, art);
-    }
+}  // namespace
+
+// The launch code is split into parts by cache format, so that the library
+// can be compiled as several translation units in parallel (ART_PART = 0..3,
+// one object each); without ART_PART one translation unit holds every part.
+#ifndef ART_PART
+#define ART_PART -1
+#endif
+int run_part_bf16(const Params& p, hipStream_t s, bool art);
+int run_part_i8(const Params& p, hipStream_t s, bool art);
+int run_part_i4(const Params& p, hipStream_t s, bool art);
+int run_part_generic(const Params& p, hipStream_t s, bool art);
+
+#if ART_PART < 0 || ART_PART == 1
+int run_part_bf16(const Params& p, hipStream_t s, bool art) {
+    return p.G <= 4 ? run_fast<ART_BF16, 4>(p, s, art) : run_fast<ART_BF16, 8>(p, s, art);
+}
+#endif
+#if ART_PART < 0 || ART_PART == 2
+int run_part_i8(const Params& p, hipStream_t s, bool art) {
+    return p.G <= 4 ? run_fast<ART_I8, 4>(p, s, art) : run_fast<ART_I8, 8>(p, s, art);
+}
+#endif
+#if ART_PART < 0 || ART_PART == 3
+int run_part_i4(const Params& p, hipStream_t s, bool art) {
+    return p.G <= 4 ? run_fast<ART_I4, 4>(p, s, art) : run_fast<ART_I4, 8>(p, s, art);
+}
+#endif
+#if ART_PART < 0 || ART_PART == 0
+int run_part_generic(const Params& p, hipStream_t s, bool art) {
     if (p.D == 64) {
         if (p.kv_dtype == ART_F32) return run_tile<GenericTile<64, ART_F32>>(p, s, art);
         if (p.kv_dtype == ART_BF16) return run_tile<GenericTile<64, ART_BF16>>(p, s, art);
@@ -3612,6 +3636,15 @@ int run(const Params& p, hipStream_t s, bool art) {
     return run_tile<GenericTile<128, ART_I4>>(p, s, art);
 }
 
+namespace {
+int run(const Params& p, hipStream_t s, bool art) {
+    if (fast_path(p)) {
+        if (p.kv_dtype == ART_BF16) return run_part_bf16(p, s, art);
+        if (p.kv_dtype == ART_I8) return run_part_i8(p, s, art);
+        return run_part_i4(p, s, art);
+    }
+    return run_part_generic(p, s, art);
+}
 }  // namespace
 
 int launch_art(const Params& p, void* stream) {
@@ -3625,5 +3658,6 @@ int launch_full(const Params& p, void* stream) {
     if (p.NG == 0) return 0;
     return run(p, static_cast<hipStream_t>(stream), false);
 }
+#endif
 
 }  // namespace art
