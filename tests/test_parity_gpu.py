@@ -323,3 +323,29 @@ def test_int4_group_sizes(G):
     _run_and_check(c, f"int4 G={G} art")
     _run_and_check(c, f"int4 G={G} art+vskip", v_skip_eps=1e-4)
     _run_and_check(c, f"int4 G={G} full", eps_scale=0.0, eps_dir=0.0)
+
+
+@pytest.mark.parametrize("variant", ["recent_first", "random_list", "retained", "int4"])
+def test_full_size_sampled_rows_variants(variant):
+    # the 32K workload at full size with a tile order, per-head retained tables
+    # or (workload 5) an int4 cache, in the launch configuration bench.py times;
+    # the oracle checks the first and last rows
+    log(f"[parity] generating full-size case for {variant}")
+    if variant == "int4":
+        c = A.config(5, kv_dtype="i4")
+    else:
+        c = A.config(3)
+        if variant == "recent_first":
+            c.order = 1
+        elif variant == "random_list":
+            c.order = 2
+            c.tile_perm = A.sink_first_orders(c.ctx_lens, c.tile, stride=-(-c.max_ctx // c.tile), seed=1)
+        else:
+            c = A.retained_tables(c, sink_blocks=4, recent_blocks=512, keep_frac=0.25, seed=1)
+    dev = to_device(c)
+    rows = [0, c.B - 1]
+    out, used = run_gpu(c, dev)
+    r = check_parity(c, out, used, rows=rows)
+    log(f"[parity] {variant} full size: max_abs={r['max_abs']:.3e} near={r['near']} "
+        f"mean tiles_used (sampled)={np.mean(r['tiles_used']):.1f}")
+    assert (used >= 1).all()
