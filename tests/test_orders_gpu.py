@@ -132,3 +132,12 @@ def test_order_does_not_change_full_attention():
         o, u = run_gpu(c, dev, eps_scale=0.0, eps_dir=0.0)
         assert np.array_equal(u, u0)
         np.testing.assert_allclose(o, o0, rtol=0, atol=2e-5)
+
+
+@pytest.mark.parametrize("tile", [16, 32, 128])
+@pytest.mark.parametrize("order", [ORDER_RECENT, ORDER_LIST])
+def test_orders_other_tile_sizes(tile, order):
+    # tiles other than 64 tokens run the one-tile-at-a-time matrix-core kernels
+    c = ordered(A.config(3, small=True, batch=2, ctx=1000, tile=tile), order, seed=tile)
+    _run_and_check(c, f"tile {tile} order {order} art")
+    _run_and_check(c, f"tile {tile} order {order} full", eps_scale=0.0, eps_dir=0.0)

@@ -105,3 +105,12 @@ def test_invalid_per_head_entries_reported_per_group():
     good.block_table[2, 0, 3] = 0
     out, used = run_gpu(c)
     check_parity(good, out, used, rows=[0])
+
+
+@pytest.mark.parametrize("tile", [16, 32, 128])
+def test_retained_other_tile_sizes(tile):
+    c = retained(A.config(3, small=True, batch=2, ctx=1500, tile=tile), 0.5, seed=tile, sink=2, recent=16)
+    c.order = ORDER_LIST
+    c.tile_perm = A.sink_first_orders(c.ctx_lens, tile, stride=-(-c.max_ctx // tile), seed=3)
+    _run_and_check(c, f"retained tile {tile} list art")
+    _run_and_check(c, f"retained tile {tile} list full", eps_scale=0.0, eps_dir=0.0)
