@@ -13,6 +13,7 @@ constexpr int kRing = 128;        // ring slots per group (tiles in flight ahead
 constexpr int kMaxG = 16;         // query heads per KV head
 constexpr int kWavesPerWG = 4;    // independent waves per work-group
 constexpr int kMaxDeciders = 512; // decider waves at most (one per group up to this many groups)
+constexpr int kMaxWorkersPerGroup = 8;  // work-sharing engine: tile workers per group at most
 // team engine, words shared through the workspace (per group)
 constexpr int kTeamRingG = 16;    // slots of the helpers' tile partials per group (a power of two)
 constexpr int kTeamRecW = 11;     // 64-bit words per (tile, head) record: max, sum, probe dims 0..7, error flag

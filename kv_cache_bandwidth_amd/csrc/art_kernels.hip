@@ -3457,6 +3457,7 @@ int launch_persistent(const Params& p0, hipStream_t s, K kernel) {
         long long w = resident - p.deciders;
         const long long tiles = (long long)p.NG * p.nt_max;
         if (w > tiles) w = tiles;
+        if (w > (long long)kMaxWorkersPerGroup * p.NG) w = (long long)kMaxWorkersPerGroup * p.NG;
         p.workers = (int)max(w, 1LL);
     }
     hipLaunchKernelGGL(art_init_kernel, dim3(p.NG), dim3(256), 0, s, p);
