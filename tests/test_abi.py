@@ -136,3 +136,16 @@ def test_decode_rejects_before_touching_device():
     rc = lib.art_decode_attention(ctypes.byref(d), None, None, None, None, None, 64, 1e-3, 1e-4,
                                   None, None, None)
     assert rc == -1  # q/k/v/ctx_lens/out/tiles_used missing
+
+
+def test_plain_c_client(tmp_path):
+    # the header is valid C11 and the library serves a C program directly
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(art.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "c_abi_check.c"), "-o", exe, "-L", lib_dir, "-l:libart.so",
+                    f"-Wl,-rpath,{lib_dir}"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
