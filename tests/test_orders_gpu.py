@@ -43,13 +43,14 @@ def test_orders_every_engine(order):
 
 
 @pytest.mark.parametrize("order", [ORDER_RECENT, ORDER_LIST])
-@pytest.mark.parametrize("kv,q,d", [("f32", "f32", 128), ("bf16", "bf16", 64), ("i8", "bf16", 128)])
+@pytest.mark.parametrize("kv,q,d", [("f32", "f32", 128), ("bf16", "bf16", 64), ("i8", "bf16", 128), ("i4", "bf16", 128),
+                                    ("i4", "bf16", 64)])
 def test_orders_other_paths(order, kv, q, d):
     # fp32 caches and head dim 64 run the one-tile-at-a-time kernels; int8 with
     # a V skip runs the team kernel's skip path
     c = A.make_case("orders", B=3, Hq=8, Hkv=2, d=d, ctx_lens=[700, 333, 1000], kv_dtype=kv,
                     q_dtype=q, block_size=16, q_mode="temperature", seed=21,
-                    v_skip_eps=1e-6 if kv == "i8" else 0.0)
+                    v_skip_eps=1e-6 if kv in ("i8", "i4") else 0.0)
     ordered(c, order, seed=3)
     _run_and_check(c, f"{kv}/{q} d{d} order {order} art")
     _run_and_check(c, f"{kv}/{q} d{d} order {order} full", eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)

@@ -38,11 +38,12 @@ def test_retained_every_engine():
     _run_and_check(c, "retained helpers", team_helpers=1)
 
 
-@pytest.mark.parametrize("kv,q,d", [("f32", "f32", 128), ("bf16", "bf16", 64), ("i8", "bf16", 128)])
+@pytest.mark.parametrize("kv,q,d", [("f32", "f32", 128), ("bf16", "bf16", 64), ("i8", "bf16", 128), ("i4", "bf16", 128),
+                                    ("i4", "bf16", 64)])
 def test_retained_other_paths(kv, q, d):
     c = A.make_case("kept", B=3, Hq=8, Hkv=2, d=d, ctx_lens=[1500, 700, 333], kv_dtype=kv,
                     q_dtype=q, block_size=16, q_mode="temperature", seed=23,
-                    v_skip_eps=1e-6 if kv == "i8" else 0.0)
+                    v_skip_eps=1e-6 if kv in ("i8", "i4") else 0.0)
     c = retained(c, 0.5, seed=2, sink=2, recent=16)
     _run_and_check(c, f"{kv}/{q} d{d} retained art")
     _run_and_check(c, f"{kv}/{q} d{d} retained full", eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
