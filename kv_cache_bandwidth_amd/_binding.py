@@ -163,6 +163,11 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
                     ("tile_perm", tile_perm)):
         if t is not None and not (t.is_cuda and t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous device tensor")
+    for name, t, want in (("ctx_lens", ctx_lens, torch.int32), ("block_table", block_table, torch.int32),
+                          ("tile_perm", tile_perm, torch.int32), ("k_scale", k_scale, torch.float16),
+                          ("v_scale", v_scale, torch.float16)):
+        if t is not None and t.dtype != want:
+            raise ValueError(f"{name} must be {want}, got {t.dtype}")
     desc = make_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
                      q_dtype=_dtype_code(q), kv_dtype=_dtype_code(k_cache), block_size=bs,
                      max_blocks_per_seq=mbps, num_blocks=nb, max_ctx=max_ctx, patience=patience,
