@@ -100,7 +100,30 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     p.cap = (int)cap;
     p.nt_max = (int)((cap + tile - 1) / tile);
     p.NG = d->batch * d->num_kv_heads;
-    p.seq_div = d->per_head_tables ? 1 : d->num_kv_heads;
+    p.hkv_cache = d->num_kv_heads;
+    p.kv_shift = 0;
+    // Query-head split: decisions are per query head (a group only loads while
+    // one of its heads is active), so in ART mode on the streamed 64-token tile
+    // a KV head's G = 6, 8, 12 or 16 query heads run as 2 or 4 groups of at
+    // most 4 heads, each reading the KV head's tiles for itself: the 4-head
+    // tile runs twice the waves per CU and twice as many CUs work, which
+    // outweighs the repeated reads while the groups fit one per CU.  q, out
+    // and tiles_used keep their layout (a group's heads stay contiguous).
+    {
+        const bool art_mode = eps_scale > 0.f && eps_dir > 0.f;
+        const bool streamed = d->head_dim == 128 && d->q_dtype == ART_BF16 && tile == 64 &&
+                              (d->kv_dtype == ART_BF16 || d->kv_dtype == ART_I8 || d->kv_dtype == ART_I4);
+        int shift = 0;
+        if (G > 4 && G % 2 == 0 && G / 2 <= 4) shift = 1;
+        else if (G > 4 && G % 4 == 0 && G / 4 <= 4) shift = 2;
+        if (art_mode && streamed && shift > 0 && (long long)p.NG << shift <= art::kMaxSplitGroups) {
+            p.kv_shift = shift;
+            p.Hkv <<= shift;
+            p.G >>= shift;
+            p.NG <<= shift;
+        }
+    }
+    p.seq_div = d->per_head_tables ? (1 << p.kv_shift) : p.Hkv;
     {
         // multiply-high constants for grp / seq_div (round-up method): with
         // s = ceil(log2 seq_div), m = ceil(2^(31+s) / seq_div) < 2^32 and
@@ -120,7 +143,7 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     p.vskip = d->v_skip_eps > 0.f;
     p.eps_scale = eps_scale; p.eps_dir = eps_dir; p.v_skip_eps = d->v_skip_eps;
     p.inv_sqrt_d = 1.f / std::sqrt((float)d->head_dim);
-    p.slot = art::kSlotHeader + G * d->head_dim;
+    p.slot = art::kSlotHeader + p.G * d->head_dim;
     // full-mode split plan (part of the workspace layout, so independent of the device)
     const int target = kTargetWaves;
     int splits = p.NG ? (target + p.NG - 1) / p.NG : 1;
@@ -178,9 +201,13 @@ const char* art_last_error(void) { return g_last_error.c_str(); }
 int32_t art_abi_version(void) { return ART_ABI_VERSION; }
 
 size_t art_workspace_bytes(const art_desc* desc, int32_t tile) {
-    art::Params p;
-    if (check(desc, tile, 0.f, 0.f, p) != ART_OK) return 0;
-    return art::workspace_layout(p).total;
+    // the layout of full attention and that of ART mode (which may split a
+    // KV head's query heads into several groups): enough for either
+    art::Params full, art_mode;
+    if (check(desc, tile, 0.f, 0.f, full) != ART_OK) return 0;
+    if (check(desc, tile, 1.f, 1.f, art_mode) != ART_OK) return 0;
+    const size_t a = art::workspace_layout(full).total, b = art::workspace_layout(art_mode).total;
+    return a > b ? a : b;
 }
 
 art_status art_validate(const art_desc* desc, int32_t tile, float eps_scale, float eps_dir) {

@@ -14,6 +14,7 @@ constexpr int kMaxG = 16;         // query heads per KV head
 constexpr int kWavesPerWG = 4;    // independent waves per work-group
 constexpr int kMaxDeciders = 512; // decider waves at most (one per group up to this many groups)
 constexpr int kMaxWorkersPerGroup = 8;  // work-sharing engine: tile workers per group at most
+constexpr int kMaxSplitGroups = 256;    // query-head split only while the groups fit one per CU
 // team engine, words shared through the workspace (per group)
 constexpr int kTeamRingG = 16;    // slots of the helpers' tile partials per group (a power of two)
 constexpr int kTeamRecW = 11;     // 64-bit words per (tile, head) record: max, sum, probe dims 0..7, error flag
@@ -55,6 +56,8 @@ struct Params {
     int cap;            // tokens a row can hold
     int nt_max;         // ceil(cap / T)
     int NG;             // B * Hkv groups
+    int hkv_cache;      // KV heads of the cache; Hkv = hkv_cache << kv_shift groups per row
+    int kv_shift;       // a KV head's query heads run as 1 << kv_shift groups of G heads each
     int seq_div;        // group grp reads sequence grp / seq_div: Hkv (one per row), or 1 (per-head tables)
     unsigned seq_m;     // grp / seq_div == (grp * seq_m) >> seq_sh for 0 <= grp < 2^31
     int seq_sh;

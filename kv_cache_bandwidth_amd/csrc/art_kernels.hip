@@ -222,14 +222,17 @@ __device__ __forceinline__ int seq_of(const Params& P, int grp) {
 }
 
 // Row index of cached position j of (b, kv head g); ok=false on an invalid block id.
+// g counts groups (query-head splits of a KV head, kv_shift); the cache has
+// hkv_cache heads and group g reads head g >> kv_shift.
 __device__ __forceinline__ long long row_index(const Params& P, int b, int g, int j, bool& ok) {
-    if (P.block_size == 0) return ((long long)b * P.Hkv + g) * P.max_ctx + j;
+    const int gc = g >> P.kv_shift;
+    if (P.block_size == 0) return ((long long)b * P.hkv_cache + gc) * P.max_ctx + j;
     const int blk = P.block_table[(long long)seq_of(P, b * P.Hkv + g) * P.mbps + j / P.block_size];
     if (blk < 0 || blk >= P.num_blocks) {
         ok = false;
         return 0;
     }
-    return ((long long)blk * P.Hkv + g) * P.block_size + (j % P.block_size);
+    return ((long long)blk * P.hkv_cache + gc) * P.block_size + (j % P.block_size);
 }
 
 // The tile visited at step t of sequence sq (seq_of), which has nt tiles.  The tile sequence
@@ -887,14 +890,15 @@ struct Stream {
             r.prow[p] = 0;
             if (named(r.t) && tokp < n) {
                 if (P.block_size == 0) {
-                    r.prow[p] = ((long long)b * P.Hkv + g) * P.max_ctx + tokp;
+                    r.prow[p] = ((long long)b * P.hkv_cache + (g >> P.kv_shift)) * P.max_ctx + tokp;
                     r.pmask |= 1 << p;
                 } else {
                     const int blk = __builtin_amdgcn_readlane(blkv, p);
                     if (blk < 0 || blk >= P.num_blocks) {
                         r.err = 1;
                     } else {
-                        r.prow[p] = ((long long)blk * P.Hkv + g) * P.block_size + (unsigned)tokp % (unsigned)P.block_size;
+                        r.prow[p] = ((long long)blk * P.hkv_cache + (g >> P.kv_shift)) * P.block_size +
+                                    (unsigned)tokp % (unsigned)P.block_size;
                         r.pmask |= 1 << p;
                     }
                 }

@@ -349,3 +349,37 @@ def test_full_size_sampled_rows_variants(variant):
     log(f"[parity] {variant} full size: max_abs={r['max_abs']:.3e} near={r['near']} "
         f"mean tiles_used (sampled)={np.mean(r['tiles_used']):.1f}")
     assert (used >= 1).all()
+
+
+# ---------------------------------------------------------------- query-head split (G = 6, 8, 12, 16)
+
+@pytest.mark.parametrize("G", [6, 8, 12, 16])
+def test_query_head_split(G):
+    # in ART mode a KV head's G query heads run as groups of at most 4 heads
+    # on the 4-head tile; per-head results must not change
+    c = A.make_case(f"split-G{G}", B=3, Hq=2 * G, Hkv=2, d=128, ctx_lens=[1700, 513, 0], block_size=16,
+                    q_mode="temperature", seed=50 + G)
+    _run_and_check(c, f"G={G} art")
+    _run_and_check(c, f"G={G} art pool", engine=ENGINE_POOL)
+    _run_and_check(c, f"G={G} art work-sharing", max_workers=64)
+    _run_and_check(c, f"G={G} art+vskip", v_skip_eps=1e-4)
+    _run_and_check(c, f"G={G} full", eps_scale=0.0, eps_dir=0.0)
+
+
+@pytest.mark.parametrize("kv", ["i8", "i4"])
+def test_query_head_split_quantised_contiguous(kv):
+    c = A.make_case(f"split-{kv}", B=2, Hq=16, Hkv=2, d=128, ctx_lens=[2000, 777], kv_dtype=kv,
+                    block_size=0, q_mode="temperature", seed=61)
+    _run_and_check(c, f"G=8 {kv} contiguous art")
+    c.order, c.tile_perm = 1, None
+    _run_and_check(c, f"G=8 {kv} contiguous art recent-first")
+
+
+def test_query_head_split_per_head_tables_and_lists():
+    c = A.make_case("split-ph", B=2, Hq=16, Hkv=2, d=128, ctx_lens=[3000, 1500], block_size=16,
+                    q_mode="temperature", seed=62)
+    c = A.retained_tables(c, sink_blocks=2, recent_blocks=64, keep_frac=0.5, seed=4)
+    c.order = 2
+    c.tile_perm = A.sink_first_orders(c.ctx_lens, c.tile, stride=-(-c.max_ctx // c.tile), seed=5)
+    _run_and_check(c, "G=8 per-head tables, caller's list, art")
+    _run_and_check(c, "G=8 per-head tables, caller's list, pool", engine=ENGINE_POOL)
