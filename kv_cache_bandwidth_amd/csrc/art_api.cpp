@@ -102,24 +102,33 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     p.NG = d->batch * d->num_kv_heads;
     p.hkv_cache = d->num_kv_heads;
     p.kv_shift = 0;
+    p.gq = G;
     // Query-head split: decisions are per query head (a group only loads while
     // one of its heads is active), so in ART mode on the streamed 64-token tile
-    // a KV head's G = 6, 8, 12 or 16 query heads run as 2 or 4 groups of at
+    // a KV head's G = 5..8 or 10..16 query heads run as 2 or 4 groups of at
     // most 4 heads, each reading the KV head's tiles for itself: the 4-head
     // tile runs twice the waves per CU and twice as many CUs work, which
     // outweighs the repeated reads while the groups fit one per CU.  q, out
     // and tiles_used keep their layout (a group's heads stay contiguous).
+    // G = 5 or 7 (and 10, 11, 13..15) split unevenly: groups of ceil(G / 2)
+    // (or ceil(G / 4)) heads with a smaller last one; only the team and pool
+    // engines track the per-group head count, so an uneven split is not used
+    // with the work-sharing engine or helper work-groups.
     {
         const bool art_mode = eps_scale > 0.f && eps_dir > 0.f;
         const bool streamed = d->head_dim == 128 && d->q_dtype == ART_BF16 && tile == 64 &&
                               (d->kv_dtype == ART_BF16 || d->kv_dtype == ART_I8 || d->kv_dtype == ART_I4);
+        const bool sharing = d->max_workers > 0 || d->engine == ART_ENGINE_SHARED || d->team_helpers > 0;
         int shift = 0;
-        if (G > 4 && G % 2 == 0 && G / 2 <= 4) shift = 1;
-        else if (G > 4 && G % 4 == 0 && G / 4 <= 4) shift = 2;
-        if (art_mode && streamed && shift > 0 && (long long)p.NG << shift <= art::kMaxSplitGroups) {
+        if (G > 4 && G <= 8) shift = 1;
+        else if (G > 8 && 3 * ((G + 3) / 4) < G) shift = 2;  // every one of the 4 groups keeps a head
+        const int gv = (G + (1 << shift) - 1) >> shift;
+        const bool even = (gv << shift) == G;
+        if (art_mode && streamed && shift > 0 && (even || !sharing) &&
+            (long long)p.NG << shift <= art::kMaxSplitGroups) {
             p.kv_shift = shift;
             p.Hkv <<= shift;
-            p.G >>= shift;
+            p.G = gv;
             p.NG <<= shift;
         }
     }

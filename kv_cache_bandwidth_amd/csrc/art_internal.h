@@ -58,6 +58,7 @@ struct Params {
     int NG;             // B * Hkv groups
     int hkv_cache;      // KV heads of the cache; Hkv = hkv_cache << kv_shift groups per row
     int kv_shift;       // a KV head's query heads run as 1 << kv_shift groups of G heads each
+    int gq;             // query heads per KV head (the last group of a KV head may hold fewer than G)
     int seq_div;        // group grp reads sequence grp / seq_div: Hkv (one per row), or 1 (per-head tables)
     unsigned seq_m;     // grp / seq_div == (grp * seq_m) >> seq_sh for 0 <= grp < 2^31
     int seq_sh;

@@ -221,6 +221,18 @@ __device__ __forceinline__ int seq_of(const Params& P, int grp) {
     return (int)(((unsigned long long)(unsigned)grp * P.seq_m) >> P.seq_sh);
 }
 
+// Query heads of group grp: G, except that when a KV head's gq query heads do
+// not split evenly (kv_shift > 0) its last group holds fewer.
+__device__ __forceinline__ int heads_in(const Params& P, int grp) {
+    const int s = (grp % P.Hkv) & ((1 << P.kv_shift) - 1);
+    return min(P.G, P.gq - s * P.G);
+}
+// Row of q, out and tiles_used ([batch][query head]) of head h of group grp.
+__device__ __forceinline__ long long qrow(const Params& P, int grp, int h) {
+    const int b = grp / P.Hkv, gv = grp % P.Hkv;
+    return (long long)b * P.Hq + (long long)(gv >> P.kv_shift) * P.gq + (gv & ((1 << P.kv_shift) - 1)) * P.G + h;
+}
+
 // Row index of cached position j of (b, kv head g); ok=false on an invalid block id.
 // g counts groups (query-head splits of a KV head, kv_shift); the cache has
 // hkv_cache heads and group g reads head g >> kv_shift.
@@ -770,15 +782,13 @@ struct Stream {
     }
 
     __device__ __forceinline__ void load_q(const Params& P, int grp) {
-        const int b = grp / P.Hkv, g = grp % P.Hkv;
         const int lane = lane_id(), h = lane & 15, kg = lane >> 4;
         const uint16_t* q = static_cast<const uint16_t*>(P.q);
+        const int hv = heads_in(P, grp);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             u4 v = {0u, 0u, 0u, 0u};
-            if (h < P.G)
-                v = *reinterpret_cast<const u4*>(q + ((long long)b * P.Hq + (long long)g * P.G + h) * D +
-                                                 32 * s + 8 * kg);
+            if (h < hv) v = *reinterpret_cast<const u4*>(q + qrow(P, grp, h) * D + 32 * s + 8 * kg);
             qB[s] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -1087,7 +1097,7 @@ struct Stream {
                     const float pr = valid ? exp_fast(sv - mu) : 0.f;
                     const bool keep = valid && expf(sv - M) >= P.v_skip_eps;
                     lsum += pr;
-                    skipped += (valid && !keep && r16 < G) ? 1 : 0;
+                    skipped += (valid && !keep && r16 < heads_in(P, r.grp)) ? 1 : 0;
                     if (r16 < GMAX) pl[(32 * u + 16 * pp + 4 * rg + i) * GMAX + r16] = keep ? pr : 0.f;
                 }
         l_run = lsum;
@@ -1208,8 +1218,7 @@ struct Stream {
 // ------------------------------------------------------------------ output of a finished head
 __device__ __forceinline__ void write_head_out(const Params& P, int grp, int h, const FoldLanes& fl,
                                                const float (&a8)[8], float L, int err, int U) {
-    const int b = grp / P.Hkv, g = grp % P.Hkv;
-    const long long row = (long long)b * P.Hq + (long long)g * P.G + h;
+    const long long row = qrow(P, grp, h);
     if (fl.cvalid) {
         float* o = P.out + row * P.D + 8 * fl.cid;
         const float inv = 1.f / L;
@@ -1635,10 +1644,11 @@ __global__ __launch_bounds__(256) void art_init_kernel(Params P) {
         for (int i = tid; i < P.nt_max; i += blockDim.x) P.vmax_tag[(long long)grp * P.nt_max + i] = 0;
     // outputs of finished rows now; the others are marked unfinished (-2, NaN)
     // until the fold writes them
-    const long long row0 = (long long)b * P.Hq + (long long)g * P.G;
-    for (int i = tid; i < P.G * P.D; i += blockDim.x)
+    const long long row0 = qrow(P, grp, 0);
+    const int Gh = heads_in(P, grp);
+    for (int i = tid; i < Gh * P.D; i += blockDim.x)
         P.out[row0 * P.D + i] = (nt == 0 && !bad) ? 0.f : NAN;
-    for (int h = tid; h < P.G; h += blockDim.x) P.tiles_used[row0 + h] = nt > 0 ? -2 : (bad ? -1 : 0);
+    for (int h = tid; h < Gh; h += blockDim.x) P.tiles_used[row0 + h] = nt > 0 ? -2 : (bad ? -1 : 0);
 }
 
 // A caller's tile list (ART_ORDER_LIST) turned into a step table for the
@@ -2434,7 +2444,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
     const FoldLanes fl(P);
     const TeamGlobal tg(P, grp);
     const bool glb = plan.nH > 0;
-    D.init(fl, P.G);
+    D.init(fl, heads_in(P, grp));
     acc.clear();
     accH.clear();
     int relA = 0, relH = 0;
@@ -2625,9 +2635,10 @@ __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     if (nt == 0) {
         // empty row: zero output, no tiles; invalid length: NaN, -1
         if (team == 0 && wv == 0) {
-            const long long row0 = (long long)b * P.Hq + (long long)g * G;
-            for (int k = lane; k < G * P.D; k += 64) P.out[row0 * P.D + k] = bad ? NAN : 0.f;
-            for (int h = lane; h < G; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
+            const long long row0 = qrow(P, grp, 0);
+            const int Gh = heads_in(P, grp);
+            for (int k = lane; k < Gh * P.D; k += 64) P.out[row0 * P.D + k] = bad ? NAN : 0.f;
+            for (int h = lane; h < Gh; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
         }
         return;
     }
@@ -2771,13 +2782,14 @@ __device__ __forceinline__ void pool_decider(const Params& P, int grp, int T) {
     }
     if (nt == 0) {
         // empty row: zero output, no tiles; invalid length: NaN, -1
-        const long long row0 = (long long)b * P.Hq + (long long)g * G;
-        for (int k = lane; k < G * P.D; k += 64) P.out[row0 * P.D + k] = bad ? NAN : 0.f;
-        for (int h = lane; h < G; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
+        const long long row0 = qrow(P, grp, 0);
+        const int Gh = heads_in(P, grp);
+        for (int k = lane; k < Gh * P.D; k += 64) P.out[row0 * P.D + k] = bad ? NAN : 0.f;
+        for (int h = lane; h < Gh; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
         return;
     }
     ProbeState<HBM> D;
-    D.init(fl, G);
+    D.init(fl, heads_in(P, grp));
     bool finished = false, gave_up = false;
     auto publish = [&](int decided) {
 #pragma unroll
@@ -2961,8 +2973,8 @@ __device__ __forceinline__ void pool_worker(const Params& P, S& st, int widx, fl
     const FoldLanes fl(P);
     const unsigned e = P.epoch;
     unsigned long long loaded = 0, rows = 0;
-    auto head_ok = [&](int hb) { return hb < fl.HB && hb * 4 + fl.hl < P.G; };
     int grp = widx % P.NG;
+    auto head_ok = [&](int hb) { return hb < fl.HB && hb * 4 + fl.hl < heads_in(P, grp); };
     for (int round = 0;; ++round) {
         if (round > 0) {
             grp = uni(pool_pick(P, grp, T));

@@ -353,10 +353,11 @@ def test_full_size_sampled_rows_variants(variant):
 
 # ---------------------------------------------------------------- query-head split (G = 6, 8, 12, 16)
 
-@pytest.mark.parametrize("G", [6, 8, 12, 16])
+@pytest.mark.parametrize("G", [5, 6, 7, 8, 10, 12, 13, 16])
 def test_query_head_split(G):
     # in ART mode a KV head's G query heads run as groups of at most 4 heads
-    # on the 4-head tile; per-head results must not change
+    # on the 4-head tile (the last group smaller when G does not divide);
+    # per-head results must not change
     c = A.make_case(f"split-G{G}", B=3, Hq=2 * G, Hkv=2, d=128, ctx_lens=[1700, 513, 0], block_size=16,
                     q_mode="temperature", seed=50 + G)
     _run_and_check(c, f"G={G} art")
@@ -373,6 +374,21 @@ def test_query_head_split_quantised_contiguous(kv):
     _run_and_check(c, f"G=8 {kv} contiguous art")
     c.order, c.tile_perm = 1, None
     _run_and_check(c, f"G=8 {kv} contiguous art recent-first")
+
+
+def test_query_head_split_uneven_edge_rows():
+    # G = 5 (groups of 3 and 2): empty, one-token and invalid rows write only
+    # their own heads
+    c = A.make_case("split-edge", B=4, Hq=10, Hkv=2, d=128, ctx_lens=[900, 0, 1, 333], block_size=16,
+                    q_mode="temperature", seed=63)
+    c.ctx_lens[3] = c.block_table.shape[1] * 16 + 1   # longer than its table
+    out, used = run_gpu(c)
+    assert (used[1] == 0).all() and (out[1] == 0).all()
+    assert (used[3] == -1).all() and np.isnan(out[3]).all()
+    check_parity(c, out, used, rows=[0, 1, 2])
+    out, used = run_gpu(c, engine=ENGINE_POOL)
+    assert (used[3] == -1).all() and np.isnan(out[3]).all()
+    check_parity(c, out, used, rows=[0, 1, 2])
 
 
 def test_query_head_split_per_head_tables_and_lists():
