@@ -108,7 +108,7 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     // a KV head's G = 5..8 or 10..16 query heads run as 2 or 4 groups of at
     // most 4 heads, each reading the KV head's tiles for itself: the 4-head
     // tile runs twice the waves per CU and twice as many CUs work, which
-    // outweighs the repeated reads while the groups fit one per CU.  q, out
+    // outweighs the repeated reads (measured up to two groups per CU).  q, out
     // and tiles_used keep their layout (a group's heads stay contiguous).
     // G = 5 or 7 (and 10, 11, 13..15) split unevenly: groups of ceil(G / 2)
     // (or ceil(G / 4)) heads with a smaller last one; only the team and pool

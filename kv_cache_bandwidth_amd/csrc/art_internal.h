@@ -14,7 +14,7 @@ constexpr int kMaxG = 16;         // query heads per KV head
 constexpr int kWavesPerWG = 4;    // independent waves per work-group
 constexpr int kMaxDeciders = 512; // decider waves at most (one per group up to this many groups)
 constexpr int kMaxWorkersPerGroup = 8;  // work-sharing engine: tile workers per group at most
-constexpr int kMaxSplitGroups = 256;    // query-head split only while the groups fit one per CU
+constexpr int kMaxSplitGroups = 1024;   // query-head split up to this many groups (still a gain at 2 per CU)
 // team engine, words shared through the workspace (per group)
 constexpr int kTeamRingG = 16;    // slots of the helpers' tile partials per group (a power of two)
 constexpr int kTeamRecW = 11;     // 64-bit words per (tile, head) record: max, sum, probe dims 0..7, error flag
