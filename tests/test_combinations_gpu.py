@@ -11,7 +11,7 @@ from tests.test_parity_gpu import _run_and_check
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+N_CASES = 96
 
 
 def draw(seed):
