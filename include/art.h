@@ -114,7 +114,10 @@ typedef struct {
     void* workspace;             /* device scratch, 256-byte aligned, caller-owned    */
     size_t workspace_bytes;      /* >= art_workspace_bytes(desc, tile)                */
     int64_t* stats;              /* optional device int64[4] accumulator, or NULL:
-                                    [0] K tiles loaded, [1] V rows loaded,
+                                    [0] K tiles loaded (in ART mode a KV head's 5-16
+                                    query heads may run as several groups of at most
+                                    4, each loading the tiles it needs), [1] V rows
+                                    loaded,
                                     [2] tiles loaded after their group had stopped,
                                     [3] (query head, position) pairs whose V row was
                                         skipped (v_skip_eps > 0; counted by the
