@@ -151,6 +151,7 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     p.art = eps_scale > 0.f && eps_dir > 0.f;
     p.vskip = d->v_skip_eps > 0.f;
     p.eps_scale = eps_scale; p.eps_dir = eps_dir; p.v_skip_eps = d->v_skip_eps;
+    p.v_skip_ln = p.vskip ? (float)std::log((double)d->v_skip_eps) : -INFINITY;
     p.inv_sqrt_d = 1.f / std::sqrt((float)d->head_dim);
     p.slot = art::kSlotHeader + p.G * d->head_dim;
     // full-mode split plan (part of the workspace layout, so independent of the device)

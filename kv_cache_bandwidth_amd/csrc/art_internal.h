@@ -70,6 +70,7 @@ struct Params {
     int art;            // stop rule active
     int vskip;          // V-row skip active
     float eps_scale, eps_dir, v_skip_eps, inv_sqrt_d;
+    float v_skip_ln;    // ln(v_skip_eps) (-inf without the V skip): exp(x) >= eps  <=>  x >= ln eps
     // inputs / outputs (device)
     const void* q;
     const void* k;

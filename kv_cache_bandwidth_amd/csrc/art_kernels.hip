@@ -387,7 +387,7 @@ struct GenericTile {
                 if (h < G) {
                     const float p = valid[ps] ? expf(s[ps][h] - o.m[h]) : 0.f;
                     lsum[h] += p;
-                    const bool keep = valid[ps] && (!P.vskip || expf(s[ps][h] - Mt[h]) >= P.v_skip_eps);
+                    const bool keep = valid[ps] && (!P.vskip || s[ps][h] - Mt[h] >= P.v_skip_ln);
                     row_keep |= keep;
                     if (jj < T) p_lds[h * T + jj] = keep ? p : 0.f;
                 }
@@ -600,7 +600,7 @@ struct FastTile {
                 const bool valid = s[p][i] != kNegInf;
                 const float pr = valid ? expf(s[p][i] - mx) : 0.f;
                 lsum += pr;
-                const bool keep = valid && r16 < G && (!P.vskip || expf(s[p][i] - mt) >= P.v_skip_eps);
+                const bool keep = valid && r16 < G && (!P.vskip || s[p][i] - mt >= P.v_skip_ln);
                 const int tok = 16 * p + 4 * rg + i;
                 if (r16 < GMAX) pl[tok * GMAX + r16] = keep ? pr : 0.f;
                 const uint64_t bal = __ballot(keep);
@@ -1065,7 +1065,8 @@ struct Stream {
     // The whole tile r (both units loaded) under the V-skip rule: the scores of
     // both units give the tile max m; chain(m) returns M, the running max
     // through this tile, for the lane's head (lane & 15); a row j of head h
-    // enters P.V only when exp(s_hj - M_h) >= v_skip_eps, while its weight
+    // enters P.V only when exp(s_hj - M_h) >= v_skip_eps (tested as
+    // s_hj - M_h >= ln v_skip_eps, no exponential), while its weight
     // exp(s_hj - m_h) always enters l.  The tile becomes the running state
     // (the state is empty before: a tile at a time).  Returns the number of
     // (head, row) pairs left out, counted in lane 0.
@@ -1095,7 +1096,7 @@ struct Stream {
                     const float sv = u ? s1[pp][i] : s0[pp][i];
                     const bool valid = sv != kNegInf;
                     const float pr = valid ? exp_fast(sv - mu) : 0.f;
-                    const bool keep = valid && expf(sv - M) >= P.v_skip_eps;
+                    const bool keep = valid && sv - M >= P.v_skip_ln;
                     lsum += pr;
                     skipped += (valid && !keep && r16 < heads_in(P, r.grp)) ? 1 : 0;
                     if (r16 < GMAX) pl[(32 * u + 16 * pp + 4 * rg + i) * GMAX + r16] = keep ? pr : 0.f;
