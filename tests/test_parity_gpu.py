@@ -293,6 +293,24 @@ def test_vskip_bf16_cache(n):
     _run_and_check(c, f"config{n} bf16 art+vskip patience 3", patience=3)
 
 
+@pytest.mark.parametrize("kv,q", [("bf16", "bf16"), ("i8", "bf16"), ("i4", "bf16"), ("bf16", "f32")])
+def test_vskip_predicate_limits(kv, q):
+    # exp(s - M) >= eps at its limits, on the streamed tile (bf16/int8/int4
+    # caches), the work-sharing engine and the one-tile-at-a-time kernel (fp32
+    # queries): eps > 1 leaves every V row out (out = 0, every weight still in
+    # l); eps = 1 keeps only the rows that reach the running max; a tiny eps
+    # keeps every row
+    c = A.make_case("vskip limits", B=3, Hq=8, Hkv=2, d=128, ctx_lens=[1500, 700, 333], kv_dtype=kv,
+                    q_dtype=q, block_size=16, q_mode="temperature", seed=31)
+    full = dict(eps_scale=0.0, eps_dir=0.0)
+    for kw in (dict(), dict(max_workers=96)):
+        out, _, _ = _run_and_check(c, f"{kv}/{q} eps_v 1.0001 {kw}", v_skip_eps=1.0001, **full, **kw)
+        assert (out == 0).all()
+        _run_and_check(c, f"{kv}/{q} eps_v 1 {kw}", v_skip_eps=1.0, **full, **kw)
+        _run_and_check(c, f"{kv}/{q} eps_v 1e-30 art {kw}", v_skip_eps=1e-30, **kw)
+        _run_and_check(c, f"{kv}/{q} eps_v 1e-30 full {kw}", v_skip_eps=1e-30, **full, **kw)
+
+
 # ---------------------------------------------------------------- int4 caches
 
 @pytest.mark.parametrize("d,paged", [(128, True), (64, True), (128, False)])
