@@ -311,6 +311,42 @@ def test_vskip_predicate_limits(kv, q):
         _run_and_check(c, f"{kv}/{q} eps_v 1e-30 full {kw}", v_skip_eps=1e-30, **full, **kw)
 
 
+def _host_skipped_pairs(c, eps):
+    """(head, row) pairs with s - M_t < ln eps over every tile, ascending order,
+    M_t the running max through tile t (float64), and how many of them lie
+    within 1e-3 of the threshold (their decision may go either way in fp32)."""
+    from tests import bruteforce as BF
+    G = c.Hq // c.Hkv
+    ln = np.log(eps)
+    count = near = 0
+    for b in range(c.B):
+        n = int(c.ctx_lens[b])
+        for h in range(c.Hq):
+            K = BF.logical_rows(c, "k", b, h // G, n)
+            sc = K @ BF.query(c, b, h) / np.sqrt(c.d)
+            for t0 in range(0, n, c.tile):
+                M = sc[:t0 + c.tile].max()
+                x = sc[t0:t0 + c.tile] - M - ln
+                count += int((x < 0).sum())
+                near += int((np.abs(x) < 1e-3).sum())
+    return count, near
+
+
+@pytest.mark.parametrize("n", [3, 5])
+def test_vskip_pair_count(n):
+    # stats[3], the (head, row) pairs left out of P.V (counted by the default
+    # engine): exact in full mode, where every tile is consumed once
+    import torch
+    c = A.config(n, small=True, v_skip_eps=1e-4)
+    want, near = _host_skipped_pairs(c, 1e-4)
+    assert want > 0
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    _run_and_check(c, f"config{n} full+vskip count", eps_scale=0.0, eps_dir=0.0, stats=stats)
+    got = int(stats[3].item())
+    log(f"[parity] config{n} skipped pairs: gpu {got} host {want} (near threshold {near})")
+    assert abs(got - want) <= near, (got, want, near)
+
+
 # ---------------------------------------------------------------- int4 caches
 
 @pytest.mark.parametrize("d,paged", [(128, True), (64, True), (128, False)])
