@@ -118,7 +118,9 @@ typedef struct {
                                     query heads may run as several groups of at most
                                     4, each loading the tiles it needs), [1] V rows
                                     loaded,
-                                    [2] tiles loaded after their group had stopped,
+                                    [2] reserved (left unchanged; the tiles loaded
+                                        past a group's stop are [0] minus the
+                                        tiles its heads' tiles_used name),
                                     [3] (query head, position) pairs whose V row was
                                         skipped (v_skip_eps > 0; counted by the
                                         default engine for 64-token tiles only)       */

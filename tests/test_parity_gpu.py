@@ -347,6 +347,46 @@ def test_vskip_pair_count(n):
     assert abs(got - want) <= near, (got, want, near)
 
 
+@pytest.mark.parametrize("kv,q", [("bf16", "bf16"), ("i8", "bf16"), ("i4", "bf16"), ("f32", "f32")])
+def test_load_statistics(kv, q):
+    # stats[0] K tiles loaded, stats[1] V rows loaded: in full mode every tile
+    # of every (row, KV head) is loaded once; stats[2] is left unchanged
+    import torch
+    c = A.make_case("load stats", B=3, Hq=8, Hkv=2, d=128, ctx_lens=[1500, 700, 333], kv_dtype=kv,
+                    q_dtype=q, block_size=16, q_mode="temperature", seed=37)
+    all_tiles = c.Hkv * int((-(-c.ctx_lens // c.tile)).sum())
+    all_rows = c.Hkv * int(c.ctx_lens.sum())
+    for kw in (dict(), dict(max_workers=96)):
+        stats = torch.full((4,), 0, dtype=torch.int64, device="cuda")
+        stats[2] = 7
+        run_gpu(c, eps_scale=0.0, eps_dir=0.0, stats=stats, **kw)
+        st = stats.cpu().numpy()
+        assert st[0] == all_tiles and st[1] == all_rows and st[2] == 7 and st[3] == 0, (kw, st)
+
+
+@pytest.mark.parametrize("n", [2, 3])
+def test_load_statistics_art(n):
+    # ART mode: at least the tiles the stop rule needs (the max of tiles_used
+    # over a group's heads), at most every tile; V rows within the same bounds
+    # (workloads whose heads stop early, at full size)
+    import torch
+    c = A.config(n)
+    G = c.Hq // c.Hkv
+    nt = -(-c.ctx_lens // c.tile)
+    all_tiles = c.Hkv * int(nt.sum())
+    for kw in (dict(), dict(engine=2), dict(max_workers=96)):
+        stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+        _, used = run_gpu(c, stats=stats, **kw)
+        st = stats.cpu().numpy()
+        used_g = used.reshape(c.B, c.Hkv, G).max(axis=-1)
+        needed = int(used_g.sum())
+        rows_needed = int(np.minimum(used_g * c.tile, c.ctx_lens[:, None]).sum())
+        log(f"[stats] config{n} ART {kw}: loaded {st[0]} needed {needed} of {all_tiles}, rows {st[1]}")
+        assert needed < all_tiles  # the heads stop early here
+        assert needed <= st[0] <= all_tiles and rows_needed <= st[1] <= c.Hkv * int(c.ctx_lens.sum()), (kw, st)
+        assert st[2] == 0 and st[3] == 0
+
+
 # ---------------------------------------------------------------- int4 caches
 
 @pytest.mark.parametrize("d,paged", [(128, True), (64, True), (128, False)])
