@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define ART_ABI_VERSION 6
+#define ART_ABI_VERSION 7
 
 typedef enum {
     ART_OK = 0,
@@ -57,7 +57,12 @@ typedef enum {
     ART_ENGINE_POOL = 2,    /* waves on every CU move to the groups with work left; no
                                V skip (falls back to TEAM) and at most one group per
                                resident work-group                                     */
-    ART_ENGINE_SHARED = 3   /* work-sharing engine: max_workers waves claim tiles      */
+    ART_ENGINE_SHARED = 3,  /* work-sharing engine: max_workers waves claim tiles      */
+    ART_ENGINE_XCD = 4      /* one work-group per CU; every (row, KV head) group served
+                               by waves of one XCD (chiplet), which move to the groups
+                               of that XCD with work left; deciders on CUs that load
+                               no tiles; no V skip (falls back to TEAM); at most 512
+                               groups                                                  */
 } art_engine;
 
 /* Order in which a row's tiles are visited (ART summary, section 2.4: the tile
@@ -141,6 +146,12 @@ typedef struct {
                                     1: per (row, KV head) -- the positions a per-head
                                     retention or eviction policy kept, in order (ART
                                     summary, section 2.4: ART runs unchanged on top) */
+    int32_t workers_per_cu;      /* XCD engine: tile-loading waves per CU, 0 = library
+                                    default; capped by what fits in a CU's LDS       */
+    int32_t window;              /* XCD engine: a tile is loaded only while it lies less
+                                    than this many tiles past the decided frontier
+                                    (bounds the tiles loaded past a stop); 0 = library
+                                    default; at most 112                             */
 } art_desc;
 
 /*

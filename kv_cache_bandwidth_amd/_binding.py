@@ -56,13 +56,15 @@ class ArtDesc(ctypes.Structure):
         ("tile_perm_stride", ctypes.c_int32),
         ("tile_perm", ctypes.c_void_p),
         ("per_head_tables", ctypes.c_int32),
+        ("workers_per_cu", ctypes.c_int32),
+        ("window", ctypes.c_int32),
     ]
 
 
 _lib = None
 
 
-ABI_VERSION = 6  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
+ABI_VERSION = 7  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
 
 
 def load():
@@ -105,12 +107,12 @@ def make_desc(*, batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, 
               max_blocks_per_seq=0, num_blocks=0, max_ctx=0, patience=1, v_skip_eps=0.0,
               k_scale=0, v_scale=0, workspace=0, workspace_bytes=0, stats=0, max_workers=0,
               team_helpers=0, engine=0, tile_order=0, tile_perm_stride=0, tile_perm=0,
-              per_head_tables=0) -> ArtDesc:
+              per_head_tables=0, workers_per_cu=0, window=0) -> ArtDesc:
     return ArtDesc(batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, block_size,
                    max_blocks_per_seq, num_blocks, max_ctx, patience, v_skip_eps, k_scale or None,
                    v_scale or None, workspace or None, workspace_bytes, stats or None, max_workers,
                    team_helpers, engine, tile_order, tile_perm_stride, tile_perm or None,
-                   int(per_head_tables))
+                   int(per_head_tables), workers_per_cu, window)
 
 
 def workspace_bytes(desc: ArtDesc, tile: int) -> int:
@@ -131,7 +133,7 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
                      eps_dir=1e-4, patience=1, v_skip_eps=0.0, k_scale=None, v_scale=None,
                      out=None, tiles_used=None, workspace=None, stats=None, max_workers=0, team_helpers=0,
                      engine=0, tile_order=0, tile_perm=None, per_head_tables=False,
-                     stream=None):
+                     workers_per_cu=0, window=0, stream=None):
     """ART decode attention on device tensors; returns (out fp32, tiles_used int32).
 
     q [B, Hq, d] fp32/bf16; k_cache/v_cache paged [num_blocks, Hkv, bs, d] when
@@ -178,7 +180,7 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
                      team_helpers=team_helpers, engine=engine, tile_order=tile_order,
                      tile_perm_stride=tile_perm.shape[-1] if tile_perm is not None else 0,
                      tile_perm=tile_perm.data_ptr() if tile_perm is not None else 0,
-                     per_head_tables=per_head_tables)
+                     per_head_tables=per_head_tables, workers_per_cu=workers_per_cu, window=window)
     need = workspace_bytes(desc, tile)
     if need == 0:
         _check(validate(desc, tile, eps_scale, eps_dir))

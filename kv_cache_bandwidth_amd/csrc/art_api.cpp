@@ -79,8 +79,11 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     if (d->max_workers < 0) return fail(ART_E_PARAM, "max_workers %d < 0", d->max_workers);
     if (d->team_helpers < 0 || d->team_helpers > art::kMaxHelpers)
         return fail(ART_E_PARAM, "team_helpers %d not in 0..%d", d->team_helpers, art::kMaxHelpers);
-    if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_SHARED)
-        return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_SHARED);
+    if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_XCD)
+        return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_XCD);
+    if (d->workers_per_cu < 0) return fail(ART_E_PARAM, "workers_per_cu %d < 0", d->workers_per_cu);
+    if (d->window < 0 || d->window > art::kXpMaxWindow)
+        return fail(ART_E_PARAM, "window %d not in 0..%d", d->window, art::kXpMaxWindow);
     if (d->per_head_tables != 0 && d->per_head_tables != 1)
         return fail(ART_E_PARAM, "per_head_tables %d not 0 or 1", d->per_head_tables);
     if (d->tile_order < ART_ORDER_ASCENDING || d->tile_order > ART_ORDER_LIST)
@@ -265,6 +268,8 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     p.workers = (int)workers;
     p.helpers = desc->team_helpers;
     p.engine = desc->engine;
+    p.xp_wpc_req = desc->workers_per_cu;
+    p.xp_window_req = desc->window;
     const art::Layout L = art::workspace_layout(p);
     char* ws = static_cast<char*>(desc->workspace);
     p.abort_flag = reinterpret_cast<int*>(ws + L.abort_flag);

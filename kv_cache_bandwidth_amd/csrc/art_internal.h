@@ -27,6 +27,8 @@ constexpr int kTeamHelpGroups = 512;  // helpers and the pool engine serve launc
                                       // groups (the workspace holds their shared words only then)
 constexpr int kPoolRing = 128;    // pool engine: record slots per group, by tile index (a power of two)
 constexpr int kPoolContrib = 32;  // pool engine: workers per group at most (each leaves its running state)
+constexpr int kXpMaxWindow = 112; // XCD engine: the load window at most (records live in a ring of
+                                  // kPoolRing slots, released a 16-tile block at a time)
 constexpr int kPoolCtl = 16;      // pool engine control words: [0] tiles released, [1] bound, [2] claim counter,
                                   // [3] workers joined, [4..11] per-head decision, [12] workers active
 constexpr unsigned long long kWaitTicks = 50000000ull;  // 0.5 s of the 100 MHz device clock:
@@ -100,6 +102,11 @@ struct Params {
     int helpers;        // helper work-groups per group (team kernel)
     int pool_cap;       // pool kernel: workers that may join one group (<= kPoolContrib)
     int engine;         // art_engine requested
+    int xp_wpc_req;     // XCD engine: worker waves per CU requested (0 = default)
+    int xp_window_req;  // XCD engine: load window requested (0 = default)
+    int xp_dec_wgs;     // XCD engine: decider work-groups per XCD (set at launch)
+    int xp_wpc;         // XCD engine: worker waves per CU (set at launch)
+    int xp_window;      // XCD engine: tiles past the decided frontier a worker may load
     int slot;           // floats per partial: kSlotHeader + G*D
     // launch
     int deciders;       // decider waves of the persistent kernel (each owns whole groups)

@@ -724,10 +724,12 @@ struct FastTile {
 // accumulator) state that flush() reduces into the fold mapping.  ORD: the
 // art_order the call visits the tiles in (tile_at), fixed at compile time so
 // that each instance carries only its own remap (none for ascending).
-template <int KV, int GMAX, int ORD = ART_ORDER_ASCENDING>
+template <int KV, int GMAX, int ORD = ART_ORDER_ASCENDING, int NB = 2>
 struct Stream {
     static constexpr int D = 128, UP = 2, T = 64, PAGES = 4;
     static constexpr int ORDER = ORD;
+    static constexpr int KVT = KV, GM = GMAX;
+    static constexpr int NBUF = NB;  // unit buffers (a tile is two units: NB = 4 holds two tiles)
     static_assert(PAGES == kStepPages, "step-table records hold one block id per page");
     static constexpr bool SCALED = KV == ART_I8 || KV == ART_I4;  // codes times per-row fp16 scales
     static constexpr int HBM = GMAX / 4;
@@ -747,7 +749,7 @@ struct Stream {
     typedef typename std::conditional<KV == ART_I4, uint32_t,
                                       typename std::conditional<KV == ART_I8, u2, u4>::type>::type vvec;
 
-    static constexpr int LDS_FLOATS = (2 * UP * PAGEB) / 4 + 64 * GMAX;
+    static constexpr int LDS_FLOATS = (NB * UP * PAGEB) / 4 + 64 * GMAX;
     __host__ __device__ static size_t lds_floats(const Params&) { return LDS_FLOATS; }
 
     struct TileRef {             // one tile of one group (wave-uniform)
@@ -757,9 +759,9 @@ struct Stream {
         int err;                 // an invalid block id was met in the tile
     };
 
-    vvec vb[2][UP][4];
-    float ksc[2][UP][4];         // int8: key scale / sqrt(d) of the score rows
-    float vsc[2][UP][4];         // int8: value scale of the P.V rows
+    vvec vb[NB][UP][4];
+    float ksc[NB][UP][4];        // int8: key scale / sqrt(d) of the score rows
+    float vsc[NB][UP][4];        // int8: value scale of the P.V rows
     bf16x8 qB[4];
     float m_run, l_run;
     float acc[GMAX][8];
@@ -768,7 +770,7 @@ struct Stream {
 
     __device__ __forceinline__ void init(float* lds_wave) {
         kl = reinterpret_cast<char*>(lds_wave);
-        pl = lds_wave + (2 * UP * PAGEB) / 4;
+        pl = lds_wave + (NB * UP * PAGEB) / 4;
         reset();
     }
 
@@ -1025,11 +1027,21 @@ struct Stream {
     // `pending`: the next unit's loads were issued after this one's.
     template <int BUF>
     __device__ __forceinline__ void consume(const Params& P, const TileRef& r, int u, bool pending) {
+        if (pending) consume_after<BUF, 1>(P, r, u);
+        else consume_after<BUF, 0>(P, r, u);
+    }
+
+    // consume() once at least NY units' loads (NY * OPS instructions) were
+    // issued after this unit's: waits until at most that many are outstanding
+    // (vector-memory operations complete in issue order), fewer when the count
+    // does not fit the counter (a longer wait, never a shorter one)
+    template <int BUF, int NY>
+    __device__ __forceinline__ void consume_after(const Params& P, const TileRef& r, int u) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         const int G = P.G;
+        constexpr int N = NY * OPS < 63 ? NY * OPS : 63;
         __builtin_amdgcn_sched_barrier(0);
-        if (pending) wait_vm<OPS>();  // this unit's loads, K in LDS included, have landed
-        else wait_vm<0>();
+        wait_vm<N>();  // this unit's loads, K in LDS included, have landed
         __builtin_amdgcn_sched_barrier(0);
         float s[UP][4];
         const float mu = scores<BUF>(P, r, u, s);
@@ -3241,6 +3253,497 @@ size_t pool_lds_bytes(const Params&) {
     return (size_t)PoolShape<S>::WAVES * PoolShape<S>::WAVE_FLOATS * sizeof(float);
 }
 
+// ------------------------------------------------------------------ XCD engine (ART, streamed tiles)
+//
+// Work-group i of a grid of one work-group per CU runs on XCD i % 8 (the
+// dispatcher deals work-groups round-robin over the XCDs), and the CUs of one
+// XCD share an L2.  The engine keeps every group on one XCD: group grp lives on
+// XCD grp % 8, its decider runs on that XCD and so do all the workers that
+// serve it, so every word the group's waves share crosses one L2 only.
+//
+//  * Decider work-groups: the first `xp_dec_wgs` work-groups of each XCD run
+//    one decider wave per group (the pool kernel's decider: records scanned in
+//    aligned 16-tile blocks, per-head decision words, the final merge of the
+//    workers' states in slot order).  These CUs load no tiles, so their polls
+//    of the records never queue behind a CU's stream of tile loads.
+//  * Worker work-groups: `xp_wpc` worker waves per CU.  A worker joins a
+//    group of its XCD (the pool kernel's join: a state slot, the claim
+//    counter), claims tiles two ahead, and pipelines by unit: the next tile's
+//    first unit is issued as soon as the current tile's first unit is consumed,
+//    so one or two units are always in flight while it computes.  Decisions are
+//    read with scalar loads that bypass the scalar cache (the scalar path does
+//    not queue behind the CU's vector loads).  A tile's partial waits in one of
+//    kXpPend LDS slots until its decision, then enters the worker's running
+//    state or is dropped.  A tile is loaded only while it lies less than
+//    `xp_window` tiles past the decided frontier, which bounds the tiles
+//    loaded past a stop.  When its group has no tile left to claim, the
+//    worker leaves its running state in its slot and joins the group of its
+//    XCD with the fewest workers among those with tiles left.
+constexpr int kXcd = 8;              // XCDs of the chip: work-group i runs on XCD i % kXcd
+constexpr int kXpDeciderWaves = 4;   // decider waves per decider work-group
+constexpr int kXpWaves = 4;          // waves per work-group (deciders or workers): one per SIMD, so
+                                     // that a wave may hold 512 registers (VGPRs and AGPRs)
+
+// The XCD engine's tile (two tiles of unit buffers: one in flight while the
+// other is consumed) and the tiles a worker keeps awaiting their decision.
+template <class S>
+struct XpShape {
+    using T = Stream<S::KVT, S::GM, S::ORDER, 4>;
+    static constexpr int HBM = T::HBM;
+    static constexpr int PEND = HBM == 1 ? 4 : 2;             // tiles awaiting their decision (registers)
+    static constexpr int INTS = 48;                            // block ids (16), control words (32)
+    static constexpr int WAVE_FLOATS = T::LDS_FLOATS + INTS;
+    static constexpr int FIT = (160 * 1024 / 4) / WAVE_FLOATS;
+    static constexpr int MAXW = FIT < kXpWaves ? FIT : kXpWaves;  // worker waves per CU at most
+};
+
+// A worker's view of its group's decisions, read with scalar loads that
+// bypass the scalar cache (they do not queue behind the CU's outstanding
+// vector loads; the loads are waited for inside the same statement): words
+// 0..3 and the per-head decision words 4..11 of the group's control block.
+// Per lane: hw[hb] = the decision word of the lane's head in head block hb
+// (kHdStop | 0 for a lane without a head); bnd = the bound (tiles that may
+// still be needed); F = the decided frontier (the smallest count of a head
+// still running, nt once every head has stopped); c2, c3 = words 2 and 3.
+template <int HBM>
+struct XpView {
+    int hw[HBM];
+    int bnd, F;
+    unsigned long long c2, c3;
+    __device__ __forceinline__ void read(const unsigned long long* ctl, unsigned e, int nt, int hv, const FoldLanes& fl) {
+        typedef unsigned u16s __attribute__((ext_vector_type(16)));
+        typedef unsigned u8s __attribute__((ext_vector_type(8)));
+        u16s a;
+        u8s b;
+        asm volatile(
+            "s_load_dwordx16 %0, %2, 0x20 glc\n\t"
+            "s_load_dwordx8 %1, %2, 0x0 glc\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=s"(a), "=s"(b)
+            : "s"(ctl)
+            : "memory");
+        c2 = ((unsigned long long)b[5] << 32) | b[4];
+        c3 = ((unsigned long long)b[7] << 32) | b[6];
+        bnd = b[3] == e ? min(nt, (int)b[2]) : nt;
+        int f = nt;
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const int w = a[2 * h + 1] == e ? (int)a[2 * h] : 0;
+            if (h < hv && !(w & kHdStop)) f = min(f, (w & kHdGaveUp) ? nt : (w & kHdCount));
+        }
+        F = f;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            const int h = hb * 4 + fl.hl;
+            int w = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w = h == k ? (a[2 * k + 1] == e ? (int)a[2 * k] : 0) : w;
+            hw[hb] = (hb < fl.HB && h < hv) ? w : (kHdStop | 0);
+        }
+    }
+};
+
+// The group a worker of XCD x moves to after `cur`: among the XCD's groups with
+// tiles left to claim and room for a worker, the one with the fewest workers
+// (ties: the nearest after cur); -1 if none is left.
+__device__ __forceinline__ int xp_pick(const Params& P, int cur, int x, int nx, int T) {
+    const int lane = lane_id();
+    const unsigned e = P.epoch;
+    const int kc = (cur - x) / kXcd;
+    unsigned long long best = ~0ull;
+    for (int k0 = 0; k0 < nx; k0 += 64) {
+        const int k = k0 + lane;
+        if (k < nx) {
+            const int g = x + kXcd * k;
+            const unsigned long long* ctl = P.team_ctl + (long long)g * kTeamCtl;
+            const unsigned long long cw = cld(ctl + 2), bw = cld(ctl + 1), jw = cld(ctl + 3), aw = cld(ctl + 12);
+            const int nt = group_tiles(P, g, T);
+            bool cand;
+            int act = 0;
+            if ((unsigned)(cw >> 32) != e) {
+                cand = nt > 0;  // not open yet
+            } else {
+                const int lim = min(nt, unstamp(bw, e, nt));
+                cand = (int)(unsigned)cw < lim && unstamp(jw, e, 0) < P.pool_cap;
+                act = unstamp(aw, e, 0);
+            }
+            const unsigned dist = (unsigned)((k - kc - 1 + nx) % nx);
+            const unsigned long long key = ((unsigned long long)act << 32) | dist;
+            if (cand && key < best) best = key;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long other = __shfl_xor(best, o);
+        best = other < best ? other : best;
+    }
+    if (best == ~0ull) return -1;
+    return x + kXcd * (int)(((unsigned)best + kc + 1) % (unsigned)nx);
+}
+
+// Records and decisions of the XCD engine's workers.
+//
+// A tile's probe record (per head: max, sum, dims 0..7, error flag) is
+// stored with one instruction: lane 16*hl + j holds word j of head 4*hb + hl,
+// taken from the head's lane 16*hl by lane permutes.
+template <int HBM>
+__device__ __forceinline__ void xp_store_record(unsigned long long* rb, unsigned tag, const Part<HBM>& o, int err,
+                                                const FoldLanes& fl, int hv) {
+    const int lane = lane_id(), j = lane & 15, src = lane & ~15;
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        // (every permute runs in all lanes: one evaluated under a condition
+        // would read 0 from the source lane where that condition is false)
+        const float mv = __shfl(o.m[hb], src), lv = __shfl(o.l[hb], src);
+        float v = j == 1 ? lv : mv;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float ak = __shfl(o.a[hb][k], src);
+            v = j == 2 + k ? ak : v;
+        }
+        v = j == 10 ? __int_as_float(err) : v;
+        if (j < kTeamRecW && hb < fl.HB && hb * 4 + fl.hl < hv) cst(rb + j * kTeamRecHeads + hb * 4 + fl.hl, tagw(tag, v));
+    }
+}
+
+// The decisions as loaded by a vector load of the control words (lane i < 16
+// holds word i), taken once the load has landed: the bound, the decided
+// frontier and each lane's decision words.
+template <int HBM>
+__device__ __forceinline__ void xp_take(XpView<HBM>& V, unsigned long long q, unsigned e, int nt, int hv,
+                                        const FoldLanes& fl) {
+    const unsigned lo = (unsigned)q, hi = (unsigned)(q >> 32);
+    auto word = [&](int i) -> int {
+        const unsigned l = (unsigned)__builtin_amdgcn_readlane((int)lo, i), h = (unsigned)__builtin_amdgcn_readlane((int)hi, i);
+        return h == e ? (int)l : -1;
+    };
+    const int b = word(1);
+    V.bnd = b < 0 ? nt : min(nt, b);
+    int f = nt;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+        int w = word(4 + h);
+        w = w < 0 ? 0 : w;
+        if (h < hv && !(w & kHdStop)) f = min(f, (w & kHdGaveUp) ? nt : (w & kHdCount));
+    }
+    V.F = f;
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        const int src = 4 + min(h, 7);
+        const unsigned l = (unsigned)__shfl((int)lo, src), hh = (unsigned)__shfl((int)hi, src);
+        const int w = hh == e ? (int)l : 0;
+        V.hw[hb] = (hb < fl.HB && h < hv) ? w : (kHdStop | 0);
+    }
+}
+
+// One worker of XCD x (index wi among the XCD's workers): joins groups of its
+// XCD and processes their tiles until none is left.  Tiles are claimed four
+// ahead of the one consumed; tile k's two units are loaded into buffer pair
+// k % 2 while tile k - 1 (the other pair) is consumed.  `wint`: 8 LDS ints
+// for block ids (LDS-direct loads).
+template <class S>
+__device__ __forceinline__ void xp_worker(const Params& P, S& st, int x, int wi, int* wint) {
+    constexpr int HBM = S::HBM, T = S::T, KP = XpShape<S>::PEND;
+    const int lane = lane_id();
+    const FoldLanes fl(P);
+    const unsigned e = P.epoch;
+    const int nx = (P.NG - x + kXcd - 1) / kXcd;  // groups of this XCD: x, x + 8, ...
+    if (nx <= 0) return;
+    unsigned long long loaded = 0, rows = 0;
+    int* blk = wint;        // block ids of the tile whose loads come next but one (LDS-direct)
+    int* ctlw = wint + 16;  // the group's control words 0..15 (LDS-direct, coherent)
+    int grp = x + kXcd * (wi % nx);
+    bool gv = false;  // a wait outlasted kWaitTicks: stop working
+    for (int round = 0; !gv; ++round) {
+        if (round > 0) {
+            grp = uni(xp_pick(P, grp, x, nx, T));
+            if (grp < 0) break;
+        }
+        const PoolGlobal pg(P, grp);
+        const int n = P.ctx_lens[seq_of(P, grp)];
+        const int nt = group_tiles(P, grp, T);
+        if (nt == 0) continue;
+        const int hv = heads_in(P, grp);
+        // join: once the decider has reset the group's counters, take a state slot
+        XpView<HBM> V;
+        {
+            const Deadline dl;
+            for (;;) {
+                V.read(pg.ctl, e, nt, hv, fl);
+                const unsigned long long aw = uni64(cld(pg.ctl + 12));
+                if ((unsigned)(V.c2 >> 32) == e && (unsigned)(V.c3 >> 32) == e && (unsigned)(aw >> 32) == e) break;
+                if (dl.passed()) {
+                    gv = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+        }
+        if (gv) break;  // the group's decider never opened it (it reports its heads)
+        if ((int)(unsigned)V.c2 >= V.bnd) continue;  // nothing left to claim
+        const int slot = (int)(unsigned)faa64(pg.ctl + 3, 1ull);
+        if (slot >= P.pool_cap) continue;  // the group has had as many workers as it may
+        add64(pg.ctl + 12, 1ull);
+        Part<HBM> run;
+        run.clear();
+        // tiles awaiting their decision, oldest first: tile ptl[k], partial pq[k]
+        Part<HBM> pq[KP];
+        int ptl[KP];
+        int np = 0;
+        // merges (or drops) the oldest pending tile once every head has decided it
+        auto try_front = [&]() -> bool {
+            const int tp = ptl[0];
+            int fate[HBM];
+            bool und = false;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                fate[hb] = tile_fate(V.hw[hb], tp);
+                und |= fate[hb] < 0;
+            }
+            if (__ballot(und) != 0ull) return false;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb)
+                if (fate[hb] > 0) sm_merge_fast(run.m[hb], run.l[hb], run.a[hb], pq[0].m[hb], pq[0].l[hb], pq[0].a[hb]);
+#pragma unroll
+            for (int k = 0; k + 1 < KP; ++k) {
+                pq[k] = pq[k + 1];
+                ptl[k] = ptl[k + 1];
+            }
+            --np;
+            return true;
+        };
+        auto drain_decided = [&]() {
+            while (np > 0 && try_front()) {
+            }
+        };
+        auto refresh = [&]() { V.read(pg.ctl, e, nt, hv, fl); };
+        // merges what is decided; then, polling, until at most `keep` tiles are pending
+        auto retire = [&](int keep) {
+            drain_decided();
+            if (np <= keep) return;
+            const Deadline dl;
+            for (;;) {
+                __builtin_amdgcn_s_sleep(2);
+                refresh();
+                drain_decided();
+                if (np <= keep) return;
+                if (dl.passed()) {
+                    gv = true;
+                    np = 0;
+                    return;
+                }
+            }
+        };
+        // waits (polling) until tile tq may be loaded or is no longer needed:
+        // true when it may be loaded
+        auto admit = [&](int tq) -> bool {
+            if (tq >= V.bnd) return false;
+            if (tq < V.F + P.xp_window) return true;
+            const Deadline dl;
+            for (;;) {
+                __builtin_amdgcn_s_sleep(2);
+                refresh();
+                drain_decided();
+                if (tq >= V.bnd) return false;
+                if (tq < V.F + P.xp_window) return true;
+                if (dl.passed()) {
+                    gv = true;
+                    return false;
+                }
+            }
+        };
+        auto claim = [&]() { return (int)(unsigned)faa64(pg.ctl + 2, 1ull); };
+        // every lane takes part (lane 0 adds 1, the others 0), so that no
+        // branch around the atomic leaves a result to be merged (and waited
+        // for) at once; lane 0's old value is the tile claimed.  A 32-bit add
+        // on the count, the low half of the stamped word: the whole result
+        // register is used, so none of it is reallocated while the atomic is
+        // in flight.
+        auto claim_async = [&]() -> int {
+            return (int)__hip_atomic_fetch_add(reinterpret_cast<unsigned*>(pg.ctl + 2), lane == 0 ? 1u : 0u,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        // the control words, fetched into LDS (no register waits for them):
+        // lane i < 32 loads dword i coherently; read once the load has landed
+        auto load_ctl = [&]() {
+            if (lane < 32)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const int*>(pg.ctl) + lane,
+                                                 (__attribute__((address_space(3))) void*)ctlw, 4, 0, 16 /* sc1 */);
+        };
+        auto ctl_word = [&]() -> unsigned long long {
+            const int i = lane & 15;
+            return ((unsigned long long)(unsigned)lds_ld(ctlw + 2 * i + 1) << 32) | (unsigned)lds_ld(ctlw + 2 * i);
+        };
+        // pushes a consumed tile's partial (room made first) and stores its record
+        auto push = [&](int tq, const typename S::Out& o, int err) {
+            retire(KP - 1);
+            if (gv) return;
+            Part<HBM> pn;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                pn.m[hb] = o.mf[hb];
+                pn.l[hb] = o.lf[hb];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pn.a[hb][j] = o.a[hb][j];
+            }
+#pragma unroll
+            for (int k = 0; k < KP; ++k)
+                if (k == np) {
+                    pq[k] = pn;
+                    ptl[k] = tq;
+                }
+            ++np;
+            unsigned long long* rb = pg.rec + (long long)(tq & (kPoolRing - 1)) * kTeamRecW * kTeamRecHeads;
+            xp_store_record<HBM>(rb, rec_tag<kPoolRing>(e, tq), pn, err, fl, hv);
+        };
+        // Steady state: tile t in pair A (landed or landing), tile tN in pair B
+        // (issued after t), t2's block ids in LDS or on their way, t3 claimed
+        // in flight.  A step consumes pair A and issues t2 into it.  When t2
+        // is not needed (past the bound: it never becomes needed again) the
+        // step issues a dummy tile instead -- rows 0..15 of the cache, held in
+        // L2 -- and the loop ends once both pairs hold dummies.  So on every
+        // path into a step, t's units, a few single instructions and tN's
+        // units were issued in this order: the waits count on at least 3 and
+        // 2 units' instructions being younger, and the compiler, seeing the
+        // same history on every path, adds no wait of its own.
+        typename S::TileRef CA, CB;
+        bool realA = false, realB = false;
+        auto dummy = [&](typename S::TileRef& r) {
+            r.grp = grp;
+            r.t = -1;
+            r.n = 0;
+            r.pmask = 0;
+            r.err = 0;
+#pragma unroll
+            for (int p = 0; p < S::PAGES; ++p) r.prow[p] = 0;
+        };
+        st.load_q(P, grp);
+        int t = claim();
+        if (!admit(t)) t = nt;
+        int tN = nt, t2 = nt, t3r = nt;
+        // A tile past the load window is never waited for while this worker
+        // holds a loaded tile whose record is not yet published (the frontier
+        // may be waiting for that record): it is deferred -- the pair gets a
+        // dummy, the held tile is consumed and published at the next step, and
+        // only then does the worker wait for the window.
+        auto step = [&](auto pbc, typename S::TileRef& Ccur, bool& realCur, bool realNext) {
+            constexpr int PB = decltype(pbc)::value;
+            st.template consume_after<2 * PB, 3>(P, Ccur, 0);
+            st.template consume_after<2 * PB + 1, 2>(P, Ccur, 1);
+            // everything issued before tN's units has landed: t2's block ids,
+            // the claim after it and the control words
+            typename S::Out o;
+            st.flush(P, o);
+            xp_take<HBM>(V, ctl_word(), e, nt, hv, fl);
+            drain_decided();
+            if (realCur && t < V.bnd && !gv) push(t, o, Ccur.err);
+            bool issue2 = false;
+            if (!gv && t2 < V.bnd) {
+                if (t2 < V.F + P.xp_window) issue2 = true;
+                else if (!realNext) issue2 = admit(t2);  // nothing unpublished is held: waiting is safe
+            }
+            const bool defer = !gv && !issue2 && realNext && t2 < V.bnd;
+            int t3 = nt;
+            if (issue2) {
+                t3 = uni(t3r);
+                S::resolve_lds(P, grp, n, t2, blk, Ccur);  // (the ids landed with t's loads)
+                ++loaded;
+                rows += S::rows_in(Ccur);
+                if (t3 < V.bnd) S::fetch_blocks_lds(P, grp, n, t3, blk);
+                // (claimed whatever happens, so that no select waits for the result;
+                // a claim past the bound is never loaded)
+                t3r = claim_async();
+            } else {
+                dummy(Ccur);
+            }
+            load_ctl();
+            st.template issue<2 * PB>(P, Ccur, 0);
+            st.template issue<2 * PB + 1>(P, Ccur, 1);
+            realCur = issue2;
+            t = tN;
+            if (issue2) {
+                tN = t2;
+                t2 = t3 < V.bnd ? t3 : nt;
+            } else {
+                tN = nt;
+                if (!defer) t2 = nt;  // (a deferred t2 keeps its block ids in LDS and its claim)
+            }
+        };
+        if (t < nt) {
+            // (one branch holds the prologue and the loop, so that the loop is
+            // entered only after both pairs were issued)
+            S::resolve_from(P, grp, n, t, S::fetch_blocks(P, grp, n, t), CA);
+            st.template issue<0>(P, CA, 0);
+            st.template issue<1>(P, CA, 1);
+            ++loaded;
+            rows += S::rows_in(CA);
+            realA = true;
+            tN = claim();
+            // tile x0 is held unpublished: tN is not waited for (deferred past the window)
+            realB = tN < V.bnd && tN < V.F + P.xp_window;
+            if (realB) {
+                S::resolve_from(P, grp, n, tN, S::fetch_blocks(P, grp, n, tN), CB);
+                t2 = claim();
+            } else {
+                dummy(CB);
+                t2 = tN < V.bnd ? tN : nt;  // deferred, or not needed
+                tN = nt;
+            }
+            if (t2 < V.bnd) S::fetch_blocks_lds(P, grp, n, t2, blk);
+            t3r = claim_async();  // (lane 0)
+            load_ctl();
+            st.template issue<2>(P, CB, 0);
+            st.template issue<3>(P, CB, 1);
+            if (realB) {
+                ++loaded;
+                rows += S::rows_in(CB);
+            }
+            for (;;) {
+                step(std::integral_constant<int, 0>{}, CA, realA, realB);
+                step(std::integral_constant<int, 1>{}, CB, realB, realA);
+                if (!realA && !realB) break;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // loads of a dropped tile may still be landing (in LDS too)
+        if (!gv) retire(0);
+        // leave the running state in the slot, then leave the group
+        const unsigned stg = state_tag(e);
+        unsigned long long* dst = pg.state + (long long)slot * HBM * kTeamStateW * 64 + lane;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            unsigned long long* w = dst + hb * kTeamStateW * 64;
+            cst(w, tagw(stg, run.m[hb]));
+            cst(w + 64, tagw(stg, run.l[hb]));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cst(w + 64 * (2 + j), tagw(stg, run.a[hb][j]));
+        }
+        add64(pg.ctl + 12, ~0ull);  // one worker less
+    }
+    count_stats(P, loaded, rows);
+}
+
+// Grid: one work-group per CU (all resident: cooperative launch).
+template <class S>
+__global__ __launch_bounds__(kXpWaves * 64) void art_xp_kernel(Params P) {
+    extern __shared__ float lds[];
+    using TS = typename XpShape<S>::T;
+    constexpr int WF = XpShape<S>::WAVE_FLOATS;
+    const int wv = wave_id(), wg = blockIdx.x;
+    const int x = wg % kXcd, j = wg / kXcd;
+    if (j < P.xp_dec_wgs) {
+        const int grp = x + kXcd * (j * kXpDeciderWaves + wv);
+        if (grp < P.NG) pool_decider<TS::HBM>(P, grp, TS::T);
+        return;
+    }
+    if (wv >= P.xp_wpc) return;
+    const int wi = (j - P.xp_dec_wgs) * P.xp_wpc + wv;
+    TS st;
+    float* mine = lds + wv * WF;
+    st.init(mine);
+    xp_worker<TS>(P, st, x, wi, reinterpret_cast<int*>(mine + TS::LDS_FLOATS));
+}
+
 // Full mode, one tile at a time: split sp of group grp covers a fixed tile range.
 template <class Tile>
 __global__ __launch_bounds__(256) void art_full_kernel(Params P) {
@@ -3589,6 +4092,56 @@ int launch_pool(const Params& p0, hipStream_t s) {
     return 1;
 }
 
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+constexpr int kXpDefaultWindow = 64;  // tiles past the decided frontier a worker may load, by default
+
+// One work-group per CU, all resident (cooperative launch); returns 1 when it
+// cannot run (too many groups, a CU count not divisible over the XCDs, or the
+// grid would not be resident), so that the team engine runs instead.
+template <class S>
+int launch_xp(const Params& p0, hipStream_t s) {
+    Params p = p0;
+    const int cus = device_cus();
+    if (cus <= 0 || cus % kXcd || p.NG > kTeamHelpGroups) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    const int per_xcd = cus / kXcd;
+    const int nx = (p.NG + kXcd - 1) / kXcd;
+    p.xp_dec_wgs = (nx + kXpDeciderWaves - 1) / kXpDeciderWaves;
+    if (p.xp_dec_wgs >= per_xcd) return 1;
+    int wpc = p.xp_wpc_req > 0 ? p.xp_wpc_req : XpShape<S>::MAXW;
+    if (wpc > XpShape<S>::MAXW) wpc = XpShape<S>::MAXW;
+    if (wpc < 1) return 1;
+    p.xp_wpc = wpc;
+    p.xp_window = p.xp_window_req > 0 ? p.xp_window_req : kXpDefaultWindow;
+    if (p.xp_window > kXpMaxWindow) p.xp_window = kXpMaxWindow;
+    p.pool_cap = kPoolContrib;
+    // at least half a CU's LDS, so that no CU takes two work-groups
+    size_t lds = (size_t)wpc * XpShape<S>::WAVE_FLOATS * sizeof(float);
+    if (lds < 82 * 1024) lds = 82 * 1024;
+    void* args[] = {&p};
+    const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&art_xp_kernel<S>), dim3((unsigned)cus),
+                                                    dim3(kXpWaves * 64), args, (unsigned)lds, s);
+    if (e == hipSuccess) return 0;
+    (void)hipGetLastError();
+    return 1;
+}
+
 template <class S>
 int run_stream(const Params& p, hipStream_t s, bool art) {
     if constexpr (S::ORDER == ART_ORDER_LIST) {
@@ -3602,6 +4155,7 @@ int run_stream(const Params& p, hipStream_t s, bool art) {
     if (!art) return launch_split<decltype(&art_full_stream_kernel<S>), S>(p, s, &art_full_stream_kernel<S>);
     if (sharing(p)) return launch_persistent<decltype(&art_stream_kernel<S>), S>(p, s, &art_stream_kernel<S>);
     if (p.vskip) return launch_team<S, true>(p, s);
+    if (p.engine == ART_ENGINE_XCD && launch_xp<S>(p, s) == 0) return 0;
     // by default the pool serves few, long groups (where one CU per group
     // would leave most of the chip idle)
     const bool pool = p.engine == ART_ENGINE_POOL ||

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = art.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.art_abi_version() == 6
+    assert lib.art_abi_version() == 7
 
 
 def desc(**kw):
@@ -81,7 +81,10 @@ def test_valid_desc_passes():
     (dict(team_helpers=-1), -5),
     (dict(team_helpers=4), -5),
     (dict(engine=-1), -5),
-    (dict(engine=4), -5),
+    (dict(engine=5), -5),
+    (dict(workers_per_cu=-1), -5),
+    (dict(window=-1), -5),
+    (dict(window=113), -5),
     (dict(tile_order=-1), -5),
     (dict(tile_order=3), -5),
     (dict(tile_order=2), -1),                  # a caller's order without tile_perm

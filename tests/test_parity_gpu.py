@@ -18,7 +18,8 @@ def _run_and_check(case, label, **kw):
         f"ctx={case.ctx_lens.tolist()[:4]} kv={case.kv_dtype} T={case.tile} {kw}")
     out, used = run_gpu(case, **kw)
     r = check_parity(case, out, used,
-                     **{k: v for k, v in kw.items() if k not in ("max_workers", "team_helpers", "engine", "stats")})
+                     **{k: v for k, v in kw.items()
+                        if k not in ("max_workers", "team_helpers", "engine", "stats", "workers_per_cu", "window")})
     log(f"[parity] {label}: max_abs={r['max_abs']:.3e} near={r['near']} "
         f"mean tiles_used={np.mean(r['tiles_used']):.1f}")
     return out, used, r
@@ -202,7 +203,7 @@ def test_helper_work_groups_parity():
     _run_and_check(c, "config4-small art, 1 helper work-group per group", team_helpers=1)
 
 
-ENGINE_TEAM, ENGINE_POOL = 1, 2
+ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD = 1, 2, 4
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
@@ -222,6 +223,44 @@ def test_pool_engine_matches_team_engine():
         o2, u2 = run_gpu(c, dev, engine=ENGINE_POOL, **kw)
         assert np.array_equal(u1, u2)
         np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_xcd_engine_parity(n):
+    # every group served by the waves of one XCD, deciders on CUs that load no tiles
+    c = A.config(n, small=n != 2)
+    _run_and_check(c, f"config{n} xcd art", engine=ENGINE_XCD, v_skip_eps=0.0)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(workers_per_cu=1), dict(window=1), dict(window=4),
+                                dict(workers_per_cu=2, window=2)])
+def test_xcd_engine_knobs(kw):
+    # the load window (even a single tile past the decided frontier) and the
+    # workers per CU change only the schedule: tiles_used equals the oracle's
+    c = A.config(4, small=True)
+    _run_and_check(c, f"config4-small xcd art {kw}", engine=ENGINE_XCD, **kw)
+
+
+def test_xcd_engine_matches_team_engine():
+    c = A.config(3, small=True)
+    dev = to_device(c)
+    for kw in (dict(), dict(eps_scale=1e-30, eps_dir=1e-30), dict(patience=3)):
+        o1, u1 = run_gpu(c, dev, engine=ENGINE_TEAM, **kw)
+        o2, u2 = run_gpu(c, dev, engine=ENGINE_XCD, **kw)
+        assert np.array_equal(u1, u2)
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-5)
+
+
+def test_xcd_engine_ragged_empty_and_invalid_rows():
+    c = A.config(3, small=True, batch=5)
+    c.ctx_lens[1] = 0                                   # empty row
+    c.ctx_lens[2] = 1                                   # one token
+    c.ctx_lens[3] = 64 * 3 + 17                         # ragged tail
+    c.ctx_lens[4] = c.block_table.shape[1] * 16 + 1     # longer than its table
+    out, used = run_gpu(c, engine=ENGINE_XCD)
+    assert (used[1] == 0).all() and (out[1] == 0).all()
+    assert (used[4] == -1).all() and np.isnan(out[4]).all()
+    check_parity(c, out, used, rows=[0, 1, 2, 3])
 
 
 def test_pool_engine_ragged_empty_and_invalid_rows():
