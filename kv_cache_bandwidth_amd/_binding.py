@@ -148,7 +148,23 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
     """
     import torch
     lib = load()
+    # Every tensor's shape, dtype and placement is checked here, before the
+    # library sees a pointer: a mismatch would make the kernels read or write
+    # outside the caller's buffers.
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, Hq, d], got shape {tuple(q.shape)}")
     B, Hq, d = q.shape
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"q must be float32 or bfloat16, got {q.dtype}")
+    if k_cache.dim() != 4:
+        raise ValueError(f"k_cache must be 4-dimensional, got shape {tuple(k_cache.shape)}")
+    if k_cache.dtype not in (torch.float32, torch.bfloat16, torch.int8, torch.uint8):
+        raise ValueError(f"k_cache dtype {k_cache.dtype} not supported")
+    row = d // 2 if k_cache.dtype == torch.uint8 else d
+    if k_cache.shape[-1] != row:
+        raise ValueError(f"k_cache rows hold {k_cache.shape[-1]} elements, expected {row} for head_dim {d}")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must have the shape and dtype of k_cache")
     if block_table is not None:
         nb, Hkv, bs, _ = k_cache.shape
         mbps = block_table.shape[-1]
@@ -156,20 +172,37 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
     else:
         _, Hkv, max_ctx, _ = k_cache.shape
         nb = bs = mbps = 0
+        if k_cache.shape[0] != B:
+            raise ValueError(f"a contiguous cache leads with the batch {B}, got {k_cache.shape[0]}")
     seqs = (B, Hkv) if per_head_tables else (B,)
     if tuple(ctx_lens.shape) != seqs or (block_table is not None and tuple(block_table.shape[:-1]) != seqs) \
             or (tile_perm is not None and tuple(tile_perm.shape[:-1]) != seqs):
         raise ValueError(f"ctx_lens, block_table and tile_perm must lead with {seqs}")
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("ctx_lens", ctx_lens),
-                    ("block_table", block_table), ("k_scale", k_scale), ("v_scale", v_scale),
-                    ("tile_perm", tile_perm)):
-        if t is not None and not (t.is_cuda and t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    scaled = k_cache.dtype in (torch.int8, torch.uint8)
+    if scaled:
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t is None or tuple(t.shape) != tuple(k_cache.shape[:-1]):
+                raise ValueError(f"{name} must be given, shaped like the cache without its last dim "
+                                 f"{tuple(k_cache.shape[:-1])}")
     for name, t, want in (("ctx_lens", ctx_lens, torch.int32), ("block_table", block_table, torch.int32),
                           ("tile_perm", tile_perm, torch.int32), ("k_scale", k_scale, torch.float16),
-                          ("v_scale", v_scale, torch.float16)):
+                          ("v_scale", v_scale, torch.float16), ("stats", stats, torch.int64)):
         if t is not None and t.dtype != want:
             raise ValueError(f"{name} must be {want}, got {t.dtype}")
+    if stats is not None and stats.numel() < 4:
+        raise ValueError(f"stats must hold at least 4 int64 counters, got {stats.numel()}")
+    if out is not None and (tuple(out.shape) != (B, Hq, d) or out.dtype != torch.float32):
+        raise ValueError(f"out must be float32 {(B, Hq, d)}, got {out.dtype} {tuple(out.shape)}")
+    if tiles_used is not None and (tuple(tiles_used.shape) != (B, Hq) or tiles_used.dtype != torch.int32):
+        raise ValueError(f"tiles_used must be int32 {(B, Hq)}, got {tiles_used.dtype} {tuple(tiles_used.shape)}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("ctx_lens", ctx_lens),
+                    ("block_table", block_table), ("k_scale", k_scale), ("v_scale", v_scale),
+                    ("tile_perm", tile_perm), ("out", out), ("tiles_used", tiles_used), ("stats", stats),
+                    ("workspace", workspace)):
+        if t is not None and not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
     desc = make_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
                      q_dtype=_dtype_code(q), kv_dtype=_dtype_code(k_cache), block_size=bs,
                      max_blocks_per_seq=mbps, num_blocks=nb, max_ctx=max_ctx, patience=patience,
@@ -187,7 +220,7 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     desc.workspace = workspace.data_ptr()
-    desc.workspace_bytes = workspace.numel()
+    desc.workspace_bytes = workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if tiles_used is None:

@@ -147,3 +147,12 @@ def decode(q, k, v, ctx_lens, *, tile=64, eps_scale=1e-3, eps_dir=1e-4, patience
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return OracleResult(out, U, tr)
+
+
+def widen_f16(bits) -> np.ndarray:
+    """The oracle's widening of fp16 bit patterns (uint16 array) to float64."""
+    lib = _load()
+    f = lib.art_oracle_widen_f16
+    f.argtypes, f.restype = [ctypes.c_int], ctypes.c_double
+    flat = np.asarray(bits, np.uint16).ravel()
+    return np.array([f(int(x)) for x in flat], np.float64).reshape(np.shape(bits))

@@ -327,3 +327,7 @@ int art_oracle_decode(int B, int Hq, int Hkv, int d, int q_dtype, int kv_dtype,
 }
 
 int art_oracle_trace_fields(void) { return TRACE_FIELDS; }
+
+/* The widening of one fp16 bit pattern, exported so that the tests can check
+   it against an independent IEEE binary16 decoder for every pattern. */
+double art_oracle_widen_f16(int bits) { return widen_f16((uint16_t)bits); }

@@ -152,3 +152,61 @@ def test_plain_c_client(tmp_path):
                     f"-Wl,-rpath,{lib_dir}"], check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+
+
+def _cpu_args(**over):
+    """Host tensors of a small paged bf16 call (never launched: every case
+    below is rejected before the library sees a pointer)."""
+    import torch
+    B, Hq, Hkv, d, nb, bs = 2, 8, 2, 128, 8, 16
+    a = dict(q=torch.zeros(B, Hq, d, dtype=torch.bfloat16),
+             k_cache=torch.zeros(nb, Hkv, bs, d, dtype=torch.bfloat16),
+             v_cache=torch.zeros(nb, Hkv, bs, d, dtype=torch.bfloat16),
+             ctx_lens=torch.zeros(B, dtype=torch.int32),
+             block_table=torch.zeros(B, 4, dtype=torch.int32))
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,match", [
+    (dict(q="q2d"), "q must be"),
+    (dict(k_cache="bad_last_dim"), "k_cache rows"),
+    (dict(v_cache="other_shape"), "v_cache must have"),
+    (dict(v_cache="other_dtype"), "v_cache must have"),
+    (dict(k_cache="int8_no_scales", v_cache="int8_no_scales"), "k_scale must be given"),
+    (dict(k_cache="int8", v_cache="int8", k_scale="bad_scale", v_scale="good_scale"), "k_scale must be given"),
+    (dict(k_cache="int8", v_cache="int8", k_scale="f32_scale", v_scale="good_scale"), "k_scale must be"),
+    (dict(out="bad_out"), "out must be"),
+    (dict(tiles_used="bad_used"), "tiles_used must be"),
+    (dict(stats="short_stats"), "stats must hold"),
+    (dict(stats="int32_stats"), "stats must be"),
+    (dict(ctx_lens="int64_lens"), "ctx_lens must be"),
+    (dict(block_table="short_table_rows"), "must lead with"),
+    (dict(), "contiguous device tensor"),  # well formed, but host tensors
+])
+def test_binding_rejects_mismatched_tensors(over, match):
+    import torch
+    nb, Hkv, bs, d = 8, 2, 16, 128
+    make = {
+        "q2d": torch.zeros(2, 128, dtype=torch.bfloat16),
+        "bad_last_dim": torch.zeros(nb, Hkv, bs, 64, dtype=torch.bfloat16),
+        "other_shape": torch.zeros(nb, Hkv, bs + 16, d, dtype=torch.bfloat16),
+        "other_dtype": torch.zeros(nb, Hkv, bs, d, dtype=torch.float32),
+        "int8_no_scales": torch.zeros(nb, Hkv, bs, d, dtype=torch.int8),
+        "int8": torch.zeros(nb, Hkv, bs, d, dtype=torch.int8),
+        "bad_scale": torch.zeros(nb, Hkv, bs + 1, dtype=torch.float16),
+        "good_scale": torch.zeros(nb, Hkv, bs, dtype=torch.float16),
+        "f32_scale": torch.zeros(nb, Hkv, bs, dtype=torch.float32),
+        "bad_out": torch.zeros(2, 8, 64, dtype=torch.float32),
+        "bad_used": torch.zeros(2, 8, dtype=torch.int64),
+        "short_stats": torch.zeros(3, dtype=torch.int64),
+        "int32_stats": torch.zeros(4, dtype=torch.int32),
+        "int64_lens": torch.zeros(2, dtype=torch.int64),
+        "short_table_rows": torch.zeros(3, 4, dtype=torch.int32),
+    }
+    kw = {k: make[v] for k, v in over.items()}
+    args = _cpu_args(**{k: kw[k] for k in ("q", "k_cache", "v_cache", "ctx_lens", "block_table") if k in kw})
+    rest = {k: v for k, v in kw.items() if k not in args}
+    with pytest.raises(ValueError, match=match):
+        art.decode_attention(args["q"], args["k_cache"], args["v_cache"], args["ctx_lens"],
+                             block_table=args["block_table"], **rest)

@@ -145,6 +145,68 @@ def test_constant_values(patience):
     assert (full.tiles_used == n // 16).all()  # 0 is never strictly below 0
 
 
+# ---------------------------------------------------------------- reading 14: a zero probe never passes
+
+def zero_probe_case(k, patience, nt=10, T=4, d=16, seed=11):
+    """Keys all equal (uniform weights); the V rows of tiles 0..k-1 are zero in
+    the probe dims 0..7 and those of later tiles equal a constant c there, so
+    the probe is exactly 0 through tile k - 1 and (t - k + 1) / (t + 1) * c
+    after.  Dims beyond 8 are random (outside the probe)."""
+    rng = np.random.default_rng(seed)
+    c_vec = rng.uniform(0.5, 2.0, size=8)
+    V = np.zeros((1, 1, nt * T, d))
+    V[0, 0, k * T:, :8] = c_vec
+    V[0, 0, :, 8:] = rng.uniform(-3, 3, size=(nt * T, d - 8))
+    K = np.zeros((1, 1, nt * T, d))
+    q = rng.standard_normal((1, 2, d))
+    # thresholds no finite metric reaches: every tile passes unless a norm is 0
+    return contiguous_case(q, K, V, tile=T, eps_scale=1e30, eps_dir=1e30, patience=patience)
+
+
+@pytest.mark.parametrize("k,patience", [(0, 1), (1, 1), (3, 1), (3, 2), (6, 3)])
+def test_zero_norm_probe_never_passes(k, patience):
+    # Closed form: a metric against a probe of norm 0 is +inf (reading 14), so
+    # no tile passes while the probe or the previous one is 0: tiles k and
+    # later are the first whose probe is nonzero, the first comparison of two
+    # nonzero probes is at tile k + 1 (tile 1 when k = 0), and the stop comes
+    # `patience` passing tiles later
+    c = zero_probe_case(k, patience)
+    r = run_oracle(c, trace=True)
+    first = max(k + 1, 1)
+    assert (r.tiles_used == first + patience).all(), (r.tiles_used, first + patience)
+    ds = r.trace[0, 0, 1:first, 2]
+    assert np.isinf(ds).all()  # every comparison before: a zero norm on either side
+
+
+def test_widen_f16_every_pattern():
+    # the oracle's fp16 widening (normal, subnormal, zero, inf, nan, both
+    # signs) against numpy's IEEE binary16 conversion, for all 65536 patterns
+    import oracle
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.widen_f16(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(ours, ref, equal_nan=True)
+    assert np.array_equal(np.signbit(ours), np.signbit(ref))
+
+
+def test_int8_with_subnormal_scales_equals_dequantised_fp32():
+    # fp16 scales below 2^-14 take the subnormal branch of the widening; the
+    # int8 oracle must still equal the fp64 oracle on the dequantised cache
+    # (code * scale is exact in fp32: an 8-bit code times a 10-bit fraction)
+    c = A.config(5, small=True, seed=3, batch=1, ctx=256)
+    rng = np.random.default_rng(4)
+    c.k_scale = rng.integers(1, 0x400, size=c.k_scale.shape).astype(np.uint16)
+    c.v_scale = rng.integers(1, 0x400, size=c.v_scale.shape).astype(np.uint16)
+    deq = lambda codes, sc: (codes.astype(np.float32) * sc.view(np.float16).astype(np.float32)[..., None])
+    f = A.Case(name="deq", B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, q=c.q,
+               k=deq(c.k, c.k_scale), v=deq(c.v, c.v_scale), ctx_lens=c.ctx_lens,
+               block_size=c.block_size, block_table=c.block_table, tile=c.tile)
+    for kw in (dict(v_skip_eps=0.0), dict(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)):
+        a = run_oracle(c, **kw)
+        b = run_oracle(f, **kw)
+        assert np.array_equal(a.out, b.out) and np.array_equal(a.tiles_used, b.tiles_used)
+
+
 # ---------------------------------------------------------------- P6: designed probe sequences
 
 FIXTURES = sorted(glob.glob(os.path.join(GOLDEN, "*.json")))

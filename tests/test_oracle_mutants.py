@@ -61,6 +61,11 @@ MUTANTS = {
     "per_head_list_row_shared": ("const int pt = visit_tile(J, sq, nt, t);", "const int pt = visit_tile(J, b, nt, t);"),
     "int8_scale_ignored": ("double s = widen_f16(scale[row]);", "double s = 1.0;"),
     "direction_not_clamped_half": ("dd = 1.0 - dot / (xn * prev_norm);", "dd = 0.5 * (1.0 - dot / (xn * prev_norm));"),
+    "zero_norm_probe_passes": ("                ds = INFINITY;\n                dd = INFINITY;",
+                               "                ds = 0.0;\n                dd = 0.0;"),
+    "f16_subnormal_exponent": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "f16_inf_as_max": ("v = m ? NAN : INFINITY;", "v = m ? NAN : 65504.0;"),
+    "f16_sign_dropped": ("return sign ? -v : v;", "return v;"),
 }
 
 # pins to run against every mutant (name -> callable with fixed arguments)
@@ -91,6 +96,9 @@ PINS = [
     lambda: [P.test_per_head_tables_equal_separate_calls(o, k) for o in (0, 2) for k in (0.0, 0.5)],
     P.test_retained_full_mode_is_attention_over_kept_positions,
     P.test_int4_equals_dequantised_fp32,
+    lambda: [P.test_zero_norm_probe_never_passes(k, p) for k, p in ((0, 1), (3, 1), (3, 2))],
+    P.test_widen_f16_every_pattern,
+    P.test_int8_with_subnormal_scales_equals_dequantised_fp32,
 ]
 
 

@@ -299,20 +299,56 @@ def test_invalid_block_and_length_reported_per_row():
     assert np.isfinite(out[0]).all() and (used[0] > 0).all()
 
 
-# ---------------------------------------------------------------- full-size workloads (sampled rows)
+# ---------------------------------------------------------------- full-size workloads (every row)
 
+@pytest.mark.parametrize("mode", ["art", "full"])
 @pytest.mark.parametrize("n", [3, 4, 5])
-def test_full_size_sampled_rows(n):
-    log(f"[parity] generating config {n} at full size")
+def test_full_size_every_row(n, mode):
+    # the headline sizes in the launch configuration bench.py times (library
+    # defaults), every row against the oracle
+    log(f"[parity] generating config {n} at full size ({mode})")
     c = A.config(n)
     dev = to_device(c)
-    rows = [0, c.B - 1]
-    for kw in (dict(), dict(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)):
-        out, used = run_gpu(c, dev, **kw)
-        r = check_parity(c, out, used, rows=rows, **kw)
-        log(f"[parity] config{n} full size {kw}: max_abs={r['max_abs']:.3e} near={r['near']} "
-            f"mean tiles_used (sampled)={np.mean(r['tiles_used']):.1f}")
-        assert (used <= -(-c.ctx_lens[:, None] // c.tile)).all() and (used >= 1).all()
+    kw = dict() if mode == "art" else dict(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
+    out, used = run_gpu(c, dev, **kw)
+    r = check_parity(c, out, used, **kw)
+    log(f"[parity] config{n} full size {mode}: max_abs={r['max_abs']:.3e} near={r['near']} "
+        f"mean tiles_used={np.mean(r['tiles_used']):.1f}")
+    assert (used <= -(-c.ctx_lens[:, None] // c.tile)).all() and (used >= 1).all()
+
+
+# ---------------------------------------------------------------- zero probe and fp16 subnormal scales
+
+@pytest.mark.parametrize("shape", ["fp32 d64 T16", "bf16 d128 T64"])
+@pytest.mark.parametrize("engine", [0, ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD])
+def test_zero_norm_probe_in_art_mode(shape, engine):
+    # the designed case of the oracle pin (probe exactly 0 through tile k - 1,
+    # thresholds no finite metric reaches): a metric against a zero probe is
+    # +inf on the GPU too, so every head stops at tile k + 1 + patience.
+    # fp32 runs the one-tile-at-a-time kernels, bf16 the streamed tile.
+    from tests.test_oracle import zero_probe_case
+    fp32 = shape.startswith("fp32")
+    for k, patience in ((3, 1), (2, 2)):
+        c = zero_probe_case(k, patience, nt=12, T=16 if fp32 else 64, d=64 if fp32 else 128)
+        if not fp32:
+            c = contiguous_case(c.q, c.k, c.v, tile=c.tile, eps_scale=c.eps_scale, eps_dir=c.eps_dir,
+                                patience=patience, kv="bf16", qd="bf16")
+        out, used, _ = _run_and_check(c, f"zero probe k={k} p={patience} {shape} engine {engine}",
+                                      engine=engine)
+        assert (used == k + 1 + patience).all(), used
+
+
+@pytest.mark.parametrize("engine", [0, ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD])
+def test_int8_subnormal_scales(engine):
+    # fp16 scales below 2^-14 (subnormal) widen exactly on both sides
+    c = A.config(5, small=True, seed=6)
+    rng = np.random.default_rng(6)
+    c.k_scale = rng.integers(0x200, 0x400, size=c.k_scale.shape).astype(np.uint16)
+    c.v_scale = rng.integers(1, 0x400, size=c.v_scale.shape).astype(np.uint16)
+    # scores this small give near-uniform weights: thresholds that stop
+    c.eps_scale, c.eps_dir = 1e-2, 1e-3
+    _run_and_check(c, f"config5-small subnormal scales art engine {engine}", engine=engine, v_skip_eps=0.0)
+    _run_and_check(c, "config5-small subnormal scales full", eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
 
 
 # ---------------------------------------------------------------- V skip on bf16 caches
@@ -345,6 +381,12 @@ def test_vskip_predicate_limits(kv, q):
     for kw in (dict(), dict(max_workers=96)):
         out, _, _ = _run_and_check(c, f"{kv}/{q} eps_v 1.0001 {kw}", v_skip_eps=1.0001, **full, **kw)
         assert (out == 0).all()
+        # in ART mode too: every V row left out makes every probe 0, and a
+        # zero probe never passes (reading 14): no head stops
+        out, used, _ = _run_and_check(c, f"{kv}/{q} eps_v 1.0001 art {kw}", v_skip_eps=1.0001,
+                                      eps_scale=1e30, eps_dir=1e30, **kw)
+        assert (out == 0).all()
+        assert (used == -(-c.ctx_lens[:, None] // c.tile)).all()
         _run_and_check(c, f"{kv}/{q} eps_v 1 {kw}", v_skip_eps=1.0, **full, **kw)
         _run_and_check(c, f"{kv}/{q} eps_v 1e-30 art {kw}", v_skip_eps=1e-30, **kw)
         _run_and_check(c, f"{kv}/{q} eps_v 1e-30 full {kw}", v_skip_eps=1e-30, **full, **kw)
