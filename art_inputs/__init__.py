@@ -367,3 +367,26 @@ def config(n: int, seed: int = 0, *, small: bool = False, batch=None, ctx=None,
     kw.update(params)  # a caller's setting (e.g. kv_dtype) overrides the workload's
     return make_case(f"config{n}{'-small' if small else ''}", B=B, Hq=Hq, Hkv=Hkv, d=d,
                      ctx_lens=[n_ctx] * B, seed=seed, **kw)
+
+
+def to_device(case):
+    """The case's arrays as device tensors (torch, cuda:0): bf16 and fp16 bit
+    patterns are reinterpreted, not converted, so the GPU reads the bytes the
+    oracle reads.  Plumbing only: no attention arithmetic."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def t(a, as_f16=False):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            x = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+            x = x.view(torch.float16 if as_f16 else torch.bfloat16)
+        else:
+            x = torch.from_numpy(np.ascontiguousarray(a))
+        return x.to(dev)
+
+    return dict(q=t(case.q), k=t(case.k), v=t(case.v), ctx=t(case.ctx_lens.astype(np.int32)),
+                bt=t(case.block_table), ks=t(case.k_scale, as_f16=True),
+                vs=t(case.v_scale, as_f16=True),
+                perm=t(None if case.tile_perm is None else case.tile_perm.astype(np.int32)))

@@ -63,11 +63,11 @@ def alg_bytes(case, used_g, kv_rows_loaded=None):
     K and V rows of the tiles each group reads (V only where loaded when rows
     are skipped), their int8 scales, the block-table entries of those tiles,
     the queries, the outputs and tiles_used."""
-    e = case.k.dtype.itemsize
     rows = np.minimum(used_g.astype(np.int64) * case.tile, case.ctx_lens[:, None].astype(np.int64))
     k_rows = int(rows.sum())
     v_rows = k_rows if kv_rows_loaded is None else int(kv_rows_loaded)
-    per_row = case.d * e + (2 if case.kv_dtype == "i8" else 0)
+    # bytes of one cache row (an int4 row holds d / 2 bytes) and its fp16 scale
+    per_row = case.k.shape[-1] * case.k.dtype.itemsize + (2 if case.kv_dtype in ("i8", "i4") else 0)
     kv = (k_rows + v_rows) * per_row
     table = 0
     if case.block_size:
@@ -117,7 +117,7 @@ def main():
         return
     import art_inputs as A
     import kv_cache_bandwidth_amd as art
-    from tests.gpu_util import to_device
+    from art_inputs import to_device
 
     log(f"generating workload config {args.config} (seed {args.seed})")
     t0 = time.time()
@@ -289,7 +289,7 @@ def per_head_retention(case, flush_buf, steps=7):
     quarter of the blocks between, drawn per head -- against full attention
     over the same retained tables (median us per call)."""
     import art_inputs as A
-    from tests.gpu_util import to_device
+    from art_inputs import to_device
     log("context timing: per-head retention tables")
     kept = A.retained_tables(case, sink_blocks=4, recent_blocks=512, keep_frac=0.25, seed=1)
     dev = to_device(kept)
@@ -322,7 +322,7 @@ def threshold_sweep(args, steps=5):
     import torch
     import art_inputs as A
     import kv_cache_bandwidth_amd as art
-    from tests.gpu_util import to_device
+    from art_inputs import to_device
     flush_buf = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device="cuda")
     res = {"grid": {"eps_scale": SWEEP_SCALE, "eps_dir": SWEEP_DIR, "patience": SWEEP_PATIENCE},
            "workloads": {}}
@@ -425,7 +425,7 @@ def other_workloads(args, flush_buf, steps=7):
     import torch
     import art_inputs as A
     import kv_cache_bandwidth_amd as art
-    from tests.gpu_util import to_device
+    from art_inputs import to_device
     stream = torch.cuda.current_stream()
     res = {}
     for n in (2, 4, 5, "5i4"):

@@ -43,6 +43,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "art_internal.h"
@@ -3974,6 +3975,56 @@ __global__ __launch_bounds__(64 * kCombineWaves) void art_combine_kernel(Params 
 }
 
 // ------------------------------------------------------------------ launches
+// Compute units of the current device, queried once per device.
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+// Resident work-groups per CU of `kernel` at this block size and dynamic LDS,
+// queried once per (device, kernel, block size, LDS) and kept.
+int resident_per_cu(const void* kernel, hipError_t (*query)(int*, const void*, int, size_t), int block,
+                    size_t lds) {
+    struct Entry {
+        const void* kernel;
+        int dev, block;
+        size_t lds;
+        int value;
+    };
+    static Entry cache[256];
+    static int used = 0;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].kernel == kernel && cache[i].dev == dev && cache[i].block == block && cache[i].lds == lds)
+            return cache[i].value;
+    int v = 0;
+    if (query(&v, kernel, block, lds) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (used < 256) cache[used++] = Entry{kernel, dev, block, lds, v};
+    return v;
+}
+template <class K>
+hipError_t occupancy_of(int* v, const void* kernel, int block, size_t lds) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(v, reinterpret_cast<K>(const_cast<void*>(kernel)), block, lds);
+}
+template <class K>
+int resident(K kernel, int block, size_t lds) {
+    return resident_per_cu(reinterpret_cast<const void*>(kernel), &occupancy_of<K>, block, lds);
+}
+
 // Persistent grid: the deciders first (the lowest work-groups are dispatched
 // first, so they are resident from the start), then the tile workers; without
 // a requested worker count, as many as are resident together with them.
@@ -3982,11 +4033,8 @@ int launch_persistent(const Params& p0, hipStream_t s, K kernel) {
     Params p = p0;
     const size_t lds = (size_t)kWavesPerWG * Tile::lds_floats(p) * sizeof(float);
     if (p.workers == 0) {
-        int dev = 0, cus = 0, per_cu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds);
-        if (e != hipSuccess) return (int)e;
+        const int cus = device_cus(), per_cu = resident(kernel, 256, lds);
+        if (cus <= 0) return (int)hipErrorInvalidDevice;
         const long long resident = (long long)max(per_cu, 1) * cus * kWavesPerWG;
         long long w = resident - p.deciders;
         const long long tiles = (long long)p.NG * p.nt_max;
@@ -3996,6 +4044,17 @@ int launch_persistent(const Params& p0, hipStream_t s, K kernel) {
     }
     hipLaunchKernelGGL(art_init_kernel, dim3(p.NG), dim3(256), 0, s, p);
     const int blocks = (p.deciders + p.workers + kWavesPerWG - 1) / kWavesPerWG;
+    // Deciders wait for workers and workers for deciders: the grid must be
+    // resident as a whole.  A cooperative launch guarantees it where it fits
+    // (the default worker count is sized so that it does); a larger grid
+    // asked for by the caller is launched plainly, its deciders first.
+    {
+        void* args[] = {&p};
+        const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(blocks), dim3(256),
+                                                        args, (unsigned)lds, s);
+        if (e == hipSuccess) return 0;
+        (void)hipGetLastError();
+    }
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), lds, s, p);
     return (int)hipGetLastError();
 }
@@ -4041,11 +4100,9 @@ int launch_team(const Params& p0, hipStream_t s) {
     Params p = p0;
     const size_t lds = team_lds_bytes<S>(p);
     p.helpers = 0;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (!VSKIP && p0.helpers > 0 && p.NG <= kTeamHelpGroups && hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_team_kernel<S, VSKIP>, S::TEAM * 64, lds) == hipSuccess &&
-        per_cu > 0) {
+    int cus = 0, per_cu = 0;
+    if (!VSKIP && p0.helpers > 0 && p.NG <= kTeamHelpGroups && (cus = device_cus()) > 0 &&
+        (per_cu = resident(&art_team_kernel<S, VSKIP>, S::TEAM * 64, lds)) > 0) {
         const long long resident = (long long)per_cu * cus;
         long long h = resident / p.NG - 1;
         if (h > p0.helpers) h = p0.helpers;
@@ -4072,12 +4129,8 @@ template <class S>
 int launch_pool(const Params& p0, hipStream_t s) {
     Params p = p0;
     const size_t lds = pool_lds_bytes<S>(p);
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, art_pool_kernel<S>, PoolShape<S>::WAVES * 64, lds) !=
-            hipSuccess ||
-        per_cu < 1) {
+    const int cus = device_cus(), per_cu = resident(&art_pool_kernel<S>, PoolShape<S>::WAVES * 64, lds);
+    if (cus <= 0 || per_cu < 1) {
         (void)hipGetLastError();
         return 1;
     }
@@ -4092,20 +4145,6 @@ int launch_pool(const Params& p0, hipStream_t s) {
     return 1;
 }
 
-
-// Compute units of the current device, queried once per device.
-int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cached[dev] = cus;
-    }
-    return cached[dev];
-}
 
 constexpr int kXpDefaultWindow = 64;  // tiles past the decided frontier a worker may load, by default
 

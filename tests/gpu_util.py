@@ -6,6 +6,7 @@ import sys
 
 import numpy as np
 
+from art_inputs import to_device  # noqa: F401  (re-exported for the tests)
 from tests import bruteforce as BF
 from tests.helpers import run_oracle
 
@@ -14,26 +15,6 @@ NEAR_REL = 1e-3  # metric within 1e-3 relative of its threshold: the decision ma
 
 def tol_for(case) -> float:
     return 1e-5 if case.kv_dtype == "f32" else 2e-3
-
-
-def to_device(case):
-    import torch
-    dev = torch.device("cuda:0")
-
-    def t(a, as_bf16=False, as_f16=False):
-        if a is None:
-            return None
-        if a.dtype == np.uint16:
-            x = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
-            x = x.view(torch.float16 if as_f16 else torch.bfloat16)
-        else:
-            x = torch.from_numpy(np.ascontiguousarray(a))
-        return x.to(dev)
-
-    return dict(q=t(case.q), k=t(case.k), v=t(case.v), ctx=t(case.ctx_lens.astype(np.int32)),
-                bt=t(case.block_table), ks=t(case.k_scale, as_f16=True),
-                vs=t(case.v_scale, as_f16=True),
-                perm=t(None if case.tile_perm is None else case.tile_perm.astype(np.int32)))
 
 
 def run_gpu(case, dev=None, **kw):
