@@ -131,7 +131,9 @@ typedef struct {
                                         default engine for 64-token tiles only)       */
     int32_t max_workers;         /* 0 = library default; > 0 (engine AUTO or SHARED):
                                     the work-sharing engine with this many waves (at
-                                    most 8 per (row, KV head) group are used)         */
+                                    most 8 per (row, KV head) group are used, and no
+                                    more than fit on the device beside its deciders:
+                                    the launch is cooperative, every wave resident) */
     int32_t team_helpers;        /* team engine (ART, streamed tiles): helper work-groups
                                     per group on other CUs, 0..3; 0 = none (default).
                                     Used only where every work-group of the launch can

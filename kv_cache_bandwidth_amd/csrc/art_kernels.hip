@@ -4032,31 +4032,28 @@ template <class K, class Tile>
 int launch_persistent(const Params& p0, hipStream_t s, K kernel) {
     Params p = p0;
     const size_t lds = (size_t)kWavesPerWG * Tile::lds_floats(p) * sizeof(float);
+    // Deciders wait for workers and workers for deciders (ring space, the V
+    // skip's running maxima): every wave of the grid must be resident at
+    // once, which only a cooperative launch guarantees.  The worker count is
+    // therefore capped at what fits beside the deciders, and the launch is
+    // cooperative or fails.
+    const int cus = device_cus(), per_cu = resident(kernel, 256, lds);
+    if (cus <= 0) return (int)hipErrorInvalidDevice;
+    const long long fit = (long long)per_cu * cus * kWavesPerWG - p.deciders;
+    if (fit < 1) return (int)hipErrorCooperativeLaunchTooLarge;
+    long long w = p.workers > 0 ? p.workers : fit;
+    if (w > fit) w = fit;
     if (p.workers == 0) {
-        const int cus = device_cus(), per_cu = resident(kernel, 256, lds);
-        if (cus <= 0) return (int)hipErrorInvalidDevice;
-        const long long resident = (long long)max(per_cu, 1) * cus * kWavesPerWG;
-        long long w = resident - p.deciders;
         const long long tiles = (long long)p.NG * p.nt_max;
         if (w > tiles) w = tiles;
         if (w > (long long)kMaxWorkersPerGroup * p.NG) w = (long long)kMaxWorkersPerGroup * p.NG;
-        p.workers = (int)max(w, 1LL);
     }
+    p.workers = (int)max(w, 1LL);
     hipLaunchKernelGGL(art_init_kernel, dim3(p.NG), dim3(256), 0, s, p);
     const int blocks = (p.deciders + p.workers + kWavesPerWG - 1) / kWavesPerWG;
-    // Deciders wait for workers and workers for deciders: the grid must be
-    // resident as a whole.  A cooperative launch guarantees it where it fits
-    // (the default worker count is sized so that it does); a larger grid
-    // asked for by the caller is launched plainly, its deciders first.
-    {
-        void* args[] = {&p};
-        const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(blocks), dim3(256),
-                                                        args, (unsigned)lds, s);
-        if (e == hipSuccess) return 0;
-        (void)hipGetLastError();
-    }
-    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), lds, s, p);
-    return (int)hipGetLastError();
+    void* args[] = {&p};
+    return (int)hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(blocks), dim3(256), args,
+                                           (unsigned)lds, s);
 }
 
 template <class K, class Tile>
