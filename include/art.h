@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define ART_ABI_VERSION 7
+#define ART_ABI_VERSION 8
 
 typedef enum {
     ART_OK = 0,
@@ -192,6 +192,32 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
                                 const void* v_cache, const int32_t* block_table,
                                 const int32_t* ctx_lens, int32_t tile, float eps_scale,
                                 float eps_dir, float* out, int32_t* tiles_used, void* stream);
+
+/*
+ * art_decode_attention_noalloc -- art_decode_attention for callers that cannot
+ * allocate device memory (code under stream capture, serving loops or
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors;
+ * desc->workspace and desc->workspace_bytes are ignored: the workspace is a
+ * fixed array of ART_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device it runs on (from the first call there until the process ends).  The
+ * call runs on the current device; `stream` must belong to it.  It allocates
+ * nothing and calls no allocating routine.
+ *
+ * A call whose workspace (art_workspace_bytes for that desc, tile and mode)
+ * exceeds ART_NOALLOC_SCRATCH_BYTES returns ART_E_WORKSPACE before anything is
+ * touched on the device.  Nothing in the array needs to start at zero: each
+ * call initialises the words it reads and stamps the words shared between
+ * its waves with a per-call epoch.  Every call on one device shares that
+ * device's array, so calls that may run at the same time on one device (on
+ * different streams, or from several threads) race and give wrong results:
+ * order them on one stream, or use art_decode_attention with a workspace each.
+ */
+#define ART_NOALLOC_SCRATCH_BYTES (96u << 20)
+
+art_status art_decode_attention_noalloc(const art_desc* desc, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* block_table,
+                                        const int32_t* ctx_lens, int32_t tile, float eps_scale,
+                                        float eps_dir, float* out, int32_t* tiles_used, void* stream);
 
 /* Bytes of workspace a call with this desc and tile needs (0 on an invalid desc). */
 size_t art_workspace_bytes(const art_desc* desc, int32_t tile);

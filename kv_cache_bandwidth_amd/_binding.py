@@ -19,8 +19,8 @@ ORDER_ASCENDING, ORDER_RECENT, ORDER_LIST = 0, 1, 2
 STATUS = {0: "ART_OK", -1: "ART_E_NULL", -2: "ART_E_SHAPE", -3: "ART_E_DTYPE", -4: "ART_E_TILE",
           -5: "ART_E_PARAM", -6: "ART_E_WORKSPACE", -7: "ART_E_HIP"}
 
-EXPORTS = ("art_decode_attention", "art_workspace_bytes", "art_validate", "art_status_string",
-           "art_last_error", "art_abi_version")
+EXPORTS = ("art_decode_attention", "art_decode_attention_noalloc", "art_workspace_bytes", "art_validate",
+           "art_status_string", "art_last_error", "art_abi_version")
 
 
 class ArtError(RuntimeError):
@@ -64,7 +64,7 @@ class ArtDesc(ctypes.Structure):
 _lib = None
 
 
-ABI_VERSION = 7  # art_desc layout this binding marshals (ART_ABI_VERSION in art.h)
+ABI_VERSION = 8  # art_desc layout and entry points this binding marshals (ART_ABI_VERSION in art.h)
 
 
 def load():
@@ -81,6 +81,8 @@ def load():
     lib.art_decode_attention.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_float,
                                          ctypes.c_float, vp, vp, vp]
     lib.art_decode_attention.restype = ctypes.c_int32
+    lib.art_decode_attention_noalloc.argtypes = lib.art_decode_attention.argtypes
+    lib.art_decode_attention_noalloc.restype = ctypes.c_int32
     lib.art_workspace_bytes.argtypes = [P, ctypes.c_int32]
     lib.art_workspace_bytes.restype = ctypes.c_size_t
     lib.art_validate.argtypes = [P, ctypes.c_int32, ctypes.c_float, ctypes.c_float]
@@ -133,7 +135,7 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
                      eps_dir=1e-4, patience=1, v_skip_eps=0.0, k_scale=None, v_scale=None,
                      out=None, tiles_used=None, workspace=None, stats=None, max_workers=0, team_helpers=0,
                      engine=0, tile_order=0, tile_perm=None, per_head_tables=False,
-                     workers_per_cu=0, window=0, stream=None):
+                     workers_per_cu=0, window=0, stream=None, noalloc=False):
     """ART decode attention on device tensors; returns (out fp32, tiles_used int32).
 
     q [B, Hq, d] fp32/bf16; k_cache/v_cache paged [num_blocks, Hkv, bs, d] when
@@ -145,6 +147,9 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
     an int32 device tensor [B, stride], row b listing its tiles in visiting order).
     per_head_tables: ctx_lens [B, Hkv], block_table [B, Hkv, mbps] and tile_perm
     [B, Hkv, stride]: every (row, KV head) has its own sequence.
+    noalloc: call art_decode_attention_noalloc (the library's static workspace;
+    out and tiles_used must then be given, and no workspace): nothing is
+    allocated.
     """
     import torch
     lib = load()
@@ -214,6 +219,19 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, *, block_table=None, tile=64
                      tile_perm_stride=tile_perm.shape[-1] if tile_perm is not None else 0,
                      tile_perm=tile_perm.data_ptr() if tile_perm is not None else 0,
                      per_head_tables=per_head_tables, workers_per_cu=workers_per_cu, window=window)
+    if noalloc:
+        if out is None or tiles_used is None or workspace is not None:
+            raise ValueError("noalloc needs out and tiles_used and takes no workspace")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        with torch.cuda.device(q.device):  # the entry point runs on the current device
+            rc = lib.art_decode_attention_noalloc(ctypes.byref(desc), q.data_ptr(), k_cache.data_ptr(),
+                                                  v_cache.data_ptr(),
+                                                  block_table.data_ptr() if block_table is not None else None,
+                                                  ctx_lens.data_ptr(), tile, eps_scale, eps_dir, out.data_ptr(),
+                                                  tiles_used.data_ptr(), stream)
+        _check(rc)
+        return out, tiles_used
     need = workspace_bytes(desc, tile)
     if need == 0:
         _check(validate(desc, tile, eps_scale, eps_dir))

@@ -23,8 +23,8 @@ HIPCC_FLAGS = [
 
 
 # art_kernels.hip is compiled once per launch part (ART_PART, see the end of
-# that file) so that the parts build in parallel; the objects and art_api.cpp
-# are then linked into the shared library.
+# that file) so that the parts build in parallel; the objects, art_api.cpp and
+# art_scratch.hip are then linked into the shared library.
 PARTS = (0, 1, 2, 3)
 
 
@@ -41,6 +41,8 @@ def build(verbose: bool = False) -> str:
                            os.path.join(CSRC, "art_kernels.hip"), "-o", obj]))
     api = os.path.join(out, "art_api.o")
     jobs.append((api, [hipcc, *flags, *inc, "-c", os.path.join(CSRC, "art_api.cpp"), "-o", api]))
+    scr = os.path.join(out, "art_scratch.o")
+    jobs.append((scr, [hipcc, *flags, *inc, "-c", os.path.join(CSRC, "art_scratch.hip"), "-o", scr]))
     procs = []
     for obj, cmd in jobs:
         if verbose:

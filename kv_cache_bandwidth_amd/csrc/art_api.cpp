@@ -191,6 +191,25 @@ Layout workspace_layout(const Params& p) {
     return L;
 }
 
+art_status set_error(art_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+art_status call_workspace_bytes(const art_desc* desc, int tile, float eps_scale, float eps_dir, size_t* need) {
+    g_last_error.clear();
+    Params p;
+    const art_status s = check(desc, tile, eps_scale, eps_dir, p);
+    if (s != ART_OK) return s;
+    *need = workspace_layout(p).total;
+    return ART_OK;
+}
+
 }  // namespace art
 
 extern "C" {

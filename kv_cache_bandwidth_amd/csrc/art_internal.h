@@ -129,6 +129,13 @@ struct Layout {
 };
 Layout workspace_layout(const Params& p);
 
+// Host side (art_api.cpp): records a printf-style detail for art_last_error()
+// and returns s.
+art_status set_error(art_status s, const char* fmt, ...);
+// Validates a call's desc, tile and thresholds like art_validate (workspace
+// aside) and stores the workspace bytes that exact call needs in *need.
+art_status call_workspace_bytes(const art_desc* desc, int tile, float eps_scale, float eps_dir, size_t* need);
+
 // Kernel launches (art_kernels.hip); return a hipError_t value.
 int launch_art(const Params& p, void* stream);
 int launch_full(const Params& p, void* stream);

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = art.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.art_abi_version() == 7
+    assert lib.art_abi_version() == 8
 
 
 def desc(**kw):
@@ -139,6 +139,27 @@ def test_decode_rejects_before_touching_device():
     rc = lib.art_decode_attention(ctypes.byref(d), None, None, None, None, None, 64, 1e-3, 1e-4,
                                   None, None, None)
     assert rc == -1  # q/k/v/ctx_lens/out/tiles_used missing
+
+
+def test_noalloc_refuses_on_the_host():
+    # art_decode_attention_noalloc checks the call and its workspace size
+    # before it looks up its static array on the device
+    lib = art.load()
+    limit = int(re.search(r"#define ART_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+                .expand(r"\1")) << 20
+    assert limit == 96 << 20
+    assert lib.art_decode_attention_noalloc(None, None, None, None, None, None, 64, 1e-3, 1e-4,
+                                            None, None, None) == -1
+    d = desc(patience=0)
+    assert lib.art_decode_attention_noalloc(ctypes.byref(d), None, None, None, None, None, 64, 1e-3, 1e-4,
+                                            None, None, None) == -5
+    # 64 rows of 64K tokens: more workspace than the array holds, whatever desc.workspace says
+    d = desc(batch=64, num_q_heads=32, num_kv_heads=8, max_blocks_per_seq=4096, num_blocks=1)
+    assert B.workspace_bytes(d, 64) > limit
+    d.workspace, d.workspace_bytes = 1 << 20, 1 << 40
+    assert lib.art_decode_attention_noalloc(ctypes.byref(d), None, None, None, None, None, 64, 1e-3, 1e-4,
+                                            None, None, None) == -6
+    assert b"static scratch holds 100663296" in lib.art_last_error()
 
 
 def test_plain_c_client(tmp_path):
