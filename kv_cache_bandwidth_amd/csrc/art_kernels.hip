@@ -740,7 +740,7 @@ struct Stream {
     static constexpr int KDMA = PAGEB / 1024;    // LDS-direct loads per page
     static constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
     // vector-memory instructions one issue() emits (all unconditional)
-    static constexpr int OPS = UP * (4 + KDMA + (SCALED ? 5 : 0));
+    static constexpr int OPS = UP * (4 + KDMA + (SCALED ? 2 : 0));
     // resident waves per SIMD the register budget is cut for (two when it fits without heavy spills)
     static constexpr int MIN_WAVES = GMAX == 4 ? 2 : 1;
     // waves of a team (one work-group, one CU): as many as are resident on a CU
@@ -750,7 +750,7 @@ struct Stream {
     typedef typename std::conditional<KV == ART_I4, uint32_t,
                                       typename std::conditional<KV == ART_I8, u2, u4>::type>::type vvec;
 
-    static constexpr int LDS_FLOATS = (NB * UP * PAGEB) / 4 + 64 * GMAX;
+    static constexpr int LDS_FLOATS = (NB * UP * PAGEB) / 4;
     __host__ __device__ static size_t lds_floats(const Params&) { return LDS_FLOATS; }
 
     struct TileRef {             // one tile of one group (wave-uniform)
@@ -764,14 +764,14 @@ struct Stream {
     float ksc[NB][UP][4];        // int8: key scale / sqrt(d) of the score rows
     float vsc[NB][UP][4];        // int8: value scale of the P.V rows
     bf16x8 qB[4];
-    float m_run, l_run;
-    float acc[GMAX][8];
-    char* kl;                    // LDS: [2 buffers][UP pages][PAGEB]
-    float* pl;                   // LDS: [64 tokens][GMAX heads] (a unit uses the first 32)
+    float m_run, l_run;          // per head (lane & 15): running max and (this lane's part of the) sum
+    // P.V accumulators in the matrix-core output layout: cacc[j][c] of lane
+    // (n, mb) = (lane & 15, lane >> 4) holds head 4mb + c, head dim 8n + j
+    f4 cacc[8];
+    char* kl;                    // LDS: [NB buffers][UP pages][PAGEB]
 
     __device__ __forceinline__ void init(float* lds_wave) {
         kl = reinterpret_cast<char*>(lds_wave);
-        pl = lds_wave + (NB * UP * PAGEB) / 4;
         reset();
     }
 
@@ -779,9 +779,7 @@ struct Stream {
         m_run = kNegInf;
         l_run = 0.f;
 #pragma unroll
-        for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+        for (int j = 0; j < 8; ++j) cacc[j] = f4{0.f, 0.f, 0.f, 0.f};
     }
 
     __device__ __forceinline__ void load_q(const Params& P, int grp) {
@@ -934,15 +932,22 @@ struct Stream {
             const int p = UP * u + pp;
             const long long pr = ((r.pmask >> p) & 1) ? r.prow[p] : 0;
             const char* vbase = static_cast<const char*>(P.v) + pr * ROWB;
+            // lane (r16, rg) holds rows 4rg .. 4rg + 3 of the page, the tokens
+            // whose scores it computes, head dims 8 r16 .. 8 r16 + 7
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = 4 * v + rg;
+                const int row = 4 * rg + v;
                 vb[BUF][pp][v] = __builtin_nontemporal_load(
                     reinterpret_cast<const vvec*>(vbase + row * ROWB + (ROWB / 16) * r16));
             }
             if constexpr (SCALED) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) vsc[BUF][pp][v] = f16_to_f32(P.vs[pr + 4 * v + rg]);
+                // the value scales of rows 4rg .. 4rg + 3 and the key scales of
+                // the score rows (the same rows): one 8-byte load each
+                const u2 vw = *reinterpret_cast<const u2*>(P.vs + pr + 4 * rg);
+                vsc[BUF][pp][0] = f16_to_f32(vw.x & 0xffff);
+                vsc[BUF][pp][1] = f16_to_f32(vw.x >> 16);
+                vsc[BUF][pp][2] = f16_to_f32(vw.y & 0xffff);
+                vsc[BUF][pp][3] = f16_to_f32(vw.y >> 16);
                 const u2 w = *reinterpret_cast<const u2*>(P.ks + pr + 4 * rg);
                 ksc[BUF][pp][0] = f16_to_f32(w.x & 0xffff) * P.inv_sqrt_d;
                 ksc[BUF][pp][1] = f16_to_f32(w.x >> 16) * P.inv_sqrt_d;
@@ -1049,30 +1054,43 @@ struct Stream {
         const float m_new = fmaxf(m_run, mu);
         const float alpha = m_run == kNegInf ? 0.f : exp_fast(m_run - m_new);
         float lsum = 0.f;
-        wave_lds_sync();  // the previous unit's P.V reads of pl are done
+        float pw[UP][4];
 #pragma unroll
         for (int pp = 0; pp < UP; ++pp)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pr = s[pp][i] != kNegInf ? exp_fast(s[pp][i] - m_new) : 0.f;
-                lsum += pr;
-                if (r16 < GMAX) pl[(16 * pp + 4 * rg + i) * GMAX + r16] = pr;
+                pw[pp][i] = s[pp][i] != kNegInf ? exp_fast(s[pp][i] - m_new) : 0.f;
+                lsum += pw[pp][i];
             }
         l_run = fmaf(alpha, l_run, lsum);
         m_run = m_new;
-        float ah[GMAX];
-#pragma unroll
-        for (int h = 0; h < GMAX; ++h) ah[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
-        wave_lds_sync();
-#pragma unroll
-        for (int h = 0; h < GMAX; ++h)
-            if (h < G)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[h][j] *= ah[h];
+        rescale(alpha);
         // rows outside the sequence hold whatever the fallback rows hold: zero them
         const bool full = ((r.pmask >> (UP * u)) & 3) == 3 && r.t * T + 32 * (u + 1) <= r.n;
-        if (full) pv_accumulate<BUF, false>(P, r, u, 0);
-        else pv_accumulate<BUF, true>(P, r, u, 0);
+        if (full) pv_mfma<BUF, false>(P, r, u, pw);
+        else pv_mfma<BUF, true>(P, r, u, pw);
+    }
+
+    // cacc of head h *= the factor alpha holds in lane h (the heads' running
+    // max rose); skipped when no head's max changed
+    __device__ __forceinline__ void rescale(float alpha) {
+        if (__ballot(alpha != 1.f) == 0ull) return;
+        const int rg = lane_id() >> 4;
+        float ai[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), c));
+            if constexpr (GMAX == 8) {
+                const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 + c));
+                ai[c] = rg == 1 ? a1 : a0;
+            } else {
+                ai[c] = a0;  // lanes of rg > 0 hold no head of the group
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cacc[j][c] *= ai[c];
     }
 
     // The whole tile r (both units loaded) under the V-skip rule: the scores of
@@ -1100,7 +1118,7 @@ struct Stream {
         const float M = chain(mu);
         float lsum = 0.f;
         int skipped = 0;
-        wave_lds_sync();  // the previous tile's P.V reads of pl are done
+        float pw0[UP][4], pw1[UP][4];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -1112,7 +1130,7 @@ struct Stream {
                     const float pr = valid ? exp_fast(sv - mu) : 0.f;
                     const bool keep = valid && sv - M >= P.v_skip_ln;
                     lsum += pr;
-                    if (r16 < GMAX) pl[(32 * u + 16 * pp + 4 * rg + i) * GMAX + r16] = keep ? pr : 0.f;
+                    (u ? pw1 : pw0)[pp][i] = keep ? pr : 0.f;
                 }
         // the statistics' count of left-out pairs, only when the caller asks for it
         if (P.stats) {
@@ -1130,72 +1148,81 @@ struct Stream {
         }
         l_run = lsum;
         m_run = mu;
-        wave_lds_sync();
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const bool full = ((r.pmask >> (UP * u)) & 3) == 3 && r.t * T + 32 * (u + 1) <= r.n;
             if (u == 0) {
-                if (full) pv_accumulate<0, false>(P, r, 0, 0);
-                else pv_accumulate<0, true>(P, r, 0, 0);
+                if (full) pv_mfma<0, false>(P, r, 0, pw0);
+                else pv_mfma<0, true>(P, r, 0, pw0);
             } else {
-                if (full) pv_accumulate<1, false>(P, r, 1, 32);
-                else pv_accumulate<1, true>(P, r, 1, 32);
+                if (full) pv_mfma<1, false>(P, r, 1, pw1);
+                else pv_mfma<1, true>(P, r, 1, pw1);
             }
         }
         return skipped;
     }
 
+    // Element j (head dim 8 r16 + j) of the lane's V rows k and k + 1 of a
+    // unit (k = 4pp + i: token 16pp + 4rg + i) as a bf16 pair, row k low.
+    template <int BUF>
+    __device__ __forceinline__ uint32_t v_pair(int j, int pp, int i) const {
+        if constexpr (KV == ART_I8) {
+            // int8 codes are exact in bf16 (at most 8 significant bits)
+            const u2 a = vb[BUF][pp][i], b = vb[BUF][pp][i + 1];
+            const uint32_t wa = j < 4 ? a.x : a.y, wb = j < 4 ? b.x : b.y;
+            return bf16_pair(sbyte(wa, j & 3), sbyte(wb, j & 3));
+        } else if constexpr (KV == ART_I4) {
+            return bf16_pair(snib(vb[BUF][pp][i], j), snib(vb[BUF][pp][i + 1], j));
+        } else {
+            const u4 a = vb[BUF][pp][i], b = vb[BUF][pp][i + 1];
+            const uint32_t wa = a[j >> 1], wb = b[j >> 1];
+            // v_perm_b32 bytes 0-3 come from the second operand, 4-7 from the first
+            return __builtin_amdgcn_perm(wb, wa, (j & 1) ? 0x07060302u : 0x05040100u);
+        }
+    }
+
+    // P.V of unit u on the matrix cores: C[head][dim] += P[head][token] V[token][dim]
+    // with v_mfma_f32_16x16x32_bf16, K = the unit's 32 tokens (lane group rg
+    // supplies the 8 tokens 16pp + 4rg + i it scored and loaded), M = heads
+    // (rows past the group's heads are zero), N = 16 head dims 8n + j per
+    // instruction (j = 0..7).  The weights pw (lane (r16, rg): head r16, token
+    // 16pp + 4rg + i, times the row's value scale for int8/int4) enter as a
+    // bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi): 16 significant bits),
+    // each against the same V operand.
     template <int BUF, bool MASK>
-    __device__ __forceinline__ void pv_accumulate(const Params& P, const TileRef& r, int u, int pbase) {
+    __device__ __forceinline__ void pv_mfma(const Params& P, const TileRef& r, int u, const float (&pw)[UP][4]) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
-        const int G = P.G;
+        const bool hv = r16 < P.G;
+        bf16x8 ahi, alo;
 #pragma unroll
-        for (int pp = 0; pp < UP; ++pp) {
+        for (int pp = 0; pp < UP; ++pp)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int tok = 16 * pp + 4 * v + rg;
-                bool rv = true;
-                if constexpr (MASK) rv = ((r.pmask >> (UP * u + pp)) & 1) && r.t * T + 32 * u + tok < r.n;
-                float pw[GMAX];
-                const f4 w0 = *reinterpret_cast<const f4*>(pl + (pbase + tok) * GMAX);
-                pw[0] = w0.x; pw[1] = w0.y; pw[2] = w0.z; pw[3] = w0.w;
-                if constexpr (GMAX == 8) {
-                    const f4 w1 = *reinterpret_cast<const f4*>(pl + (pbase + tok) * GMAX + 4);
-                    pw[4] = w1.x; pw[5] = w1.y; pw[6] = w1.z; pw[7] = w1.w;
-                }
-                float vf[8];
-                if constexpr (KV == ART_I8) {
-#pragma unroll
-                    for (int h = 0; h < GMAX; ++h) pw[h] *= vsc[BUF][pp][v];
-                    const u2 w = vb[BUF][pp][v];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        vf[k] = sbyte(w.x, k);
-                        vf[4 + k] = sbyte(w.y, k);
-                    }
-                } else if constexpr (KV == ART_I4) {
-#pragma unroll
-                    for (int h = 0; h < GMAX; ++h) pw[h] *= vsc[BUF][pp][v];
-                    const uint32_t w = vb[BUF][pp][v];
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) vf[k] = snib(w, k);
-                } else {
-                    const u4 w = vb[BUF][pp][v];
-                    vf[0] = bf16lo(w.x); vf[1] = bf16hi(w.x); vf[2] = bf16lo(w.y); vf[3] = bf16hi(w.y);
-                    vf[4] = bf16lo(w.z); vf[5] = bf16hi(w.z); vf[6] = bf16lo(w.w); vf[7] = bf16hi(w.w);
-                }
-                if constexpr (MASK) {
-#pragma unroll
-                    for (int h = 0; h < GMAX; ++h) pw[h] = rv ? pw[h] : 0.f;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) vf[j] = rv ? vf[j] : 0.f;
-                }
-#pragma unroll
-                for (int h = 0; h < GMAX; ++h)
-                    if (h < G)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pw[h], vf[j], acc[h][j]);
+            for (int i = 0; i < 4; ++i) {
+                float w = hv ? pw[pp][i] : 0.f;
+                if constexpr (SCALED) w *= vsc[BUF][pp][i];
+                const __bf16 h = (__bf16)w;
+                ahi[4 * pp + i] = h;
+                alo[4 * pp + i] = (__bf16)(w - (float)h);
             }
+        if constexpr (MASK) {
+            // a row outside the sequence (or of an invalid block) has weight 0;
+            // its V row (a fallback row) must not bring in a NaN or an infinity
+#pragma unroll
+            for (int pp = 0; pp < UP; ++pp)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool rv = ((r.pmask >> (UP * u + pp)) & 1) && r.t * T + 32 * u + 16 * pp + 4 * rg + i < r.n;
+                    if (!rv) vb[BUF][pp][i] = vvec{};
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            u4 bw;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bw[q] = v_pair<BUF>(j, q >> 1, 2 * (q & 1));
+            const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+            cacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, cacc[j], 0, 0, 0);
+            cacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, cacc[j], 0, 0, 0);
         }
     }
 
@@ -1219,26 +1246,17 @@ struct Stream {
             o.mf[hb] = 4 * hb + rg < G ? __shfl(m_run, 4 * hb + rg) : kNegInf;
             o.lf[hb] = 4 * hb + rg < G ? __shfl(lt, 4 * hb + rg) : 0.f;
         }
-        const bool hi2 = rg >> 1, hi1 = rg & 1;
+        // the accumulators: head 4hb + rg, dims 8n + j (n = lane & 15) sit in
+        // component rg of cacc[j] in lane n + 16hb
+        const int n = lane & 15;
 #pragma unroll
-        for (int hb = 0; hb < HBM; ++hb) {
-            // step 1 (lanes l ^ 32): keep heads 4hb + 2*hi2 + {0,1}, send the other pair
-            float keep[2][8];
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float mine_lo = acc[4 * hb + e][j], mine_hi = acc[4 * hb + 2 + e][j];
-                    const float send = hi2 ? mine_lo : mine_hi;
-                    keep[e][j] = (hi2 ? mine_hi : mine_lo) + __shfl_xor(send, 32);
-                }
-            // step 2 (lanes l ^ 16): keep head 4hb + 2*hi2 + hi1
+        for (int hb = 0; hb < HBM; ++hb)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float send = hi1 ? keep[0][j] : keep[1][j];
-                o.a[hb][j] = (hi1 ? keep[1][j] : keep[0][j]) + __shfl_xor(send, 16);
+                const float c0 = __shfl(cacc[j][0], n + 16 * hb), c1 = __shfl(cacc[j][1], n + 16 * hb);
+                const float c2 = __shfl(cacc[j][2], n + 16 * hb), c3 = __shfl(cacc[j][3], n + 16 * hb);
+                o.a[hb][j] = rg == 0 ? c0 : rg == 1 ? c1 : rg == 2 ? c2 : c3;
             }
-        }
         reset();
     }
 };
