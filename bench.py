@@ -29,6 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+# HBM bytes per launch of the dominant kernel, from hardware counters, by workload
+TRAFFIC_FILES = {3: "traffic_art_team_kernel_ctx32k.txt", 5: "traffic_art_team_kernel_vskip_int8_ctx32k.txt"}
 
 
 def log(msg):
@@ -217,9 +219,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(
-                         os.path.join(ROOT, "profiles", "traffic_art_team_kernel_ctx32k.txt"),
+                         os.path.join(ROOT, "profiles", TRAFFIC_FILES[args.config]),
                          os.path.join(ROOT, "kv_cache_bandwidth_amd", "csrc", "art_kernels.hip"))
-                     if args.config == 3 else None,
+                     if args.config in TRAFFIC_FILES else None,
                      "alg_bytes_per_step": int(b_alg)},
         "wall_s_timed_region": round(wall, 4),
     }
@@ -435,11 +437,18 @@ def other_workloads(args, flush_buf, steps=7):
         case = A.config(5, seed=args.seed, kv_dtype="i4") if n == "5i4" else A.config(n, seed=args.seed)
         dev = to_device(case)
 
+        rows_loaded, tiles_loaded = {}, {}
+
         def med(**kw):
             a = dict(block_table=dev["bt"], tile=case.tile, eps_scale=case.eps_scale, eps_dir=case.eps_dir,
                      patience=case.patience, v_skip_eps=case.v_skip_eps, k_scale=dev["ks"], v_scale=dev["vs"])
             a.update(kw)
-            out, used = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], **a)
+            # one counting call first: V rows loaded, for the algorithmic bytes under the V skip
+            stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+            out, used = art.decode_attention(dev["q"], dev["k"], dev["v"], dev["ctx"], stats=stats, **a)
+            torch.cuda.synchronize()
+            rows_loaded[a["v_skip_eps"]] = int(stats[1])
+            tiles_loaded[a["v_skip_eps"]] = int(stats[0])
             ms = []
             for _ in range(steps + 2):
                 flush_buf.fill_(1)
@@ -451,14 +460,30 @@ def other_workloads(args, flush_buf, steps=7):
                 ms.append(e0.elapsed_time(e1))
             return statistics.median(ms[2:]) * 1e3, used.cpu().numpy()
 
+        def roof(us, used_heads, vskip):
+            # algorithmic bytes of the call (its own tiles_used; with the V skip
+            # the V rows it loaded) over its median time, against HBM peak
+            G = case.Hq // case.Hkv
+            used_g = used_heads.reshape(case.B, case.Hkv, G).max(axis=-1)
+            b = alg_bytes(case, used_g, kv_rows_loaded=rows_loaded[vskip] if vskip > 0 else None)
+            gbs = b / (us * 1e-6) / 1e9
+            return {"alg_bytes": int(b), "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
         t_art, used = med()
-        t_full, _ = med(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
+        t_full, used_full = med(eps_scale=0.0, eps_dir=0.0, v_skip_eps=0.0)
         nt = -(-case.ctx_lens // case.tile)
         name = A.WORKLOADS[5].replace("int8", "int4 (two codes per byte)") if n == "5i4" else A.WORKLOADS[n]
         entry = {"workload": name, "art_us": round(t_art, 1), "full_us": round(t_full, 1),
-                 "kv_tiles_skipped_head_level": round(float(1.0 - used.sum() / (nt[:, None] * case.Hq).sum()), 4)}
+                 "kv_tiles_skipped_head_level": round(float(1.0 - used.sum() / (nt[:, None] * case.Hq).sum()), 4),
+                 "art_roofline": roof(t_art, used, case.v_skip_eps),
+                 "full_roofline": roof(t_full, used_full, 0.0)}
         if case.v_skip_eps > 0:
-            entry["art_no_vskip_us"] = round(med(v_skip_eps=0.0)[0], 1)
+            t_nv, used_nv = med(v_skip_eps=0.0)
+            entry["art_no_vskip_us"] = round(t_nv, 1)
+            entry["art_no_vskip_roofline"] = roof(t_nv, used_nv, 0.0)
+            # V rows loaded over the rows of the K tiles loaded, in the V-skip call
+            entry["v_rows_loaded_share"] = round(
+                rows_loaded[case.v_skip_eps] / max(1, tiles_loaded[case.v_skip_eps] * case.tile), 4)
         res[f"workload{n}"] = entry
         del dev
     return res
