@@ -884,36 +884,37 @@ struct Stream {
         resolve_from(P, grp, n, t, blkv, r);
     }
 
-    // resolve() from the block ids fetch_blocks() returned for tile t
+    // resolve() from the block ids fetch_blocks() returned for tile t: lane
+    // p < PAGES works out page p (validity, row index) in one vector pass, and
+    // the results are read back as wave-uniform values
     __device__ __forceinline__ static void resolve_from(const Params& P, int grp, int n, int t, int blkv, TileRef& r) {
-        const int b = grp / P.Hkv, g = grp % P.Hkv;
+        const int lane = lane_id();
+        const int b = grp / P.Hkv, g = grp % P.Hkv, gc = g >> P.kv_shift;
         r.grp = grp;
         if constexpr (ORD == ART_ORDER_LIST)
             r.t = t < (n + T - 1) / T ? __builtin_amdgcn_readlane(blkv, PAGES) : t;
         else
             r.t = phys(P, grp, n, t);
         r.n = n;
-        r.pmask = 0;
-        r.err = !named(r.t);
+        const int tokp = r.t * T + 16 * lane;
+        const bool in = lane < PAGES && named(r.t) && tokp < n;
+        bool ok = in;
+        long long pr;
+        if (P.block_size == 0) {
+            pr = ((long long)b * P.hkv_cache + gc) * P.max_ctx + tokp;
+        } else {
+            ok = in && blkv >= 0 && blkv < P.num_blocks;
+            pr = ((long long)blkv * P.hkv_cache + gc) * P.block_size + (unsigned)tokp % (unsigned)P.block_size;
+        }
+        const uint64_t okm = __ballot(ok), inm = __ballot(in);
+        r.pmask = (int)(okm & ((1u << PAGES) - 1));
+        r.err = !named(r.t) || ((inm & ~okm) & ((1u << PAGES) - 1)) != 0;
+        const int lo = (int)(uint32_t)pr, hi = (int)(pr >> 32);
 #pragma unroll
         for (int p = 0; p < PAGES; ++p) {
-            const int tokp = r.t * T + 16 * p;
-            r.prow[p] = 0;
-            if (named(r.t) && tokp < n) {
-                if (P.block_size == 0) {
-                    r.prow[p] = ((long long)b * P.hkv_cache + (g >> P.kv_shift)) * P.max_ctx + tokp;
-                    r.pmask |= 1 << p;
-                } else {
-                    const int blk = __builtin_amdgcn_readlane(blkv, p);
-                    if (blk < 0 || blk >= P.num_blocks) {
-                        r.err = 1;
-                    } else {
-                        r.prow[p] = ((long long)blk * P.hkv_cache + (g >> P.kv_shift)) * P.block_size +
-                                    (unsigned)tokp % (unsigned)P.block_size;
-                        r.pmask |= 1 << p;
-                    }
-                }
-            }
+            const long long v = ((long long)__builtin_amdgcn_readlane(hi, p) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane(lo, p);
+            r.prow[p] = ((okm >> p) & 1) ? v : 0;
         }
     }
 
@@ -2748,7 +2749,7 @@ size_t team_lds_bytes(const Params& p) {
 
 // ------------------------------------------------------------------ pool kernel (workers shared by the groups)
 constexpr int kPoolAutoGroups = 64;  // library default: the pool for at most this many groups ...
-constexpr int kPoolAutoTiles = 512;  // ... of at least this many tiles
+constexpr int kPoolAutoTiles = 1024;  // ... of at least this many tiles
 //
 // Every CU runs one persistent work-group.  Wave 0 of work-group g < NG
 // decides group g; every other wave is a tile worker that serves whichever
