@@ -5,9 +5,11 @@
  * cache tile by tile with an online softmax, and the traversal stops early
  * once a cheap probe of the running output has stabilised (ART, "Runtime
  * Attention Termination", gist.science technical summary of arXiv
- * 2606.00024, sections 2.1-2.4).  An optional mode skips the V rows whose
- * softmax weight is negligible, before they are loaded or dequantised
- * (puntofijo.es article on skipping V dequantisation in llama.cpp).
+ * 2606.00024, sections 2.1-2.4).  An optional mode leaves out of P.V the V
+ * rows whose softmax weight is negligible (puntofijo.es article on skipping
+ * V dequantisation in llama.cpp); with bf16 caches on the streamed 64-token
+ * tiles (head_dim 128, bf16 queries) a row that no query head of its KV head
+ * keeps is not loaded at all.
  *
  * Every pointer passed to art_decode_attention is device memory allocated and
  * owned by the caller; the library keeps none of them after the call returns,
@@ -113,7 +115,11 @@ typedef struct {
     int32_t max_ctx;             /* contiguous: row stride in tokens (multiple of 16) */
     int32_t patience;            /* >= 1: consecutive passing tiles needed to stop    */
     float v_skip_eps;            /* 0 = off; else skip V row j when exp(s_j - M_t) <
-                                    v_skip_eps, M_t the running max through tile t     */
+                                    v_skip_eps, M_t the running max through tile t
+                                    (its weight still enters the softmax sum).  bf16
+                                    caches, streamed 64-token tiles: rows no head of
+                                    the KV head keeps are not loaded; otherwise they
+                                    are loaded and left out of the arithmetic       */
     const void* k_scale;         /* I8 caches only (device, fp16 bits)                */
     const void* v_scale;
     void* workspace;             /* device scratch, 256-byte aligned, caller-owned    */
@@ -122,7 +128,8 @@ typedef struct {
                                     [0] K tiles loaded (in ART mode a KV head's 5-16
                                     query heads may run as several groups of at most
                                     4, each loading the tiles it needs), [1] V rows
-                                    loaded,
+                                    loaded (under the V skip on bf16 streamed tiles,
+                                    only the rows some head keeps),
                                     [2] reserved (left unchanged; the tiles loaded
                                         past a group's stop are [0] minus the
                                         tiles its heads' tiles_used name),

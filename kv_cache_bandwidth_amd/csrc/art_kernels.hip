@@ -922,7 +922,9 @@ struct Stream {
     // exactly OPS unconditional vector-memory instructions.  Pages outside the
     // sequence (or with an invalid block) read the first rows of the cache
     // instead; consume() masks them.
-    template <int BUF>
+    // WITH_V = false leaves the V rows out (the V skip loads them once the
+    // scores are known: issue_v)
+    template <int BUF, bool WITH_V = true>
     __device__ __forceinline__ void issue(const Params& P, const TileRef& r, int u) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         // keep every load of this unit after the previous unit's LDS reads and
@@ -935,11 +937,13 @@ struct Stream {
             const char* vbase = static_cast<const char*>(P.v) + pr * ROWB;
             // lane (r16, rg) holds rows 4rg .. 4rg + 3 of the page, the tokens
             // whose scores it computes, head dims 8 r16 .. 8 r16 + 7
+            if constexpr (WITH_V) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = 4 * rg + v;
-                vb[BUF][pp][v] = __builtin_nontemporal_load(
-                    reinterpret_cast<const vvec*>(vbase + row * ROWB + (ROWB / 16) * r16));
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 4 * rg + v;
+                    vb[BUF][pp][v] = __builtin_nontemporal_load(
+                        reinterpret_cast<const vvec*>(vbase + row * ROWB + (ROWB / 16) * r16));
+                }
             }
             if constexpr (SCALED) {
                 // the value scales of rows 4rg .. 4rg + 3 and the key scales of
@@ -968,6 +972,28 @@ struct Stream {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // The V rows of unit u that some head keeps: bit v of keep[pp] is this
+    // lane's row 4rg + v of page pp.  A row left out is neither loaded nor
+    // dequantised; its registers read as zero.
+    template <int BUF>
+    __device__ __forceinline__ void issue_v(const Params& P, const TileRef& r, int u, const unsigned (&keep)[UP]) {
+        const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+#pragma unroll
+        for (int pp = 0; pp < UP; ++pp) {
+            const int p = UP * u + pp;
+            const long long pr = ((r.pmask >> p) & 1) ? r.prow[p] : 0;
+            const char* vbase = static_cast<const char*>(P.v) + pr * ROWB;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                vvec x{};
+                if ((keep[pp] >> v) & 1)
+                    x = __builtin_nontemporal_load(
+                        reinterpret_cast<const vvec*>(vbase + (4 * rg + v) * ROWB + (ROWB / 16) * r16));
+                vb[BUF][pp][v] = x;
+            }
+        }
     }
 
     template <int N>
@@ -1094,32 +1120,35 @@ struct Stream {
             for (int c = 0; c < 4; ++c) cacc[j][c] *= ai[c];
     }
 
-    // The whole tile r (both units loaded) under the V-skip rule: the scores of
-    // both units give the tile max m; chain(m) returns M, the running max
-    // through this tile, for the lane's head (lane & 15); a row j of head h
-    // enters P.V only when exp(s_hj - M_h) >= v_skip_eps (tested as
-    // s_hj - M_h >= ln v_skip_eps, no exponential), while its weight
-    // exp(s_hj - m_h) always enters l.  The tile becomes the running state
-    // (the state is empty before: a tile at a time).  Returns the number of
-    // (head, row) pairs left out when the call collects statistics (P.stats),
-    // else 0: the count costs ~5 % of the step.
-    template <class Chain>
-    __device__ __forceinline__ int consume_tile_vskip(const Params& P, const TileRef& r, Chain&& chain) {
+    // The whole tile r under the V-skip rule, its K (both units) loaded and
+    // its V not yet: the scores of both units give the tile max m; chain(m)
+    // returns M, the running max through this tile, for the lane's head (lane
+    // & 15); a row j of head h enters P.V only when exp(s_hj - M_h) >= v_skip_eps
+    // (tested as s_hj - M_h >= ln v_skip_eps, no exponential), while its weight
+    // exp(s_hj - m_h) always enters l.  Only the V rows some head of the group
+    // keeps are then loaded (row by row, and a unit with none is not
+    // multiplied), and the tile becomes the running state (the state is empty
+    // before: a tile at a time).  vrows receives the V rows loaded.  Without
+    // DEFER the tile's V rows came with its K and are only masked (vrows 0:
+    // counted at issue).  Returns the number of (head, row) pairs left out
+    // when the call collects statistics (P.stats), else 0.
+    template <bool DEFER, class Chain>
+    __device__ __forceinline__ int consume_tile_vskip(const Params& P, const TileRef& r, Chain&& chain,
+                                                      unsigned& vrows) {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
-        const int G = P.G;
+        const int hin = heads_in(P, r.grp);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<OPS>();
+        wait_vm<0>();  // the tile's K and scales (and the next block ids)
         __builtin_amdgcn_sched_barrier(0);
         float s0[UP][4], s1[UP][4];
         float mu = scores<0>(P, r, 0, s0);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<0>();
-        __builtin_amdgcn_sched_barrier(0);
         mu = fmaxf(mu, scores<1>(P, r, 1, s1));
         const float M = chain(mu);
         float lsum = 0.f;
         int skipped = 0;
         float pw0[UP][4], pw1[UP][4];
+        unsigned keep0[UP] = {}, keep1[UP] = {};
+        unsigned rows0 = 0, rows1 = 0;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -1132,10 +1161,21 @@ struct Stream {
                     const bool keep = valid && sv - M >= P.v_skip_ln;
                     lsum += pr;
                     (u ? pw1 : pw0)[pp][i] = keep ? pr : 0.f;
+                    // row 16pp + 4rg' + i of the unit is loaded when a head of
+                    // lane group rg' keeps it
+                    const unsigned long long b = __ballot(keep && r16 < hin);
+                    const bool rowk = ((b >> (16 * rg)) & 0xffffull) != 0ull;
+                    (u ? keep1 : keep0)[pp] |= (unsigned)rowk << i;
+                    const unsigned nk = ((b & 0xffffull) != 0) + (((b >> 16) & 0xffffull) != 0) +
+                                        (((b >> 32) & 0xffffull) != 0) + ((b >> 48) != 0);
+                    (u ? rows1 : rows0) += nk;
                 }
+        if constexpr (DEFER) {
+            issue_v<0>(P, r, 0, keep0);
+            issue_v<1>(P, r, 1, keep1);
+        }
         // the statistics' count of left-out pairs, only when the caller asks for it
         if (P.stats) {
-            const bool hin = r16 < heads_in(P, r.grp);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -1143,23 +1183,29 @@ struct Stream {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float sv = u ? s1[pp][i] : s0[pp][i];
-                        skipped += (hin && sv != kNegInf && !(sv - M >= P.v_skip_ln)) ? 1 : 0;
+                        skipped += (r16 < hin && sv != kNegInf && !(sv - M >= P.v_skip_ln)) ? 1 : 0;
                     }
             skipped = wave_sum_int(skipped);
         }
         l_run = lsum;
         m_run = mu;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const bool full = ((r.pmask >> (UP * u)) & 3) == 3 && r.t * T + 32 * (u + 1) <= r.n;
-            if (u == 0) {
-                if (full) pv_mfma<0, false>(P, r, 0, pw0);
-                else pv_mfma<0, true>(P, r, 0, pw0);
-            } else {
-                if (full) pv_mfma<1, false>(P, r, 1, pw1);
-                else pv_mfma<1, true>(P, r, 1, pw1);
-            }
+        if constexpr (!DEFER) {
+            // every row came in: those outside the sequence hold fallback rows
+            vrows = 0;
+            const bool full0 = (r.pmask & 3) == 3 && r.t * T + 32 <= r.n;
+            const bool full1 = ((r.pmask >> UP) & 3) == 3 && r.t * T + 64 <= r.n;
+            if (full0) pv_mfma<0, false>(P, r, 0, pw0);
+            else pv_mfma<0, true>(P, r, 0, pw0);
+            if (full1) pv_mfma<1, false>(P, r, 1, pw1);
+            else pv_mfma<1, true>(P, r, 1, pw1);
+            return skipped;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<0>();  // the kept V rows
+        __builtin_amdgcn_sched_barrier(0);
+        if (rows0) pv_mfma<0, false>(P, r, 0, pw0);
+        if (rows1) pv_mfma<1, false>(P, r, 1, pw1);
+        vrows = rows0 + rows1;
         return skipped;
     }
 
@@ -2148,7 +2194,7 @@ __device__ __forceinline__ void team_helper_worker(const Params& P, int grp, int
 
 // A primary worker: tiles first, first + W, ... of the group, each handed
 // over whole to the decider through the LDS slots.
-template <class S, bool VSKIP>
+template <class S, int VSKIP>
 __device__ __forceinline__ void team_primary_worker(const Params& P, int grp, int n, int nt, int first,
                                                     const TeamPlan& plan, S& st, TeamShared<S::HBM>* sh) {
     constexpr int HBM = S::HBM;
@@ -2161,11 +2207,14 @@ __device__ __forceinline__ void team_primary_worker(const Params& P, int grp, in
     typename S::TileRef C;
     st.load_q(P, grp);  // before the tile's loads: consume() counts those in issue order
     S::resolve(P, grp, t, C);
-    st.template issue<0>(P, C, 0);
-    st.template issue<1>(P, C, 1);
+    // (VSKIP 2, the V skip with V loaded late: K only, a tile's V rows are
+    // loaded once its scores are known)
+    st.template issue<0, VSKIP != 2>(P, C, 0);
+    st.template issue<1, VSKIP != 2>(P, C, 1);
     int blkN = S::fetch_blocks(P, grp, n, plan.nextA(t));  // block ids of the next tile
-    // tiles (and rows) loaded, counted when their loads are issued
-    unsigned long long loaded = 1, rows = S::rows_in(C), skipped = 0;
+    // tiles (and rows) loaded, counted when their loads are issued (V rows
+    // under the V skip: when consumed)
+    unsigned long long loaded = 1, rows = VSKIP == 2 ? 0 : S::rows_in(C), skipped = 0;
     for (;;) {
         if constexpr (VSKIP) {
             // the running max through tile t: that through tile t - 1 (from its
@@ -2189,7 +2238,9 @@ __device__ __forceinline__ void team_primary_worker(const Params& P, int grp, in
                 if (lane == 0) lds_st(&sh->ptag[sn], t + 1);
                 return M;
             };
-            skipped += (unsigned)st.consume_tile_vskip(P, C, chain);
+            unsigned vr = 0;
+            skipped += (unsigned)st.template consume_tile_vskip<VSKIP == 2>(P, C, chain, vr);
+            rows += vr;
         } else {
             st.template consume<0>(P, C, 0, true);
             st.template consume<1>(P, C, 1, false);
@@ -2204,11 +2255,11 @@ __device__ __forceinline__ void team_primary_worker(const Params& P, int grp, in
         const int cerr = C.err;
         if (haveN) {
             S::resolve_from(P, grp, n, tn, blkN, C);
-            st.template issue<0>(P, C, 0);
-            st.template issue<1>(P, C, 1);
+            st.template issue<0, VSKIP != 2>(P, C, 0);
+            st.template issue<1, VSKIP != 2>(P, C, 1);
             blkN = S::fetch_blocks(P, grp, n, plan.nextA(tn));
             ++loaded;
-            rows += S::rows_in(C);
+            if constexpr (VSKIP != 2) rows += S::rows_in(C);
         }
         // the slot must have been released (the decider releases no further
         // slot once the group is done: then the tile is past the bound)
@@ -2667,7 +2718,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
 
 // Grid: NG primaries, then P.helpers rounds of NG helpers (helper r of group
 // g is work-group (1 + r) * NG + g).
-template <class S, bool VSKIP>
+template <class S, int VSKIP>
 __global__ __launch_bounds__(S::TEAM * 64) void art_team_kernel(Params P) {
     extern __shared__ float lds[];
     constexpr int HBM = S::HBM, TEAM = S::TEAM;
@@ -4111,7 +4162,7 @@ int run_tile(const Params& p, hipStream_t s, bool art) {
 // Helpers (as many as requested, up to what fits) only where every
 // work-group of the grid can be resident at once (cooperative launch); else
 // the primaries alone.
-template <class S, bool VSKIP>
+template <class S, int VSKIP>
 int launch_team(const Params& p0, hipStream_t s) {
     Params p = p0;
     const size_t lds = team_lds_bytes<S>(p);
@@ -4209,14 +4260,19 @@ int run_stream(const Params& p, hipStream_t s, bool art) {
     }
     if (!art) return launch_split<decltype(&art_full_stream_kernel<S>), S>(p, s, &art_full_stream_kernel<S>);
     if (sharing(p)) return launch_persistent<decltype(&art_stream_kernel<S>), S>(p, s, &art_stream_kernel<S>);
-    if (p.vskip) return launch_team<S, true>(p, s);
+    // The V skip on bf16 caches: a tile's V rows are loaded after its scores,
+    // only those some head keeps.  On int8 and int4 caches the tile is bound
+    // by its arithmetic rather than its loads, the second round trip costs
+    // more than the rows left out save, and the V rows come with the tile's
+    // K (the skip leaves out their share of P.V).
+    if (p.vskip) return S::KVT == ART_BF16 ? launch_team<S, 2>(p, s) : launch_team<S, 1>(p, s);
     if (p.engine == ART_ENGINE_XCD && launch_xp<S>(p, s) == 0) return 0;
     // by default the pool serves few, long groups (where one CU per group
     // would leave most of the chip idle)
     const bool pool = p.engine == ART_ENGINE_POOL ||
                       (p.engine == ART_ENGINE_AUTO && p.NG <= kPoolAutoGroups && p.nt_max >= kPoolAutoTiles);
     if (pool && launch_pool<S>(p, s) == 0) return 0;
-    return launch_team<S, false>(p, s);
+    return launch_team<S, 0>(p, s);
 }
 
 template <int KV, int GMAX>

@@ -413,19 +413,54 @@ def _host_skipped_pairs(c, eps):
     return count, near
 
 
+def _host_vskip_rows(c, eps):
+    """V rows some query head of their KV head keeps (s - M_t >= ln eps for
+    at least one head, ascending order, float64), the rows whose keep
+    decision lies within 1e-3 of the threshold, and all rows."""
+    from tests import bruteforce as BF
+    G = c.Hq // c.Hkv
+    ln = np.log(eps)
+    kept = near = total = 0
+    for b in range(c.B):
+        n = int(c.ctx_lens[b])
+        for g in range(c.Hkv):
+            K = BF.logical_rows(c, "k", b, g, n)
+            best = np.full(n, -np.inf)
+            for h in range(g * G, (g + 1) * G):
+                sc = K @ BF.query(c, b, h) / np.sqrt(c.d)
+                M = np.maximum.accumulate(np.array([sc[:t0 + c.tile].max() for t0 in range(0, n, c.tile)]))
+                x = sc - np.repeat(M, c.tile)[:n] - ln
+                best = np.maximum(best, x)
+            kept += int((best >= 0).sum())
+            near += int((np.abs(best) < 1e-3).sum())
+            total += n
+    return kept, near, total
+
+
 @pytest.mark.parametrize("n", [3, 5])
 def test_vskip_pair_count(n):
     # stats[3], the (head, row) pairs left out of P.V (counted by the default
-    # engine): exact in full mode, where every tile is consumed once
+    # engine): exact in full mode, where every tile is consumed once; stats[1],
+    # the V rows loaded: on a bf16 cache only those some head of the group
+    # keeps, so at eps_v = 1e-4 below the rows of the tiles read; on an int8
+    # cache every row (the skip leaves out their arithmetic only)
     import torch
     c = A.config(n, small=True, v_skip_eps=1e-4)
     want, near = _host_skipped_pairs(c, 1e-4)
     assert want > 0
+    rows_kept, rows_near, rows_all = _host_vskip_rows(c, 1e-4)
     stats = torch.zeros(4, dtype=torch.int64, device="cuda")
     _run_and_check(c, f"config{n} full+vskip count", eps_scale=0.0, eps_dir=0.0, stats=stats)
     got = int(stats[3].item())
     log(f"[parity] config{n} skipped pairs: gpu {got} host {want} (near threshold {near})")
     assert abs(got - want) <= near, (got, want, near)
+    got_rows = int(stats[1].item())
+    log(f"[parity] config{n} V rows loaded: gpu {got_rows} host {rows_kept} of {rows_all} (near {rows_near})")
+    if c.kv_dtype == "bf16":
+        assert abs(got_rows - rows_kept) <= rows_near, (got_rows, rows_kept, rows_near)
+        assert got_rows < rows_all
+    else:
+        assert got_rows == rows_all, (got_rows, rows_all)
 
 
 @pytest.mark.parametrize("kv,q", [("bf16", "bf16"), ("i8", "bf16"), ("i4", "bf16"), ("f32", "f32")])
