@@ -67,7 +67,9 @@ def alg_bytes(case, used_g, kv_rows_loaded=None):
     the queries, the outputs and tiles_used."""
     rows = np.minimum(used_g.astype(np.int64) * case.tile, case.ctx_lens[:, None].astype(np.int64))
     k_rows = int(rows.sum())
-    v_rows = k_rows if kv_rows_loaded is None else int(kv_rows_loaded)
+    # under the V skip the V rows loaded, capped at those of the needed tiles
+    # (rows of tiles loaded past a stop are not the method's)
+    v_rows = k_rows if kv_rows_loaded is None else min(int(kv_rows_loaded), k_rows)
     # bytes of one cache row (an int4 row holds d / 2 bytes) and its fp16 scale
     per_row = case.k.shape[-1] * case.k.dtype.itemsize + (2 if case.kv_dtype in ("i8", "i4") else 0)
     kv = (k_rows + v_rows) * per_row
@@ -160,9 +162,12 @@ def main():
         return ms, wall, out, used
 
     def _desc(eps):
+        # sizes only: the scale pointers just have to be non-null (nothing is read)
+        scaled = case.kv_dtype in ("i8", "i4")
         return art.make_desc(batch=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
                              head_dim=case.d, q_dtype=1 if case.q_dtype == "bf16" else 0,
-                             kv_dtype={"f32": 0, "bf16": 1, "i8": 2}[case.kv_dtype],
+                             kv_dtype={"f32": 0, "bf16": 1, "i8": 2, "i4": 3}[case.kv_dtype],
+                             k_scale=1 if scaled else 0, v_scale=1 if scaled else 0,
                              block_size=case.block_size,
                              max_blocks_per_seq=case.block_table.shape[1] if case.block_size else 0,
                              num_blocks=case.num_blocks,
