@@ -60,11 +60,16 @@ typedef enum {
                                V skip (falls back to TEAM) and at most one group per
                                resident work-group                                     */
     ART_ENGINE_SHARED = 3,  /* work-sharing engine: max_workers waves claim tiles      */
-    ART_ENGINE_XCD = 4      /* one work-group per CU; every (row, KV head) group served
+    ART_ENGINE_XCD = 4,     /* one work-group per CU; every (row, KV head) group served
                                by waves of one XCD (chiplet), which move to the groups
                                of that XCD with work left; deciders on CUs that load
                                no tiles; no V skip (falls back to TEAM); at most 512
                                groups                                                  */
+    ART_ENGINE_PAIR = 5     /* two CUs per group on one XCD: one loads K and computes
+                               the scores, the other loads V, folds and decides; at
+                               most 4 query heads per group, no V skip, the number
+                               of groups a multiple of 8 and at most half the CUs
+                               (else TEAM)                                             */
 } art_engine;
 
 /* Order in which a row's tiles are visited (ART summary, section 2.4: the tile

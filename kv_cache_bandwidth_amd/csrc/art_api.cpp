@@ -79,8 +79,8 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     if (d->max_workers < 0) return fail(ART_E_PARAM, "max_workers %d < 0", d->max_workers);
     if (d->team_helpers < 0 || d->team_helpers > art::kMaxHelpers)
         return fail(ART_E_PARAM, "team_helpers %d not in 0..%d", d->team_helpers, art::kMaxHelpers);
-    if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_XCD)
-        return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_XCD);
+    if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_PAIR)
+        return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_PAIR);
     if (d->workers_per_cu < 0) return fail(ART_E_PARAM, "workers_per_cu %d < 0", d->workers_per_cu);
     if (d->window < 0 || d->window > art::kXpMaxWindow)
         return fail(ART_E_PARAM, "window %d not in 0..%d", d->window, art::kXpMaxWindow);

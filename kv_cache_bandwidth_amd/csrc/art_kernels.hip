@@ -974,6 +974,64 @@ struct Stream {
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // V rows (all four of the lane's rows per page) and, for int8/int4, their
+    // value scales: UP * (4 + SCALED) instructions.  K is not loaded (the
+    // scores come from elsewhere: consume_given).
+    template <int BUF>
+    __device__ __forceinline__ void issue_vs(const Params& P, const TileRef& r, int u) {
+        const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pp = 0; pp < UP; ++pp) {
+            const int p = UP * u + pp;
+            const long long pr = ((r.pmask >> p) & 1) ? r.prow[p] : 0;
+            const char* vbase = static_cast<const char*>(P.v) + pr * ROWB;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                vb[BUF][pp][v] = __builtin_nontemporal_load(
+                    reinterpret_cast<const vvec*>(vbase + (4 * rg + v) * ROWB + (ROWB / 16) * r16));
+            if constexpr (SCALED) {
+                const u2 vw = *reinterpret_cast<const u2*>(P.vs + pr + 4 * rg);
+                vsc[BUF][pp][0] = f16_to_f32(vw.x & 0xffff);
+                vsc[BUF][pp][1] = f16_to_f32(vw.x >> 16);
+                vsc[BUF][pp][2] = f16_to_f32(vw.y & 0xffff);
+                vsc[BUF][pp][3] = f16_to_f32(vw.y >> 16);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Fold unit u into the running state from its scores s (the layout
+    // scores() returns: token 16pp + 4(lane>>4) + i, head lane & 15, -inf
+    // outside the sequence), its V already loaded and landed.
+    template <int BUF>
+    __device__ __forceinline__ void consume_given(const Params& P, const TileRef& r, int u, const float (&s)[UP][4]) {
+        float mu = kNegInf;
+#pragma unroll
+        for (int pp = 0; pp < UP; ++pp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mu = fmaxf(mu, s[pp][i]);
+        mu = fmaxf(mu, __shfl_xor(mu, 16));
+        mu = fmaxf(mu, __shfl_xor(mu, 32));
+        const float m_new = fmaxf(m_run, mu);
+        const float alpha = m_run == kNegInf ? 0.f : exp_fast(m_run - m_new);
+        float lsum = 0.f;
+        float pw[UP][4];
+#pragma unroll
+        for (int pp = 0; pp < UP; ++pp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pw[pp][i] = s[pp][i] != kNegInf ? exp_fast(s[pp][i] - m_new) : 0.f;
+                lsum += pw[pp][i];
+            }
+        l_run = fmaf(alpha, l_run, lsum);
+        m_run = m_new;
+        rescale(alpha);
+        const bool full = ((r.pmask >> (UP * u)) & 3) == 3 && r.t * T + 32 * (u + 1) <= r.n;
+        if (full) pv_mfma<BUF, false>(P, r, u, pw);
+        else pv_mfma<BUF, true>(P, r, u, pw);
+    }
+
     // The V rows of unit u that some head keeps: bit v of keep[pp] is this
     // lane's row 4rg + v of page pp.  A row left out is neither loaded nor
     // dequantised; its registers read as zero.
@@ -2537,11 +2595,12 @@ __device__ __forceinline__ int present_prefix(bool have, int kmax) {
 template <int HBM, bool HELPERS>
 __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, const TeamPlan& plan,
                                              TeamShared<HBM>* sh, ProbeState<HBM>& D, Part<HBM>& acc,
-                                             Part<HBM>& accH) {
+                                             Part<HBM>& accH, bool publish = false) {
     const int lane = lane_id(), i = lane & 15;
     const FoldLanes fl(P);
     const TeamGlobal tg(P, grp);
     const bool glb = plan.nH > 0;
+    const bool pub = glb || publish;  // progress and bound go to global memory (helpers, score workers)
     D.init(fl, heads_in(P, grp));
     acc.clear();
     accH.clear();
@@ -2686,12 +2745,12 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
                 }
                 kdone = kk;
                 finished = D.finished();
-                if (glb && lane == 0) cst(tg.ctl + 2, stamp(P.epoch, (unsigned)(f0 + kdone)));  // progress, for helpers
+                if (pub && lane == 0) cst(tg.ctl + 2, stamp(P.epoch, (unsigned)(f0 + kdone)));  // progress, for helpers
                 if (finished) {
                     const int ug = D.bound();
                     if (lane == 0) {
                         lds_st(&sh->bound, ug);
-                        if (glb) cst(tg.ctl + 1, stamp(P.epoch, (unsigned)ug));
+                        if (pub) cst(tg.ctl + 1, stamp(P.epoch, (unsigned)ug));
                     }
                     break;
                 }
@@ -2711,7 +2770,7 @@ __device__ __forceinline__ void team_decider(const Params& P, int grp, int nt, c
         for (int hb = 0; hb < HBM; ++hb) D.U[hb] = D.hv[hb] ? -1 : 0;
         if (lane == 0) {
             lds_st(&sh->bound, 0);
-            if (glb) cst(tg.ctl + 1, stamp(P.epoch, 0u));
+            if (pub) cst(tg.ctl + 1, stamp(P.epoch, 0u));
         }
     }
 }
@@ -2796,6 +2855,360 @@ size_t team_lds_bytes(const Params& p) {
         (size_t)(S::TEAM - 1) * S::lds_floats(p) * sizeof(float) + sizeof(TeamShared<S::HBM>);
     const size_t helper = (size_t)S::TEAM * S::lds_floats(p) * sizeof(float);
     return primary > helper ? primary : helper;
+}
+
+// ------------------------------------------------------------------ pair kernel (K and V of a group on two CUs)
+//
+// A CU's vector-memory pipeline, not HBM, bounds the team kernel: one group
+// streams ~45 GB/s on one CU whether its tiles come from HBM or from cache,
+// and a tile's 32 one-KB load instructions take most of a worker's cycle.
+// The pair kernel gives every group two CUs of one XCD: a score work-group
+// loads the K rows (into registers), computes the scores with the matrix
+// cores and publishes them per tile (1 KB: 4 heads x 64 tokens); the primary
+// work-group loads only the V rows, takes each tile's scores, does the online
+// softmax and P.V, and decides as the team kernel does (same decider, same
+// LDS slots, same results).  The score workers keep within kPairWindow tiles
+// of the decided frontier (the primary's workers run at most kTeamSlots + 7
+// tiles ahead of it) and stop at the bound.  A record slot is reused kPairRing
+// tiles later, when its tile is decided (kPairRing >= kPairWindow).
+constexpr int kPairRing = 32;    // score records per group (a power of two)
+constexpr int kPairWindow = 24;  // score workers stay below decided + kPairWindow
+constexpr size_t kPairMinLds = 96 * 1024;  // one work-group per CU: the two roles never share a CU
+
+// Scalar load that bypasses the scalar cache (coherent with other CUs' stores).
+__device__ __forceinline__ unsigned long long sload_glc(const unsigned long long* p) {
+    unsigned long long v;
+    asm volatile("s_load_dwordx2 %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
+struct PairRing {
+    unsigned long long* flag;  // [kPairRing]: stamp(epoch, t + 1) once slot t % kPairRing holds tile t
+    float* rec;                // [kPairRing][256]: lane (h, g) of the primary reads [16 (4g + h) .. +16)
+    __device__ PairRing(const Params& P, int grp) {
+        unsigned long long* base = P.team_ring + (long long)grp * group_words(P.G);
+        flag = base;
+        rec = reinterpret_cast<float*>(base + kPairRing);
+    }
+};
+
+// Score worker: tiles first, first + step, ... of the group.  K rows go to
+// registers in the matrix-core operand layout (lane (r, g): row r of a page,
+// head dims 32 st + 8 g .. + 7), one v_mfma_f32_16x16x32_bf16 per 32 dims.
+template <class S>
+__device__ __forceinline__ void pair_score_worker(const Params& P, int grp, int n, int nt, int first, int step,
+                                                  S& st) {
+    constexpr int KV = S::KVT, ROWB = S::ROWB, T = S::T, PAGES = S::PAGES;
+    // vector-memory instructions of one tile's K loads (rows, then scales)
+    constexpr int NK = PAGES * 4 + (S::SCALED ? PAGES : 0);
+    const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+    const TeamGlobal tg(P, grp);
+    const PairRing ring(P, grp);
+    int t = first;
+    if (t >= nt) return;
+    st.load_q(P, grp);
+    int dec = 0, bnd = nt;
+    unsigned long long ktiles = 0;  // K tiles loaded (stats[0])
+    typedef typename std::conditional<KV == ART_I4, uint32_t, typename std::conditional<KV == ART_I8, u2, u4>::type>::type kvec;
+    kvec kr[PAGES][4];
+    float ksc[PAGES][4];
+    typename S::TileRef C;
+    // the K rows (registers, matrix-core operand layout) and scales of tile r: NK instructions
+    auto issue_k = [&](const typename S::TileRef& r) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p) {
+            const long long pr = ((r.pmask >> p) & 1) ? r.prow[p] : 0;
+            const char* kb = static_cast<const char*>(P.k) + pr * ROWB + r16 * ROWB;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (KV == ART_I8) kr[p][q] = __builtin_nontemporal_load(reinterpret_cast<const u2*>(kb + 32 * q + 8 * rg));
+                else if constexpr (KV == ART_I4) kr[p][q] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 16 * q + 4 * rg));
+                else kr[p][q] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(kb + 16 * (4 * q + rg)));
+            }
+            if constexpr (S::SCALED) {
+                const u2 w = *reinterpret_cast<const u2*>(P.ks + pr + 4 * rg);
+                ksc[p][0] = f16_to_f32(w.x & 0xffff) * P.inv_sqrt_d;
+                ksc[p][1] = f16_to_f32(w.x >> 16) * P.inv_sqrt_d;
+                ksc[p][2] = f16_to_f32(w.y & 0xffff) * P.inv_sqrt_d;
+                ksc[p][3] = f16_to_f32(w.y >> 16) * P.inv_sqrt_d;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto flag = [&](int tt) {
+        if (lane == 0) cst(ring.flag + (tt & (kPairRing - 1)), stamp(P.epoch, (unsigned)(tt + 1)));
+    };
+    S::resolve(P, grp, t, C);
+    int blkN = t + step < nt ? S::fetch_blocks(P, grp, n, t + step) : 0;
+    issue_k(C);
+    for (;;) {
+        // scores of tile t (waits for its K)
+        float sc[PAGES][4];
+#pragma unroll
+        for (int p = 0; p < PAGES; ++p) {
+            f4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x8 a;
+                if constexpr (KV == ART_I8) {
+                    const u2 w = kr[p][q];
+                    u4 cv;
+                    cv.x = bf16_pair(sbyte(w.x, 0), sbyte(w.x, 1));
+                    cv.y = bf16_pair(sbyte(w.x, 2), sbyte(w.x, 3));
+                    cv.z = bf16_pair(sbyte(w.y, 0), sbyte(w.y, 1));
+                    cv.w = bf16_pair(sbyte(w.y, 2), sbyte(w.y, 3));
+                    a = __builtin_bit_cast(bf16x8, cv);
+                } else if constexpr (KV == ART_I4) {
+                    const uint32_t w = kr[p][q];
+                    u4 cv;
+                    cv.x = bf16_pair(snib(w, 0), snib(w, 1));
+                    cv.y = bf16_pair(snib(w, 2), snib(w, 3));
+                    cv.z = bf16_pair(snib(w, 4), snib(w, 5));
+                    cv.w = bf16_pair(snib(w, 6), snib(w, 7));
+                    a = __builtin_bit_cast(bf16x8, cv);
+                } else {
+                    a = __builtin_bit_cast(bf16x8, kr[p][q]);
+                }
+                a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.qB[q], a4, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = ((C.pmask >> p) & 1) && C.t * T + 16 * p + 4 * rg + i < C.n;
+                const float k = S::SCALED ? ksc[p][i] : P.inv_sqrt_d;
+                sc[p][i] = valid ? a4[i] * k : kNegInf;
+            }
+        }
+        ++ktiles;
+        // the record: lanes of the group's (at most 4) heads write their 16 scores
+        if (r16 < 4) {
+            float* dst = ring.rec + (t & (kPairRing - 1)) * 256 + 16 * (4 * rg + r16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u4 v = {__float_as_uint(sc[q][0]), __float_as_uint(sc[q][1]), __float_as_uint(sc[q][2]),
+                              __float_as_uint(sc[q][3])};
+                asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(dst + 4 * q), "v"(v) : "memory");
+            }
+        }
+        const int tn = t + step;
+        bool more = tn < nt && tn < bnd;
+        // stay within the window of the decided frontier; stop at the bound
+        if (more && tn >= dec + kPairWindow) {
+            drain();  // this record has reached memory: flag it before waiting
+            flag(t);
+            const Deadline dl;
+            for (;;) {
+                const unsigned long long wb = sload_glc(tg.ctl + 1), wd = sload_glc(tg.ctl + 2);
+                bnd = min(nt, unstamp(wb, P.epoch, nt));
+                dec = unstamp(wd, P.epoch, 0);
+                if (tn >= bnd || tn < dec + kPairWindow) break;
+                if (dl.passed()) return;  // the primary gives up on its own
+                __builtin_amdgcn_s_sleep(2);
+            }
+            more = tn < bnd;
+            if (!more) break;
+            S::resolve_from(P, grp, n, tn, blkN, C);
+            blkN = tn + step < nt ? S::fetch_blocks(P, grp, n, tn + step) : 0;
+            issue_k(C);
+        } else if (more) {
+            // the next tile's K goes out behind this record; once only those
+            // NK loads may still be in flight the record has reached memory
+            S::resolve_from(P, grp, n, tn, blkN, C);
+            blkN = tn + step < nt ? S::fetch_blocks(P, grp, n, tn + step) : 0;
+            issue_k(C);
+            S::template wait_vm<NK>();
+            flag(t);
+        } else {
+            drain();
+            flag(t);
+            break;
+        }
+        t = tn;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    count_stats(P, ktiles, 0ull);
+}
+
+// Primary worker of the pair kernel: tiles first, first + nA, ... ; V rows
+// only, the scores from the tile's record; hand-over to the decider as in the
+// team kernel.
+template <class S>
+__device__ __forceinline__ void pair_primary_worker(const Params& P, int grp, int n, int nt, int first,
+                                                    const TeamPlan& plan, S& st, TeamShared<S::HBM>* sh,
+                                                    float* rec_lds) {
+    constexpr int HBM = S::HBM, UP = S::UP;
+    const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
+    const PairRing ring(P, grp);
+    int t = first;
+    if (t >= nt) return;
+    int o1 = first;
+    int bnd = nt, rel = 0;
+    bool gv = false;
+    typename S::TileRef C;
+    S::resolve(P, grp, t, C);
+    st.template issue_vs<0>(P, C, 0);
+    st.template issue_vs<1>(P, C, 1);
+    int blkN = S::fetch_blocks(P, grp, n, plan.nextA(t));
+    unsigned long long loaded = 1, rows = S::rows_in(C);
+    for (;;) {
+        // the tile's scores: wait for its record, then copy it into LDS
+        const int slot = t & (kPairRing - 1);
+        const unsigned long long want = stamp(P.epoch, (unsigned)(t + 1));
+        if (sload_glc(ring.flag + slot) != want) {
+            const Deadline dl;
+            for (;;) {
+                __builtin_amdgcn_s_sleep(1);
+                if (sload_glc(ring.flag + slot) == want) break;
+                bnd = uni(lds_ld(&sh->bound));
+                if (t >= bnd) break;
+                if (dl.passed()) {
+                    gv = true;
+                    break;
+                }
+            }
+            if (gv || t >= bnd) break;
+        }
+        __builtin_amdgcn_global_load_lds(ring.rec + slot * 256 + 4 * lane,
+                                         (__attribute__((address_space(3))) void*)rec_lds, 16, 0, 17 /* sc0 sc1 */);
+        S::template wait_vm<0>();  // the tile's V, the next block ids and the record
+        float s0[UP][4], s1[UP][4];
+        {
+            const float* e = rec_lds + 16 * (4 * rg + (r16 & 3));
+            f4 w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const f4*>(e + 4 * q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s0[0][i] = r16 < 4 ? w[0][i] : kNegInf;
+                s0[1][i] = r16 < 4 ? w[1][i] : kNegInf;
+                s1[0][i] = r16 < 4 ? w[2][i] : kNegInf;
+                s1[1][i] = r16 < 4 ? w[3][i] : kNegInf;
+            }
+        }
+        st.template consume_given<0>(P, C, 0, s0);
+        st.template consume_given<1>(P, C, 1, s1);
+        typename S::Out o;
+        st.flush(P, o);
+        bnd = uni(lds_ld(&sh->bound));
+        if (t >= bnd) break;
+        const int tn = plan.nextA(t);
+        const bool haveN = tn < nt && tn < bnd;
+        const int cerr = C.err;
+        if (haveN) {
+            S::resolve_from(P, grp, n, tn, blkN, C);
+            st.template issue_vs<0>(P, C, 0);
+            st.template issue_vs<1>(P, C, 1);
+            blkN = S::fetch_blocks(P, grp, n, plan.nextA(tn));
+            ++loaded;
+            rows += S::rows_in(C);
+        }
+        rel = uni(lds_ld(&sh->released));
+        if (o1 - kTeamSlots >= rel) {
+            const Deadline dl;
+            for (;;) {
+                __builtin_amdgcn_s_sleep(1);
+                rel = uni(lds_ld(&sh->released));
+                bnd = uni(lds_ld(&sh->bound));
+                if (o1 - kTeamSlots < rel || t >= bnd) break;
+                if (dl.passed()) {
+                    gv = true;
+                    break;
+                }
+            }
+            if (gv || t >= bnd) break;
+        }
+        {
+            const int sl = o1 & (kTeamSlots - 1);
+            float* e = sh->part[sl] + lane;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                e[(hb * kTeamStateW + 0) * 64] = o.mf[hb];
+                e[(hb * kTeamStateW + 1) * 64] = o.lf[hb];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) e[(hb * kTeamStateW + 2 + j) * 64] = o.a[hb][j];
+            }
+            if (lane == 0) lds_st(&sh->err[sl], cerr);
+            wait_lds();  // the partial is written before its tag
+            if (lane == 0) lds_st(&sh->tag[sl], t + 1);
+        }
+        if (!haveN) break;
+        t = tn;
+        o1 += plan.nA;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    (void)loaded;  // the K tiles are counted by the score workers
+    count_stats(P, 0ull, rows);
+}
+
+// Grid: NG primaries, then NG score work-groups (score work-group NG + g
+// serves group g; with NG a multiple of 8 both sit on the same XCD).
+template <class S>
+__global__ __launch_bounds__(S::TEAM * 64) void art_pair_kernel(Params P) {
+    extern __shared__ float lds[];
+    constexpr int HBM = S::HBM, TEAM = S::TEAM;
+    static_assert(HBM == 1, "the pair kernel serves groups of at most 4 query heads");
+    const int wv = wave_id(), lane = lane_id();
+    const FoldLanes fl(P);
+    const int grp = blockIdx.x % P.NG, role = blockIdx.x / P.NG;
+    const int n = P.ctx_lens[seq_of(P, grp)];
+    const bool bad = n < 0 || n > P.cap;
+    const int nt = (bad || n == 0) ? 0 : (n + S::T - 1) / S::T;
+    if (nt == 0) {
+        if (role == 0 && wv == 0) {
+            const long long row0 = qrow(P, grp, 0);
+            const int Gh = heads_in(P, grp);
+            for (int k = lane; k < Gh * P.D; k += 64) P.out[row0 * P.D + k] = bad ? NAN : 0.f;
+            for (int h = lane; h < Gh; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
+        }
+        return;
+    }
+    if (role == 1) {
+        S st;
+        st.init(lds);  // (no LDS use: K stays in registers)
+        pair_score_worker<S>(P, grp, n, nt, wv, TEAM, st);
+        return;
+    }
+    const TeamPlan plan(TEAM - 1, 0, kTeamHelpFrom);
+    TeamShared<HBM>* sh = reinterpret_cast<TeamShared<HBM>*>(lds + (TEAM - 1) * 256);
+    if (wv == 0) {
+        if (lane < kTeamSlots) sh->tag[lane] = 0;
+        if (lane < kChain) sh->ptag[lane] = 0;
+        if (lane == 0) {
+            sh->released = 0;
+            sh->bound = nt;
+        }
+    }
+    __syncthreads();
+    if (wv != 0) {
+        S st;
+        st.init(lds + (wv - 1) * 256);
+        pair_primary_worker<S>(P, grp, n, nt, wv - 1, plan, st, sh, lds + (wv - 1) * 256);
+        return;
+    }
+    __builtin_amdgcn_s_setprio(3);
+    ProbeState<HBM> D;
+    Part<HBM> tot, toth;
+    team_decider<HBM, false>(P, grp, nt, plan, sh, D, tot, toth, true);
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = hb * 4 + fl.hl;
+        if (!D.hv[hb]) continue;
+        if (D.U[hb] < 0) {
+            float nan8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) nan8[j] = NAN;
+            write_head_out(P, grp, h, fl, nan8, 1.f, 0, -2);
+        } else {
+            write_head_out(P, grp, h, fl, tot.a[hb], tot.l[hb], D.err[hb], D.U[hb]);
+        }
+    }
+}
+
+template <class S>
+size_t pair_lds_bytes() {
+    const size_t need = (size_t)(S::TEAM - 1) * 256 * sizeof(float) + sizeof(TeamShared<S::HBM>);
+    return need > kPairMinLds ? need : kPairMinLds;
 }
 
 // ------------------------------------------------------------------ pool kernel (workers shared by the groups)
@@ -4159,6 +4572,30 @@ int run_tile(const Params& p, hipStream_t s, bool art) {
     return launch_split<decltype(&art_full_kernel<Tile>), Tile>(p, s, &art_full_kernel<Tile>);
 }
 
+// The pair kernel where it applies (both roles resident at once, one
+// work-group per CU); 0 if launched, else nonzero (the caller falls back).
+template <class S>
+int launch_pair(const Params& p0, hipStream_t s) {
+    if constexpr (S::GM != 4) {
+        return 1;
+    } else {
+        Params p = p0;
+        if (p.vskip || p.NG % 8 != 0 || p.NG > kTeamHelpGroups) return 1;
+        const int cus = device_cus();
+        const size_t lds = pair_lds_bytes<S>();
+        const int per_cu = resident(&art_pair_kernel<S>, S::TEAM * 64, lds);
+        if (cus <= 0 || per_cu < 1 || 2LL * p.NG > (long long)cus * per_cu) return 1;
+        void* args[] = {&p};
+        const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&art_pair_kernel<S>),
+                                                        dim3(2 * p.NG), dim3(S::TEAM * 64), args, (unsigned)lds, s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return 1;
+        }
+        return 0;
+    }
+}
+
 // Helpers (as many as requested, up to what fits) only where every
 // work-group of the grid can be resident at once (cooperative launch); else
 // the primaries alone.
@@ -4267,6 +4704,7 @@ int run_stream(const Params& p, hipStream_t s, bool art) {
     // K (the skip leaves out their share of P.V).
     if (p.vskip) return S::KVT == ART_BF16 ? launch_team<S, 2>(p, s) : launch_team<S, 1>(p, s);
     if (p.engine == ART_ENGINE_XCD && launch_xp<S>(p, s) == 0) return 0;
+    if (p.engine == ART_ENGINE_PAIR && launch_pair<S>(p, s) == 0) return 0;
     // by default the pool serves few, long groups (where one CU per group
     // would leave most of the chip idle)
     const bool pool = p.engine == ART_ENGINE_POOL ||

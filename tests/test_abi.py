@@ -81,7 +81,7 @@ def test_valid_desc_passes():
     (dict(team_helpers=-1), -5),
     (dict(team_helpers=4), -5),
     (dict(engine=-1), -5),
-    (dict(engine=5), -5),
+    (dict(engine=6), -5),
     (dict(workers_per_cu=-1), -5),
     (dict(window=-1), -5),
     (dict(window=113), -5),

@@ -203,7 +203,7 @@ def test_helper_work_groups_parity():
     _run_and_check(c, "config4-small art, 1 helper work-group per group", team_helpers=1)
 
 
-ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD = 1, 2, 4
+ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD, ENGINE_PAIR = 1, 2, 4, 5
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
@@ -261,6 +261,48 @@ def test_xcd_engine_ragged_empty_and_invalid_rows():
     assert (used[1] == 0).all() and (out[1] == 0).all()
     assert (used[4] == -1).all() and np.isnan(out[4]).all()
     check_parity(c, out, used, rows=[0, 1, 2, 3])
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_pair_engine_parity(n):
+    # K and scores on one CU of an XCD, V, folding and decisions on another
+    c = A.config(n, small=n != 2)
+    _run_and_check(c, f"config{n} pair art", engine=ENGINE_PAIR, v_skip_eps=0.0)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "i4"])
+def test_pair_engine_matches_team_engine(kv):
+    # the same scores (same operands, same instruction) and the same fold:
+    # identical stops, outputs equal to rounding
+    c = A.config(3, small=True, kv_dtype=kv)
+    dev = to_device(c)
+    for kw in (dict(), dict(eps_scale=1e-30, eps_dir=1e-30), dict(patience=3)):
+        o1, u1 = run_gpu(c, dev, engine=ENGINE_TEAM, **kw)
+        o2, u2 = run_gpu(c, dev, engine=ENGINE_PAIR, **kw)
+        assert np.array_equal(u1, u2), kw
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-6)
+
+
+def test_pair_engine_ragged_empty_and_invalid_rows():
+    c = A.config(3, small=True, batch=8)
+    c.ctx_lens[1] = 0                                   # empty row
+    c.ctx_lens[2] = 1                                   # one token
+    c.ctx_lens[3] = 64 * 3 + 17                         # ragged tail
+    c.ctx_lens[4] = c.block_table.shape[1] * 16 + 1     # longer than its table
+    c.block_table[5, 7] = -3                            # an invalid block id inside the row
+    out, used = run_gpu(c, engine=ENGINE_PAIR)
+    assert (used[1] == 0).all() and (out[1] == 0).all()
+    assert (used[4] == -1).all() and np.isnan(out[4]).all()
+    check_parity(c, out, used, rows=[0, 1, 2, 3, 6, 7])
+    assert (used[5] == -1).all() or (used[5] > 0).all()  # stops before the bad block, else reports it
+
+
+def test_pair_engine_full_size():
+    # the 32K workload at full size (128 groups on 256 CUs), every row
+    c = A.config(3)
+    out, used = run_gpu(c, engine=ENGINE_PAIR)
+    r = check_parity(c, out, used)
+    log(f"[parity] config3 full size pair: max_abs={r['max_abs']:.3e} near={r['near']}")
 
 
 def test_pool_engine_ragged_empty_and_invalid_rows():
