@@ -141,9 +141,11 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 __device__ __forceinline__ float sbyte(uint32_t w, int k) { return (float)(int)(int8_t)(w >> (8 * k)); }
 // signed 4-bit code k of a 32-bit word (code k in bits 4k..4k+3), sign-extended
 __device__ __forceinline__ float snib(uint32_t w, int k) { return (float)((int)(w << (28 - 4 * k)) >> 28); }
-// two small integers (|x| <= 127) as a packed bf16 pair: exact, since they need at most 8 bits
+// two small integers (|x| <= 128) as a packed bf16 pair: exact, since they need at most 8 bits,
+// so the upper halves of their fp32 words are their bf16 values (one v_perm_b32: bytes 0-3 of
+// the selection come from the second operand, 4-7 from the first)
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-    return (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // Eight consecutive cache elements starting at element `off` (a multiple of 8), widened to fp32.
