@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define ART_ABI_VERSION 8
+#define ART_ABI_VERSION 9
 
 typedef enum {
     ART_OK = 0,
@@ -65,11 +65,20 @@ typedef enum {
                                of that XCD with work left; deciders on CUs that load
                                no tiles; no V skip (falls back to TEAM); at most 512
                                groups                                                  */
-    ART_ENGINE_PAIR = 5     /* two CUs per group on one XCD: one loads K and computes
+    ART_ENGINE_PAIR = 5,    /* two CUs per group on one XCD: one loads K and computes
                                the scores, the other loads V, folds and decides; at
                                most 4 query heads per group, no V skip, the number
                                of groups a multiple of 8 and at most half the CUs
                                (else TEAM)                                             */
+    ART_ENGINE_ROUND = 6    /* the steps run in rounds over every CU (one launch per
+                               round): round r loads steps [a_r, a_{r+1}) of every
+                               group with heads left undecided, all at once, and the
+                               last wave of each group decides them; rounds of 32
+                               steps at first, then half the steps before them (at
+                               most 512).  No V skip (falls back to TEAM).  Its
+                               workspace keeps every step's running state and probe
+                               record (art_workspace_bytes counts them for engines
+                               AUTO and ROUND)                                         */
 } art_engine;
 
 /* Order in which a row's tiles are visited (ART summary, section 2.4: the tile

@@ -64,7 +64,7 @@ class ArtDesc(ctypes.Structure):
 _lib = None
 
 
-ABI_VERSION = 8  # art_desc layout and entry points this binding marshals (ART_ABI_VERSION in art.h)
+ABI_VERSION = 9  # art_desc layout and entry points this binding marshals (ART_ABI_VERSION in art.h)
 
 
 def load():

@@ -79,8 +79,8 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     if (d->max_workers < 0) return fail(ART_E_PARAM, "max_workers %d < 0", d->max_workers);
     if (d->team_helpers < 0 || d->team_helpers > art::kMaxHelpers)
         return fail(ART_E_PARAM, "team_helpers %d not in 0..%d", d->team_helpers, art::kMaxHelpers);
-    if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_PAIR)
-        return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_PAIR);
+    if (d->engine < ART_ENGINE_AUTO || d->engine > ART_ENGINE_ROUND)
+        return fail(ART_E_PARAM, "engine %d not in %d..%d", d->engine, ART_ENGINE_AUTO, ART_ENGINE_ROUND);
     if (d->workers_per_cu < 0) return fail(ART_E_PARAM, "workers_per_cu %d < 0", d->workers_per_cu);
     if (d->window < 0 || d->window > art::kXpMaxWindow)
         return fail(ART_E_PARAM, "window %d not in 0..%d", d->window, art::kXpMaxWindow);
@@ -127,13 +127,23 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
         else if (G > 8 && 3 * ((G + 3) / 4) < G) shift = 2;  // every one of the 4 groups keeps a head
         const int gv = (G + (1 << shift) - 1) >> shift;
         const bool even = (gv << shift) == G;
-        if (art_mode && streamed && shift > 0 && (even || !sharing) &&
+        // (the round engine loads a KV head's tiles once for all its query heads)
+        if (art_mode && streamed && shift > 0 && (even || !sharing) && d->engine != ART_ENGINE_ROUND &&
             (long long)p.NG << shift <= art::kMaxSplitGroups) {
             p.kv_shift = shift;
             p.Hkv <<= shift;
             p.G = gv;
             p.NG <<= shift;
         }
+    }
+    // the round engine's regions: ART mode on the streamed tile without the
+    // V skip, engine AUTO or ROUND, no work-sharing engine or helpers
+    {
+        const bool streamed = d->head_dim == 128 && d->q_dtype == ART_BF16 && tile == 64 &&
+                              (d->kv_dtype == ART_BF16 || d->kv_dtype == ART_I8 || d->kv_dtype == ART_I4);
+        p.round_ok = eps_scale > 0.f && eps_dir > 0.f && streamed && p.G <= 8 && !(d->v_skip_eps > 0.f) &&
+                     d->max_workers == 0 && d->team_helpers == 0 &&
+                     (d->engine == ART_ENGINE_AUTO || d->engine == ART_ENGINE_ROUND);
     }
     p.seq_div = d->per_head_tables ? (1 << p.kv_shift) : p.Hkv;
     {
@@ -187,6 +197,14 @@ Layout workspace_layout(const Params& p) {
     L.team_ctl = o; o = align256(o + NT * kTeamCtl * sizeof(unsigned long long));
     const size_t NS = p.order == ART_ORDER_LIST ? (size_t)(p.NG / p.seq_div) * p.nt_max : 0;  // step-table records
     L.steps = o; o = align256(o + NS * kStepW * sizeof(int));
+    // round engine: every step's running state and probe record, the groups'
+    // decision states and control words
+    const RoundPlan rp = p.round_ok ? round_plan(p.nt_max, p.NG) : RoundPlan{};
+    const size_t NR = rp.R > 0 ? NG : 0, HB = (G + 3) / 4;
+    L.round_rec = o; o = align256(o + NR * (size_t)p.nt_max * p.slot * sizeof(float));
+    L.round_probe = o; o = align256(o + NR * (size_t)p.nt_max * G * kRoundRecW * sizeof(float));
+    L.round_state = o; o = align256(o + NR * HB * kRoundProbeW * 64 * sizeof(float));
+    L.round_ctl = o; o = align256(o + NR * kRoundCtlW * sizeof(unsigned long long));
     L.total = o;
     return L;
 }
@@ -301,6 +319,11 @@ art_status art_decode_attention(const art_desc* desc, const void* q, const void*
     p.team_ring = reinterpret_cast<unsigned long long*>(ws + L.team_ring);
     p.team_ctl = reinterpret_cast<unsigned long long*>(ws + L.team_ctl);
     p.steps = reinterpret_cast<int*>(ws + L.steps);
+    const bool rounds = p.round_ok && L.round_ctl < L.total;
+    p.round_rec = rounds ? reinterpret_cast<float*>(ws + L.round_rec) : nullptr;
+    p.round_probe = rounds ? reinterpret_cast<float*>(ws + L.round_probe) : nullptr;
+    p.round_state = rounds ? reinterpret_cast<float*>(ws + L.round_state) : nullptr;
+    p.round_ctl = rounds ? reinterpret_cast<unsigned long long*>(ws + L.round_ctl) : nullptr;
     p.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
     if (p.epoch == 0) p.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;  // 0 never stamps
     const int rc = (p.art || p.vskip) ? art::launch_art(p, stream) : art::launch_full(p, stream);

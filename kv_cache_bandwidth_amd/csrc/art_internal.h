@@ -39,6 +39,56 @@ constexpr int kSlotHeader = 48;   // floats before the accumulator block of a pa
                                   // [0,16) tile max per head, [16,32) tile sum per head,
                                   // [32] error flag (as int), [33] V rows kept (as int)
 
+// Round engine (ART mode, streamed 64-token tiles): the visiting steps run in
+// rounds, one launch each; round r takes steps [a[r], a[r+1]) of every group
+// still undecided, spread over waves[r] waves per group of pw[r] consecutive
+// steps each.  The first rounds take kRoundFirst steps, later ones half the
+// steps before them (at most kRoundMaxSteps): a group that stops past the
+// first rounds has loaded at most half again the steps it needs.
+constexpr int kRoundFirst = 64;          // steps of a round at least (multiple of 16)
+constexpr int kRoundMaxSteps = 512;      // steps of a round at most (multiple of 16)
+constexpr int kMaxRounds = 32;           // rounds of a call at most (else the engine does not apply)
+constexpr int kRoundWavesTarget = 2048;  // waves of a round over all groups (256 CUs x 8)
+constexpr int kRoundMaxPW = 4;           // steps per wave at most
+constexpr int kRoundRecW = 12;           // floats of a probe record per (step, head): max, sum,
+                                         // accumulator dims 0..7, error flag (as int), padding
+constexpr int kRoundProbeW = 22;         // words per lane per head block of a group's decision state
+constexpr int kRoundCtlW = 2 + kMaxRounds;  // 64-bit words per group (zeroed by each call): [0] (epoch, next round) once a
+                                            // round left heads undecided, [1 + r] arrivals in round r,
+                                            // [1 + kMaxRounds] slices of the final launch done
+
+struct RoundPlan {
+    int R;                     // rounds (0: the engine does not apply)
+    int a[kMaxRounds + 1];     // first step of each round; a[R] = steps of the longest row
+    int pw[kMaxRounds];        // steps per wave
+    int waves[kMaxRounds];     // waves per group
+};
+
+// The rounds of a call with NG groups and rows of at most nt_max tiles.
+inline RoundPlan round_plan(int nt_max, int NG) {
+    RoundPlan rp{};
+    rp.R = 0;
+    rp.a[0] = 0;
+    while (rp.a[rp.R] < nt_max) {
+        if (rp.R == kMaxRounds) {
+            rp.R = 0;
+            return rp;
+        }
+        const int a = rp.a[rp.R];
+        int c = (a / 2 + 15) / 16 * 16;
+        if (c < kRoundFirst) c = kRoundFirst;
+        if (c > kRoundMaxSteps) c = kRoundMaxSteps;
+        const int b = a + c < nt_max ? a + c : nt_max;
+        long long pw = (long long)(b - a) * NG / kRoundWavesTarget;
+        if (pw < 1) pw = 1;
+        if (pw > kRoundMaxPW) pw = kRoundMaxPW;
+        rp.pw[rp.R] = (int)pw;
+        rp.waves[rp.R] = (b - a + (int)pw - 1) / (int)pw;
+        rp.a[++rp.R] = b;
+    }
+    return rp;
+}
+
 // Per-group control block; the allocation counter on its own 128-byte line.
 struct alignas(128) GroupCtl {
     int next;          // tile allocation counter (atomic)
@@ -108,6 +158,11 @@ struct Params {
     int xp_wpc;         // XCD engine: worker waves per CU (set at launch)
     int xp_window;      // XCD engine: tiles past the decided frontier a worker may load
     int slot;           // floats per partial: kSlotHeader + G*D
+    int round_ok;       // the workspace holds the round engine's regions (set from the call's desc)
+    float* round_rec;   // [NG][nt_max][slot]: a wave's running state through each of its steps
+    float* round_probe; // [NG][nt_max][G][kRoundRecW]: each step's own probe record
+    float* round_state; // [NG][HB][kRoundProbeW][64]: a group's decision state between rounds
+    unsigned long long* round_ctl;  // [NG][kRoundCtlW]
     // launch
     int deciders;       // decider waves of the persistent kernel (each owns whole groups)
     int workers;        // tile worker waves of the persistent kernel
@@ -125,7 +180,9 @@ constexpr size_t group_words(int G) { return team_words(G) > pool_words(G) ? tea
 
 // Workspace layout for a Params (offsets in bytes, all 256-byte aligned).
 struct Layout {
-    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, team_ring, team_ctl, steps, total;
+    size_t abort_flag, ctl, ring_tag, ring, vmax_tag, vmax, partials, team_ring, team_ctl, steps;
+    size_t round_rec, round_probe, round_state, round_ctl;  // round engine (0 bytes unless round_ok)
+    size_t total;
 };
 Layout workspace_layout(const Params& p);
 

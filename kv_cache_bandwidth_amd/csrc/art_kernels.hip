@@ -4231,6 +4231,379 @@ __global__ __launch_bounds__(kXpWaves * 64) void art_xp_kernel(Params P) {
 }
 
 // Full mode, one tile at a time: split sp of group grp covers a fixed tile range.
+// ------------------------------------------------------------------ round engine
+//
+// ART mode over every CU, with no hand-over per tile: the visiting steps are
+// taken in rounds, one launch each.  In round r every group that still has
+// undecided heads loads steps [a_r, a_{r+1}), all at once, over waves[r]
+// waves of pw[r] consecutive steps.  For each step a wave leaves (1) that
+// tile's own probe record (max, sum and accumulator dims 0..7 per head:
+// what the stop rule reads) and (2) its running state through the step (the
+// whole accumulator per head).  The last wave of a group to arrive decides
+// the round's steps with the block scan the team engine uses, over records
+// formed the same way (the same tile partials), so the stops agree with that
+// engine's.  A group whose heads are all decided takes no further round; its
+// tiles_used are written.  Steps past a group's stop inside its last round
+// were loaded for nothing.  A final launch merges, per head, the running
+// states of the waves' step ranges below its tiles_used (the range holding
+// the stop cut there) and writes the outputs.
+
+struct RoundArgs {
+    int r, a0, a1, pw, waves;  // round, its steps [a0, a1), steps per wave, waves per group
+};
+
+// a group's decision state between rounds: [HB][kRoundProbeW][64]
+__device__ __forceinline__ float* round_state_of(const Params& P, int grp) {
+    return P.round_state + (long long)grp * ((P.G + 3) >> 2) * kRoundProbeW * 64;
+}
+
+template <int HBM>
+__device__ __forceinline__ void round_save(const Params& P, int grp, const ProbeState<HBM>& D) {
+    float* cs = round_state_of(P, grp) + lane_id();
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        float* w = cs + hb * kRoundProbeW * 64;
+        cst(w + 0 * 64, D.M[hb]);
+        cst(w + 1 * 64, D.L[hb]);
+        cst(w + 2 * 64, D.Xn[hb]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            cst(w + (3 + j) * 64, D.Pd[hb][j]);
+            cst(w + (11 + j) * 64, D.X[hb][j]);
+        }
+        cst(w + 19 * 64, __int_as_float(D.streak[hb]));
+        cst(w + 20 * 64, __int_as_float(D.U[hb]));
+        cst(w + 21 * 64, __int_as_float(D.err[hb]));
+    }
+}
+
+template <int HBM>
+__device__ __forceinline__ void round_load(const Params& P, int grp, ProbeState<HBM>& D) {
+    const float* cs = round_state_of(P, grp) + lane_id();
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const float* w = cs + hb * kRoundProbeW * 64;
+        D.M[hb] = cld(w + 0 * 64);
+        D.L[hb] = cld(w + 1 * 64);
+        D.Xn[hb] = cld(w + 2 * 64);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            D.Pd[hb][j] = cld(w + (3 + j) * 64);
+            D.X[hb][j] = cld(w + (11 + j) * 64);
+        }
+        D.streak[hb] = __float_as_int(cld(w + 19 * 64));
+        D.U[hb] = __float_as_int(cld(w + 20 * 64));
+        D.err[hb] = __float_as_int(cld(w + 21 * 64));
+    }
+}
+
+// The last wave of group grp to finish round R decides its steps.
+template <int HBM>
+__device__ __forceinline__ void round_decide(const Params& P, int grp, const RoundArgs& R, int nt, bool bad) {
+    const int lane = lane_id(), i = lane & 15;
+    const FoldLanes fl(P);
+    const int gh = heads_in(P, grp);
+    if (nt == 0) {
+        // empty row: tiles_used 0; invalid length: -1 (the final launch writes the outputs)
+        const long long row0 = qrow(P, grp, 0);
+        for (int h = lane; h < gh; h += 64) P.tiles_used[row0 + h] = bad ? -1 : 0;
+        return;
+    }
+    ProbeState<HBM> D;
+    D.init(fl, gh);
+    if (R.r > 0) round_load<HBM>(P, grp, D);
+    const int b = min(R.a1, nt);
+    // lane i of each head's row: the probe record of step f0 + i
+    auto load = [&](BlockRecs<HBM>& B, int f0) {
+        B.clear();
+        if (f0 + i < b) {
+            const long long rec = (long long)grp * P.nt_max + f0 + i;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                if (D.hv[hb]) {
+                    const float* pr = P.round_probe + (rec * P.G + 4 * hb + fl.hl) * kRoundRecW;
+                    B.m[hb] = cld(pr + 0);
+                    B.l[hb] = cld(pr + 1);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) B.p[hb][j] = cld(pr + 2 + j);
+                    B.e[hb] = __float_as_int(cld(pr + 10));
+                }
+            }
+        }
+    };
+    // three blocks of records in flight: blocks f + 16 and f + 32 load while
+    // block f is decided
+    BlockRecs<HBM> B0, B1, B2;
+    load(B0, R.a0);
+    load(B1, R.a0 + 16);
+    for (int f0 = R.a0; f0 < b; f0 += 48) {
+        load(B2, f0 + 32);
+        decide_pass<HBM>(P, D, B0, f0, min(16, b - f0), min(16, b - f0), nt);
+        if (D.finished() || f0 + 16 >= b) break;
+        load(B0, f0 + 48);
+        decide_pass<HBM>(P, D, B1, f0 + 16, min(16, b - f0 - 16), min(16, b - f0 - 16), nt);
+        if (D.finished() || f0 + 32 >= b) break;
+        load(B1, f0 + 64);
+        decide_pass<HBM>(P, D, B2, f0 + 32, min(16, b - f0 - 32), min(16, b - f0 - 32), nt);
+        if (D.finished()) break;
+    }
+    if (D.finished()) {
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb)
+            if (D.hv[hb] && i == 0) P.tiles_used[qrow(P, grp, 4 * hb + fl.hl)] = D.err[hb] ? -1 : D.U[hb];
+        return;  // no further round for this group
+    }
+    round_save<HBM>(P, grp, D);
+    drain();
+    if (lane == 0) cst(P.round_ctl + (long long)grp * kRoundCtlW, stamp(P.epoch, (unsigned)(R.r + 1)));
+}
+
+// zeroes the groups' control words (arrival counters, round stamps)
+__global__ __launch_bounds__(256) void art_round_init_kernel(Params P) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < (long long)P.NG * kRoundCtlW) cst(P.round_ctl + i, 0ull);
+}
+
+template <class S>
+__global__ __launch_bounds__(256, S::MIN_WAVES) void art_round_kernel(Params P, RoundArgs R) {
+    extern __shared__ float lds[];
+    constexpr int HBM = S::HBM;
+    const int wv = wave_id(), lane = lane_id();
+    const FoldLanes fl(P);
+    S st;
+    st.init(lds + wv * S::lds_floats(P));
+    // the round's items (group, range) = (item / waves, item % waves), taken by
+    // the grid's waves in turn: w, w + W, ...
+    const long long items = (long long)P.NG * R.waves;
+    const long long W = (long long)gridDim.x * kWavesPerWG;
+    for (long long item = (long long)blockIdx.x * kWavesPerWG + wv; item < items; item += W) {
+        const int grp = (int)(item / R.waves), k = (int)(item % R.waves);
+        unsigned long long* ctl = P.round_ctl + (long long)grp * kRoundCtlW;
+        // a group takes round r > 0 only if round r - 1 left heads undecided
+        if (R.r > 0 && uni64(cld(ctl)) != stamp(P.epoch, (unsigned)R.r)) continue;
+        const int n = P.ctx_lens[seq_of(P, grp)];
+        const bool bad = n < 0 || n > P.cap;
+        const int nt = bad ? 0 : (n + S::T - 1) / S::T;
+        const int t0 = R.a0 + k * R.pw;
+        const int t1 = min(min(t0 + R.pw, R.a1), nt);
+        unsigned long long loaded = 0, rows = 0;
+        if (t0 < t1) {
+            st.load_q(P, grp);  // before the tile's loads: consume() counts those in issue order
+            // (like a team worker: a tile's loads are issued once the previous
+            // tile is consumed; the next block ids are loaded a tile ahead)
+            typename S::TileRef C;
+            S::resolve(P, grp, t0, C);
+            st.template issue<0>(P, C, 0);
+            st.template issue<1>(P, C, 1);
+            int blkN = t0 + 1 < t1 ? S::fetch_blocks(P, grp, n, t0 + 1) : 0;
+            Part<HBM> run;  // the running state through the current step
+            run.clear();
+            for (int t = t0;; ++t) {
+                ++loaded;
+                rows += S::rows_in(C);
+                st.template consume<0>(P, C, 0, true);
+                st.template consume<1>(P, C, 1, false);
+                typename S::Out o;
+                st.flush(P, o);
+                const long long rec = (long long)grp * P.nt_max + t;
+                float* slot = P.round_rec + rec * P.slot;
+#pragma unroll
+                for (int hb = 0; hb < HBM; ++hb) {
+                    const int h = 4 * hb + fl.hl;
+                    if (hb < fl.HB && h < P.G) {
+                        // (1) the tile's own probe record (lane (hl, 0) of each head)
+                        if (fl.cid == 0) {
+                            float* pr = P.round_probe + (rec * P.G + h) * kRoundRecW;
+                            cst(pr + 0, o.mf[hb]);
+                            cst(pr + 1, o.lf[hb]);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) cst(pr + 2 + j, o.a[hb][j]);
+                            cst(pr + 10, __int_as_float(C.err));
+                        }
+                        // (2) the running state through step t (read only by the
+                        // final launch: plain stores, seen there after the launch boundary)
+                        sm_merge(run.m[hb], run.l[hb], run.a[hb], o.mf[hb], o.lf[hb], o.a[hb]);
+                        f4* a = reinterpret_cast<f4*>(slot + kSlotHeader + h * P.D + 8 * fl.cid);
+                        a[0] = f4{run.a[hb][0], run.a[hb][1], run.a[hb][2], run.a[hb][3]};
+                        a[1] = f4{run.a[hb][4], run.a[hb][5], run.a[hb][6], run.a[hb][7]};
+                        if (fl.cid == 0) {
+                            slot[h] = run.m[hb];
+                            slot[16 + h] = run.l[hb];
+                        }
+                    }
+                }
+                if (t + 1 >= t1) break;
+                S::resolve_from(P, grp, n, t + 1, blkN, C);
+                st.template issue<0>(P, C, 0);
+                st.template issue<1>(P, C, 1);
+                if (t + 2 < t1) blkN = S::fetch_blocks(P, grp, n, t + 2);
+            }
+        }
+        if (loaded) count_stats(P, loaded, rows);
+        drain();  // every record of this item stored before its arrival
+        // arrival: one atomic add per item (the call's first launch zeroed the counters)
+        int cnt = 0;
+        if (lane == 0)
+            cnt = (int)__hip_atomic_fetch_add(ctl + 1 + R.r, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+        cnt = bcast0(cnt);
+        if (cnt == R.waves) round_decide<HBM>(P, grp, R, nt, bad);
+    }
+}
+
+// The outputs: per head, the running states of the waves' step ranges below
+// its tiles_used (the range holding the stop cut there), merged.  SL
+// work-groups of NW waves per group; wave w of slice sl takes ranges
+// sl * NW + w, + SL * NW, ... (loaded NB at a time); the waves' states are
+// merged in wave order through LDS, and the slices' states (through the
+// full-mode partial slots) by the slice that finishes last, in slice order:
+// a fixed order, so the output is deterministic.
+template <int HBM, int NW, int NB>
+__global__ __launch_bounds__(64 * NW) void art_round_combine_kernel(Params P, RoundPlan rp, int SL) {
+    __shared__ float part[NW][HBM][64][10];  // per wave, head block, lane: M, L, 8 dims
+    const int grp = blockIdx.x / SL, sl = blockIdx.x % SL;
+    const int wv = wave_id(), lane = lane_id();
+    const FoldLanes fl(P);
+    const int gh = heads_in(P, grp);
+    int U[HBM];
+    int umax = 0;
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = 4 * hb + fl.hl;
+        U[hb] = hb < fl.HB && h < gh ? P.tiles_used[qrow(P, grp, h)] : 0;
+        umax = max(umax, U[hb]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) umax = max(umax, __shfl_xor(umax, o));
+    umax = uni(umax);
+    Part<HBM> acc;
+    acc.clear();
+    // the ranges of this wave, a batch at a time
+    const int me = sl * NW + wv, stride = SL * NW;
+    int c = 0, nb = 0;
+    int lo[NB] = {}, hi[NB] = {};
+    auto flush_batch = [&]() {
+        float m2[NB][HBM], l2[NB][HBM], a2[NB][HBM][8];
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                m2[q][hb] = kNegInf;
+                l2[q][hb] = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a2[q][hb][j] = 0.f;
+                const int h = 4 * hb + fl.hl;
+                if (q < nb && U[hb] > lo[q] && fl.cvalid) {
+                    const int last = min(hi[q], U[hb]) - 1;
+                    const float* slot = P.round_rec + ((long long)grp * P.nt_max + last) * P.slot;
+                    m2[q][hb] = slot[h];
+                    l2[q][hb] = slot[16 + h];
+                    const f4* a = reinterpret_cast<const f4*>(slot + kSlotHeader + h * P.D + 8 * fl.cid);
+                    const f4 x = a[0], y = a[1];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        a2[q][hb][j] = x[j];
+                        a2[q][hb][4 + j] = y[j];
+                    }
+                }
+            }
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) sm_merge(acc.m[hb], acc.l[hb], acc.a[hb], m2[q][hb], l2[q][hb], a2[q][hb]);
+        nb = 0;
+    };
+    // range k of round r has index c + k (c: the ranges of the rounds before)
+    for (int r = 0; r < rp.R && rp.a[r] < umax; c += rp.waves[r], ++r) {
+        for (int k = ((me - c) % stride + stride) % stride; k < rp.waves[r]; k += stride) {
+            const int c0 = rp.a[r] + k * rp.pw[r];
+            if (c0 >= umax) break;
+            const int c1 = min(c0 + rp.pw[r], rp.a[r + 1]);
+#pragma unroll
+            for (int q = 0; q < NB; ++q)
+                if (q == nb) {
+                    lo[q] = c0;
+                    hi[q] = c1;
+                }
+            if (++nb == NB) flush_batch();
+        }
+    }
+    if (nb > 0) flush_batch();
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        float* e = part[wv][hb][lane];
+        e[0] = acc.m[hb];
+        e[1] = acc.l[hb];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[2 + j] = acc.a[hb][j];
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    // this slice's state: its waves in order
+    Part<HBM> tot;
+    tot.clear();
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb)
+        for (int w = 0; w < NW; ++w) {
+            const float* e = part[w][hb][lane];
+            float a2[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a2[j] = e[2 + j];
+            sm_merge(tot.m[hb], tot.l[hb], tot.a[hb], e[0], e[1], a2);
+        }
+    if (SL > 1) {
+        // through slot sl of the group's partials; the last slice merges them all
+        // (the full-mode partial layout: max and sum at [h] and [16 + h], the
+        // accumulator at kSlotHeader + h * D)
+        float* base = P.partials + (long long)grp * P.splits * P.slot;
+        float* slot = base + (long long)sl * P.slot;
+#pragma unroll
+        for (int hb = 0; hb < HBM; ++hb) {
+            const int h = 4 * hb + fl.hl;
+            if (hb >= fl.HB || h >= gh) continue;
+            if (fl.cid == 0) {
+                cst(slot + h, tot.m[hb]);
+                cst(slot + 16 + h, tot.l[hb]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cst(slot + kSlotHeader + h * P.D + 8 * fl.cid + j, tot.a[hb][j]);
+        }
+        drain();
+        int cnt = 0;
+        if (lane == 0)
+            cnt = (int)__hip_atomic_fetch_add(P.round_ctl + (long long)grp * kRoundCtlW + kRoundCtlW - 1, 1ull,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+        if (bcast0(cnt) != SL) return;
+        tot.clear();
+        for (int q = 0; q < SL; ++q) {
+            const float* src = base + (long long)q * P.slot;
+#pragma unroll
+            for (int hb = 0; hb < HBM; ++hb) {
+                const int h = 4 * hb + fl.hl;
+                if (hb >= fl.HB || h >= gh) continue;
+                float a2[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a2[j] = cld(src + kSlotHeader + h * P.D + 8 * fl.cid + j);
+                sm_merge(tot.m[hb], tot.l[hb], tot.a[hb], cld(src + h), cld(src + 16 + h), a2);
+            }
+        }
+    }
+#pragma unroll
+    for (int hb = 0; hb < HBM; ++hb) {
+        const int h = 4 * hb + fl.hl;
+        if (hb >= fl.HB || h >= gh) continue;
+        float A[8], L = tot.l[hb];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) A[j] = tot.a[hb][j];
+        if (U[hb] == 0) {
+            // empty row: out = 0
+#pragma unroll
+            for (int j = 0; j < 8; ++j) A[j] = 0.f;
+            L = 1.f;
+        }
+        write_head_out(P, grp, h, fl, A, L, U[hb] < 0, U[hb]);
+    }
+}
+
 template <class Tile>
 __global__ __launch_bounds__(256) void art_full_kernel(Params P) {
     extern __shared__ float lds[];
@@ -4652,6 +5025,9 @@ int launch_pool(const Params& p0, hipStream_t s) {
 }
 
 
+constexpr int kRoundAutoGroups = 64;  // engine AUTO takes the rounds for at most this many groups
+constexpr int kRoundCombineCUs = 256;  // work-groups of the round engine's final launch, about
+constexpr int kRoundMaxSlices = 8;     // work-groups per group of that launch at most
 constexpr int kXpDefaultWindow = 64;  // tiles past the decided frontier a worker may load, by default
 
 // One work-group per CU, all resident (cooperative launch); returns 1 when it
@@ -4687,6 +5063,50 @@ int launch_xp(const Params& p0, hipStream_t s) {
     return 1;
 }
 
+// The round engine: one launch per round, then the outputs; returns 1 when it
+// does not apply (its workspace regions were not laid out, or the rows need
+// more than kMaxRounds rounds), so that the team engine runs instead.
+template <class S>
+int launch_round(const Params& p, hipStream_t s) {
+    if (!p.round_rec || S::HBM > 2) return 1;
+    const RoundPlan rp = round_plan(p.nt_max, p.NG);
+    if (rp.R == 0) return 1;
+    const size_t lds = (size_t)kWavesPerWG * S::lds_floats(p) * sizeof(float);
+    const long long words = (long long)p.NG * kRoundCtlW;
+    hipLaunchKernelGGL(art_round_init_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, p);
+    // each round: at most as many work-groups as are resident at once, their
+    // waves taking the round's items in turn
+    const int cus = device_cus(), per_cu = resident(&art_round_kernel<S>, 64 * kWavesPerWG, lds);
+    const long long slots = cus > 0 && per_cu > 0 ? (long long)cus * per_cu : 1024;
+    for (int r = 0; r < rp.R; ++r) {
+        const RoundArgs ra{r, rp.a[r], rp.a[r + 1], rp.pw[r], rp.waves[r]};
+        long long blocks = ((long long)p.NG * ra.waves + kWavesPerWG - 1) / kWavesPerWG;
+        if (blocks > slots) blocks = slots;
+        hipLaunchKernelGGL((art_round_kernel<S>), dim3((unsigned)blocks), dim3(64 * kWavesPerWG), lds, s, p, ra);
+    }
+    // slices per group: about one work-group per CU over all groups, within
+    // the partial slots the workspace holds
+    int sl = kRoundCombineCUs / p.NG;
+    if (sl > kRoundMaxSlices) sl = kRoundMaxSlices;
+    if (sl > p.splits) sl = p.splits;
+    if (sl < 1) sl = 1;
+    const unsigned grid = (unsigned)((long long)p.NG * sl);
+    if constexpr (S::HBM == 1)
+        hipLaunchKernelGGL((art_round_combine_kernel<1, 16, 8>), dim3(grid), dim3(64 * 16), 0, s, p, rp, sl);
+    else
+        hipLaunchKernelGGL((art_round_combine_kernel<2, 8, 4>), dim3(grid), dim3(64 * 8), 0, s, p, rp, sl);
+    return (int)hipGetLastError();
+}
+
+// Engine AUTO takes the rounds for ART without the V skip where they were
+// measured faster than one CU per group: few groups (the team engine would
+// leave most CUs idle) of 256 to 1024 tiles and at most 4 query heads (on
+// B8 x 8 KV heads at 32K context, int8: 120 us against 132 us; with 128
+// groups, or rows of 2048 tiles, the team and pool engines are faster)
+bool round_auto(const Params& p) {
+    return p.NG <= kRoundAutoGroups && p.G <= 4 && p.nt_max >= 256 && p.nt_max <= 1024;
+}
+
 template <class S>
 int run_stream(const Params& p, hipStream_t s, bool art) {
     if constexpr (S::ORDER == ART_ORDER_LIST) {
@@ -4705,6 +5125,8 @@ int run_stream(const Params& p, hipStream_t s, bool art) {
     // more than the rows left out save, and the V rows come with the tile's
     // K (the skip leaves out their share of P.V).
     if (p.vskip) return S::KVT == ART_BF16 ? launch_team<S, 2>(p, s) : launch_team<S, 1>(p, s);
+    if ((p.engine == ART_ENGINE_ROUND || (p.engine == ART_ENGINE_AUTO && round_auto(p))) && launch_round<S>(p, s) == 0)
+        return 0;
     if (p.engine == ART_ENGINE_XCD && launch_xp<S>(p, s) == 0) return 0;
     if (p.engine == ART_ENGINE_PAIR && launch_pair<S>(p, s) == 0) return 0;
     // by default the pool serves few, long groups (where one CU per group

@@ -55,9 +55,17 @@ extern "C" art_status art_decode_attention_noalloc(const art_desc* desc, const v
     if (!desc) return art::set_error(ART_E_NULL, "desc is NULL");
     // size check first, on the host alone: a call too large for the scratch
     // is refused before the device is touched
+    art_desc d = *desc;
     size_t need = 0;
-    const art_status v = art::call_workspace_bytes(desc, tile, eps_scale, eps_dir, &need);
+    art_status v = art::call_workspace_bytes(&d, tile, eps_scale, eps_dir, &need);
     if (v != ART_OK) return v;
+    if (need > (size_t)ART_NOALLOC_SCRATCH_BYTES && d.engine == ART_ENGINE_AUTO) {
+        // the round engine keeps every step's records; where they do not fit,
+        // the team engine (no such records) serves the call
+        d.engine = ART_ENGINE_TEAM;
+        v = art::call_workspace_bytes(&d, tile, eps_scale, eps_dir, &need);
+        if (v != ART_OK) return v;
+    }
     if (need > (size_t)ART_NOALLOC_SCRATCH_BYTES)
         return art::set_error(ART_E_WORKSPACE,
                               "the call needs %zu bytes of workspace; the static scratch holds %zu "
@@ -66,7 +74,6 @@ extern "C" art_status art_decode_attention_noalloc(const art_desc* desc, const v
     art_status st = ART_OK;
     void* ws = scratch_on_current_device(&st);
     if (!ws) return st;
-    art_desc d = *desc;
     d.workspace = ws;
     d.workspace_bytes = ART_NOALLOC_SCRATCH_BYTES;
     return art_decode_attention(&d, q, k_cache, v_cache, block_table, ctx_lens, tile, eps_scale, eps_dir, out,

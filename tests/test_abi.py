@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = art.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.art_abi_version() == 8
+    assert lib.art_abi_version() == 9
 
 
 def desc(**kw):
@@ -81,7 +81,7 @@ def test_valid_desc_passes():
     (dict(team_helpers=-1), -5),
     (dict(team_helpers=4), -5),
     (dict(engine=-1), -5),
-    (dict(engine=6), -5),
+    (dict(engine=7), -5),
     (dict(workers_per_cu=-1), -5),
     (dict(window=-1), -5),
     (dict(window=113), -5),

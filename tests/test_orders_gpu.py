@@ -13,7 +13,7 @@ from tests.test_parity_gpu import _run_and_check
 pytestmark = pytest.mark.gpu
 
 ORDER_RECENT, ORDER_LIST = 1, 2
-ENGINE_TEAM, ENGINE_POOL = 1, 2
+ENGINE_TEAM, ENGINE_POOL, ENGINE_ROUND = 1, 2, 6
 
 
 def ordered(c, order, seed=0):
@@ -38,6 +38,9 @@ def test_orders_every_engine(order):
     c = ordered(A.config(3, small=True), order, seed=11)
     _run_and_check(c, f"config3 order {order} team", engine=ENGINE_TEAM)
     _run_and_check(c, f"config3 order {order} pool", engine=ENGINE_POOL)
+    _run_and_check(c, f"config3 order {order} round", engine=ENGINE_ROUND)
+    c8 = ordered(A.config(3, small=True, ctx=8192), order, seed=12)  # several rounds
+    _run_and_check(c8, f"config3 ctx 8192 order {order} round", engine=ENGINE_ROUND)
     _run_and_check(c, f"config3 order {order} work-sharing", max_workers=96)
     _run_and_check(c, f"config3 order {order} helpers", team_helpers=1)
 

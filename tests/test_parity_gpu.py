@@ -203,7 +203,7 @@ def test_helper_work_groups_parity():
     _run_and_check(c, "config4-small art, 1 helper work-group per group", team_helpers=1)
 
 
-ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD, ENGINE_PAIR = 1, 2, 4, 5
+ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD, ENGINE_PAIR, ENGINE_ROUND = 1, 2, 4, 5, 6
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
@@ -303,6 +303,76 @@ def test_pair_engine_full_size():
     out, used = run_gpu(c, engine=ENGINE_PAIR)
     r = check_parity(c, out, used)
     log(f"[parity] config3 full size pair: max_abs={r['max_abs']:.3e} near={r['near']}")
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_round_engine_parity(n):
+    # the steps in rounds over every CU; the last wave of a group decides them
+    c = A.config(n, small=n != 2)
+    _run_and_check(c, f"config{n} round art", engine=ENGINE_ROUND, v_skip_eps=0.0)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "i4"])
+def test_round_engine_matches_team_engine(kv):
+    # the same tile partials and the same block scan: identical stops; the
+    # outputs merge the same partials in another order (rounding only)
+    c = A.config(3, small=True, ctx=8192, kv_dtype=kv)  # 128 steps: four rounds
+    dev = to_device(c)
+    for kw in (dict(), dict(eps_scale=1e-30, eps_dir=1e-30), dict(patience=3), dict(eps_scale=1e-2, eps_dir=1e-3)):
+        o1, u1 = run_gpu(c, dev, engine=ENGINE_TEAM, **kw)
+        o2, u2 = run_gpu(c, dev, engine=ENGINE_ROUND, **kw)
+        assert np.array_equal(u1, u2), kw
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-5)
+
+
+def test_round_engine_ragged_empty_and_invalid_rows():
+    c = A.config(3, small=True, batch=8, ctx=8192)
+    c.ctx_lens[1] = 0                                   # empty row
+    c.ctx_lens[2] = 1                                   # one token
+    c.ctx_lens[3] = 64 * 3 + 17                         # ragged tail
+    c.ctx_lens[4] = c.block_table.shape[1] * 16 + 1     # longer than its table
+    c.block_table[5, 7] = -3                            # an invalid block id inside the row
+    c.ctx_lens[6] = 64 * 100 + 5                        # a ragged tail in the fourth round
+    out, used = run_gpu(c, engine=ENGINE_ROUND)
+    assert (used[1] == 0).all() and (out[1] == 0).all()
+    assert (used[4] == -1).all() and np.isnan(out[4]).all()
+    check_parity(c, out, used, rows=[0, 1, 2, 3, 6, 7])
+    assert (used[5] == -1).all() or (used[5] > 0).all()  # stops before the bad block, else reports it
+
+
+def test_round_engine_repeated_calls_and_statistics():
+    # successive calls (each with its own epoch) give the same result; the
+    # tiles loaded are at least those the stops need and at most what the
+    # rounds that hold each group's stop cover
+    import torch
+    c = A.config(3, small=True, ctx=8192)
+    dev = to_device(c)
+    first = None
+    for _ in range(3):
+        stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+        out, used = run_gpu(c, dev, engine=ENGINE_ROUND, stats=stats)
+        if first is None:
+            first = (out, used)
+            check_parity(c, out, used)
+        else:
+            assert np.array_equal(used, first[1])
+            assert np.array_equal(out, first[0])  # deterministic
+        per_group = used.reshape(c.B, c.Hkv, -1).max(axis=2)
+        nt = -(-c.ctx_lens // c.tile)
+        bounds = [0, 64, 128, 192, 288, 432, 648]  # the round plan's first steps
+        cover = np.array([[min(next(b for b in bounds if b >= u), nt[i]) for u in row]
+                          for i, row in enumerate(per_group)])
+        loaded = int(stats[0].item())
+        assert per_group.sum() <= loaded <= cover.sum(), (per_group.sum(), loaded, cover.sum())
+
+
+@pytest.mark.parametrize("n", [3, 4, 5])
+def test_round_engine_full_size(n):
+    # every row of the full-size workload against the oracle
+    c = A.config(n)
+    out, used = run_gpu(c, engine=ENGINE_ROUND, v_skip_eps=0.0)
+    r = check_parity(c, out, used, v_skip_eps=0.0)
+    log(f"[parity] config{n} full size round: max_abs={r['max_abs']:.3e} near={r['near']}")
 
 
 def test_pool_engine_ragged_empty_and_invalid_rows():

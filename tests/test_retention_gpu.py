@@ -14,7 +14,7 @@ from tests.test_parity_gpu import _run_and_check
 
 pytestmark = pytest.mark.gpu
 
-ENGINE_TEAM, ENGINE_POOL = 1, 2
+ENGINE_TEAM, ENGINE_POOL, ENGINE_ROUND = 1, 2, 6
 ORDER_RECENT, ORDER_LIST = 1, 2
 
 
@@ -34,6 +34,7 @@ def test_retained_every_engine():
     c = retained(A.config(3, small=True), 0.5, seed=9)
     _run_and_check(c, "retained team", engine=ENGINE_TEAM)
     _run_and_check(c, "retained pool", engine=ENGINE_POOL)
+    _run_and_check(c, "retained round", engine=ENGINE_ROUND)
     _run_and_check(c, "retained work-sharing", max_workers=96)
     _run_and_check(c, "retained helpers", team_helpers=1)
 

@@ -74,6 +74,15 @@ def test_noalloc_matches_workspace_call(engine):
     _compare(A.config(1, seed=4), f"{engine} config1", **kw)
 
 
+def test_noalloc_round_engine():
+    # the round engine keeps every step's records: calls whose records fit the
+    # static array run it, larger ones are refused (engine ROUND) or served by
+    # the team engine (engine AUTO, see test_noalloc_matches_workspace_call)
+    _compare(A.config(3, small=True, ctx=8192, seed=5), "round config3 ctx 8192", engine=6)
+    _compare(A.config(3, small=True, seed=6), "round config3 small", engine=6)
+    _compare(A.config(4, small=True, seed=7), "round config4 small", engine=6)
+
+
 def test_noalloc_empty_batch_and_zero_lengths():
     import torch
     c = A.config(3, small=True, seed=5)
