@@ -482,6 +482,12 @@ def other_workloads(args, flush_buf, steps=7):
                  "kv_tiles_skipped_head_level": round(float(1.0 - used.sum() / (nt[:, None] * case.Hq).sum()), 4),
                  "art_roofline": roof(t_art, used, case.v_skip_eps),
                  "full_roofline": roof(t_full, used_full, 0.0)}
+        # detector overhead (thresholds that never pass, no V skip) and ART
+        # without the V skip on each engine (the default engine picks one of them)
+        entry["never_firing_art_us"] = round(med(eps_scale=1e-30, eps_dir=1e-30, v_skip_eps=0.0)[0], 1)
+        entry["art_no_vskip_us_by_engine"] = {
+            name: round(med(v_skip_eps=0.0, engine=e)[0], 1)
+            for name, e in (("team", 1), ("pool", 2), ("round", 6))}
         if case.v_skip_eps > 0:
             t_nv, used_nv = med(v_skip_eps=0.0)
             entry["art_no_vskip_us"] = round(t_nv, 1)
