@@ -42,10 +42,14 @@ constexpr int kSlotHeader = 48;   // floats before the accumulator block of a pa
 // Round engine (ART mode, streamed 64-token tiles): the visiting steps run in
 // rounds, one launch each; round r takes steps [a[r], a[r+1]) of every group
 // still undecided, spread over waves[r] waves per group of pw[r] consecutive
-// steps each.  The first rounds take kRoundFirst steps, later ones half the
-// steps before them (at most kRoundMaxSteps): a group that stops past the
-// first rounds has loaded at most half again the steps it needs.
+// steps each.  The first rounds take enough steps for about kRoundFirstPW
+// steps per wave of a round over all groups (kRoundFirst to kRoundFirstMax),
+// later ones half the steps before them (at most kRoundMaxSteps): a group
+// that stops past the first rounds has loaded at most half again the steps
+// it needs.
 constexpr int kRoundFirst = 64;          // steps of a round at least (multiple of 16)
+constexpr int kRoundFirstMax = 256;      // steps of the first rounds at most (multiple of 16)
+constexpr int kRoundFirstPW = 4;         // steps per wave the first rounds aim for
 constexpr int kRoundMaxSteps = 512;      // steps of a round at most (multiple of 16)
 constexpr int kMaxRounds = 32;           // rounds of a call at most (else the engine does not apply)
 constexpr int kRoundWavesTarget = 2048;  // waves of a round over all groups (256 CUs x 8)
@@ -69,6 +73,9 @@ inline RoundPlan round_plan(int nt_max, int NG) {
     RoundPlan rp{};
     rp.R = 0;
     rp.a[0] = 0;
+    long long first = NG > 0 ? ((long long)kRoundFirstPW * kRoundWavesTarget / NG + 15) / 16 * 16 : kRoundFirst;
+    if (first < kRoundFirst) first = kRoundFirst;
+    if (first > kRoundFirstMax) first = kRoundFirstMax;
     while (rp.a[rp.R] < nt_max) {
         if (rp.R == kMaxRounds) {
             rp.R = 0;
@@ -76,7 +83,7 @@ inline RoundPlan round_plan(int nt_max, int NG) {
         }
         const int a = rp.a[rp.R];
         int c = (a / 2 + 15) / 16 * 16;
-        if (c < kRoundFirst) c = kRoundFirst;
+        if (c < (int)first) c = (int)first;
         if (c > kRoundMaxSteps) c = kRoundMaxSteps;
         const int b = a + c < nt_max ? a + c : nt_max;
         long long pw = (long long)(b - a) * NG / kRoundWavesTarget;

@@ -340,6 +340,18 @@ def test_round_engine_ragged_empty_and_invalid_rows():
     assert (used[5] == -1).all() or (used[5] > 0).all()  # stops before the bad block, else reports it
 
 
+def _round_bounds(nt_max, ng):
+    # the rounds' first steps as the library plans them: about 4 steps per wave
+    # of 2048 in the first rounds (64 to 256 steps), then half the steps
+    # before, at most 512
+    first = min(max((4 * 2048 // ng + 15) // 16 * 16, 64), 256)
+    a = [0]
+    while a[-1] < nt_max:
+        c = min(max((a[-1] // 2 + 15) // 16 * 16, first), 512)
+        a.append(min(a[-1] + c, nt_max))
+    return a
+
+
 def test_round_engine_repeated_calls_and_statistics():
     # successive calls (each with its own epoch) give the same result; the
     # tiles loaded are at least those the stops need and at most what the
@@ -359,7 +371,7 @@ def test_round_engine_repeated_calls_and_statistics():
             assert np.array_equal(out, first[0])  # deterministic
         per_group = used.reshape(c.B, c.Hkv, -1).max(axis=2)
         nt = -(-c.ctx_lens // c.tile)
-        bounds = [0, 64, 128, 192, 288, 432, 648]  # the round plan's first steps
+        bounds = _round_bounds(int(nt.max()), c.B * c.Hkv)
         cover = np.array([[min(next(b for b in bounds if b >= u), nt[i]) for u in row]
                           for i, row in enumerate(per_group)])
         loaded = int(stats[0].item())
