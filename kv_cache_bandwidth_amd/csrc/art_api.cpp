@@ -32,6 +32,7 @@ art_status fail(art_status s, const char* fmt, ...) {
 
 // worker waves the full-mode split aims for: 256 CUs x 8 resident waves
 constexpr int kTargetWaves = 2048;
+constexpr int kMinTilesPerSplit = 4;  // full mode: tiles per split at least (rows permitting)
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -170,6 +171,10 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
     // full-mode split plan (part of the workspace layout, so independent of the device)
     const int target = kTargetWaves;
     int splits = p.NG ? (target + p.NG - 1) / p.NG : 1;
+    // at least kMinTilesPerSplit tiles per split: a wave of one tile is all
+    // latency, and each split adds a partial to the combine
+    const int most = (p.nt_max + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
+    if (splits > most) splits = most;
     if (splits > p.nt_max) splits = p.nt_max > 0 ? p.nt_max : 1;
     if (splits < 1) splits = 1;
     p.tiles_per_split = p.nt_max > 0 ? (p.nt_max + splits - 1) / splits : 1;

@@ -1198,10 +1198,19 @@ struct Stream {
         const int lane = lane_id(), r16 = lane & 15, rg = lane >> 4;
         const int hin = heads_in(P, r.grp);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<0>();  // the tile's K and scales (and the next block ids)
+        // the tile's K and scales (and the next block ids); with V coming with
+        // K, unit 0's scores start once unit 0 has landed (at most the later
+        // unit's OPS instructions outstanding: they complete in issue order)
+        if constexpr (DEFER) wait_vm<0>();
+        else wait_vm<OPS>();
         __builtin_amdgcn_sched_barrier(0);
         float s0[UP][4], s1[UP][4];
         float mu = scores<0>(P, r, 0, s0);
+        if constexpr (!DEFER) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm<0>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
         mu = fmaxf(mu, scores<1>(P, r, 1, s1));
         const float M = chain(mu);
         float lsum = 0.f;
@@ -4749,12 +4758,12 @@ __global__ __launch_bounds__(256, S::MIN_WAVES) void art_full_stream_kernel(Para
 }
 
 // One work-group of kCombineWaves waves per group merges the splits and
-// writes the outputs.  Wave w takes splits w, w + kCombineWaves, ...: it first
-// finds their largest max per head, then sums their weighted sums and
-// accumulators (independent loads, many in flight); the waves' results are
-// then merged in wave order through LDS.  The order is fixed: the output is
-// deterministic.
+// writes the outputs.  Wave w takes splits w, w + kCombineWaves, ...,
+// kCombineBatch of them loaded at once (independent loads, many in flight)
+// and merged in split order; the waves' results are then merged in wave
+// order through LDS.  The order is fixed: the output is deterministic.
 constexpr int kCombineWaves = 4;
+constexpr int kCombineBatch = 8;  // splits a wave loads at once
 
 __global__ __launch_bounds__(64 * kCombineWaves) void art_combine_kernel(Params P) {
     __shared__ float part[kCombineWaves][4][64][10];  // per wave, head block, lane: M, L, 8 dims
@@ -4776,26 +4785,30 @@ __global__ __launch_bounds__(64 * kCombineWaves) void art_combine_kernel(Params 
         const int h = hb * 4 + fl.hl;
         float M = kNegInf, L = 0.f, A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (hb < fl.HB && h < G) {
-            // splits with no rows (l = 0) take no part
-#pragma unroll 8
-            for (int sp = wv; sp < P.splits; sp += kCombineWaves) {
-                const float* slot = base + (long long)sp * P.slot;
-                const float ll = slot[16 + h];
-                M = fmaxf(M, ll > 0.f ? slot[h] : kNegInf);
-            }
-            if (M != kNegInf) {
-#pragma unroll 4
-                for (int sp = wv; sp < P.splits; sp += kCombineWaves) {
-                    const float* slot = base + (long long)sp * P.slot;
-                    const float ll = slot[16 + h];
-                    const float w = ll > 0.f ? expf(slot[h] - M) : 0.f;
-                    L = fmaf(w, ll, L);
-                    if (fl.cvalid) {
-                        const float* a = slot + kSlotHeader + h * D + 8 * fl.cid;
+            // one pass, kCombineBatch splits loaded at a time and merged in
+            // order; splits with no rows (l = 0) take no part
+            for (int s0 = wv; s0 < P.splits; s0 += kCombineWaves * kCombineBatch) {
+                float m2[kCombineBatch], l2[kCombineBatch], a2[kCombineBatch][8];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) A[j] = fmaf(w, a[j], A[j]);
+                for (int q = 0; q < kCombineBatch; ++q) {
+                    const int sp = s0 + q * kCombineWaves;
+                    m2[q] = kNegInf;
+                    l2[q] = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) a2[q][j] = 0.f;
+                    if (sp < P.splits) {
+                        const float* slot = base + (long long)sp * P.slot;
+                        l2[q] = slot[16 + h];
+                        m2[q] = l2[q] > 0.f ? slot[h] : kNegInf;
+                        if (fl.cvalid) {
+                            const float* a = slot + kSlotHeader + h * D + 8 * fl.cid;
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) a2[q][j] = a[j];
+                        }
                     }
                 }
+#pragma unroll
+                for (int q = 0; q < kCombineBatch; ++q) sm_merge(M, L, A, m2[q], l2[q], a2[q]);
             }
         }
         float* e = part[wv][hb][lane];
