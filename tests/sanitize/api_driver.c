@@ -18,7 +18,7 @@ int main(void) {
                 for (int order = 0; order < 3; ++order)
                     for (int per_head = 0; per_head < 2; ++per_head)
                         for (int ti = 0; ti < 5; ++ti)
-                            for (int art = 0; art < 2; ++art) {
+                            for (int art = 0; art < 3; ++art) {  /* full, ART + V skip, ART */
                                 art_desc d;
                                 memset(&d, 0, sizeof d);
                                 d.batch = 3;
@@ -32,13 +32,13 @@ int main(void) {
                                 d.num_blocks = paged ? 40 : 0;
                                 d.max_ctx = paged ? 0 : 144;
                                 d.patience = 1 + order;
-                                d.v_skip_eps = art ? 1e-6f : 0.f;
+                                d.v_skip_eps = art == 1 ? 1e-6f : 0.f;
                                 d.k_scale = d.v_scale = (kvi >= 2) ? (const void*)(uintptr_t)0x1000 : NULL;
                                 d.tile_order = order;
                                 d.tile_perm_stride = 16;
                                 d.tile_perm = order == 2 ? (const int32_t*)(uintptr_t)0x2000 : NULL;
                                 d.per_head_tables = per_head;
-                                d.engine = (ti + order) % 5;
+                                d.engine = (ti + order + art) % 7;  /* every engine, the round engine too */
                                 const int tile = tiles[ti];
                                 const size_t need = art_workspace_bytes(&d, tile);
                                 d.workspace = (void*)(uintptr_t)(1u << 20);

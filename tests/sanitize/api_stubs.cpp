@@ -25,6 +25,36 @@ int check_params(const art::Params& p) {
             std::abort();
         }
     }
+    // the round engine's regions, when laid out: each inside the workspace
+    // with the extent the kernels index (every step of every group)
+    if (p.round_rec) {
+        const art::RoundPlan rp = art::round_plan(p.nt_max, p.NG);
+        const size_t NG = (size_t)p.NG, HB = (size_t)(p.G + 3) / 4;
+        struct Region {
+            const char* at;
+            size_t bytes;
+        } regions[] = {
+            {reinterpret_cast<const char*>(p.round_rec), NG * p.nt_max * p.slot * sizeof(float)},
+            {reinterpret_cast<const char*>(p.round_probe), NG * p.nt_max * p.G * art::kRoundRecW * sizeof(float)},
+            {reinterpret_cast<const char*>(p.round_state), NG * HB * art::kRoundProbeW * 64 * sizeof(float)},
+            {reinterpret_cast<const char*>(p.round_ctl), NG * art::kRoundCtlW * sizeof(unsigned long long)},
+        };
+        for (const Region& r : regions) {
+            if (r.at < base || r.at + r.bytes > base + L.total) {
+                std::fprintf(stderr, "round engine region outside the layout\n");
+                std::abort();
+            }
+        }
+        if (rp.R < 0 || rp.R > art::kMaxRounds || (p.nt_max > 0 && rp.R > 0 && rp.a[rp.R] != p.nt_max)) {
+            std::fprintf(stderr, "inconsistent round plan\n");
+            std::abort();
+        }
+        // the final launch's slices use the full-mode partial slots
+        if (p.splits < 1) {
+            std::fprintf(stderr, "no partial slots for the round engine's final launch\n");
+            std::abort();
+        }
+    }
     if (p.NG < 0 || p.G < 1 || p.G > art::kMaxG || p.nt_max < 0) {
         std::fprintf(stderr, "inconsistent shape in Params\n");
         std::abort();
