@@ -77,8 +77,10 @@ typedef enum {
                                steps at first, then half the steps before them (at
                                most 512).  No V skip (falls back to TEAM).  Its
                                workspace keeps every step's running state and probe
-                               record (art_workspace_bytes counts them for engines
-                               AUTO and ROUND)                                         */
+                               record (art_workspace_bytes counts them for engine
+                               ROUND, and for AUTO on the shapes where AUTO takes
+                               it: at most 64 groups of 256-1024 tiles, at most 4
+                               query heads per group)                                  */
 } art_engine;
 
 /* Order in which a row's tiles are visited (ART summary, section 2.4: the tile

@@ -138,13 +138,15 @@ art_status check(const art_desc* d, int tile, float eps_scale, float eps_dir, ar
         }
     }
     // the round engine's regions: ART mode on the streamed tile without the
-    // V skip, engine AUTO or ROUND, no work-sharing engine or helpers
+    // V skip, no work-sharing engine or helpers, and engine ROUND, or engine
+    // AUTO on the shapes where it takes the rounds
     {
         const bool streamed = d->head_dim == 128 && d->q_dtype == ART_BF16 && tile == 64 &&
                               (d->kv_dtype == ART_BF16 || d->kv_dtype == ART_I8 || d->kv_dtype == ART_I4);
         p.round_ok = eps_scale > 0.f && eps_dir > 0.f && streamed && p.G <= 8 && !(d->v_skip_eps > 0.f) &&
                      d->max_workers == 0 && d->team_helpers == 0 &&
-                     (d->engine == ART_ENGINE_AUTO || d->engine == ART_ENGINE_ROUND);
+                     (d->engine == ART_ENGINE_ROUND ||
+                      (d->engine == ART_ENGINE_AUTO && art::round_auto(p.NG, p.G, p.nt_max)));
     }
     p.seq_div = d->per_head_tables ? (1 << p.kv_shift) : p.Hkv;
     {

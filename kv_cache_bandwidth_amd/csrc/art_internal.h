@@ -96,6 +96,17 @@ inline RoundPlan round_plan(int nt_max, int NG) {
     return rp;
 }
 
+// Engine AUTO takes the rounds for ART without the V skip where they were
+// measured faster than one CU per group: few groups (the team engine would
+// leave most CUs idle) of 256 to 1024 tiles and at most 4 query heads (on
+// B8 x 8 KV heads at 32K context, int8: 116-120 us against 131-133 us on the
+// team engine; with 128 groups, or rows of 2048 tiles, the team and pool
+// engines are faster).  Shapes only, so that the workspace layout can follow.
+constexpr int kRoundAutoGroups = 64;  // groups at most
+inline bool round_auto(int NG, int G, int nt_max) {
+    return NG <= kRoundAutoGroups && G <= 4 && nt_max >= 256 && nt_max <= 1024;
+}
+
 // Per-group control block; the allocation counter on its own 128-byte line.
 struct alignas(128) GroupCtl {
     int next;          // tile allocation counter (atomic)

@@ -5038,7 +5038,6 @@ int launch_pool(const Params& p0, hipStream_t s) {
 }
 
 
-constexpr int kRoundAutoGroups = 64;  // engine AUTO takes the rounds for at most this many groups
 constexpr int kRoundCombineCUs = 256;  // work-groups of the round engine's final launch, about
 constexpr int kRoundMaxSlices = 8;     // work-groups per group of that launch at most
 constexpr int kXpDefaultWindow = 64;  // tiles past the decided frontier a worker may load, by default
@@ -5111,14 +5110,8 @@ int launch_round(const Params& p, hipStream_t s) {
     return (int)hipGetLastError();
 }
 
-// Engine AUTO takes the rounds for ART without the V skip where they were
-// measured faster than one CU per group: few groups (the team engine would
-// leave most CUs idle) of 256 to 1024 tiles and at most 4 query heads (on
-// B8 x 8 KV heads at 32K context, int8: 120 us against 132 us; with 128
-// groups, or rows of 2048 tiles, the team and pool engines are faster)
-bool round_auto(const Params& p) {
-    return p.NG <= kRoundAutoGroups && p.G <= 4 && p.nt_max >= 256 && p.nt_max <= 1024;
-}
+// engine AUTO takes the rounds on the shapes art::round_auto names
+bool round_auto(const Params& p) { return art::round_auto(p.NG, p.G, p.nt_max); }
 
 template <class S>
 int run_stream(const Params& p, hipStream_t s, bool art) {
