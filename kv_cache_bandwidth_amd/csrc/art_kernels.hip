@@ -763,8 +763,17 @@ struct Stream {
     };
 
     vvec vb[NB][UP][4];
-    float ksc[NB][UP][4];        // int8: key scale / sqrt(d) of the score rows
-    float vsc[NB][UP][4];        // int8: value scale of the P.V rows
+    // int8/int4: the fp16 key and value scales of the lane's four rows per
+    // page, as loaded (two per word); widened where they are used, so that no
+    // wait for their loads sits in issue() (the wait counter is in order: it
+    // would also wait for every load issued before them)
+    u2 ksr[NB][UP];
+    u2 vsr[NB][UP];
+    // scale i (0..3) of a pair of words
+    __device__ __forceinline__ static float scale_of(const u2& w, int i) {
+        const uint32_t x = i < 2 ? w.x : w.y;
+        return f16_to_f32((i & 1) ? (uint16_t)(x >> 16) : (uint16_t)(x & 0xffff));
+    }
     bf16x8 qB[4];
     float m_run, l_run;          // per head (lane & 15): running max and (this lane's part of the) sum
     // P.V accumulators in the matrix-core output layout: cacc[j][c] of lane
@@ -950,16 +959,8 @@ struct Stream {
             if constexpr (SCALED) {
                 // the value scales of rows 4rg .. 4rg + 3 and the key scales of
                 // the score rows (the same rows): one 8-byte load each
-                const u2 vw = *reinterpret_cast<const u2*>(P.vs + pr + 4 * rg);
-                vsc[BUF][pp][0] = f16_to_f32(vw.x & 0xffff);
-                vsc[BUF][pp][1] = f16_to_f32(vw.x >> 16);
-                vsc[BUF][pp][2] = f16_to_f32(vw.y & 0xffff);
-                vsc[BUF][pp][3] = f16_to_f32(vw.y >> 16);
-                const u2 w = *reinterpret_cast<const u2*>(P.ks + pr + 4 * rg);
-                ksc[BUF][pp][0] = f16_to_f32(w.x & 0xffff) * P.inv_sqrt_d;
-                ksc[BUF][pp][1] = f16_to_f32(w.x >> 16) * P.inv_sqrt_d;
-                ksc[BUF][pp][2] = f16_to_f32(w.y & 0xffff) * P.inv_sqrt_d;
-                ksc[BUF][pp][3] = f16_to_f32(w.y >> 16) * P.inv_sqrt_d;
+                vsr[BUF][pp] = *reinterpret_cast<const u2*>(P.vs + pr + 4 * rg);
+                ksr[BUF][pp] = *reinterpret_cast<const u2*>(P.ks + pr + 4 * rg);
             }
             const char* kbase = static_cast<const char*>(P.k) + pr * ROWB;
             char* dst = kl + (BUF * UP + pp) * PAGEB;
@@ -992,13 +993,7 @@ struct Stream {
             for (int v = 0; v < 4; ++v)
                 vb[BUF][pp][v] = __builtin_nontemporal_load(
                     reinterpret_cast<const vvec*>(vbase + (4 * rg + v) * ROWB + (ROWB / 16) * r16));
-            if constexpr (SCALED) {
-                const u2 vw = *reinterpret_cast<const u2*>(P.vs + pr + 4 * rg);
-                vsc[BUF][pp][0] = f16_to_f32(vw.x & 0xffff);
-                vsc[BUF][pp][1] = f16_to_f32(vw.x >> 16);
-                vsc[BUF][pp][2] = f16_to_f32(vw.y & 0xffff);
-                vsc[BUF][pp][3] = f16_to_f32(vw.y >> 16);
-            }
+            if constexpr (SCALED) vsr[BUF][pp] = *reinterpret_cast<const u2*>(P.vs + pr + 4 * rg);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -1106,7 +1101,7 @@ struct Stream {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool valid = ((r.pmask >> p) & 1) && r.t * T + 16 * p + 4 * rg + i < r.n;
-                const float sc = SCALED ? ksc[BUF][pp][i] : P.inv_sqrt_d;
+                const float sc = SCALED ? scale_of(ksr[BUF][pp], i) * P.inv_sqrt_d : P.inv_sqrt_d;
                 s[pp][i] = valid ? a4[i] * sc : kNegInf;
                 mu = fmaxf(mu, s[pp][i]);
             }
@@ -1315,7 +1310,7 @@ struct Stream {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float w = hv ? pw[pp][i] : 0.f;
-                if constexpr (SCALED) w *= vsc[BUF][pp][i];
+                if constexpr (SCALED) w *= scale_of(vsr[BUF][pp], i);
                 const __bf16 h = (__bf16)w;
                 ahi[4 * pp + i] = h;
                 alo[4 * pp + i] = (__bf16)(w - (float)h);
