@@ -134,8 +134,13 @@ typedef struct {
                                     v_skip_eps, M_t the running max through tile t
                                     (its weight still enters the softmax sum).  bf16
                                     caches, streamed 64-token tiles: rows no head of
-                                    the KV head keeps are not loaded; otherwise they
-                                    are loaded and left out of the arithmetic       */
+                                    the KV head keeps are not loaded.  int8/int4
+                                    caches, streamed 64-token tiles: the rows come
+                                    with K and a skipped row's weight is zero (the
+                                    matrix-core P.V still runs over every row: the
+                                    faster arrangement at eps 1e-6).  Other tiles:
+                                    only the kept rows are loaded, dequantised and
+                                    accumulated                                     */
     const void* k_scale;         /* I8 caches only (device, fp16 bits)                */
     const void* v_scale;
     void* workspace;             /* device scratch, 256-byte aligned, caller-owned    */
