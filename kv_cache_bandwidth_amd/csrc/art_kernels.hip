@@ -4368,8 +4368,10 @@ __global__ __launch_bounds__(256) void art_round_init_kernel(Params P) {
     if (i < (long long)P.NG * kRoundCtlW) cst(P.round_ctl + i, 0ull);
 }
 
+// two waves per SIMD for the 8-head tile too (its register budget halves: on
+// B4 x 40q/8kv at 128K the rounds took 888 us against 1 053 us at one wave)
 template <class S>
-__global__ __launch_bounds__(256, S::MIN_WAVES) void art_round_kernel(Params P, RoundArgs R) {
+__global__ __launch_bounds__(256, 2) void art_round_kernel(Params P, RoundArgs R) {
     extern __shared__ float lds[];
     constexpr int HBM = S::HBM;
     const int wv = wave_id(), lane = lane_id();
