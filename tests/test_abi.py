@@ -231,3 +231,40 @@ def test_binding_rejects_mismatched_tensors(over, match):
     with pytest.raises(ValueError, match=match):
         art.decode_attention(args["q"], args["k_cache"], args["v_cache"], args["ctx_lens"],
                              block_table=args["block_table"], **rest)
+
+
+def _round_region_bytes(ng, nt_max, g, d=128):
+    # the round engine's workspace regions: every step's running state (a
+    # partial slot of 48 + G*d floats) and probe record (12 floats per head),
+    # the groups' decision states (22 words per lane per head block) and
+    # control words (2 + 32 per group), each 256-byte aligned
+    def a256(x):
+        return (x + 255) // 256 * 256
+    slot = 48 + g * d
+    hb = (g + 3) // 4
+    return (a256(ng * nt_max * slot * 4) + a256(ng * nt_max * g * 12 * 4) + a256(ng * hb * 22 * 64 * 4)
+            + a256(ng * 34 * 8))
+
+
+@pytest.mark.parametrize("batch", [8, 16])
+def test_round_engine_workspace_layout(batch):
+    # engine ROUND lays out exactly the round regions on top of the team
+    # engine's workspace; engine AUTO only where it takes the rounds (at most
+    # 64 groups of 256-1024 tiles, at most 4 query heads per group); no
+    # round regions with the V skip or off the 64-token streamed tile
+    ctx, bs = 32768, 16
+
+    def ws(engine, v_skip=0.0, tile=64, kv=2):
+        d = B.make_desc(batch=batch, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype=1, kv_dtype=kv,
+                        block_size=bs, max_blocks_per_seq=ctx // bs, num_blocks=batch * ctx // bs,
+                        k_scale=1, v_scale=1, engine=engine, v_skip_eps=v_skip)
+        return B.workspace_bytes(d, tile)
+
+    ng, nt = batch * 8, ctx // 64
+    team, rnd, auto = ws(1), ws(6), ws(0)
+    assert team > 0
+    assert rnd - team == _round_region_bytes(ng, nt, 4)
+    assert auto == (rnd if ng <= 64 else team)
+    assert ws(6, v_skip=1e-6) == ws(1, v_skip=1e-6)    # the V skip runs on the team engine
+    assert ws(6, tile=32) == ws(1, tile=32)            # only the streamed 64-token tile
+    assert ws(6, kv=1) - ws(1, kv=1) == _round_region_bytes(ng, nt, 4)  # bf16 alike
