@@ -50,9 +50,11 @@ typedef enum {
 typedef enum { ART_F32 = 0, ART_BF16 = 1, ART_I8 = 2, ART_I4 = 3 } art_dtype;
 
 /* How ART-mode work is spread over the GPU (results agree to rounding; tiles_used
- * is the same whichever runs).  The choice applies to bf16/int8 caches with
- * head_dim 128, bf16 queries, at most 8 query heads per KV head and 64-token
- * tiles; other shapes always run the work-sharing engine. */
+ * is the same whichever runs).  The choice applies to bf16, int8 and int4
+ * caches with head_dim 128, bf16 queries and 64-token tiles, at most 8 query
+ * heads per KV head (ART mode runs 10 to 16 as groups of at most 4, each
+ * reading the KV head's tiles); other shapes always run the work-sharing
+ * engine. */
 typedef enum {
     ART_ENGINE_AUTO = 0,    /* library default                                         */
     ART_ENGINE_TEAM = 1,    /* one work-group per (row, KV head), plus team_helpers    */
@@ -73,9 +75,11 @@ typedef enum {
     ART_ENGINE_ROUND = 6    /* the steps run in rounds over every CU (one launch per
                                round): round r loads steps [a_r, a_{r+1}) of every
                                group with heads left undecided, all at once, and the
-                               last wave of each group decides them; rounds of 32
-                               steps at first, then half the steps before them (at
-                               most 512).  No V skip (falls back to TEAM).  Its
+                               last wave of each group decides them; the first
+                               round takes 8192 / groups steps (rounded up to 16,
+                               within 64..256), each later one half the steps
+                               before it, at least the first's and at most 512.
+                               No V skip (falls back to TEAM).  Its
                                workspace keeps every step's running state and probe
                                record (art_workspace_bytes counts them for engine
                                ROUND, and for AUTO on the shapes where AUTO takes

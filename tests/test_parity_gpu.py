@@ -444,7 +444,7 @@ def test_full_size_every_row(n, mode):
 # ---------------------------------------------------------------- zero probe and fp16 subnormal scales
 
 @pytest.mark.parametrize("shape", ["fp32 d64 T16", "bf16 d128 T64"])
-@pytest.mark.parametrize("engine", [0, ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD])
+@pytest.mark.parametrize("engine", [0, ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD, ENGINE_PAIR, ENGINE_ROUND])
 def test_zero_norm_probe_in_art_mode(shape, engine):
     # the designed case of the oracle pin (probe exactly 0 through tile k - 1,
     # thresholds no finite metric reaches): a metric against a zero probe is
@@ -462,7 +462,7 @@ def test_zero_norm_probe_in_art_mode(shape, engine):
         assert (used == k + 1 + patience).all(), used
 
 
-@pytest.mark.parametrize("engine", [0, ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD])
+@pytest.mark.parametrize("engine", [0, ENGINE_TEAM, ENGINE_POOL, ENGINE_XCD, ENGINE_PAIR, ENGINE_ROUND])
 def test_int8_subnormal_scales(engine):
     # fp16 scales below 2^-14 (subnormal) widen exactly on both sides
     c = A.config(5, small=True, seed=6)
