@@ -76,9 +76,10 @@ typedef enum {
                                round): round r loads steps [a_r, a_{r+1}) of every
                                group with heads left undecided, all at once, and the
                                last wave of each group decides them; the first
-                               round takes 8192 / groups steps (rounded up to 16,
-                               within 64..256), each later one half the steps
-                               before it, at least the first's and at most 512.
+                               round takes 6144 / groups steps (rounded up to 16,
+                               within 64..256), each later one as many steps as
+                               came before it, at least the first's and at most
+                               512.
                                No V skip (falls back to TEAM).  Its
                                workspace keeps every step's running state and probe
                                record (art_workspace_bytes counts them for engine

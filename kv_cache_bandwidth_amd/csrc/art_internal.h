@@ -44,12 +44,15 @@ constexpr int kSlotHeader = 48;   // floats before the accumulator block of a pa
 // still undecided, spread over waves[r] waves per group of pw[r] consecutive
 // steps each.  The first rounds take enough steps for about kRoundFirstPW
 // steps per wave of a round over all groups (kRoundFirst to kRoundFirstMax),
-// later ones half the steps before them (at most kRoundMaxSteps): a group
-// that stops past the first rounds has loaded at most half again the steps
-// it needs.
+// later ones as many steps as came before them (at most kRoundMaxSteps): a
+// group that stops past the first round has loaded at most twice the steps
+// it needs.  (On B8 x 8 KV heads at 32K context, int8, a first round of 96
+// steps then doubling took ART 100-101 us and never-firing ART 269 us,
+// against 110-111 and 262 us for 128 steps then half again, and 103 and
+// 295 us for 96 then half again.)
 constexpr int kRoundFirst = 64;          // steps of a round at least (multiple of 16)
 constexpr int kRoundFirstMax = 256;      // steps of the first rounds at most (multiple of 16)
-constexpr int kRoundFirstPW = 4;         // steps per wave the first rounds aim for
+constexpr int kRoundFirstPW = 3;         // steps per wave the first rounds aim for
 constexpr int kRoundMaxSteps = 512;      // steps of a round at most (multiple of 16)
 constexpr int kMaxRounds = 32;           // rounds of a call at most (else the engine does not apply)
 constexpr int kRoundWavesTarget = 2048;  // waves of a round over all groups (256 CUs x 8)
@@ -82,7 +85,7 @@ inline RoundPlan round_plan(int nt_max, int NG) {
             return rp;
         }
         const int a = rp.a[rp.R];
-        int c = (a / 2 + 15) / 16 * 16;
+        int c = (a + 15) / 16 * 16;
         if (c < (int)first) c = (int)first;
         if (c > kRoundMaxSteps) c = kRoundMaxSteps;
         const int b = a + c < nt_max ? a + c : nt_max;
@@ -99,7 +102,7 @@ inline RoundPlan round_plan(int nt_max, int NG) {
 // Engine AUTO takes the rounds for ART without the V skip where they were
 // measured faster than one CU per group: few groups (the team engine would
 // leave most CUs idle) of 256 to 1024 tiles and at most 4 query heads (on
-// B8 x 8 KV heads at 32K context, int8: 116-120 us against 131-133 us on the
+// B8 x 8 KV heads at 32K context, int8: 100-101 us against 122 us on the
 // team engine; with 128 groups, or rows of 2048 tiles, the team and pool
 // engines are faster).  Shapes only, so that the workspace layout can follow.
 constexpr int kRoundAutoGroups = 64;  // groups at most

@@ -39,7 +39,8 @@ def test_orders_every_engine(order):
     _run_and_check(c, f"config3 order {order} team", engine=ENGINE_TEAM)
     _run_and_check(c, f"config3 order {order} pool", engine=ENGINE_POOL)
     _run_and_check(c, f"config3 order {order} round", engine=ENGINE_ROUND)
-    c8 = ordered(A.config(3, small=True, ctx=8192), order, seed=12)  # several rounds
+    # 128 groups of 128 steps: two rounds
+    c8 = ordered(A.config(3, small=True, batch=16, ctx=8192), order, seed=12)
     _run_and_check(c8, f"config3 ctx 8192 order {order} round", engine=ENGINE_ROUND)
     _run_and_check(c, f"config3 order {order} work-sharing", max_workers=96)
     _run_and_check(c, f"config3 order {order} helpers", team_helpers=1)

@@ -316,7 +316,8 @@ def test_round_engine_parity(n):
 def test_round_engine_matches_team_engine(kv):
     # the same tile partials and the same block scan: identical stops; the
     # outputs merge the same partials in another order (rounding only)
-    c = A.config(3, small=True, ctx=8192, kv_dtype=kv)  # 128 steps: four rounds
+    # 128 groups of 128 steps: two rounds, steps [0, 64) and [64, 128)
+    c = A.config(3, small=True, batch=16, ctx=8192, kv_dtype=kv)
     dev = to_device(c)
     for kw in (dict(), dict(eps_scale=1e-30, eps_dir=1e-30), dict(patience=3), dict(eps_scale=1e-2, eps_dir=1e-3)):
         o1, u1 = run_gpu(c, dev, engine=ENGINE_TEAM, **kw)
@@ -332,7 +333,7 @@ def test_round_engine_ragged_empty_and_invalid_rows():
     c.ctx_lens[3] = 64 * 3 + 17                         # ragged tail
     c.ctx_lens[4] = c.block_table.shape[1] * 16 + 1     # longer than its table
     c.block_table[5, 7] = -3                            # an invalid block id inside the row
-    c.ctx_lens[6] = 64 * 100 + 5                        # a ragged tail in the fourth round
+    c.ctx_lens[6] = 64 * 100 + 5                        # a ragged tail in the second round (steps 96..127)
     out, used = run_gpu(c, engine=ENGINE_ROUND)
     assert (used[1] == 0).all() and (out[1] == 0).all()
     assert (used[4] == -1).all() and np.isnan(out[4]).all()
@@ -341,13 +342,13 @@ def test_round_engine_ragged_empty_and_invalid_rows():
 
 
 def _round_bounds(nt_max, ng):
-    # the rounds' first steps as the library plans them: about 4 steps per wave
-    # of 2048 in the first rounds (64 to 256 steps), then half the steps
-    # before, at most 512
-    first = min(max((4 * 2048 // ng + 15) // 16 * 16, 64), 256)
+    # the rounds' first steps as the library plans them: about 3 steps per wave
+    # of 2048 in the first rounds (64 to 256 steps), then as many steps as
+    # came before, at most 512
+    first = min(max((3 * 2048 // ng + 15) // 16 * 16, 64), 256)
     a = [0]
     while a[-1] < nt_max:
-        c = min(max((a[-1] // 2 + 15) // 16 * 16, first), 512)
+        c = min(max((a[-1] + 15) // 16 * 16, first), 512)
         a.append(min(a[-1] + c, nt_max))
     return a
 
